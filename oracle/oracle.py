@@ -1,0 +1,199 @@
+"""ctypes wrapper around the fp64 CPU oracle (orc.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product package.  Inputs are numpy
+arrays holding fp32 values or bf16 bit patterns (uint16); every result is
+float64 (or int32 for routing).  See orc.c for the step-by-step definition and
+its source: "LongCat-Flash Technical Report", section 2.1 Eq.(1) and section
+2.1.1 Eq.(2).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+F32, BF16 = 0, 1
+_i64, _i32, _f64 = C.c_int64, C.c_int, C.c_double
+_p = C.c_void_p
+
+
+def lib():
+    global _LIB
+    if _LIB is None:
+        path = os.path.join(HERE, "liborc.so")
+        if not os.path.exists(path):
+            from oracle import build as _b  # noqa: WPS433
+            _b.build()
+        L = C.CDLL(path)
+        L.orc_exp.restype = C.c_double
+        L.orc_exp.argtypes = [C.c_double]
+        L.orc_logits.argtypes = [_i64, _i64, _i64, _i32, _p, _p, _p]
+        L.orc_route.argtypes = [_i64, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p]
+        L.orc_forward.argtypes = [_i64, _i64, _i64, _i64, _i64, _i32, _f64, _p, _p, _p, _p,
+                                  _p, _p, _i64, _p, _p, _p]
+        L.orc_backward.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i32, _i32, _f64, _p, _p,
+                                   _p, _p, _p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _p]
+        L.orc_pid_update.argtypes = [_i64, _i64, _i64, _p, _i64, _f64, _f64, _p]
+        for f in ("orc_logits", "orc_route", "orc_forward", "orc_backward", "orc_pid_update"):
+            getattr(L, f).restype = C.c_int
+        _LIB = L
+    return _LIB
+
+
+def _dt(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle inputs are fp32 or bf16 bits (uint16), got {a.dtype}")
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a if dtype is None else a.astype(dtype, copy=False))
+    return a
+
+
+def exp(z: float) -> float:
+    """Routing-key exponential (Cody-Waite + degree-13 Taylor, see orc.c)."""
+    return lib().orc_exp(float(z))
+
+
+def logits(x: np.ndarray, wr: np.ndarray) -> np.ndarray:
+    """O1: l = x Wr^T in fp64.  x [T,d], wr [E,d]."""
+    x, wr = _c(x), _c(wr)
+    T, d = x.shape
+    E = wr.shape[0]
+    assert wr.shape[1] == d and _dt(x) == _dt(wr)
+    out = np.empty((T, E), np.float64)
+    rc = lib().orc_logits(T, d, E, _dt(x), _ptr(x), _ptr(wr), _ptr(out))
+    assert rc == 0
+    return out
+
+
+class Route:
+    """Result of O2..O5."""
+
+    def __init__(self, T, E, N, K):
+        self.keys = np.empty((T, E), np.float64)
+        self.topk_idx = np.empty((T, K), np.int32)
+        self.gates = np.empty((T, K), np.float64)
+        self.counts = np.empty(E, np.int32)
+        self.offsets = np.empty(N + 1, np.int32)
+        self.perm = np.full(T * K, -1, np.int32)
+        self.inv = np.empty(T * K, np.int32)
+
+    @property
+    def p_real(self) -> int:
+        return int(self.offsets[-1])
+
+
+def route(lg: np.ndarray, bias: np.ndarray, N: int, K: int, gate_norm: int = 1,
+          want_keys: bool = True) -> Route:
+    """O2..O5 from logits (any float array, widened exactly to fp64)."""
+    lg = _c(lg, np.float64)
+    bias = _c(bias, np.float32)
+    T, E = lg.shape
+    assert bias.shape == (E,)
+    r = Route(T, E, N, K)
+    if not want_keys:
+        r.keys = None
+    rc = lib().orc_route(T, E, N, K, int(gate_norm), _ptr(lg), _ptr(bias), _ptr(r.keys),
+                         _ptr(r.topk_idx), _ptr(r.gates), _ptr(r.counts), _ptr(r.offsets),
+                         _ptr(r.perm), _ptr(r.inv))
+    assert rc == 0
+    r.perm = r.perm[: r.p_real].copy()
+    return r
+
+
+def _table(ws, N):
+    """Per-expert pointer table from a list/array/dict of expert weight blocks."""
+    arr = (C.c_void_p * N)()
+    keep = []
+    for e in range(N):
+        w = ws.get(e) if isinstance(ws, dict) else ws[e]
+        if w is None:
+            arr[e] = None
+            continue
+        w = np.ascontiguousarray(w)
+        keep.append(w)
+        arr[e] = w.ctypes.data
+    return arr, keep
+
+
+def forward(x, wg, wu, wd, topk_idx, gates, N, out_scale=1.0, toks=None, want_y=False):
+    """O6+O7 for tokens `toks` (all when None).  wg/wu/wd: [N,...] arrays or
+    per-expert dicts {e: block}; blocks must share x's storage dtype."""
+    x = _c(x)
+    T, d = x.shape
+    K = topk_idx.shape[1]
+    e0 = next(iter(wg.values())) if isinstance(wg, dict) else wg[0]
+    I = e0.shape[0]
+    tg, kg = _table(wg, N)
+    tu, ku = _table(wu, N)
+    td, kd = _table(wd, N)
+    ti = _c(topk_idx, np.int32)
+    gg = _c(gates, np.float64)
+    tk = None if toks is None else _c(np.asarray(toks), np.int64)
+    n = T if tk is None else len(tk)
+    out = np.empty((n, d), np.float64)
+    y = np.empty((n, K, d), np.float64) if want_y else None
+    rc = lib().orc_forward(T, d, N, I, K, _dt(x), float(out_scale), _ptr(x), tg, tu, td,
+                           _ptr(ti), _ptr(gg), n, _ptr(tk), _ptr(out), _ptr(y))
+    assert rc == 0, "oracle forward failed (missing expert weights or bad token)"
+    del kg, ku, kd
+    return (out, y) if want_y else out
+
+
+def backward(x, wr, wg, wu, wd, lg, topk_idx, gates, dY, N, Z, gate_norm=1, out_scale=1.0,
+             toks=None, want_experts=None, want_dwr=True):
+    """O9.  Returns dict with dx [n,d], dwr [E,d] (or None), dwg/dwu/dwd as
+    {e: array} for experts in want_experts (all N when None)."""
+    x, wr, dY = _c(x), _c(wr), _c(dY)
+    T, d = x.shape
+    E = N + Z
+    K = topk_idx.shape[1]
+    e0 = next(iter(wg.values())) if isinstance(wg, dict) else wg[0]
+    I = e0.shape[0]
+    tg, kg = _table(wg, N)
+    tu, ku = _table(wu, N)
+    td, kd = _table(wd, N)
+    lg = _c(lg, np.float64)
+    ti = _c(topk_idx, np.int32)
+    gg = _c(gates, np.float64)
+    tk = None if toks is None else _c(np.asarray(toks), np.int64)
+    n = T if tk is None else len(tk)
+    dx = np.empty((n, d), np.float64)
+    dwr = np.zeros((E, d), np.float64) if want_dwr else None
+    wanted = range(N) if want_experts is None else want_experts
+    dwg = {e: np.zeros((I, d), np.float64) for e in wanted}
+    dwu = {e: np.zeros((I, d), np.float64) for e in wanted}
+    dwd = {e: np.zeros((d, I), np.float64) for e in wanted}
+    pg, qg = _table(dwg, N)
+    pu, qu = _table(dwu, N)
+    pd, qd = _table(dwd, N)
+    rc = lib().orc_backward(T, d, N, Z, I, K, _dt(x), int(gate_norm), float(out_scale), _ptr(x),
+                            _ptr(wr), tg, tu, td, _ptr(lg), _ptr(ti), _ptr(gg), _ptr(dY), n,
+                            _ptr(tk), _ptr(dx), _ptr(dwr), pg, pu, pd)
+    assert rc == 0, f"oracle backward failed rc={rc}"
+    del kg, ku, kd, qg, qu, qd
+    return {"dx": dx, "dwr": dwr, "dwg": dwg, "dwu": dwu, "dwd": dwd}
+
+
+def pid_update(counts, T_all, bias, N, Z, K, mu, K_e) -> np.ndarray:
+    """O8 (Eq.(2)); returns the updated fp32 bias (input left untouched)."""
+    c = _c(counts, np.int32)
+    b = np.array(bias, dtype=np.float32, copy=True)
+    rc = lib().orc_pid_update(N, Z, K, _ptr(c), int(T_all), float(mu), float(K_e), _ptr(b))
+    assert rc == 0
+    return b

@@ -1,0 +1,478 @@
+/*
+ * orc.c -- fp64 CPU oracle for the MoE layer with zero-computation experts.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header or constant table with the
+ * HIP library; the two sides agree only through the written specification of
+ * each step below.
+ *
+ * Source: "LongCat-Flash Technical Report" (Chinese translation on
+ * 171host.com), section 2.1 "Zero-computation experts", Eq.(1) and the
+ * expert definition E_i that follows it, and section 2.1.1 "Computation
+ * budget control", Eq.(2).  The FFN expert form (SwiGLU without biases) and
+ * the linear softmax router are readings of points the page leaves open.
+ *
+ * Every floating-point step runs in binary64 on the exact values of the
+ * (fp32 or bf16) inputs, in plain loop order.  The only place where the
+ * oracle follows an arithmetic recipe rather than "whatever libm does" is
+ * the routing key (orc_exp + 64-way partial sums), because a float value
+ * there decides an integer (the top-K set) and both sides must take that
+ * decision with the same binary64 operations.  Build with
+ * -ffp-contract=off so that no multiply-add is fused behind our back.
+ *
+ * Parity pins: every function here is pinned by the CPU tests (brute-force
+ * top-K, closed forms, library special cases, finite differences); none is
+ * "parity unpinned".
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+/* Exact widening of one stored input element to binary64. */
+static double ld(const void* base, int dt, int64_t i) {
+  if (dt == ORC_F32) return (double)((const float*)base)[i];
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;
+  float f;
+  memcpy(&f, &bits, 4);
+  return (double)f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Routing-key exponential.
+ *
+ * Cody-Waite argument reduction (W. J. Cody and W. Waite, "Software Manual
+ * for the Elementary Functions", 1980): z = k ln2 + r with k = rint(z/ln2)
+ * and ln2 split into a 32-significant-bit head and a binary64 tail, then the
+ * Taylor series of e^r to degree 13 by Horner's rule with fused
+ * multiply-adds, then scaling by 2^k.  Inputs below -700 return 0 (the
+ * probability is then below 1e-304 and only matters through exact ties).
+ *   head = 2977044472 / 2^32                (ln 2 rounded to 32 bits)
+ *   tail = ln 2 - head, rounded to binary64
+ *   inv  = 1/ln 2 rounded to binary64
+ */
+static const double ORC_LN2_HEAD = 0x1.62e42ff000000p-1;
+static const double ORC_LN2_TAIL = -0x1.718432a1b0e26p-35;
+static const double ORC_INV_LN2 = 0x1.71547652b82fep+0;
+
+double orc_exp(double z) {
+  if (z < -700.0) return 0.0;
+  double k = rint(z * ORC_INV_LN2);
+  double r = (z - k * ORC_LN2_HEAD) - k * ORC_LN2_TAIL;
+  /* 1/n! for n = 13 .. 0, each the correctly rounded quotient. */
+  static const double inv_fact[14] = {
+      1.0 / 6227020800.0, 1.0 / 479001600.0, 1.0 / 39916800.0,
+      1.0 / 3628800.0,    1.0 / 362880.0,    1.0 / 40320.0,
+      1.0 / 5040.0,       1.0 / 720.0,       1.0 / 120.0,
+      1.0 / 24.0,         1.0 / 6.0,         1.0 / 2.0,
+      1.0,                1.0};
+  double p = inv_fact[0];
+  for (int n = 1; n < 14; ++n) p = fma(p, r, inv_fact[n]);
+  return ldexp(p, (int)k);
+}
+
+/* Sum of e[0..E) in the fixed order used for the routing denominator:
+ * 64 partial sums (partial lambda takes indices j with j mod 64 == lambda,
+ * ascending, starting from 0.0), then six pairwise rounds in which every
+ * partial becomes itself plus its partner at xor distance 32, 16, 8, 4, 2, 1.
+ * All partials end equal; return partial 0. */
+static double orc_sum64(const double* e, int64_t E) {
+  double part[64], nxt[64];
+  for (int l = 0; l < 64; ++l) part[l] = 0.0;
+  for (int64_t j = 0; j < E; ++j) part[j % 64] = part[j % 64] + e[j];
+  for (int o = 32; o >= 1; o >>= 1) {
+    for (int l = 0; l < 64; ++l) nxt[l] = part[l] + part[l ^ o];
+    for (int l = 0; l < 64; ++l) part[l] = nxt[l];
+  }
+  return part[0];
+}
+
+/* ------------------------------------------------------------------------ */
+/* O1 -- router logits l[t][j] = sum_k x[t][k] * Wr[j][k]  (k ascending).
+ * The page calls R a softmax router and prints no formula for its scores;
+ * the plain reading is a bias-free linear map of x_t, one row per expert. */
+int orc_logits(int64_t T, int64_t d, int64_t E, int dt, const void* x,
+               const void* wr, double* logits) {
+  if (T < 0 || d <= 0 || E <= 0 || !x || !wr || !logits) return 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t j = 0; j < E; ++j) {
+      double s = 0.0;
+      for (int64_t k = 0; k < d; ++k) s += ld(x, dt, t * d + k) * ld(wr, dt, j * d + k);
+      logits[t * E + j] = s;
+    }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O2..O5 -- Eq.(1): keys R_i + b_i, TopK, gates; then the per-expert token
+ * counts T_i of Eq.(2) and the canonical dispatch order.
+ *
+ *  keys:   m = max_j l_j; e_j = orc_exp(l_j - m); S = orc_sum64(e);
+ *          p_j = e_j / S; key_j = p_j + (double)b_j.
+ *  top-K:  K rounds; round r takes the unselected j with the largest key,
+ *          equal keys going to the smaller j.  Slot r is the r-th pick.
+ *  gates:  gate_norm = 1: g_r = e_{s_r} / (sum_{q<K} e_{s_q}, q ascending)
+ *          (softmax restricted to the picks: the selected R_i rescaled to
+ *          sum to one); gate_norm = 0: g_r = p_{s_r} (Eq.(1) as printed).
+ *  counts: counts[j] = number of tokens whose picks include j (all E).
+ *  offsets[e] = sum of counts over FFN experts e' < e, e = 0..N.
+ *  perm:   for e = 0..N-1, for t ascending with e among its picks, append
+ *          the flat slot t*K + r.  (expert, token) pairs are unique, so this
+ *          order is the only stable one.
+ *  inv:    inv[t*K + r] = position of that slot in perm, or -1 when the
+ *          pick is a zero-computation expert (j >= N).
+ * Any output pointer except topk_idx may be NULL. */
+int orc_route(int64_t T, int64_t E, int64_t N, int64_t K, int gate_norm,
+              const double* logits, const float* bias, double* keys_out,
+              int32_t* topk_idx, double* gates, int32_t* counts,
+              int32_t* offsets, int32_t* perm, int32_t* inv) {
+  if (T < 0 || E <= 0 || N < 0 || N > E || K < 1 || K > E || !logits || !bias || !topk_idx)
+    return 1;
+#pragma omp parallel
+  {
+    double* e = (double*)malloc(sizeof(double) * (size_t)E);
+    double* key = (double*)malloc(sizeof(double) * (size_t)E);
+    unsigned char* taken = (unsigned char*)malloc((size_t)E);
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      const double* l = logits + t * E;
+      double m = l[0];
+      for (int64_t j = 1; j < E; ++j)
+        if (l[j] > m) m = l[j];
+      for (int64_t j = 0; j < E; ++j) e[j] = orc_exp(l[j] - m);
+      double S = orc_sum64(e, E);
+      for (int64_t j = 0; j < E; ++j) {
+        key[j] = e[j] / S + (double)bias[j];
+        taken[j] = 0;
+      }
+      if (keys_out)
+        for (int64_t j = 0; j < E; ++j) keys_out[t * E + j] = key[j];
+      for (int64_t r = 0; r < K; ++r) {
+        int64_t best = -1;
+        for (int64_t j = 0; j < E; ++j) {
+          if (taken[j]) continue;
+          if (best < 0 || key[j] > key[best]) best = j;
+        }
+        taken[best] = 1;
+        topk_idx[t * K + r] = (int32_t)best;
+      }
+      if (gates) {
+        double den = 0.0;
+        for (int64_t r = 0; r < K; ++r) den = den + e[topk_idx[t * K + r]];
+        for (int64_t r = 0; r < K; ++r) {
+          double er = e[topk_idx[t * K + r]];
+          gates[t * K + r] = gate_norm ? er / den : er / S;
+        }
+      }
+    }
+    free(e);
+    free(key);
+    free(taken);
+  }
+  if (counts || offsets || perm || inv) {
+    int32_t* cnt = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+    for (int64_t i = 0; i < T * K; ++i) cnt[topk_idx[i]] += 1;
+    if (counts) memcpy(counts, cnt, sizeof(int32_t) * (size_t)E);
+    int32_t* off = (int32_t*)malloc(sizeof(int32_t) * (size_t)(N + 1));
+    off[0] = 0;
+    for (int64_t j = 0; j < N; ++j) off[j + 1] = off[j] + cnt[j];
+    if (offsets) memcpy(offsets, off, sizeof(int32_t) * (size_t)(N + 1));
+    if (inv)
+      for (int64_t i = 0; i < T * K; ++i) inv[i] = -1;
+    if (perm || inv) {
+      int32_t* cur = (int32_t*)malloc(sizeof(int32_t) * (size_t)(N + 1));
+      memcpy(cur, off, sizeof(int32_t) * (size_t)(N + 1));
+      /* walking tokens in ascending order and appending to each expert's
+       * segment yields exactly the (expert, token) order */
+      for (int64_t t = 0; t < T; ++t)
+        for (int64_t r = 0; r < K; ++r) {
+          int32_t j = topk_idx[t * K + r];
+          if (j >= N) continue;
+          int32_t pos = cur[j]++;
+          if (perm) perm[pos] = (int32_t)(t * K + r);
+          if (inv) inv[t * K + r] = pos;
+        }
+      free(cur);
+    }
+    free(off);
+    free(cnt);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O6 -- one FFN expert on one token row (SwiGLU, no biases):
+ *   a = Wg x,  u = Wu x,  h = silu(a) * u,  y = Wd h,  silu(z) = z/(1+e^-z).
+ * Wg, Wu are [I][d] and Wd is [d][I], row-major ("out x in"). */
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+static void ffn_row(int64_t d, int64_t I, int dt, const void* x, int64_t xoff,
+                    const void* wg, const void* wu, const void* wd, double* a,
+                    double* u, double* h, double* y) {
+  for (int64_t i = 0; i < I; ++i) {
+    double sa = 0.0, su = 0.0;
+    for (int64_t k = 0; k < d; ++k) {
+      double xv = ld(x, dt, xoff + k);
+      sa += ld(wg, dt, i * d + k) * xv;
+      su += ld(wu, dt, i * d + k) * xv;
+    }
+    a[i] = sa;
+    u[i] = su;
+    h[i] = silu(sa) * su;
+  }
+  for (int64_t n = 0; n < d; ++n) {
+    double s = 0.0;
+    for (int64_t i = 0; i < I; ++i) s += ld(wd, dt, n * I + i) * h[i];
+    y[n] = s;
+  }
+}
+
+/* O6 + O7 -- layer output for the tokens toks[0..n_tok) (all tokens when
+ * toks is NULL, n_tok = T):
+ *   out_t = out_scale * ( (sum of gates on zero-computation picks) * x_t
+ *                         + sum over FFN picks r ascending of g_r * FFN(x_t) )
+ * which is sum_i g_i E_i(x_t) with E_i(x_t) = x_t for N < i <= N+Z.
+ * wg/wu/wd are per-expert pointer tables of length N; an entry may be NULL
+ * when no listed token picks that expert.  y_slot (nullable) receives the
+ * unscaled expert output per slot, [n_tok][K][d], zero on identity slots. */
+int orc_forward(int64_t T, int64_t d, int64_t N, int64_t I, int64_t K, int dt,
+                double out_scale, const void* x, const void* const* wg,
+                const void* const* wu, const void* const* wd,
+                const int32_t* topk_idx, const double* gates, int64_t n_tok,
+                const int64_t* toks, double* out, double* y_slot) {
+  if (!x || !wg || !wu || !wd || !topk_idx || !gates || !out) return 1;
+  if (!toks) n_tok = T;
+  int bad = 0;
+#pragma omp parallel
+  {
+    double* a = (double*)malloc(sizeof(double) * (size_t)I);
+    double* u = (double*)malloc(sizeof(double) * (size_t)I);
+    double* h = (double*)malloc(sizeof(double) * (size_t)I);
+    double* y = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t q = 0; q < n_tok; ++q) {
+      int64_t t = toks ? toks[q] : q;
+      if (t < 0 || t >= T) { bad = 1; continue; }
+      double* o = out + q * d;
+      double c = 0.0;
+      for (int64_t r = 0; r < K; ++r)
+        if (topk_idx[t * K + r] >= N) c += gates[t * K + r];
+      for (int64_t n = 0; n < d; ++n) o[n] = c * ld(x, dt, t * d + n);
+      for (int64_t r = 0; r < K; ++r) {
+        int64_t e = topk_idx[t * K + r];
+        double* ys = y_slot ? y_slot + (q * K + r) * d : NULL;
+        if (e >= N) {
+          if (ys) memset(ys, 0, sizeof(double) * (size_t)d);
+          continue;
+        }
+        if (!wg[e] || !wu[e] || !wd[e]) { bad = 1; continue; }
+        ffn_row(d, I, dt, x, t * d, wg[e], wu[e], wd[e], a, u, h, y);
+        for (int64_t n = 0; n < d; ++n) o[n] += gates[t * K + r] * y[n];
+        if (ys) memcpy(ys, y, sizeof(double) * (size_t)d);
+      }
+      for (int64_t n = 0; n < d; ++n) o[n] *= out_scale;
+    }
+    free(a);
+    free(u);
+    free(h);
+    free(y);
+  }
+  return bad ? 1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O9 -- backward of O1..O7 with the routing held fixed (the top-K set is
+ * piecewise constant; the bias is decoupled from the objective, so it gets
+ * no gradient).  Given dY for the tokens toks[0..n_tok):
+ *   dYs = out_scale * dY_t
+ *   real pick r, e = s_r:  dg_r = <dYs, y_r>;  dy = g_r dYs;
+ *        dh = Wd^T dy;  da = dh*u*silu'(a);  du = dh*silu(a);
+ *        dx += Wg^T da + Wu^T du;  dWd[e] += dy h^T;
+ *        dWg[e] += da x^T;  dWu[e] += du x^T
+ *   identity pick r:       dg_r = <dYs, x_t>;  dx += g_r dYs
+ *   router, gate_norm = 1: dl_j = g_j (dg_j - sum_S g dg) on the picks, 0 off
+ *          gate_norm = 0:  dl_j = p_j (dg~_j - sum_S p dg) for every j, with
+ *                          dg~ the pick's dg or 0
+ *        (p = softmax of the logits, from orc_exp and orc_sum64 as in O2)
+ *   dWr += dl x_t^T;  dx += Wr^T dl
+ * silu'(z) = s (1 + z (1 - s)), s = 1/(1+e^-z).
+ * Weight gradients are accumulated (+=) over the listed tokens in ascending
+ * list order; expert tables dwg/dwu/dwd may hold NULL for experts whose
+ * gradient is not wanted; dwr may be NULL.  dx is [n_tok][d], overwritten.
+ * gates must be the gates of the same gate_norm mode. */
+int orc_backward(int64_t T, int64_t d, int64_t N, int64_t Z, int64_t I,
+                 int64_t K, int dt, int gate_norm, double out_scale,
+                 const void* x, const void* wr, const void* const* wg,
+                 const void* const* wu, const void* const* wd,
+                 const double* logits, const int32_t* topk_idx,
+                 const double* gates, const void* dY, int64_t n_tok,
+                 const int64_t* toks, double* dx, double* dwr,
+                 double* const* dwg, double* const* dwu, double* const* dwd) {
+  const int64_t E = N + Z;
+  if (!x || !wr || !wg || !wu || !wd || !logits || !topk_idx || !gates || !dY || !dx)
+    return 1;
+  if (!toks) n_tok = T;
+  for (int64_t q = 0; q < n_tok; ++q) {
+    int64_t t = toks ? toks[q] : q;
+    if (t < 0 || t >= T) return 1;
+    for (int64_t r = 0; r < K; ++r) {
+      int64_t e = topk_idx[t * K + r];
+      if (e < N && (!wg[e] || !wu[e] || !wd[e])) return 1;
+    }
+  }
+  /* per-slot saved quantities, needed again for the weight gradients */
+  const int64_t S = n_tok * K;
+  double* A = (double*)calloc((size_t)(S * I), sizeof(double));
+  double* U = (double*)calloc((size_t)(S * I), sizeof(double));
+  double* H = (double*)calloc((size_t)(S * I), sizeof(double));
+  double* DA = (double*)calloc((size_t)(S * I), sizeof(double));
+  double* DU = (double*)calloc((size_t)(S * I), sizeof(double));
+  double* DY = (double*)calloc((size_t)(S * d), sizeof(double));
+  double* DL = (double*)calloc((size_t)(n_tok * E), sizeof(double));
+  if (!A || !U || !H || !DA || !DU || !DY || !DL) {
+    free(A); free(U); free(H); free(DA); free(DU); free(DY); free(DL);
+    return 2;
+  }
+#pragma omp parallel
+  {
+    double* y = (double*)malloc(sizeof(double) * (size_t)d);
+    double* dys = (double*)malloc(sizeof(double) * (size_t)d);
+    double* dh = (double*)malloc(sizeof(double) * (size_t)I);
+    double* dg = (double*)malloc(sizeof(double) * (size_t)K);
+    double* ex = (double*)malloc(sizeof(double) * (size_t)E);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t q = 0; q < n_tok; ++q) {
+      int64_t t = toks ? toks[q] : q;
+      double* dxo = dx + q * d;
+      for (int64_t n = 0; n < d; ++n) {
+        dys[n] = out_scale * ld(dY, dt, t * d + n);
+        dxo[n] = 0.0;
+      }
+      for (int64_t r = 0; r < K; ++r) {
+        int64_t e = topk_idx[t * K + r];
+        double g = gates[t * K + r];
+        int64_t sl = q * K + r;
+        if (e >= N) {
+          double s = 0.0;
+          for (int64_t n = 0; n < d; ++n) s += dys[n] * ld(x, dt, t * d + n);
+          dg[r] = s;
+          for (int64_t n = 0; n < d; ++n) dxo[n] += g * dys[n];
+          continue;
+        }
+        double *a = A + sl * I, *u = U + sl * I, *h = H + sl * I;
+        ffn_row(d, I, dt, x, t * d, wg[e], wu[e], wd[e], a, u, h, y);
+        double s = 0.0;
+        for (int64_t n = 0; n < d; ++n) s += dys[n] * y[n];
+        dg[r] = s;
+        double* dyv = DY + sl * d;
+        for (int64_t n = 0; n < d; ++n) dyv[n] = g * dys[n];
+        for (int64_t i = 0; i < I; ++i) {
+          double acc = 0.0;
+          for (int64_t n = 0; n < d; ++n) acc += ld(wd[e], dt, n * I + i) * dyv[n];
+          dh[i] = acc;
+        }
+        double *da = DA + sl * I, *du = DU + sl * I;
+        for (int64_t i = 0; i < I; ++i) {
+          double sg = 1.0 / (1.0 + exp(-a[i]));
+          da[i] = dh[i] * u[i] * (sg * (1.0 + a[i] * (1.0 - sg)));
+          du[i] = dh[i] * (a[i] * sg);
+        }
+        for (int64_t k = 0; k < d; ++k) {
+          double acc = 0.0;
+          for (int64_t i = 0; i < I; ++i)
+            acc += ld(wg[e], dt, i * d + k) * da[i] + ld(wu[e], dt, i * d + k) * du[i];
+          dxo[k] += acc;
+        }
+      }
+      /* router: softmax Jacobian restricted as the gate mode dictates */
+      double* dl = DL + q * E;
+      if (gate_norm) {
+        double sgd = 0.0;
+        for (int64_t r = 0; r < K; ++r) sgd += gates[t * K + r] * dg[r];
+        for (int64_t r = 0; r < K; ++r) {
+          int64_t j = topk_idx[t * K + r];
+          dl[j] = gates[t * K + r] * (dg[r] - sgd);
+        }
+      } else {
+        const double* l = logits + t * E;
+        double m = l[0];
+        for (int64_t j = 1; j < E; ++j)
+          if (l[j] > m) m = l[j];
+        for (int64_t j = 0; j < E; ++j) ex[j] = orc_exp(l[j] - m);
+        double Ssum = orc_sum64(ex, E);
+        double spd = 0.0;
+        for (int64_t r = 0; r < K; ++r) spd += gates[t * K + r] * dg[r];
+        for (int64_t j = 0; j < E; ++j) dl[j] = -(ex[j] / Ssum) * spd;
+        for (int64_t r = 0; r < K; ++r) {
+          int64_t j = topk_idx[t * K + r];
+          dl[j] += (ex[j] / Ssum) * dg[r];
+        }
+      }
+      for (int64_t k = 0; k < d; ++k) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < E; ++j) acc += dl[j] * ld(wr, dt, j * d + k);
+        dxo[k] += acc;
+      }
+    }
+    free(y); free(dys); free(dh); free(dg); free(ex);
+  }
+  /* weight gradients: one expert (or router row) per thread, tokens in list
+   * order, so every sum has a fixed order */
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t e = 0; e < N; ++e) {
+    if (!dwg[e] && !dwu[e] && !dwd[e]) continue;
+    for (int64_t q = 0; q < n_tok; ++q) {
+      int64_t t = toks ? toks[q] : q;
+      for (int64_t r = 0; r < K; ++r) {
+        if (topk_idx[t * K + r] != e) continue;
+        int64_t sl = q * K + r;
+        if (dwd[e])
+          for (int64_t n = 0; n < d; ++n)
+            for (int64_t i = 0; i < I; ++i) dwd[e][n * I + i] += DY[sl * d + n] * H[sl * I + i];
+        for (int64_t i = 0; i < I; ++i)
+          for (int64_t k = 0; k < d; ++k) {
+            double xv = ld(x, dt, t * d + k);
+            if (dwg[e]) dwg[e][i * d + k] += DA[sl * I + i] * xv;
+            if (dwu[e]) dwu[e][i * d + k] += DU[sl * I + i] * xv;
+          }
+      }
+    }
+  }
+  if (dwr) {
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < E; ++j)
+      for (int64_t q = 0; q < n_tok; ++q) {
+        int64_t t = toks ? toks[q] : q;
+        double v = DL[q * E + j];
+        if (v == 0.0) continue;
+        for (int64_t k = 0; k < d; ++k) dwr[j * d + k] += v * ld(x, dt, t * d + k);
+      }
+  }
+  free(A); free(U); free(H); free(DA); free(DU); free(DY); free(DL);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O8 -- Eq.(2), the per-step bias increment, for FFN experts i < N:
+ *   b_i <- fp32( b_i + mu * ( K_e/(K*N) - T_i/(K*T_all) ) )
+ * in binary64 with exactly these operations:
+ *   tgt = K_e / ((double)K * N);  obs = (double)T_i / ((double)K * T_all);
+ *   b_i = (float)((double)b_i + mu * (tgt - obs)).
+ * Zero-computation experts (i >= N) keep their bias. */
+int orc_pid_update(int64_t N, int64_t Z, int64_t K, const int32_t* counts,
+                   int64_t T_all, double mu, double K_e, float* bias) {
+  (void)Z;
+  if (N < 0 || K < 1 || T_all < 1 || !counts || !bias) return 1;
+  double tgt = K_e / ((double)K * (double)N);
+  for (int64_t i = 0; i < N; ++i) {
+    double obs = (double)counts[i] / ((double)K * (double)T_all);
+    bias[i] = (float)((double)bias[i] + mu * (tgt - obs));
+  }
+  return 0;
+}
