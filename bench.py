@@ -1,0 +1,270 @@
+"""Benchmark of the MoE layer with zero-computation experts on one MI355X.
+
+Headline: the LongCat-Flash-shaped prefill layer (T=16384 tokens, d=6144,
+512 SwiGLU experts with inner size 2048 + 256 zero-computation experts,
+top-12, Zipf-skewed expert bias), forward pass; value = layer tokens/s with
+every input already in HBM.  The same JSON line also carries the decode-size
+layer (T=256, same shapes, memory-bound) and the training step (T=8192,
+d=2048, 128+64 experts, top-8: forward, backward, bias update), each timed
+the same way, and the fp64 CPU oracle timed on a bounded sample of the
+headline workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from moe_layer_zero_amd import synth, zcmoe  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def desc_of(sh, gate_norm=1):
+    return zcmoe.LayerDesc(sh.T, sh.d, sh.N, sh.Z, sh.I, sh.K, sh.torch_dtype, gate_norm)
+
+
+def timed(fn, steps, warmup):
+    """Run fn() warmup times, then time exactly `steps` calls with events on
+    the current stream; kernel phases are read from the library's events over
+    the timed region.  Returns (ms per step, {phase: (ms per launch, launches per step)})."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    zcmoe.zc_moe_profile(True)
+    zcmoe.zc_moe_profile_read()  # discard warm-up records
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    prof = zcmoe.zc_moe_profile_read()
+    zcmoe.zc_moe_profile(False)
+    phases = {k: (tot / n, n / steps) for k, (tot, n) in prof.items()}
+    return a.elapsed_time(b) / steps, phases
+
+
+def layer_forward_bench(sh, steps, warmup):
+    log(f"[bench] generating {sh.name} layer on the GPU")
+    Lg = synth.make_layer(sh, "cuda")
+    desc = desc_of(sh)
+    route = zcmoe.RouteBuffers(desc)
+    out = torch.empty((sh.T, sh.d), dtype=sh.torch_dtype, device="cuda")
+    ws = zcmoe.workspace(desc, zcmoe.ZC_OP_FORWARD)
+
+    def step():
+        zcmoe.zc_moe_forward(desc, Lg["x"], Lg["wr"], Lg["bias"], Lg["wg"], Lg["wu"], Lg["wd"],
+                             out, route, None, ws)
+
+    ms, phases = timed(step, steps, warmup)
+    counts = route.counts.cpu().numpy()
+    p_real = int(route.offsets[-1].item())
+    touched = int((counts[: sh.N] > 0).sum())
+    return Lg, ms, phases, p_real, touched, counts
+
+
+def prefill(steps, warmup):
+    sh = synth.CONFIGS["prefill_bf16"]
+    Lg, ms, ph, p_real, touched, counts = layer_forward_bench(sh, steps, warmup)
+    d, I = sh.d, sh.I
+    flops_gu = 4.0 * d * I * p_real          # gate and up projections of every FFN pick
+    flops_dn = 2.0 * d * I * p_real
+    gu_ms = ph["gate_up_gemm"][0]
+    dn_ms = ph["down_gemm"][0]
+    res = {
+        "ms_per_step": ms,
+        "tokens_per_s": sh.T / (ms / 1e3),
+        "p_real": p_real,
+        "zero_pick_fraction": 1.0 - p_real / (sh.T * sh.K),
+        "tokens_per_ffn_expert_max_over_mean": float(counts[: sh.N].max() / counts[: sh.N].mean()),
+        "kernels_ms": {k: round(v[0], 4) for k, v in ph.items()},
+        "gate_up_tflops": flops_gu / (gu_ms * 1e-3) / 1e12,
+        "down_tflops": flops_dn / (dn_ms * 1e-3) / 1e12,
+        "expert_gemms_tflops": (flops_gu + flops_dn) / ((gu_ms + dn_ms) * 1e-3) / 1e12,
+    }
+    roof = {"bound": "mfma", "kernel": "gate_up_gemm",
+            "achieved": round(res["gate_up_tflops"], 2), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(res["gate_up_tflops"] / BF16_PEAK_TFLOPS, 4),
+            "traffic": None}
+    del Lg
+    torch.cuda.empty_cache()
+    return sh, res, roof
+
+
+def decode(steps, warmup):
+    sh = synth.CONFIGS["decode_bf16"]
+    Lg, ms, ph, p_real, touched, counts = layer_forward_bench(sh, steps, warmup)
+    d, I, E = sh.d, sh.I, sh.E
+    w_bytes = 2.0 * 3 * d * I * touched       # every touched expert's weights once (bf16)
+    layer_bytes = w_bytes + 2.0 * d * E + 2 * 2.0 * sh.T * d + 4.0 * E + 8.0 * sh.T * sh.K
+    gu_ms = ph["gate_up_gemm"][0]
+    res = {
+        "ms_per_step": ms,
+        "tokens_per_s": sh.T / (ms / 1e3),
+        "p_real": p_real,
+        "touched_experts": touched,
+        "layer_gbs": layer_bytes / (ms * 1e-3) / 1e9,
+        "layer_hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "gate_up_gbs": (2.0 * 2 * d * I * touched) / (gu_ms * 1e-3) / 1e9,
+        "kernels_ms": {k: round(v[0], 4) for k, v in ph.items()},
+    }
+    del Lg
+    torch.cuda.empty_cache()
+    return res
+
+
+def train(steps, warmup):
+    sh = synth.CONFIGS["train_bf16"]
+    log("[bench] generating training layer on the GPU")
+    L = synth.make_layer(sh, "cuda")
+    desc = desc_of(sh)
+    route = zcmoe.RouteBuffers(desc)
+    out = torch.empty((sh.T, sh.d), dtype=sh.torch_dtype, device="cuda")
+    saved = zcmoe.saved_buffer(desc)
+    wsf = zcmoe.workspace(desc, zcmoe.ZC_OP_FORWARD)
+    wsb = zcmoe.workspace(desc, zcmoe.ZC_OP_BACKWARD)
+    grads = {k: torch.empty_like(L[w]) for k, w in (("dx", "x"), ("dwr", "wr"), ("dwg", "wg"),
+                                                    ("dwu", "wu"), ("dwd", "wd"))}
+    n = warmup + steps
+    xs = [synth.step_x(sh, s, "cuda") for s in range(n)]
+    dys = [synth.step_dy(sh, s, "cuda") for s in range(n)]
+    bias = torch.zeros(sh.E, device="cuda")
+    it = [0]
+
+    def step():
+        s = it[0] % n
+        it[0] += 1
+        x = xs[s]
+        zcmoe.zc_moe_forward(desc, x, L["wr"], bias, L["wg"], L["wu"], L["wd"], out, route, saved,
+                             wsf)
+        zcmoe.zc_moe_backward(desc, x, L["wr"], L["wg"], L["wu"], L["wd"], route, saved, dys[s],
+                              grads["dx"], grads["dwr"], grads["dwg"], grads["dwu"], grads["dwd"],
+                              wsb)
+        zcmoe.zc_moe_pid_update(sh.N, sh.Z, sh.K, route.counts, sh.T, synth.TRAIN_MU,
+                                synth.TRAIN_K_E, bias)
+
+    ms, ph = timed(step, steps, warmup)
+    p_real = int(route.offsets[-1].item())
+    flops = 18.0 * sh.d * sh.I * p_real + 6.0 * sh.T * sh.d * sh.E
+    res = {"ms_per_step": ms, "tokens_per_s": sh.T / (ms / 1e3), "p_real_last": p_real,
+           "mean_real_experts_last": p_real / sh.T, "tflops": flops / (ms * 1e-3) / 1e12,
+           "kernels_ms": {k: round(v[0], 4) for k, v in ph.items()}}
+    del L, xs, dys, saved
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(budget_experts=160, max_tokens=64):
+    """The fp64 oracle on a bounded sample of the prefill workload: router
+    scores, routing and layer output for a few tokens (only their experts'
+    weights are copied to the host).  Returns tokens/s of that sample."""
+    from oracle import oracle
+
+    sh = synth.CONFIGS["prefill_bf16"]
+    log("[bench] cpu baseline: regenerating the prefill layer")
+    Lg = synth.make_layer(sh, "cuda")
+    g = torch.Generator().manual_seed(2024)
+    order = torch.randperm(sh.T, generator=g).numpy()
+    xh_all = synth.to_np(Lg["x"][torch.from_numpy(order[:max_tokens]).cuda()])
+    wr = synth.to_np(Lg["wr"])
+    bias = Lg["bias"].cpu().numpy()
+    # pick the sample: tokens in random order while their experts fit the budget
+    lg0 = oracle.logits(xh_all, wr)
+    r0 = oracle.route(lg0, bias, sh.N, sh.K, want_keys=False)
+    experts, n = set(), 0
+    for i in range(max_tokens):
+        new = experts | {int(e) for e in r0.topk_idx[i] if e < sh.N}
+        if len(new) > budget_experts:
+            break
+        experts, n = new, i + 1
+    wg = {e: synth.to_np(Lg["wg"][e]) for e in experts}
+    wu = {e: synth.to_np(Lg["wu"][e]) for e in experts}
+    wd = {e: synth.to_np(Lg["wd"][e]) for e in experts}
+    xh = np.ascontiguousarray(xh_all[:n])
+    del Lg
+    torch.cuda.empty_cache()
+    t0 = time.perf_counter()
+    lg = oracle.logits(xh, wr)
+    r = oracle.route(lg, bias, sh.N, sh.K, want_keys=False)
+    oracle.forward(xh, wg, wu, wd, r.topk_idx, r.gates, sh.N)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} random tokens of the prefill workload (router scores, routing, "
+                      f"{len(experts)} FFN experts' outputs, combine), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", choices=["prefill", "decode", "train"], default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer's benchmark has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    zcmoe.lib()
+    extra = {}
+    sh = synth.CONFIGS["prefill_bf16"]
+    res = roof = None
+    if args.only in (None, "prefill"):
+        sh, res, roof = prefill(args.steps, args.warmup)
+        log(f"[bench] prefill {res['ms_per_step']:.3f} ms/step")
+    if args.only in (None, "decode"):
+        extra["decode"] = decode(args.steps, args.warmup)
+        log(f"[bench] decode {extra['decode']['ms_per_step']:.3f} ms/step")
+    if args.only in (None, "train"):
+        extra["train"] = train(args.steps, args.warmup)
+        log(f"[bench] train {extra['train']['ms_per_step']:.3f} ms/step")
+    cpu = None if args.no_cpu_baseline or args.only not in (None, "prefill") else cpu_baseline()
+    if res is None:  # a secondary workload alone: report it as the line
+        k = args.only
+        res = extra.pop(k)
+        sh = synth.CONFIGS["decode_bf16" if k == "decode" else "train_bf16"]
+        roof = None
+    line = {
+        "metric": "MoE-layer tokens/s at 1 GPU (prefill forward; % bf16 MFMA peak of the "
+                  "grouped GEMM; decode % HBM BW in 'decode')",
+        "value": round(res["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, N(0,std) weights, random init)",
+        "config": {"workload": sh.name, "T": sh.T, "d": sh.d, "N": sh.N, "Z": sh.Z, "I": sh.I,
+                   "K": sh.K, "bias": sh.bias},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "detail": res,
+        **extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

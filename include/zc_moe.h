@@ -1,0 +1,190 @@
+/*
+ * zc_moe.h -- C ABI of the MI355X (gfx950) MoE layer with zero-computation
+ * experts.
+ *
+ * The layer is the one of "LongCat-Flash Technical Report", section 2.1
+ * ("Zero-computation experts"), Eq.(1): a softmax router over N FFN experts
+ * plus Z zero-computation experts, a per-expert bias b_i that only shifts
+ * which K experts are picked, gates taken from the unbiased softmax, FFN
+ * experts evaluated on the tokens routed to them, and zero-computation
+ * experts returning their input x_t.  The bias follows Eq.(2) of section
+ * 2.1.1 ("Computation budget control").
+ *
+ * Conventions shared by every call:
+ *  - Pointers are DEVICE pointers unless a comment says "host".  The caller
+ *    owns every buffer; the library never allocates or frees device memory
+ *    and never synchronises with the host.  Scratch memory comes in through
+ *    (ws, ws_bytes); its required size is zc_moe_workspace_size().
+ *  - All work is queued on `stream` (a hipStream_t, passed as void*; NULL is
+ *    the default stream).  Outputs are valid once the stream has reached
+ *    that point; they are undefined after an error status.
+ *  - Arguments are checked on the host before anything is queued.  A bad
+ *    argument returns ZC_ERR_INVALID / ZC_ERR_UNSUPPORTED / ZC_ERR_WORKSPACE
+ *    and writes nothing.  A failed launch returns ZC_ERR_HIP.  The detail of
+ *    the last non-OK status of the calling thread is in zc_last_error().
+ *  - Every reduction has a fixed order: for fixed inputs and shapes, results
+ *    are bitwise reproducible from run to run.
+ *  - Row-major layouts, "out x in" for weights (like a linear layer's
+ *    weight), so every GEMM reads its reduction dimension contiguously:
+ *      x, out, dout, dx      [T][d]
+ *      w_router, dw_router   [E][d]          E = N + Z
+ *      w_gate, w_up (+ grads)[N][I][d]
+ *      w_down, dw_down       [N][d][I]
+ *    Expert indices 0..N-1 are FFN experts, N..E-1 zero-computation experts.
+ *  - Data pointers must be 16-byte aligned.  bf16 layers need d and I to be
+ *    multiples of 64, fp32 layers multiples of 32 (else ZC_ERR_UNSUPPORTED).
+ *  - Preconditions not checked by the kernels: finite inputs (NaN or Inf
+ *    router scores give an unspecified routing), T*K < 2^31.
+ */
+#ifndef ZC_MOE_H
+#define ZC_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ZC_OK = 0,
+  ZC_ERR_INVALID = 1,     /* null pointer, bad size, bad enum value      */
+  ZC_ERR_UNSUPPORTED = 2, /* valid layer outside the supported shapes    */
+  ZC_ERR_WORKSPACE = 3,   /* ws too small (or NULL with ws_bytes needed) */
+  ZC_ERR_HIP = 4          /* a HIP launch or runtime call failed         */
+} zc_status;
+
+typedef enum { ZC_F32 = 0, ZC_BF16 = 1 } zc_dtype;
+
+/* Layer description (host struct, passed by pointer). */
+typedef struct {
+  int64_t T;         /* tokens in the batch (0 allowed: nothing is done)      */
+  int64_t d;         /* hidden size                                           */
+  int64_t N;         /* FFN experts (>= 0)                                    */
+  int64_t Z;         /* zero-computation experts (>= 0), E = N + Z in 1..1024 */
+  int64_t I;         /* FFN inner size                                        */
+  int64_t K;         /* experts per token, 1 <= K <= min(E, 32)               */
+  int32_t dtype;     /* zc_dtype of x, weights, out, dx and weight gradients; */
+                     /* logits, gates and bias are always fp32; bf16 math     */
+                     /* accumulates in fp32                                   */
+  int32_t gate_norm; /* 1: gates renormalised over the K picks (softmax of    */
+                     /*    the picked scores; the picked R_i rescaled to sum  */
+                     /*    to 1);  0: gate = R_i exactly as Eq.(1) prints it  */
+  float out_scale;   /* scalar on the layer output (1.0 = none)               */
+} zc_moe_desc;
+
+/* Routing state: written by zc_moe_route / zc_moe_forward, read by
+ * zc_moe_backward.  All device buffers owned by the caller. */
+typedef struct {
+  float* logits;     /* [T][E] router scores x W_r^T (fp32)                   */
+  int32_t* topk_idx; /* [T][K] picked expert per slot; slot 0 = largest key   */
+  float* topk_gate;  /* [T][K] gate per slot                                  */
+  int32_t* counts;   /* [E]    tokens per expert (the T_i of Eq.(2))          */
+  int32_t* offsets;  /* [N+1]  exclusive prefix sum of counts[0..N)           */
+  int32_t* perm;     /* [T*K]  first offsets[N] entries: the flat slots t*K+r */
+                     /*        of FFN picks sorted by (expert, token)         */
+  int32_t* inv;      /* [T*K]  position of slot t*K+r in perm, -1 for a       */
+                     /*        zero-computation pick                          */
+} zc_route_buf;
+
+enum { ZC_OP_ROUTE = 0, ZC_OP_FORWARD = 1, ZC_OP_BACKWARD = 2 };
+
+/* Bytes of scratch memory `op` needs for this layer (0 for an invalid
+ * description).  The bound depends only on the description, never on the
+ * routing, so it can be sized before the first call. */
+size_t zc_moe_workspace_size(const zc_moe_desc* desc, int op);
+
+/* Bytes of the activation buffer `saved` that zc_moe_forward fills for
+ * zc_moe_backward (pre-activations, hidden and expert outputs of every FFN
+ * pick, sized for the worst case T*K picks). */
+size_t zc_moe_saved_size(const zc_moe_desc* desc);
+
+/* Router and dispatch: Eq.(1)'s scores, biased top-K and gates, then the
+ * per-expert token counts and the (expert, token) dispatch order.
+ *   logits = x W_r^T (fp32 accumulation);
+ *   key_j  = p_j + b_j with p the softmax of the token's logits, computed in
+ *            binary64 (max subtraction, Cody-Waite + degree-13 Taylor
+ *            exponential, 64 partial sums combined pairwise at xor distance
+ *            32..1, one division per key);
+ *   picks  = the K largest keys, ties to the lower expert index;
+ *   gates  = e_j / (sum of the picked e) (gate_norm 1) or p_j (gate_norm 0),
+ *            with e_j the exponentials above, rounded to fp32.
+ * If x and w_router are both NULL the scores already in r->logits are used
+ * as given (routing of scores computed elsewhere).  bias: [E] fp32. */
+zc_status zc_moe_route(const zc_moe_desc* desc, const void* x,
+                       const void* w_router, const float* bias,
+                       zc_route_buf* r, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* Full layer forward: route as above, then for every FFN pick
+ * h = silu(x W_g^T) * (x W_u^T) and y = h W_d^T on the tokens routed to that
+ * expert (grouped bf16 MFMA GEMMs, fp32 accumulation, h and y stored in the
+ * layer dtype), then
+ *   out_t = out_scale * ( (sum of gates on zero-computation picks) * x_t
+ *                         + sum over FFN picks r ascending of g_r * y_r ),
+ * accumulated in fp32.  Zero-computation experts cost one scalar per token.
+ * saved (nullable, zc_moe_saved_size bytes) receives what zc_moe_backward
+ * needs.  w_gate/w_up/w_down may be NULL only when N == 0. */
+zc_status zc_moe_forward(const zc_moe_desc* desc, const void* x,
+                         const void* w_router, const float* bias,
+                         const void* w_gate, const void* w_up,
+                         const void* w_down, void* out, zc_route_buf* r,
+                         void* saved, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of zc_moe_forward with the routing held fixed (the picked set is
+ * piecewise constant in the inputs; the bias gets no gradient, it is
+ * decoupled from the training objective).  Given dout [T][d]:
+ *   dg_r  = <out_scale*dout_t, y_r> (FFN pick) or <out_scale*dout_t, x_t>;
+ *   expert gradients through y = W_d(silu(W_g x) * W_u x);
+ *   router: dl_j = g_j (dg_j - sum_picks g dg) on the picks (gate_norm 1),
+ *           dl_j = p_j (dg_j [pick] - sum_picks p dg) (gate_norm 0);
+ *   dx = out_scale*(identity gates)*dout + expert dx + dl W_r.
+ * Every gradient buffer is overwritten (not accumulated).  r and saved must
+ * come from the zc_moe_forward call being differentiated. */
+zc_status zc_moe_backward(const zc_moe_desc* desc, const void* x,
+                          const void* w_router, const void* w_gate,
+                          const void* w_up, const void* w_down,
+                          const zc_route_buf* r, const void* saved,
+                          const void* dout, void* dx, void* dw_router,
+                          void* dw_gate, void* dw_up, void* dw_down, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Eq.(2) bias update, in place on bias [N+Z] (fp32), for FFN experts i < N:
+ *   b_i += mu * ( K_e/(K*N) - T_i/(K*T_all) ),  T_i = counts[i],
+ * in binary64 with exactly the operations
+ *   tgt = K_e/((double)K*N); obs = (double)T_i/((double)K*T_all);
+ *   b_i = (float)((double)b_i + mu*(tgt - obs));
+ * zero-computation experts keep their bias.  counts [N+Z] int32 (device).
+ * Needs T_all >= 1, K >= 1, N >= 0. */
+zc_status zc_moe_pid_update(int64_t N, int64_t Z, int64_t K,
+                            const int32_t* counts, int64_t T_all, double mu,
+                            double K_e, float* bias, void* stream);
+
+/* Kernel timing for benchmarks.  While profiling is on, every entry point
+ * brackets each of its kernel launches with a pair of HIP events recorded on
+ * the call's own stream, tagged with one of the phases below.  The events
+ * are host-side objects created by the library; no device memory is
+ * allocated.  zc_moe_profile_read waits for every recorded event, adds each
+ * duration (ms) to total_ms[phase] and one to count[phase] (both host
+ * arrays of ZC_NUM_PHASES entries, zeroed first), then forgets the events.
+ * Turning profiling off discards events not read yet. */
+enum {
+  ZC_PH_ROUTER_GEMM = 0, ZC_PH_TOPK, ZC_PH_DISPATCH, ZC_PH_GATE_UP, ZC_PH_DOWN, ZC_PH_COMBINE,
+  ZC_PH_BWD_COMBINE, ZC_PH_BWD_DOWN_DH, ZC_PH_BWD_DOWN_DW, ZC_PH_BWD_GATE_UP_DX,
+  ZC_PH_BWD_GATE_UP_DW, ZC_PH_BWD_ROUTER_DW, ZC_PH_BWD_ROUTER_DX, ZC_PH_BWD_DX_GATHER,
+  ZC_PH_BIAS_UPDATE, ZC_PH_TILE_OFFSETS, ZC_NUM_PHASES
+};
+zc_status zc_moe_profile(int on);
+zc_status zc_moe_profile_read(double* total_ms, int32_t* count);
+const char* zc_moe_phase_name(int phase); /* static text, "" if out of range */
+
+/* Static text for a status code (never NULL). */
+const char* zc_status_string(zc_status s);
+
+/* Detail of the calling thread's last non-OK status ("" if none). */
+const char* zc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZC_MOE_H */

@@ -1,0 +1,514 @@
+// C ABI of libzcmoe: argument checks, workspace carving and the launch
+// sequence of each entry point.  See include/zc_moe.h for the contract.
+#include <atomic>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/zc_moe.h"
+#include "zc_common.h"
+
+using zc::bf16_t;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+zc_status fail(zc_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+zc_status fail(zc_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+zc_status hip_fail(hipError_t e, const char* what) {
+  return fail(ZC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define ZC_HIP(call, what)                           \
+  do {                                               \
+    hipError_t e_ = (call);                          \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+// ---- optional per-phase kernel timing (zc_moe_profile)
+struct PhaseRec {
+  int phase;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+std::atomic<bool> g_prof_on{false};
+std::vector<PhaseRec> g_prof_recs;
+
+// Records a start event on construction and an end event in done(), on the
+// stream of the launch, when profiling is on.
+class PhaseScope {
+ public:
+  PhaseScope(int phase, hipStream_t s) : phase_(phase), s_(s) {
+    if (g_prof_on.load(std::memory_order_relaxed) && hipEventCreate(&a_) == hipSuccess)
+      (void)hipEventRecord(a_, s_);
+    else
+      a_ = nullptr;
+  }
+  void done() {
+    if (!a_) return;
+    hipEvent_t b = nullptr;
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a_);
+      return;
+    }
+    (void)hipEventRecord(b, s_);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_recs.push_back(PhaseRec{phase_, a_, b});
+  }
+
+ private:
+  int phase_;
+  hipStream_t s_;
+  hipEvent_t a_;
+};
+
+#define ZC_LAUNCH(phase, call, what)                 \
+  do {                                               \
+    PhaseScope ps_((phase), s);                      \
+    hipError_t e_ = (call);                          \
+    ps_.done();                                      \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+void drop_records() {
+  for (auto& r : g_prof_recs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_prof_recs.clear();
+}
+
+// Compute-unit count of the current device, cached per device.
+std::atomic<int> g_cu[64];
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64) {
+    int v = g_cu[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) g_cu[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+int64_t a256(int64_t b) { return (b + 255) & ~int64_t(255); }
+int64_t esize(const zc_moe_desc* d) { return d->dtype == ZC_F32 ? 4 : 2; }
+int64_t ldl_of(int64_t E) { return (E + 7) / 8 * 8; }
+
+zc_status check_desc(const zc_moe_desc* d) {
+  if (!d) return fail(ZC_ERR_INVALID, "desc is NULL");
+  const int64_t E = d->N + d->Z;
+  if (d->T < 0 || d->d < 1 || d->N < 0 || d->Z < 0 || d->I < 1)
+    return fail(ZC_ERR_INVALID, "bad sizes T=%lld d=%lld N=%lld Z=%lld I=%lld", (long long)d->T,
+                (long long)d->d, (long long)d->N, (long long)d->Z, (long long)d->I);
+  if (E < 1 || E > 1024) return fail(ZC_ERR_INVALID, "N+Z=%lld outside 1..1024", (long long)E);
+  if (d->K < 1 || d->K > E || d->K > 32)
+    return fail(ZC_ERR_INVALID, "K=%lld outside 1..min(N+Z, 32)", (long long)d->K);
+  if (d->dtype != ZC_F32 && d->dtype != ZC_BF16)
+    return fail(ZC_ERR_INVALID, "dtype %d is neither ZC_F32 nor ZC_BF16", d->dtype);
+  if (d->gate_norm != 0 && d->gate_norm != 1)
+    return fail(ZC_ERR_INVALID, "gate_norm %d is neither 0 nor 1", d->gate_norm);
+  if (!std::isfinite(d->out_scale)) return fail(ZC_ERR_INVALID, "out_scale is not finite");
+  if (d->T * d->K >= (int64_t(1) << 31) || d->d >= (int64_t(1) << 24) || d->I >= (int64_t(1) << 24))
+    return fail(ZC_ERR_UNSUPPORTED, "T*K, d or I too large for 32-bit indexing");
+  const int64_t mult = d->dtype == ZC_BF16 ? 64 : 32;
+  if (d->d % mult || d->I % mult)
+    return fail(ZC_ERR_UNSUPPORTED, "%s layers need d and I multiples of %lld (d=%lld I=%lld)",
+                d->dtype == ZC_BF16 ? "bf16" : "fp32", (long long)mult, (long long)d->d,
+                (long long)d->I);
+  return ZC_OK;
+}
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+zc_status check_ptr(const void* p, const char* name, bool nullable = false) {
+  if (!p) return nullable ? ZC_OK : fail(ZC_ERR_INVALID, "%s is NULL", name);
+  if (!aligned(p)) return fail(ZC_ERR_INVALID, "%s is not 16-byte aligned", name);
+  return ZC_OK;
+}
+
+#define ZC_CHECK(x)                   \
+  do {                                \
+    zc_status s_ = (x);               \
+    if (s_ != ZC_OK) return s_;       \
+  } while (0)
+
+zc_status check_route(const zc_route_buf* r) {
+  if (!r) return fail(ZC_ERR_INVALID, "route buffer is NULL");
+  ZC_CHECK(check_ptr(r->logits, "r->logits"));
+  ZC_CHECK(check_ptr(r->topk_idx, "r->topk_idx"));
+  ZC_CHECK(check_ptr(r->topk_gate, "r->topk_gate"));
+  ZC_CHECK(check_ptr(r->counts, "r->counts"));
+  ZC_CHECK(check_ptr(r->offsets, "r->offsets"));
+  ZC_CHECK(check_ptr(r->perm, "r->perm"));
+  ZC_CHECK(check_ptr(r->inv, "r->inv"));
+  return ZC_OK;
+}
+
+// ---- workspace layouts (all pieces 256-byte aligned)
+struct RouteWs {
+  int32_t* tile_off;
+  void* dispatch;
+};
+int64_t route_ws_bytes(const zc_moe_desc* d) {
+  return a256(4 * (d->N + 1)) + a256(zc::dispatch_scratch_bytes(d->T, d->N + d->Z, d->N));
+}
+RouteWs carve_route(char* p, const zc_moe_desc* d) {
+  RouteWs w;
+  w.tile_off = reinterpret_cast<int32_t*>(p);
+  w.dispatch = p + a256(4 * (d->N + 1));
+  return w;
+}
+
+struct Saved {
+  void *a, *u, *h, *y;
+};
+int64_t saved_bytes(const zc_moe_desc* d) {
+  const int64_t rows = d->T * d->K, es = esize(d);
+  return 3 * a256(rows * d->I * es) + a256(rows * d->d * es);
+}
+Saved carve_saved(char* p, const zc_moe_desc* d) {
+  const int64_t rows = d->T * d->K, es = esize(d);
+  const int64_t hi = a256(rows * d->I * es);
+  return Saved{p, p + hi, p + 2 * hi, p + 3 * hi};
+}
+
+int64_t fwd_ws_bytes(const zc_moe_desc* d) {
+  const int64_t rows = d->T * d->K, es = esize(d);
+  return route_ws_bytes(d) + a256(rows * d->I * es) + a256(rows * d->d * es);
+}
+
+struct BwdWs {
+  int32_t* tile_off;
+  void *dyg, *dl, *dadu, *dxp, *dxr;
+  float* dg;
+};
+int64_t bwd_ws_bytes(const zc_moe_desc* d) {
+  const int64_t rows = d->T * d->K, es = esize(d), E = d->N + d->Z;
+  return a256(4 * (d->N + 1)) + a256(rows * d->d * es) + a256(4 * d->T * d->K) +
+         a256(d->T * ldl_of(E) * es) + a256(rows * 2 * d->I * es) + a256(rows * d->d * es) +
+         a256(d->T * d->d * es);
+}
+BwdWs carve_bwd(char* p, const zc_moe_desc* d) {
+  const int64_t rows = d->T * d->K, es = esize(d), E = d->N + d->Z;
+  BwdWs w;
+  w.tile_off = reinterpret_cast<int32_t*>(p);
+  p += a256(4 * (d->N + 1));
+  w.dyg = p;
+  p += a256(rows * d->d * es);
+  w.dg = reinterpret_cast<float*>(p);
+  p += a256(4 * d->T * d->K);
+  w.dl = p;
+  p += a256(d->T * ldl_of(E) * es);
+  w.dadu = p;
+  p += a256(rows * 2 * d->I * es);
+  w.dxp = p;
+  p += a256(rows * d->d * es);
+  w.dxr = p;
+  return w;
+}
+
+zc_status check_ws(const void* ws, size_t ws_bytes, int64_t need) {
+  if (need > 0 && (!ws || ws_bytes < static_cast<size_t>(need)))
+    return fail(ZC_ERR_WORKSPACE, "workspace of %zu bytes at %p, %lld needed", ws_bytes, ws,
+                (long long)need);
+  if (ws && (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return fail(ZC_ERR_INVALID, "workspace is not 256-byte aligned");
+  return ZC_OK;
+}
+
+// Router + dispatch on an already validated call.
+template <typename T>
+zc_status do_route(const zc_moe_desc* d, const T* x, const T* wr, const float* bias,
+                   zc_route_buf* r, const RouteWs& w, hipStream_t s) {
+  const int Tn = static_cast<int>(d->T), E = static_cast<int>(d->N + d->Z);
+  const int N = static_cast<int>(d->N), K = static_cast<int>(d->K);
+  if (x && Tn > 0)
+    ZC_LAUNCH(ZC_PH_ROUTER_GEMM, zc::launch_router_gemm<T>(x, wr, r->logits, Tn, E, static_cast<int>(d->d), cu_count(),
+                                     s),
+           "router GEMM launch");
+  ZC_LAUNCH(ZC_PH_TOPK, zc::launch_topk(r->logits, bias, Tn, E, K, d->gate_norm, r->topk_idx, r->topk_gate, s),
+         "top-K launch");
+  ZC_LAUNCH(ZC_PH_DISPATCH, zc::launch_dispatch(r->topk_idx, Tn, E, N, K, zc::kGemmBM, r->counts, r->offsets,
+                             r->perm, r->inv, w.tile_off, w.dispatch, s),
+         "dispatch launch");
+  return ZC_OK;
+}
+
+template <typename T>
+zc_status do_forward(const zc_moe_desc* d, const T* x, const T* wr, const float* bias,
+                     const T* wg, const T* wu, const T* wd, T* out, zc_route_buf* r, void* saved,
+                     char* ws, hipStream_t s) {
+  RouteWs rw = carve_route(ws, d);
+  ZC_CHECK(do_route<T>(d, x, wr, bias, r, rw, s));
+  const int Tn = static_cast<int>(d->T), N = static_cast<int>(d->N), K = static_cast<int>(d->K);
+  const int dd = static_cast<int>(d->d), I = static_cast<int>(d->I);
+  const int64_t rows = d->T * d->K;
+  T *h, *y, *sa = nullptr, *su = nullptr;
+  if (saved) {
+    Saved sv = carve_saved(static_cast<char*>(saved), d);
+    sa = static_cast<T*>(sv.a);
+    su = static_cast<T*>(sv.u);
+    h = static_cast<T*>(sv.h);
+    y = static_cast<T*>(sv.y);
+  } else {
+    char* p = ws + route_ws_bytes(d);
+    h = reinterpret_cast<T*>(p);
+    y = reinterpret_cast<T*>(p + a256(rows * d->I * esize(d)));
+  }
+  if (N > 0 && Tn > 0) {
+    const int cu = cu_count();
+    ZC_LAUNCH(ZC_PH_GATE_UP, zc::launch_ffn_gateup<T>(x, wg, wu, r->offsets, r->perm, rw.tile_off, N, I, dd, K, rows,
+                                    h, sa, su, cu, s),
+           "gate/up GEMM launch");
+    ZC_LAUNCH(ZC_PH_DOWN, zc::launch_ffn_down<T>(h, wd, r->offsets, rw.tile_off, N, I, dd, rows, y, cu, s),
+           "down GEMM launch");
+  }
+  ZC_LAUNCH(ZC_PH_COMBINE, zc::launch_combine<T>(x, y, r->topk_idx, r->topk_gate, r->inv, Tn, dd, N, K, d->out_scale,
+                               out, s),
+         "combine launch");
+  return ZC_OK;
+}
+
+template <typename T>
+zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg, const T* wu,
+                      const T* wd, const zc_route_buf* r, const void* saved, const T* dout, T* dx,
+                      T* dwr, T* dwg, T* dwu, T* dwd, char* ws, hipStream_t s) {
+  const int Tn = static_cast<int>(d->T), N = static_cast<int>(d->N), K = static_cast<int>(d->K);
+  const int E = static_cast<int>(d->N + d->Z), dd = static_cast<int>(d->d);
+  const int I = static_cast<int>(d->I), ldl = static_cast<int>(ldl_of(E));
+  const int64_t rows = d->T * d->K;
+  const int cu = cu_count();
+  BwdWs w = carve_bwd(ws, d);
+  Saved sv = carve_saved(const_cast<char*>(static_cast<const char*>(saved)), d);
+  const T* sa = static_cast<const T*>(sv.a);
+  const T* su = static_cast<const T*>(sv.u);
+  const T* h = static_cast<const T*>(sv.h);
+  const T* y = static_cast<const T*>(sv.y);
+  T* dyg = static_cast<T*>(w.dyg);
+  T* dl = static_cast<T*>(w.dl);
+  T* dadu = static_cast<T*>(w.dadu);
+  T* dxp = static_cast<T*>(w.dxp);
+  T* dxr = static_cast<T*>(w.dxr);
+  if (N > 0) ZC_LAUNCH(ZC_PH_TILE_OFFSETS, zc::launch_tile_offsets(r->offsets, N, zc::kGemmBM, w.tile_off, s), "tile offsets");
+  ZC_LAUNCH(ZC_PH_BWD_COMBINE, zc::launch_combine_bwd<T>(x, y, dout, r->logits, r->topk_idx, r->topk_gate, r->inv, Tn, dd,
+                                   N, E, K, d->gate_norm, d->out_scale, dyg, w.dg, dl, ldl, s),
+         "combine backward launch");
+  if (N > 0) {
+    if (Tn > 0) {
+      ZC_LAUNCH(ZC_PH_BWD_DOWN_DH, zc::launch_bwd_down_dh<T>(dyg, wd, sa, su, r->offsets, w.tile_off, N, I, dd, rows,
+                                       dadu, cu, s),
+             "down backward (dh) launch");
+    }
+    ZC_LAUNCH(ZC_PH_BWD_DOWN_DW, zc::launch_bwd_down_dw<T>(dyg, h, r->offsets, N, I, dd, dwd, cu, s),
+           "down weight-gradient launch");
+    if (Tn > 0) {
+      ZC_LAUNCH(ZC_PH_BWD_GATE_UP_DX, zc::launch_bwd_gateup_dx<T>(dadu, wg, wu, r->offsets, w.tile_off, N, I, dd, rows, dxp,
+                                         cu, s),
+             "gate/up backward (dx) launch");
+    }
+    ZC_LAUNCH(ZC_PH_BWD_GATE_UP_DW, zc::launch_bwd_gateup_dw<T>(dadu, x, r->offsets, r->perm, N, I, dd, K, dwg, dwu, cu, s),
+           "gate/up weight-gradient launch");
+  }
+  ZC_LAUNCH(ZC_PH_BWD_ROUTER_DW, zc::launch_router_dw<T>(dl, ldl, x, Tn, E, dd, dwr, cu, s), "router weight-gradient launch");
+  if (Tn > 0) {
+    ZC_LAUNCH(ZC_PH_BWD_ROUTER_DX, zc::launch_router_dx<T>(dl, ldl, wr, Tn, E, dd, dxr, cu, s), "router dx launch");
+    ZC_LAUNCH(ZC_PH_BWD_DX_GATHER, zc::launch_dx_gather<T>(dout, dxp, dxr, r->topk_idx, r->topk_gate, r->inv, Tn, dd, N, K,
+                                   d->out_scale, dx, s),
+           "dx gather launch");
+  }
+  return ZC_OK;
+}
+
+zc_status check_weights(const zc_moe_desc* d, const void* wg, const void* wu, const void* wd) {
+  const bool opt = d->N == 0;
+  ZC_CHECK(check_ptr(wg, "w_gate", opt));
+  ZC_CHECK(check_ptr(wu, "w_up", opt));
+  ZC_CHECK(check_ptr(wd, "w_down", opt));
+  return ZC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t zc_moe_workspace_size(const zc_moe_desc* desc, int op) {
+  if (check_desc(desc) != ZC_OK) return 0;
+  switch (op) {
+    case ZC_OP_ROUTE: return static_cast<size_t>(route_ws_bytes(desc));
+    case ZC_OP_FORWARD: return static_cast<size_t>(fwd_ws_bytes(desc));
+    case ZC_OP_BACKWARD: return static_cast<size_t>(bwd_ws_bytes(desc));
+    default: return 0;
+  }
+}
+
+size_t zc_moe_saved_size(const zc_moe_desc* desc) {
+  if (check_desc(desc) != ZC_OK) return 0;
+  return static_cast<size_t>(saved_bytes(desc));
+}
+
+zc_status zc_moe_route(const zc_moe_desc* desc, const void* x, const void* w_router,
+                       const float* bias, zc_route_buf* r, void* ws, size_t ws_bytes,
+                       void* stream) {
+  ZC_CHECK(check_desc(desc));
+  ZC_CHECK(check_route(r));
+  ZC_CHECK(check_ptr(bias, "bias"));
+  if ((x == nullptr) != (w_router == nullptr))
+    return fail(ZC_ERR_INVALID, "x and w_router must both be set or both be NULL");
+  ZC_CHECK(check_ptr(x, "x", true));
+  ZC_CHECK(check_ptr(w_router, "w_router", true));
+  ZC_CHECK(check_ws(ws, ws_bytes, route_ws_bytes(desc)));
+  RouteWs w = carve_route(static_cast<char*>(ws), desc);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (desc->dtype == ZC_BF16)
+    return do_route<bf16_t>(desc, static_cast<const bf16_t*>(x),
+                            static_cast<const bf16_t*>(w_router), bias, r, w, s);
+  return do_route<float>(desc, static_cast<const float*>(x), static_cast<const float*>(w_router),
+                         bias, r, w, s);
+}
+
+zc_status zc_moe_forward(const zc_moe_desc* desc, const void* x, const void* w_router,
+                         const float* bias, const void* w_gate, const void* w_up,
+                         const void* w_down, void* out, zc_route_buf* r, void* saved, void* ws,
+                         size_t ws_bytes, void* stream) {
+  ZC_CHECK(check_desc(desc));
+  ZC_CHECK(check_route(r));
+  ZC_CHECK(check_ptr(x, "x"));
+  ZC_CHECK(check_ptr(w_router, "w_router"));
+  ZC_CHECK(check_ptr(bias, "bias"));
+  ZC_CHECK(check_weights(desc, w_gate, w_up, w_down));
+  ZC_CHECK(check_ptr(out, "out"));
+  ZC_CHECK(check_ptr(saved, "saved", true));
+  ZC_CHECK(check_ws(ws, ws_bytes, fwd_ws_bytes(desc)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  if (desc->dtype == ZC_BF16)
+    return do_forward<bf16_t>(desc, static_cast<const bf16_t*>(x),
+                              static_cast<const bf16_t*>(w_router), bias,
+                              static_cast<const bf16_t*>(w_gate), static_cast<const bf16_t*>(w_up),
+                              static_cast<const bf16_t*>(w_down), static_cast<bf16_t*>(out), r,
+                              saved, w, s);
+  return do_forward<float>(desc, static_cast<const float*>(x), static_cast<const float*>(w_router),
+                           bias, static_cast<const float*>(w_gate),
+                           static_cast<const float*>(w_up), static_cast<const float*>(w_down),
+                           static_cast<float*>(out), r, saved, w, s);
+}
+
+zc_status zc_moe_backward(const zc_moe_desc* desc, const void* x, const void* w_router,
+                          const void* w_gate, const void* w_up, const void* w_down,
+                          const zc_route_buf* r, const void* saved, const void* dout, void* dx,
+                          void* dw_router, void* dw_gate, void* dw_up, void* dw_down, void* ws,
+                          size_t ws_bytes, void* stream) {
+  ZC_CHECK(check_desc(desc));
+  ZC_CHECK(check_route(r));
+  ZC_CHECK(check_ptr(x, "x"));
+  ZC_CHECK(check_ptr(w_router, "w_router"));
+  ZC_CHECK(check_weights(desc, w_gate, w_up, w_down));
+  ZC_CHECK(check_ptr(saved, "saved"));
+  ZC_CHECK(check_ptr(dout, "dout"));
+  ZC_CHECK(check_ptr(dx, "dx"));
+  ZC_CHECK(check_ptr(dw_router, "dw_router"));
+  ZC_CHECK(check_weights(desc, dw_gate, dw_up, dw_down));
+  ZC_CHECK(check_ws(ws, ws_bytes, bwd_ws_bytes(desc)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  if (desc->dtype == ZC_BF16)
+    return do_backward<bf16_t>(
+        desc, static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w_router),
+        static_cast<const bf16_t*>(w_gate), static_cast<const bf16_t*>(w_up),
+        static_cast<const bf16_t*>(w_down), r, saved, static_cast<const bf16_t*>(dout),
+        static_cast<bf16_t*>(dx), static_cast<bf16_t*>(dw_router), static_cast<bf16_t*>(dw_gate),
+        static_cast<bf16_t*>(dw_up), static_cast<bf16_t*>(dw_down), w, s);
+  return do_backward<float>(desc, static_cast<const float*>(x), static_cast<const float*>(w_router),
+                            static_cast<const float*>(w_gate), static_cast<const float*>(w_up),
+                            static_cast<const float*>(w_down), r, saved,
+                            static_cast<const float*>(dout), static_cast<float*>(dx),
+                            static_cast<float*>(dw_router), static_cast<float*>(dw_gate),
+                            static_cast<float*>(dw_up), static_cast<float*>(dw_down), w, s);
+}
+
+zc_status zc_moe_pid_update(int64_t N, int64_t Z, int64_t K, const int32_t* counts, int64_t T_all,
+                            double mu, double K_e, float* bias, void* stream) {
+  if (N < 0 || Z < 0 || N + Z < 1 || N + Z > 1024)
+    return fail(ZC_ERR_INVALID, "N=%lld Z=%lld: need N, Z >= 0 and 1 <= N+Z <= 1024",
+                (long long)N, (long long)Z);
+  if (K < 1 || T_all < 1) return fail(ZC_ERR_INVALID, "K and T_all must be >= 1");
+  if (!std::isfinite(mu) || !std::isfinite(K_e)) return fail(ZC_ERR_INVALID, "mu or K_e not finite");
+  ZC_CHECK(check_ptr(counts, "counts"));
+  ZC_CHECK(check_ptr(bias, "bias"));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ZC_LAUNCH(ZC_PH_BIAS_UPDATE, zc::launch_pid(static_cast<int>(N), static_cast<int>(K), counts, T_all, mu, K_e, bias, s),
+         "bias update launch");
+  return ZC_OK;
+}
+
+zc_status zc_moe_profile(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!on) drop_records();
+  g_prof_on.store(on != 0);
+  return ZC_OK;
+}
+
+zc_status zc_moe_profile_read(double* total_ms, int32_t* count) {
+  if (!total_ms || !count) return fail(ZC_ERR_INVALID, "total_ms and count must be host arrays");
+  for (int i = 0; i < ZC_NUM_PHASES; ++i) {
+    total_ms[i] = 0.0;
+    count[i] = 0;
+  }
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  zc_status st = ZC_OK;
+  for (auto& r : g_prof_recs) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) {
+      st = hip_fail(e, "reading kernel timing events");
+      continue;
+    }
+    total_ms[r.phase] += ms;
+    count[r.phase] += 1;
+  }
+  drop_records();
+  return st;
+}
+
+const char* zc_moe_phase_name(int phase) {
+  static const char* names[ZC_NUM_PHASES] = {
+      "router_gemm", "topk", "dispatch", "gate_up_gemm", "down_gemm", "combine",
+      "bwd_combine", "bwd_down_dh", "bwd_down_dw", "bwd_gate_up_dx", "bwd_gate_up_dw",
+      "bwd_router_dw", "bwd_router_dx", "bwd_dx_gather", "bias_update", "tile_offsets"};
+  return (phase >= 0 && phase < ZC_NUM_PHASES) ? names[phase] : "";
+}
+
+const char* zc_status_string(zc_status s) {
+  switch (s) {
+    case ZC_OK: return "ok";
+    case ZC_ERR_INVALID: return "invalid argument";
+    case ZC_ERR_UNSUPPORTED: return "unsupported shape";
+    case ZC_ERR_WORKSPACE: return "workspace too small";
+    case ZC_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* zc_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,268 @@
+// Weighted combine with the zero-computation experts folded in, and the
+// token-side pieces of the backward pass.
+//
+// "LongCat-Flash Technical Report", section 2.1: the layer output is
+// sum_i g_i E_i(x_t) with E_i(x_t) = x_t for the zero-computation experts,
+// so those experts reduce to one scalar per token,
+//   c_t = sum of the gates of the token's zero-computation picks,
+// and the output is c_t x_t + sum over FFN picks of g_r y_r.  Every sum runs
+// in slot order in fp32, one workgroup per token, so results do not depend
+// on scheduling (no atomics).  Inputs and outputs are in the layer dtype;
+// y rows are found through the inverse dispatch map.
+#include "zc_common.h"
+
+namespace zc {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxK = 32;
+
+// 16-byte vector of the layer dtype, widened to fp32.
+template <typename T> struct V16;
+template <> struct V16<bf16_t> {
+  static constexpr int n = 8;
+  static __device__ __forceinline__ void load(const bf16_t* p, float* f) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = __uint_as_float(v[e] << 16);
+      f[2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float* f) {
+    u32x4_t v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = static_cast<uint32_t>(f2bf(f[2 * e])) | (static_cast<uint32_t>(f2bf(f[2 * e + 1])) << 16);
+    *reinterpret_cast<u32x4_t*>(p) = v;
+  }
+};
+template <> struct V16<float> {
+  static constexpr int n = 4;
+  static __device__ __forceinline__ void load(const float* p, float* f) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = v[e];
+  }
+  static __device__ __forceinline__ void store(float* p, const float* f) {
+    *reinterpret_cast<f32x4_t*>(p) = f32x4_t{f[0], f[1], f[2], f[3]};
+  }
+};
+
+// Token's picks into LDS; returns c_t (sum of zero-computation gates).
+__device__ __forceinline__ float load_picks(const int32_t* topk_idx, const float* gate,
+                                            const int32_t* inv, int64_t t, int N, int K,
+                                            float* s_g, int32_t* s_inv, float* s_c) {
+  if (threadIdx.x < K) {
+    const int64_t o = t * K + threadIdx.x;
+    const int e = topk_idx[o];
+    s_g[threadIdx.x] = gate[o];
+    s_inv[threadIdx.x] = e < N ? inv[o] : -1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float c = 0.f;
+    for (int r = 0; r < K; ++r)
+      if (s_inv[r] < 0) c += s_g[r];
+    *s_c = c;
+  }
+  __syncthreads();
+  return *s_c;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void combine_kernel(
+    const T* __restrict__ x, const T* __restrict__ y, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ gate, const int32_t* __restrict__ inv, int d, int N, int K,
+    float out_scale, T* __restrict__ out) {
+  __shared__ float s_g[kMaxK];
+  __shared__ int32_t s_inv[kMaxK];
+  __shared__ float s_c;
+  const int64_t t = blockIdx.x;
+  const float c = load_picks(topk_idx, gate, inv, t, N, K, s_g, s_inv, &s_c);
+  constexpr int V = V16<T>::n;
+  for (int j = threadIdx.x * V; j < d; j += kThreads * V) {
+    float acc[V], v[V];
+    V16<T>::load(x + t * d + j, v);
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[e] = c * v[e];
+    for (int r = 0; r < K; ++r) {
+      const int q = s_inv[r];
+      if (q < 0) continue;
+      V16<T>::load(y + static_cast<int64_t>(q) * d + j, v);
+      const float g = s_g[r];
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += g * v[e];
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[e] *= out_scale;
+    V16<T>::store(out + t * d + j, acc);
+  }
+}
+
+// Fixed-order block sum of one value per thread (wave butterflies, then the
+// four wave results in order).  All threads get the result.
+__device__ __forceinline__ float block_sum(float v, float* s_red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return ((s_red[0] + s_red[1]) + s_red[2]) + s_red[3];
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
+    const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ dout,
+    const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ gate, const int32_t* __restrict__ inv, int d, int N, int E, int K,
+    int gate_norm, float out_scale, T* __restrict__ dyg, float* __restrict__ dg_out,
+    T* __restrict__ dl, int ldl) {
+  __shared__ float s_g[kMaxK];
+  __shared__ int32_t s_inv[kMaxK];
+  __shared__ int32_t s_e[kMaxK];
+  __shared__ float s_dg[kMaxK];
+  __shared__ float s_c;
+  __shared__ float s_red[4];
+  const int64_t t = blockIdx.x;
+  if (threadIdx.x < K) s_e[threadIdx.x] = topk_idx[t * K + threadIdx.x];
+  load_picks(topk_idx, gate, inv, t, N, K, s_g, s_inv, &s_c);
+  constexpr int V = V16<T>::n;
+  // dg_r = <out_scale*dout_t, y_r or x_t>; gated dy rows in dispatch order
+  for (int r = 0; r < K; ++r) {
+    const int q = s_inv[r];
+    float part = 0.f;
+    for (int j = threadIdx.x * V; j < d; j += kThreads * V) {
+      float dv[V], v[V];
+      V16<T>::load(dout + t * d + j, dv);
+#pragma unroll
+      for (int e = 0; e < V; ++e) dv[e] *= out_scale;
+      V16<T>::load(q >= 0 ? y + static_cast<int64_t>(q) * d + j : x + t * d + j, v);
+#pragma unroll
+      for (int e = 0; e < V; ++e) part += dv[e] * v[e];
+      if (q >= 0) {
+        const float g = s_g[r];
+#pragma unroll
+        for (int e = 0; e < V; ++e) dv[e] *= g;
+        V16<T>::store(dyg + static_cast<int64_t>(q) * d + j, dv);
+      }
+    }
+    const float tot = block_sum(part, s_red);
+    if (threadIdx.x == 0) s_dg[r] = tot;
+  }
+  __syncthreads();
+  if (threadIdx.x < K) dg_out[t * K + threadIdx.x] = s_dg[threadIdx.x];
+  // router: softmax Jacobian, restricted to the picks (gate_norm 1) or full
+  float sgd = 0.f;
+  for (int r = 0; r < K; ++r) sgd += s_g[r] * s_dg[r];
+  T* dlr = dl + t * ldl;
+  if (gate_norm) {
+    for (int j = threadIdx.x; j < ldl; j += kThreads) Elem<T>::st(dlr + j, 0.f);
+    __syncthreads();
+    if (threadIdx.x < K) Elem<T>::st(dlr + s_e[threadIdx.x], s_g[threadIdx.x] * (s_dg[threadIdx.x] - sgd));
+  } else {
+    const float* l = logits + t * E;
+    float m = -INFINITY;
+    for (int j = threadIdx.x; j < E; j += kThreads) m = fmaxf(m, l[j]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    float part = 0.f;
+    for (int j = threadIdx.x; j < E; j += kThreads) part += __expf(l[j] - m);
+    const float S = block_sum(part, s_red);
+    for (int j = threadIdx.x; j < ldl; j += kThreads) {
+      float v = 0.f;
+      if (j < E) {
+        const float pj = __expf(l[j] - m) / S;
+        float dgj = 0.f;
+        for (int r = 0; r < K; ++r)
+          if (s_e[r] == j) dgj = s_dg[r];
+        v = pj * (dgj - sgd);
+      }
+      Elem<T>::st(dlr + j, v);
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void dx_gather_kernel(
+    const T* __restrict__ dout, const T* __restrict__ dxp, const T* __restrict__ dxr,
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ gate,
+    const int32_t* __restrict__ inv, int d, int N, int K, float out_scale, T* __restrict__ dx) {
+  __shared__ float s_g[kMaxK];
+  __shared__ int32_t s_inv[kMaxK];
+  __shared__ float s_c;
+  const int64_t t = blockIdx.x;
+  const float c = load_picks(topk_idx, gate, inv, t, N, K, s_g, s_inv, &s_c) * out_scale;
+  constexpr int V = V16<T>::n;
+  for (int j = threadIdx.x * V; j < d; j += kThreads * V) {
+    float acc[V], v[V];
+    V16<T>::load(dout + t * d + j, v);
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[e] = c * v[e];
+    for (int r = 0; r < K; ++r) {
+      const int q = s_inv[r];
+      if (q < 0) continue;
+      V16<T>::load(dxp + static_cast<int64_t>(q) * d + j, v);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += v[e];
+    }
+    V16<T>::load(dxr + t * d + j, v);
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[e] += v[e];
+    V16<T>::store(dx + t * d + j, acc);
+  }
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_combine(const T* x, const T* y, const int32_t* topk_idx, const float* gate,
+                          const int32_t* inv, int Tn, int d, int N, int K, float out_scale, T* out,
+                          hipStream_t s) {
+  if (Tn == 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel<T>, dim3(Tn), dim3(kThreads), 0, s, x, y, topk_idx, gate, inv,
+                     d, N, K, out_scale, out);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_combine_bwd(const T* x, const T* y, const T* dout, const float* logits,
+                              const int32_t* topk_idx, const float* gate, const int32_t* inv,
+                              int Tn, int d, int N, int E, int K, int gate_norm, float out_scale,
+                              T* dyg, float* dg, T* dl, int ldl, hipStream_t s) {
+  if (Tn == 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_bwd_kernel<T>, dim3(Tn), dim3(kThreads), 0, s, x, y, dout, logits,
+                     topk_idx, gate, inv, d, N, E, K, gate_norm, out_scale, dyg, dg, dl, ldl);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dx_gather(const T* dout, const T* dxp, const T* dxr, const int32_t* topk_idx,
+                            const float* gate, const int32_t* inv, int Tn, int d, int N, int K,
+                            float out_scale, T* dx, hipStream_t s) {
+  if (Tn == 0) return hipSuccess;
+  hipLaunchKernelGGL(dx_gather_kernel<T>, dim3(Tn), dim3(kThreads), 0, s, dout, dxp, dxr, topk_idx,
+                     gate, inv, d, N, K, out_scale, dx);
+  return hipGetLastError();
+}
+
+#define ZC_INST(T)                                                                              \
+  template hipError_t launch_combine<T>(const T*, const T*, const int32_t*, const float*,       \
+                                        const int32_t*, int, int, int, int, float, T*,          \
+                                        hipStream_t);                                           \
+  template hipError_t launch_combine_bwd<T>(const T*, const T*, const T*, const float*,         \
+                                            const int32_t*, const float*, const int32_t*, int,  \
+                                            int, int, int, int, int, float, T*, float*, T*,     \
+                                            int, hipStream_t);                                  \
+  template hipError_t launch_dx_gather<T>(const T*, const T*, const T*, const int32_t*,         \
+                                          const float*, const int32_t*, int, int, int, int,     \
+                                          float, T*, hipStream_t);
+ZC_INST(bf16_t)
+ZC_INST(float)
+#undef ZC_INST
+
+}  // namespace zc

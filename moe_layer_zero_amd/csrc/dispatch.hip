@@ -1,0 +1,183 @@
+// Dispatch: per-expert token counts (the T_i of Eq.(2), "LongCat-Flash
+// Technical Report" section 2.1.1), their prefix sum over the FFN experts,
+// and the canonical dispatch order perm = FFN picks sorted by
+// (expert, token), with its inverse.
+//
+// Each token picks an expert at most once, so (expert, token) keys are
+// unique and a stable order needs no sort: tokens are cut into blocks of 64;
+// a block records, per expert, the 64-bit mask of its tokens that picked the
+// expert.  The rank of a pick inside its expert's segment is then
+//   (picks of that expert in earlier blocks) + popcount(mask & lower tokens),
+// which is exact integer work with no atomics on the order.
+#include "zc_common.h"
+
+namespace zc {
+namespace {
+
+constexpr int kTokPerBlk = 64;
+constexpr int kThreads = 256;
+
+struct Scratch {
+  uint64_t* mask;  // [nblk][E]
+  int32_t* cnt;    // [nblk][E]
+  int32_t* base;   // [nblk][E]
+};
+
+__host__ __device__ inline int64_t align256(int64_t b) { return (b + 255) & ~int64_t(255); }
+
+Scratch carve(void* p, int64_t nblk, int64_t E) {
+  char* c = static_cast<char*>(p);
+  Scratch s;
+  s.mask = reinterpret_cast<uint64_t*>(c);
+  c += align256(nblk * E * 8);
+  s.cnt = reinterpret_cast<int32_t*>(c);
+  c += align256(nblk * E * 4);
+  s.base = reinterpret_cast<int32_t*>(c);
+  return s;
+}
+
+__global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restrict__ topk_idx,
+                                                        int Tn, int E, int K, uint64_t* mask,
+                                                        int32_t* cnt) {
+  extern __shared__ uint64_t smask[];
+  const int b = blockIdx.x;
+  const int t0 = b * kTokPerBlk;
+  const int nt = min(kTokPerBlk, Tn - t0);
+  for (int e = threadIdx.x; e < E; e += kThreads) smask[e] = 0;
+  __syncthreads();
+  const int n = nt * K;
+  const int32_t* idx = topk_idx + static_cast<int64_t>(t0) * K;
+  for (int i = threadIdx.x; i < n; i += kThreads)
+    atomicOr(reinterpret_cast<unsigned long long*>(&smask[idx[i]]), 1ull << (i / K));
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    const uint64_t m = smask[e];
+    mask[static_cast<int64_t>(b) * E + e] = m;
+    cnt[static_cast<int64_t>(b) * E + e] = __popcll(m);
+  }
+}
+
+// One block of 1024 threads (E <= 1024): counts, offsets, tile prefix and
+// per-(block, expert) bases.
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ cnt, int nblk,
+                                                    int E, int N, int bm, int32_t* counts,
+                                                    int32_t* offsets, int32_t* tile_off,
+                                                    int32_t* base) {
+  __shared__ int32_t s_off[1024];
+  __shared__ int32_t s_til[1024];
+  const int e = threadIdx.x;
+  int32_t tot = 0;
+  if (e < E)
+    for (int b = 0; b < nblk; ++b) tot += cnt[static_cast<int64_t>(b) * E + e];
+  if (e < E) counts[e] = tot;
+  // inclusive scans over FFN experts (Hillis-Steele; integer, order-free)
+  s_off[e] = (e < N) ? tot : 0;
+  s_til[e] = (e < N) ? (tot + bm - 1) / bm : 0;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int32_t a = e >= o ? s_off[e - o] : 0;
+    const int32_t c = e >= o ? s_til[e - o] : 0;
+    __syncthreads();
+    s_off[e] += a;
+    s_til[e] += c;
+    __syncthreads();
+  }
+  const int32_t excl = (e > 0 && e <= N) ? s_off[e - 1] : 0;
+  if (e < N) {
+    offsets[e] = excl;
+    tile_off[e] = e > 0 ? s_til[e - 1] : 0;
+  }
+  if (e == 0) {
+    offsets[N] = N > 0 ? s_off[N - 1] : 0;
+    tile_off[N] = N > 0 ? s_til[N - 1] : 0;
+  }
+  if (e < N) {
+    int32_t run = excl;
+    for (int b = 0; b < nblk; ++b) {
+      const int64_t o = static_cast<int64_t>(b) * E + e;
+      base[o] = run;
+      run += cnt[o];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __restrict__ topk_idx,
+                                                           int Tn, int E, int N, int K,
+                                                           const uint64_t* __restrict__ mask,
+                                                           const int32_t* __restrict__ base,
+                                                           int32_t* perm, int32_t* inv) {
+  extern __shared__ uint64_t smask[];
+  const int b = blockIdx.x;
+  const int t0 = b * kTokPerBlk;
+  const int nt = min(kTokPerBlk, Tn - t0);
+  for (int e = threadIdx.x; e < E; e += kThreads) smask[e] = mask[static_cast<int64_t>(b) * E + e];
+  __syncthreads();
+  const int n = nt * K;
+  const int64_t s0 = static_cast<int64_t>(t0) * K;
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const int e = topk_idx[s0 + i];
+    if (e >= N) {
+      inv[s0 + i] = -1;
+      continue;
+    }
+    const int tl = i / K;
+    const uint64_t below = tl == 0 ? 0ull : (smask[e] & ((1ull << tl) - 1ull));
+    const int32_t pos = base[static_cast<int64_t>(b) * E + e] + __popcll(below);
+    perm[pos] = static_cast<int32_t>(s0 + i);
+    inv[s0 + i] = pos;
+  }
+}
+
+__global__ __launch_bounds__(1024) void tile_off_kernel(const int32_t* __restrict__ offsets, int N,
+                                                       int bm, int32_t* tile_off) {
+  __shared__ int32_t s_til[1024];
+  const int e = threadIdx.x;
+  const int32_t w = e < N ? (offsets[e + 1] - offsets[e] + bm - 1) / bm : 0;
+  s_til[e] = w;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int32_t c = e >= o ? s_til[e - o] : 0;
+    __syncthreads();
+    s_til[e] += c;
+    __syncthreads();
+  }
+  if (e < N) tile_off[e] = s_til[e] - w;
+  if (e == 0) tile_off[N] = N > 0 ? s_til[N - 1] : 0;
+}
+
+}  // namespace
+
+hipError_t launch_tile_offsets(const int32_t* offsets, int N, int bm, int32_t* tile_off,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(tile_off_kernel, dim3(1), dim3(1024), 0, s, offsets, N, bm, tile_off);
+  return hipGetLastError();
+}
+
+size_t dispatch_scratch_bytes(int64_t Tn, int64_t E, int64_t N) {
+  (void)N;
+  const int64_t nblk = (Tn + kTokPerBlk - 1) / kTokPerBlk;
+  return static_cast<size_t>(align256(nblk * E * 8) + align256(nblk * E * 4) +
+                             align256(nblk * E * 4));
+}
+
+hipError_t launch_dispatch(const int32_t* topk_idx, int Tn, int E, int N, int K, int bm,
+                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                           int32_t* tile_off, void* scratch, hipStream_t s) {
+  const int nblk = (Tn + kTokPerBlk - 1) / kTokPerBlk;
+  Scratch sc = carve(scratch, nblk, E);
+  if (nblk > 0) {
+    hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kThreads), E * sizeof(uint64_t), s,
+                       topk_idx, Tn, E, K, sc.mask, sc.cnt);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, sc.cnt, nblk, E, N, bm, counts,
+                     offsets, tile_off, sc.base);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || nblk == 0) return err;
+  hipLaunchKernelGGL(scatter_kernel, dim3(nblk), dim3(kThreads), E * sizeof(uint64_t), s,
+                     topk_idx, Tn, E, N, K, sc.mask, sc.base, perm, inv);
+  return hipGetLastError();
+}
+
+}  // namespace zc

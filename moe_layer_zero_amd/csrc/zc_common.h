@@ -1,0 +1,126 @@
+// Internal declarations shared by the HIP translation units of libzcmoe.
+// Device helpers (bf16 <-> fp32, MFMA operand types) and the host-side
+// launcher interfaces that api.hip sequences.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zc {
+
+// ---------------------------------------------------------------- types
+typedef uint16_t bf16_t;  // storage of a bfloat16 (upper half of an fp32)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(bf16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN stays NaN).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return static_cast<bf16_t>((u >> 16) | ((u & 0xffff) ? 0x40 : 0));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+  static constexpr int kVec = 4;  // elements per 16-byte chunk
+};
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float ld(const bf16_t* p) { return bf2f(*p); }
+  static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = f2bf(v); }
+  static constexpr int kVec = 8;
+};
+
+// Row-tile height of the grouped GEMMs; the dispatch step publishes the
+// per-expert prefix of ceil(rows / kGemmBM) tiles for them.
+constexpr int kGemmBM = 128;
+
+// ---------------------------------------------------------------- launchers
+// Every launcher queues work on `s` and returns the hipError_t of the launch.
+
+// F1: logits[T][E] = x[T][d] * wr[E][d]^T (fp32 out).
+template <typename T>
+hipError_t launch_router_gemm(const T* x, const T* wr, float* logits, int Tn, int E, int d,
+                              int cu_count, hipStream_t s);
+
+// F2: routing keys, biased top-K, gates (one wavefront per token).
+hipError_t launch_topk(const float* logits, const float* bias, int Tn, int E, int K,
+                       int gate_norm, int32_t* topk_idx, float* topk_gate, hipStream_t s);
+
+// F3: per-expert counts, offsets, canonical permutation and its inverse.
+// Scratch: dispatch_scratch_bytes(T, E, N).  Also writes the per-expert
+// m-tile prefix tile_off[N+1] for the grouped GEMMs (tile height `bm`).
+size_t dispatch_scratch_bytes(int64_t Tn, int64_t E, int64_t N);
+hipError_t launch_dispatch(const int32_t* topk_idx, int Tn, int E, int N, int K, int bm,
+                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                           int32_t* tile_off, void* scratch, hipStream_t s);
+
+// tile_off[N+1] from offsets[N+1] (for a backward call that only has the
+// routing of its forward call).
+hipError_t launch_tile_offsets(const int32_t* offsets, int N, int bm, int32_t* tile_off,
+                               hipStream_t s);
+
+// Grouped / dense GEMMs (gemm.hip).  See the mode list there.
+template <typename T>
+hipError_t launch_ffn_gateup(const T* x, const T* wg, const T* wu, const int32_t* offsets,
+                             const int32_t* perm, const int32_t* tile_off, int N, int I, int d,
+                             int K, int64_t max_rows, T* h, T* save_a, T* save_u, int cu_count,
+                             hipStream_t s);
+template <typename T>
+hipError_t launch_ffn_down(const T* h, const T* wd, const int32_t* offsets,
+                           const int32_t* tile_off, int N, int I, int d, int64_t max_rows, T* y,
+                           int cu_count, hipStream_t s);
+template <typename T>
+hipError_t launch_bwd_down_dh(const T* dyg, const T* wd, const T* sa, const T* su,
+                              const int32_t* offsets, const int32_t* tile_off, int N, int I,
+                              int d, int64_t max_rows, T* dadu, int cu_count, hipStream_t s);
+template <typename T>
+hipError_t launch_bwd_down_dw(const T* dyg, const T* h, const int32_t* offsets, int N, int I,
+                              int d, T* dwd, int cu_count, hipStream_t s);
+template <typename T>
+hipError_t launch_bwd_gateup_dx(const T* dadu, const T* wg, const T* wu, const int32_t* offsets,
+                                const int32_t* tile_off, int N, int I, int d, int64_t max_rows,
+                                T* dxp, int cu_count, hipStream_t s);
+template <typename T>
+hipError_t launch_bwd_gateup_dw(const T* dadu, const T* x, const int32_t* offsets,
+                                const int32_t* perm, int N, int I, int d, int K, T* dwg, T* dwu,
+                                int cu_count, hipStream_t s);
+template <typename T>
+hipError_t launch_router_dw(const T* dl, int ldl, const T* x, int Tn, int E, int d, T* dwr,
+                            int cu_count, hipStream_t s);
+template <typename T>
+hipError_t launch_router_dx(const T* dl, int ldl, const T* wr, int Tn, int E, int d, T* dxr,
+                            int cu_count, hipStream_t s);
+
+// F6: out = out_scale * (c_t x_t + sum_r g_r y[inv]).
+template <typename T>
+hipError_t launch_combine(const T* x, const T* y, const int32_t* topk_idx, const float* gate,
+                          const int32_t* inv, int Tn, int d, int N, int K, float out_scale,
+                          T* out, hipStream_t s);
+
+// B1 + router part of B5: dg, gated dy in dispatch order, dl [T][ldl].
+template <typename T>
+hipError_t launch_combine_bwd(const T* x, const T* y, const T* dout, const float* logits,
+                              const int32_t* topk_idx, const float* gate, const int32_t* inv,
+                              int Tn, int d, int N, int E, int K, int gate_norm, float out_scale,
+                              T* dyg, float* dg, T* dl, int ldl, hipStream_t s);
+
+// B6: dx = out_scale * c_t * dout_t + sum_r dxp[inv] + dxr_t.
+template <typename T>
+hipError_t launch_dx_gather(const T* dout, const T* dxp, const T* dxr, const int32_t* topk_idx,
+                            const float* gate, const int32_t* inv, int Tn, int d, int N, int K,
+                            float out_scale, T* dx, hipStream_t s);
+
+// P1: Eq.(2).
+hipError_t launch_pid(int N, int K, const int32_t* counts, int64_t T_all, double mu, double K_e,
+                      float* bias, hipStream_t s);
+
+}  // namespace zc

@@ -38,6 +38,8 @@ def lib():
                                   _p, _p, _i64, _p, _p, _p]
         L.orc_backward.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i32, _i32, _f64, _p, _p,
                                    _p, _p, _p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _p]
+        L.orc_num_threads.restype = C.c_int
+        L.orc_num_threads.argtypes = []
         L.orc_pid_update.argtypes = [_i64, _i64, _i64, _p, _i64, _f64, _f64, _p]
         for f in ("orc_logits", "orc_route", "orc_forward", "orc_backward", "orc_pid_update"):
             getattr(L, f).restype = C.c_int
@@ -62,6 +64,10 @@ def _c(a, dtype=None):
         return None
     a = np.ascontiguousarray(a if dtype is None else a.astype(dtype, copy=False))
     return a
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
 
 
 def exp(z: float) -> float:

@@ -26,6 +26,7 @@
  * "parity unpinned".
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -91,6 +92,9 @@ static double orc_sum64(const double* e, int64_t E) {
   }
   return part[0];
 }
+
+/* Threads the OpenMP loops below will use. */
+int orc_num_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------ */
 /* O1 -- router logits l[t][j] = sum_k x[t][k] * Wr[j][k]  (k ascending).

@@ -1,0 +1,120 @@
+"""Shared plumbing of the GPU parity tests: run the HIP layer through the
+C ABI, run the fp64 oracle on the same (seeded, already rounded) inputs, and
+compare with the tolerances of the method:
+  - router scores: max|gpu - oracle| / max|oracle| <= 1e-5;
+  - routing (picked experts, counts, offsets, dispatch order, inverse):
+    bit-exact when both sides route the same scores;
+  - fp32 layers: max|gpu - oracle| / max|oracle| <= 1e-4;
+  - bf16 layers: max|gpu - oracle| <= 2e-2 * RMS(oracle).
+When the GPU routes its own fp32 scores and the oracle its own fp64 scores,
+a token whose top-K boundary is closer than the score tolerance allows may
+legitimately pick differently; such tokens are checked for validity (the
+GPU's picks are all within that margin of the oracle's boundary) and left
+out of the element-wise output comparison.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from moe_layer_zero_amd import synth, zcmoe
+from oracle import oracle
+
+LOGIT_RTOL = 1e-5
+F32_RTOL = 1e-4
+BF16_RMS_TOL = 2e-2
+
+
+def desc_of(sh: synth.LayerShape, gate_norm=1, out_scale=1.0) -> zcmoe.LayerDesc:
+    return zcmoe.LayerDesc(sh.T, sh.d, sh.N, sh.Z, sh.I, sh.K, sh.torch_dtype, gate_norm,
+                           out_scale)
+
+
+def to_dev(L: dict, dev="cuda") -> dict:
+    return {k: v.to(dev) for k, v in L.items()}
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return synth.to_np(t)
+
+
+def run_forward(desc, Lg, saved=False):
+    route = zcmoe.RouteBuffers(desc)
+    out = torch.empty((desc.T, desc.d), dtype=desc.dtype, device="cuda")
+    sv = zcmoe.saved_buffer(desc) if saved else None
+    zcmoe.zc_moe_forward(desc, Lg["x"], Lg["wr"], Lg["bias"], Lg.get("wg"), Lg.get("wu"),
+                         Lg.get("wd"), out, route, sv)
+    torch.cuda.synchronize()
+    return route, out, sv
+
+
+def run_backward(desc, Lg, route, saved, dout):
+    g = {
+        "dx": torch.empty_like(Lg["x"]),
+        "dwr": torch.empty_like(Lg["wr"]),
+        "dwg": torch.empty_like(Lg["wg"]),
+        "dwu": torch.empty_like(Lg["wu"]),
+        "dwd": torch.empty_like(Lg["wd"]),
+    }
+    zcmoe.zc_moe_backward(desc, Lg["x"], Lg["wr"], Lg["wg"], Lg["wu"], Lg["wd"], route, saved,
+                          dout, g["dx"], g["dwr"], g["dwg"], g["dwu"], g["dwd"])
+    torch.cuda.synchronize()
+    return g
+
+
+def f64(a) -> np.ndarray:
+    if isinstance(a, torch.Tensor):
+        return a.detach().double().cpu().numpy()
+    return synth.as_f64(np.asarray(a))
+
+
+def assert_logits(gpu: torch.Tensor, orc: np.ndarray):
+    g = f64(gpu)
+    err = np.abs(g - orc).max()
+    ref = np.abs(orc).max()
+    assert err <= LOGIT_RTOL * ref, f"router scores: max err {err:.3e} vs {LOGIT_RTOL} * {ref:.3e}"
+    return err / ref
+
+
+def assert_close(gpu, orc: np.ndarray, dtype, what: str):
+    g = f64(gpu)
+    assert g.shape == orc.shape, (what, g.shape, orc.shape)
+    err = float(np.abs(g - orc).max()) if g.size else 0.0
+    if dtype == torch.float32:
+        ref = float(np.abs(orc).max()) if orc.size else 0.0
+        assert err <= F32_RTOL * max(ref, 1e-30), f"{what}: max err {err:.3e}, max|ref| {ref:.3e}"
+        return err / max(ref, 1e-30)
+    rms = float(np.sqrt(np.mean(orc * orc))) if orc.size else 0.0
+    assert err <= BF16_RMS_TOL * max(rms, 1e-30), f"{what}: max err {err:.3e}, rms {rms:.3e}"
+    return err / max(rms, 1e-30)
+
+
+def routing_agreement(gpu_idx: np.ndarray, orc_keys: np.ndarray, orc_idx: np.ndarray, lg_orc,
+                      K: int, toks=None):
+    """Tokens whose picks match exactly; asserts every other token is a
+    near-tie under the score tolerance.  Returns (same mask, n_ambiguous)."""
+    T = orc_idx.shape[0]
+    gpu_idx = gpu_idx.astype(np.int64)
+    lg_max = np.abs(lg_orc).max()
+    same = (gpu_idx == orc_idx).all(1)
+    bad = np.flatnonzero(~same)
+    for t in bad:
+        k = orc_keys[t]
+        kth = k[orc_idx[t, K - 1]]
+        # a score change eps moves a softmax value p_j by about 2 eps p_j, so
+        # a pick can flip only where keys are closer than ~4 eps p_max
+        delta = 8.0 * LOGIT_RTOL * lg_max * _pmax(lg_orc[t])
+        picks = gpu_idx[t]
+        assert len(set(picks.tolist())) == K, f"token {t}: repeated pick"
+        for j in picks:
+            assert k[j] >= kth - delta, (
+                f"token {t}: GPU pick {j} key {k[j]:.17g} is below the oracle's K-th key "
+                f"{kth:.17g} by more than the tolerance margin {delta:.3e}")
+        for a, b in zip(picks[:-1], picks[1:]):
+            assert k[a] >= k[b] - delta, f"token {t}: GPU slot order contradicts the keys"
+    return same, len(bad)
+
+
+def _pmax(lg_row: np.ndarray) -> float:
+    e = np.exp(lg_row - lg_row.max())
+    return float(e.max() / e.sum())

@@ -1,0 +1,137 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes its buffers, and rejects bad arguments with the
+documented status codes before queuing any work."""
+import ctypes as C
+import os
+import re
+
+import pytest
+import torch
+
+from moe_layer_zero_amd import zcmoe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(zc_[a-z_0-9]+)\s*\(", src))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    return zcmoe.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert names == set(zcmoe.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def desc(**kw):
+    base = dict(T=64, d=128, N=8, Z=4, I=64, K=2, dtype=torch.float32)
+    base.update(kw)
+    return zcmoe.LayerDesc(**base)
+
+
+def test_sizes_are_positive_and_grow_with_T():
+    for dt in (torch.float32, torch.bfloat16):
+        a = desc(dtype=dt)
+        b = desc(dtype=dt, T=4096)
+        for op in (zcmoe.ZC_OP_ROUTE, zcmoe.ZC_OP_FORWARD, zcmoe.ZC_OP_BACKWARD):
+            assert 0 < zcmoe.zc_moe_workspace_size(a, op) < zcmoe.zc_moe_workspace_size(b, op)
+        assert 0 < zcmoe.zc_moe_saved_size(a) < zcmoe.zc_moe_saved_size(b)
+    # an invalid description sizes to 0
+    assert zcmoe.zc_moe_workspace_size(desc(K=0), zcmoe.ZC_OP_FORWARD) == 0
+    assert zcmoe.zc_moe_workspace_size(desc(), 7) == 0
+
+
+# Fake, 256-byte aligned, never dereferenced device addresses: every call
+# below fails its host-side checks before any work is queued.
+FAKE = C.c_void_p(1 << 20)
+
+
+def route_buf():
+    return zcmoe.zc_route_buf(*([FAKE] * 7))
+
+
+def call_route(L, d, ws_bytes=1 << 30, **over):
+    args = dict(x=FAKE, wr=FAKE, bias=FAKE, r=route_buf(), ws=FAKE)
+    args.update(over)
+    dd = d.c() if d is not None else None
+    return L.zc_moe_route(C.byref(dd) if dd is not None else None, args["x"], args["wr"],
+                          args["bias"], C.byref(args["r"]), args["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(K=0), zcmoe.ZC_ERR_INVALID),
+    (dict(K=13), zcmoe.ZC_ERR_INVALID),        # K > N+Z
+    (dict(N=0, Z=0), zcmoe.ZC_ERR_INVALID),
+    (dict(N=1000, Z=100), zcmoe.ZC_ERR_INVALID),  # N+Z > 1024
+    (dict(T=-1), zcmoe.ZC_ERR_INVALID),
+    (dict(d=100), zcmoe.ZC_ERR_UNSUPPORTED),
+    (dict(dtype=torch.bfloat16, d=96), zcmoe.ZC_ERR_UNSUPPORTED),
+    (dict(dtype=torch.bfloat16, I=32), zcmoe.ZC_ERR_UNSUPPORTED),
+    (dict(gate_norm=2), zcmoe.ZC_ERR_INVALID),
+    (dict(out_scale=float("nan")), zcmoe.ZC_ERR_INVALID),
+])
+def test_bad_descriptions(L, bad, code):
+    assert call_route(L, desc(**bad)) == code
+    assert L.zc_last_error().decode() != ""
+
+
+def test_bad_pointers_and_workspace(L):
+    d = desc()
+    assert call_route(L, None) == zcmoe.ZC_ERR_INVALID
+    assert call_route(L, d, bias=None) == zcmoe.ZC_ERR_INVALID
+    assert call_route(L, d, x=None) == zcmoe.ZC_ERR_INVALID       # x without w_router
+    assert call_route(L, d, x=C.c_void_p((1 << 20) + 4)) == zcmoe.ZC_ERR_INVALID  # misaligned
+    r = route_buf()
+    r.perm = None
+    assert call_route(L, d, r=r) == zcmoe.ZC_ERR_INVALID
+    need = zcmoe.zc_moe_workspace_size(d, zcmoe.ZC_OP_ROUTE)
+    assert call_route(L, d, ws_bytes=need - 1) == zcmoe.ZC_ERR_WORKSPACE
+    assert "needed" in L.zc_last_error().decode()
+    assert call_route(L, d, ws=None) == zcmoe.ZC_ERR_WORKSPACE
+
+
+def test_forward_backward_argument_checks(L):
+    d = desc()
+    dd = d.c()
+    r = route_buf()
+    big = 1 << 40
+    # N > 0 needs the expert weights
+    st = L.zc_moe_forward(C.byref(dd), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, C.byref(r), None,
+                          FAKE, big, None)
+    assert st == zcmoe.ZC_ERR_INVALID and "w_gate" in L.zc_last_error().decode()
+    st = L.zc_moe_forward(C.byref(dd), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, C.byref(r), None,
+                          FAKE, 16, None)
+    assert st == zcmoe.ZC_ERR_WORKSPACE
+    # backward needs the saved activations
+    st = L.zc_moe_backward(C.byref(dd), FAKE, FAKE, FAKE, FAKE, FAKE, C.byref(r), None, FAKE, FAKE,
+                           FAKE, FAKE, FAKE, FAKE, FAKE, big, None)
+    assert st == zcmoe.ZC_ERR_INVALID and "saved" in L.zc_last_error().decode()
+    # Eq.(2) update: T_all >= 1
+    st = L.zc_moe_pid_update(8, 4, 2, FAKE, 0, 1.0, 1.5, FAKE, None)
+    assert st == zcmoe.ZC_ERR_INVALID
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert L.zc_status_string(s)
+    assert L.zc_status_string(99) == b"unknown status"
+
+
+def test_binding_rejects_host_tensors():
+    d = desc()
+    x = torch.zeros(64, 128)
+    with pytest.raises((ValueError, zcmoe.ZcError)):
+        zcmoe.zc_moe_route(d, x, torch.zeros(12, 128), torch.zeros(12),
+                           zcmoe.RouteBuffers(d, device="cpu"), ws=x)

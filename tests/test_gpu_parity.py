@@ -1,0 +1,267 @@
+"""GPU parity: the HIP layer, called through the C ABI, against the fp64
+oracle on the same seeded inputs (tolerances in gpu_harness).
+
+Layer: "LongCat-Flash Technical Report", section 2.1, Eq.(1) (router,
+biased top-K, unbiased gates, zero-computation experts returning x) and
+section 2.1.1, Eq.(2) (bias update).  Shapes are the five workloads of
+moe_layer_zero_amd.synth plus edge cases (one token, ragged token counts,
+K = 1, K = E, E = 1024, no FFN experts, no zero-computation experts).
+"""
+import numpy as np
+import pytest
+import torch
+
+from moe_layer_zero_amd import synth, zcmoe
+from oracle import oracle
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+CF = synth.CONFIGS
+
+
+def logit_std(sh):
+    return sh.w_std * sh.d ** 0.5
+
+
+# ------------------------------------------------------------ routing from given scores
+ROUTE_CASES = [
+    # (name, T, N, Z, K, bias kind, std, gate_norm)
+    ("tiny", 64, 8, 4, 2, "zero", 0.23, 1),
+    ("tiny_literal", 64, 8, 4, 2, "uniform", 0.23, 0),
+    ("small", 4096, 64, 32, 6, "uniform", 0.64, 1),
+    ("decode", 256, 512, 256, 12, "zero", 0.47, 1),
+    ("prefill", 16384, 512, 256, 12, "zipf", 0.47, 1),
+    ("train", 8192, 128, 64, 8, "zero", 0.9, 1),
+    ("one_token", 1, 512, 256, 12, "zipf", 0.47, 1),
+    ("ragged", 65, 64, 32, 6, "uniform", 0.64, 1),
+    ("k1", 333, 40, 24, 1, "uniform", 1.0, 1),
+    ("k_eq_e", 100, 9, 3, 12, "uniform", 1.0, 1),
+    ("e1024", 300, 1024, 0, 32, "uniform", 0.5, 1),
+    ("no_ffn", 200, 0, 16, 4, "uniform", 0.5, 1),
+    ("no_identity", 500, 96, 0, 6, "uniform", 0.5, 0),
+    ("ties", 128, 24, 8, 5, "ties", 0.5, 1),
+]
+
+
+def make_bias(kind, N, Z, seed):
+    E = N + Z
+    g = torch.Generator().manual_seed(seed)
+    if kind == "zero":
+        return torch.zeros(E)
+    if kind == "uniform":
+        return torch.rand(E, generator=g) * 0.2 - 0.1
+    if kind == "zipf":
+        b = torch.zeros(E, dtype=torch.float64)
+        b[:N] = synth.ZIPF_B0 * (torch.randperm(N, generator=g) + 1).double() ** -synth.ZIPF_S
+        return b.float()
+    if kind == "ties":  # groups of experts with identical bias
+        return (torch.randint(0, 3, (E,), generator=g) * 0.01).float()
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
+def test_route_given_scores_is_bit_exact(case):
+    name, T, N, Z, K, kind, std, gate_norm = case
+    E = N + Z
+    print(f"[route] {name} T={T} N={N} Z={Z} K={K}", flush=True)
+    lg = synth.make_logits(T, E, std, 7_000 + T)
+    if kind == "ties":  # duplicate score columns as well
+        lg[:, 1::4] = lg[:, 0::4][:, : lg[:, 1::4].shape[1]]
+    bias = make_bias(kind, N, Z, 11 + T)
+    desc = zcmoe.LayerDesc(T, 64, N, Z, 64, K, torch.bfloat16, gate_norm)
+    route = zcmoe.RouteBuffers(desc)
+    route.logits.copy_(lg)
+    zcmoe.zc_moe_route(desc, None, None, bias.cuda(), route)
+    torch.cuda.synchronize()
+    o = oracle.route(lg.numpy(), bias.numpy(), N, K, gate_norm=gate_norm, want_keys=False)
+    np.testing.assert_array_equal(route.topk_idx.cpu().numpy(), o.topk_idx)
+    np.testing.assert_array_equal(route.topk_gate.cpu().numpy(), o.gates.astype(np.float32))
+    np.testing.assert_array_equal(route.counts.cpu().numpy(), o.counts)
+    np.testing.assert_array_equal(route.offsets.cpu().numpy(), o.offsets)
+    P = o.p_real
+    np.testing.assert_array_equal(route.perm.cpu().numpy()[:P], o.perm)
+    np.testing.assert_array_equal(route.inv.cpu().numpy()[: T * K], o.inv)
+
+
+def test_route_is_deterministic_and_t0_is_a_no_op():
+    T, N, Z, K = 4096, 64, 32, 6
+    desc = zcmoe.LayerDesc(T, 64, N, Z, 64, K, torch.bfloat16)
+    lg = synth.make_logits(T, N + Z, 0.6, 99).cuda()
+    bias = make_bias("uniform", N, Z, 5).cuda()
+    outs = []
+    for _ in range(2):
+        r = zcmoe.RouteBuffers(desc)
+        r.logits.copy_(lg)
+        zcmoe.zc_moe_route(desc, None, None, bias, r)
+        torch.cuda.synchronize()
+        outs.append([getattr(r, f).cpu() for f in ("topk_idx", "topk_gate", "perm", "inv")])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    d0 = zcmoe.LayerDesc(0, 64, N, Z, 64, K, torch.bfloat16)
+    r0 = zcmoe.RouteBuffers(d0)
+    zcmoe.zc_moe_route(d0, None, None, bias, r0)
+    torch.cuda.synchronize()
+    assert r0.counts.sum().item() == 0 and r0.offsets.abs().sum().item() == 0
+
+
+# ------------------------------------------------------------ Eq.(2)
+@pytest.mark.parametrize("N,Z,K,T,mu,Ke", [(128, 64, 8, 8192, 1.0, 6.0), (512, 256, 12, 256, 0.3, 8.0),
+                                          (7, 0, 3, 5, 2.5, 1.5)])
+def test_pid_update_is_bit_exact(N, Z, K, T, mu, Ke):
+    g = torch.Generator().manual_seed(N + T)
+    counts = torch.randint(0, 2 * T * K // max(N + Z, 1) + 2, (N + Z,), generator=g, dtype=torch.int32)
+    bias = torch.randn(N + Z, generator=g) * 0.01
+    b = bias.cuda()
+    zcmoe.zc_moe_pid_update(N, Z, K, counts.cuda(), T, mu, Ke, b)
+    torch.cuda.synchronize()
+    want = oracle.pid_update(counts.numpy(), T, bias.numpy(), N, Z, K, mu, Ke)
+    np.testing.assert_array_equal(b.cpu().numpy(), want)
+
+
+# ------------------------------------------------------------ forward, small layers
+def forward_case(sh, gate_norm=1, out_scale=1.0, bias=None, toks=None):
+    L = synth.make_layer(sh, "cpu")
+    if bias is not None:
+        L["bias"] = bias
+    Lg = H.to_dev(L)
+    desc = H.desc_of(sh, gate_norm, out_scale)
+    print(f"[forward] {sh.name} T={sh.T} gate_norm={gate_norm}", flush=True)
+    route, out, _ = H.run_forward(desc, Lg)
+    xh, wrh = H.host(L["x"]), H.host(L["wr"])
+    lg = oracle.logits(xh, wrh)
+    H.assert_logits(route.logits, lg)
+    o = oracle.route(lg, L["bias"].numpy(), sh.N, sh.K, gate_norm=gate_norm)
+    same, namb = H.routing_agreement(route.topk_idx.cpu().numpy(), o.keys, o.topk_idx, lg, sh.K)
+    sel = np.flatnonzero(same) if toks is None else np.array([t for t in toks if same[t]])
+    ref = oracle.forward(xh, H.host(L["wg"]), H.host(L["wu"]), H.host(L["wd"]), o.topk_idx,
+                         o.gates, sh.N, out_scale=out_scale, toks=sel)
+    err = H.assert_close(out[torch.from_numpy(sel).cuda()], ref, sh.torch_dtype, "layer output")
+    print(f"  ambiguous tokens {namb}, checked {len(sel)}, err {err:.3e}", flush=True)
+    return L, Lg, desc, route, out, o
+
+
+def test_forward_tiny_fp32():
+    forward_case(CF["tiny_fp32"])
+
+
+def test_forward_tiny_fp32_literal_gates_and_scale():
+    forward_case(CF["tiny_fp32"], gate_norm=0, out_scale=1.7)
+
+
+def test_forward_small_bf16():
+    forward_case(CF["small_bf16"])
+
+
+def test_forward_ragged_bf16():
+    # several row tiles per expert plus ragged tails
+    sh = CF["small_bf16"].with_T(1000)
+    forward_case(sh, bias=torch.zeros(sh.E))
+
+
+def test_forward_all_zero_computation_picks():
+    sh = CF["small_bf16"].with_T(300)
+    b = torch.zeros(sh.E)
+    b[sh.N:] = 1.0
+    L, Lg, desc, route, out, o = forward_case(sh, bias=b)
+    assert route.offsets[-1].item() == 0
+    # out = (sum of gates = 1) * x, up to the fp32 gate sum and bf16 rounding
+    torch.testing.assert_close(out.float(), Lg["x"].float(), rtol=1e-2, atol=0)
+
+
+def test_forward_single_expert_mlp():
+    sh = synth.LayerShape("mlp", 9, 200, 256, 1, 0, 128, 1, "bf16", 0.05, "zero")
+    forward_case(sh)
+
+
+def test_forward_dense_mixture_k_equals_e():
+    sh = synth.LayerShape("dense", 9, 130, 128, 6, 2, 64, 8, "f32", 0.05, "uniform")
+    forward_case(sh)
+
+
+def test_forward_is_deterministic():
+    sh = CF["small_bf16"]
+    Lg = H.to_dev(synth.make_layer(sh, "cpu"))
+    desc = H.desc_of(sh)
+    _, a, _ = H.run_forward(desc, Lg)
+    _, b, _ = H.run_forward(desc, Lg)
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------ forward, LongCat-Flash shapes
+def big_case(sh, n_logit_tok=256, n_out_tok=8):
+    print(f"[forward-big] {sh.name} T={sh.T}", flush=True)
+    Lg = synth.make_layer(sh, "cuda")
+    desc = H.desc_of(sh)
+    route, out, _ = H.run_forward(desc, Lg)
+    g = torch.Generator().manual_seed(123)
+    toks = torch.randperm(sh.T, generator=g)[: min(n_logit_tok, sh.T)].sort().values.numpy()
+    xh = H.host(Lg["x"][torch.from_numpy(toks).cuda()])
+    lg = oracle.logits(xh, H.host(Lg["wr"]))
+    H.assert_logits(route.logits[torch.from_numpy(toks).cuda()], lg)
+    o = oracle.route(lg, Lg["bias"].cpu().numpy(), sh.N, sh.K)
+    gidx = route.topk_idx.cpu().numpy()[toks]
+    same, namb = H.routing_agreement(gidx, o.keys, o.topk_idx, lg, sh.K)
+    pick = [i for i in range(len(toks)) if same[i]][:n_out_tok]
+    experts = sorted({int(e) for i in pick for e in o.topk_idx[i] if e < sh.N})
+    wg = {e: H.host(Lg["wg"][e]) for e in experts}
+    wu = {e: H.host(Lg["wu"][e]) for e in experts}
+    wd = {e: H.host(Lg["wd"][e]) for e in experts}
+    ref = oracle.forward(xh, wg, wu, wd, o.topk_idx, o.gates, sh.N, toks=pick)
+    got = out[torch.from_numpy(toks[pick]).cuda()]
+    err = H.assert_close(got, ref, sh.torch_dtype, "layer output")
+    # the FFN part alone (out - c x), reported: the identity term dominates
+    print(f"  ambiguous {namb}/{len(toks)}, P_real {route.offsets[-1].item()}, "
+          f"checked {len(pick)} tokens over {len(experts)} experts, err {err:.3e}", flush=True)
+    del Lg
+    torch.cuda.empty_cache()
+
+
+def test_forward_decode_full_size():
+    big_case(CF["decode_bf16"])
+
+
+def test_forward_prefill_full_size():
+    big_case(CF["prefill_bf16"])
+
+
+# ------------------------------------------------------------ backward
+def backward_case(sh, gate_norm=1, out_scale=1.0, experts_checked=None):
+    L = synth.make_layer(sh, "cpu")
+    dY = synth.make_dy(sh)
+    Lg = H.to_dev(L)
+    desc = H.desc_of(sh, gate_norm, out_scale)
+    print(f"[backward] {sh.name} T={sh.T} gate_norm={gate_norm}", flush=True)
+    route, out, saved = H.run_forward(desc, Lg, saved=True)
+    g = H.run_backward(desc, Lg, route, saved, dY.cuda())
+    xh, wrh = H.host(L["x"]), H.host(L["wr"])
+    lg = oracle.logits(xh, wrh)
+    o = oracle.route(lg, L["bias"].numpy(), sh.N, sh.K, gate_norm=gate_norm)
+    same, namb = H.routing_agreement(route.topk_idx.cpu().numpy(), o.keys, o.topk_idx, lg, sh.K)
+    assert namb == 0, "backward parity needs identical routing; pick another seed"
+    ref = oracle.backward(xh, wrh, H.host(L["wg"]), H.host(L["wu"]), H.host(L["wd"]), lg,
+                          o.topk_idx, o.gates, H.host(dY), sh.N, sh.Z, gate_norm=gate_norm,
+                          out_scale=out_scale, want_experts=experts_checked)
+    dt = sh.torch_dtype
+    errs = {"dx": H.assert_close(g["dx"], ref["dx"], dt, "dx"),
+            "dwr": H.assert_close(g["dwr"], ref["dwr"], dt, "dW_r")}
+    es = list(ref["dwg"].keys())
+    for name, key in (("dwg", "dW_g"), ("dwu", "dW_u"), ("dwd", "dW_d")):
+        got = g[name][torch.tensor(es).cuda()]
+        want = np.stack([ref[name][e] for e in es])
+        errs[name] = H.assert_close(got, want, dt, key)
+    print("  errors " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()), flush=True)
+
+
+def test_backward_tiny_fp32():
+    backward_case(CF["tiny_fp32"])
+
+
+def test_backward_tiny_fp32_literal_gates():
+    backward_case(CF["tiny_fp32"], gate_norm=0, out_scale=0.5)
+
+
+def test_backward_train_shape_bf16():
+    # the training layer's shapes with fewer tokens, so the fp64 oracle
+    # finishes in seconds; all 128 experts' gradients compared
+    backward_case(CF["train_bf16"].with_T(256))
