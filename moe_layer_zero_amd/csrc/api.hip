@@ -151,15 +151,16 @@ zc_status check_ptr(const void* p, const char* name, bool nullable = false) {
     if (s_ != ZC_OK) return s_;       \
   } while (0)
 
-zc_status check_route(const zc_route_buf* r) {
+// Per-token buffers may be NULL when there are no tokens (T == 0).
+zc_status check_route(const zc_route_buf* r, bool no_tokens) {
   if (!r) return fail(ZC_ERR_INVALID, "route buffer is NULL");
-  ZC_CHECK(check_ptr(r->logits, "r->logits"));
-  ZC_CHECK(check_ptr(r->topk_idx, "r->topk_idx"));
-  ZC_CHECK(check_ptr(r->topk_gate, "r->topk_gate"));
+  ZC_CHECK(check_ptr(r->logits, "r->logits", no_tokens));
+  ZC_CHECK(check_ptr(r->topk_idx, "r->topk_idx", no_tokens));
+  ZC_CHECK(check_ptr(r->topk_gate, "r->topk_gate", no_tokens));
   ZC_CHECK(check_ptr(r->counts, "r->counts"));
   ZC_CHECK(check_ptr(r->offsets, "r->offsets"));
-  ZC_CHECK(check_ptr(r->perm, "r->perm"));
-  ZC_CHECK(check_ptr(r->inv, "r->inv"));
+  ZC_CHECK(check_ptr(r->perm, "r->perm", no_tokens));
+  ZC_CHECK(check_ptr(r->inv, "r->inv", no_tokens));
   return ZC_OK;
 }
 
@@ -178,19 +179,26 @@ RouteWs carve_route(char* p, const zc_moe_desc* d) {
   return w;
 }
 
+// Saved activations: a, u, h of every FFN pick in fp32 (what the backward
+// differentiates through, unrounded) and the expert outputs y in the layer
+// dtype (what the combine used).
 struct Saved {
-  void *a, *u, *h, *y;
+  float *a, *u, *h;
+  void* y;
 };
 int64_t saved_bytes(const zc_moe_desc* d) {
   const int64_t rows = d->T * d->K, es = esize(d);
-  return 3 * a256(rows * d->I * es) + a256(rows * d->d * es);
+  return 3 * a256(rows * d->I * 4) + a256(rows * d->d * es);
 }
 Saved carve_saved(char* p, const zc_moe_desc* d) {
-  const int64_t rows = d->T * d->K, es = esize(d);
-  const int64_t hi = a256(rows * d->I * es);
-  return Saved{p, p + hi, p + 2 * hi, p + 3 * hi};
+  const int64_t rows = d->T * d->K;
+  const int64_t hi = a256(rows * d->I * 4);
+  return Saved{reinterpret_cast<float*>(p), reinterpret_cast<float*>(p + hi),
+               reinterpret_cast<float*>(p + 2 * hi), p + 3 * hi};
 }
 
+// Forward scratch: routing scratch, h in the layer dtype (operand of the
+// down GEMM) and y when no saved buffer takes it.
 int64_t fwd_ws_bytes(const zc_moe_desc* d) {
   const int64_t rows = d->T * d->K, es = esize(d);
   return route_ws_bytes(d) + a256(rows * d->I * es) + a256(rows * d->d * es);
@@ -198,31 +206,30 @@ int64_t fwd_ws_bytes(const zc_moe_desc* d) {
 
 struct BwdWs {
   int32_t* tile_off;
-  void *dyg, *dl, *dadu, *dxp, *dxr;
-  float* dg;
+  float *gs, *dg, *dl, *dadu, *dxp, *dxr;
 };
 int64_t bwd_ws_bytes(const zc_moe_desc* d) {
-  const int64_t rows = d->T * d->K, es = esize(d), E = d->N + d->Z;
-  return a256(4 * (d->N + 1)) + a256(rows * d->d * es) + a256(4 * d->T * d->K) +
-         a256(d->T * ldl_of(E) * es) + a256(rows * 2 * d->I * es) + a256(rows * d->d * es) +
-         a256(d->T * d->d * es);
+  const int64_t rows = d->T * d->K, E = d->N + d->Z;
+  return a256(4 * (d->N + 1)) + a256(4 * rows) + a256(4 * d->T * d->K) +
+         a256(4 * d->T * ldl_of(E)) + a256(4 * rows * 2 * d->I) + a256(4 * rows * d->d) +
+         a256(4 * d->T * d->d);
 }
 BwdWs carve_bwd(char* p, const zc_moe_desc* d) {
-  const int64_t rows = d->T * d->K, es = esize(d), E = d->N + d->Z;
+  const int64_t rows = d->T * d->K, E = d->N + d->Z;
   BwdWs w;
   w.tile_off = reinterpret_cast<int32_t*>(p);
   p += a256(4 * (d->N + 1));
-  w.dyg = p;
-  p += a256(rows * d->d * es);
-  w.dg = reinterpret_cast<float*>(p);
-  p += a256(4 * d->T * d->K);
-  w.dl = p;
-  p += a256(d->T * ldl_of(E) * es);
-  w.dadu = p;
-  p += a256(rows * 2 * d->I * es);
-  w.dxp = p;
-  p += a256(rows * d->d * es);
-  w.dxr = p;
+  auto take = [&p](int64_t bytes) {
+    float* q = reinterpret_cast<float*>(p);
+    p += a256(bytes);
+    return q;
+  };
+  w.gs = take(4 * rows);
+  w.dg = take(4 * d->T * d->K);
+  w.dl = take(4 * d->T * ldl_of(E));
+  w.dadu = take(4 * rows * 2 * d->I);
+  w.dxp = take(4 * rows * d->d);
+  w.dxr = take(4 * d->T * d->d);
   return w;
 }
 
@@ -262,25 +269,25 @@ zc_status do_forward(const zc_moe_desc* d, const T* x, const T* wr, const float*
   const int Tn = static_cast<int>(d->T), N = static_cast<int>(d->N), K = static_cast<int>(d->K);
   const int dd = static_cast<int>(d->d), I = static_cast<int>(d->I);
   const int64_t rows = d->T * d->K;
-  T *h, *y, *sa = nullptr, *su = nullptr;
+  char* p = ws + route_ws_bytes(d);
+  T* h = reinterpret_cast<T*>(p);
+  T* y = reinterpret_cast<T*>(p + a256(rows * d->I * esize(d)));
+  float *sa = nullptr, *su = nullptr, *sh = nullptr;
   if (saved) {
     Saved sv = carve_saved(static_cast<char*>(saved), d);
-    sa = static_cast<T*>(sv.a);
-    su = static_cast<T*>(sv.u);
-    h = static_cast<T*>(sv.h);
+    sa = sv.a;
+    su = sv.u;
+    sh = sv.h;
     y = static_cast<T*>(sv.y);
-  } else {
-    char* p = ws + route_ws_bytes(d);
-    h = reinterpret_cast<T*>(p);
-    y = reinterpret_cast<T*>(p + a256(rows * d->I * esize(d)));
   }
   if (N > 0 && Tn > 0) {
     const int cu = cu_count();
-    ZC_LAUNCH(ZC_PH_GATE_UP, zc::launch_ffn_gateup<T>(x, wg, wu, r->offsets, r->perm, rw.tile_off, N, I, dd, K, rows,
-                                    h, sa, su, cu, s),
-           "gate/up GEMM launch");
-    ZC_LAUNCH(ZC_PH_DOWN, zc::launch_ffn_down<T>(h, wd, r->offsets, rw.tile_off, N, I, dd, rows, y, cu, s),
-           "down GEMM launch");
+    ZC_LAUNCH(ZC_PH_GATE_UP, zc::launch_ffn_gateup<T>(x, wg, wu, r->offsets, r->perm, rw.tile_off, N,
+                                                      I, dd, K, rows, h, sa, su, sh, cu, s),
+              "gate/up GEMM launch");
+    ZC_LAUNCH(ZC_PH_DOWN, zc::launch_ffn_down<T>(h, wd, r->offsets, rw.tile_off, N, I, dd, rows, y,
+                                                 cu, s),
+              "down GEMM launch");
   }
   ZC_LAUNCH(ZC_PH_COMBINE, zc::launch_combine<T>(x, y, r->topk_idx, r->topk_gate, r->inv, Tn, dd, N, K, d->out_scale,
                                out, s),
@@ -299,41 +306,44 @@ zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg
   const int cu = cu_count();
   BwdWs w = carve_bwd(ws, d);
   Saved sv = carve_saved(const_cast<char*>(static_cast<const char*>(saved)), d);
-  const T* sa = static_cast<const T*>(sv.a);
-  const T* su = static_cast<const T*>(sv.u);
-  const T* h = static_cast<const T*>(sv.h);
   const T* y = static_cast<const T*>(sv.y);
-  T* dyg = static_cast<T*>(w.dyg);
-  T* dl = static_cast<T*>(w.dl);
-  T* dadu = static_cast<T*>(w.dadu);
-  T* dxp = static_cast<T*>(w.dxp);
-  T* dxr = static_cast<T*>(w.dxr);
-  if (N > 0) ZC_LAUNCH(ZC_PH_TILE_OFFSETS, zc::launch_tile_offsets(r->offsets, N, zc::kGemmBM, w.tile_off, s), "tile offsets");
-  ZC_LAUNCH(ZC_PH_BWD_COMBINE, zc::launch_combine_bwd<T>(x, y, dout, r->logits, r->topk_idx, r->topk_gate, r->inv, Tn, dd,
-                                   N, E, K, d->gate_norm, d->out_scale, dyg, w.dg, dl, ldl, s),
-         "combine backward launch");
+  if (N > 0)
+    ZC_LAUNCH(ZC_PH_TILE_OFFSETS, zc::launch_tile_offsets(r->offsets, N, zc::kGemmBM, w.tile_off, s),
+              "tile offsets");
+  ZC_LAUNCH(ZC_PH_BWD_COMBINE,
+            zc::launch_combine_bwd<T>(x, y, dout, r->logits, r->topk_idx, r->topk_gate, r->inv, Tn,
+                                      dd, N, E, K, d->gate_norm, d->out_scale, w.gs, w.dg, w.dl,
+                                      ldl, s),
+            "combine backward launch");
   if (N > 0) {
-    if (Tn > 0) {
-      ZC_LAUNCH(ZC_PH_BWD_DOWN_DH, zc::launch_bwd_down_dh<T>(dyg, wd, sa, su, r->offsets, w.tile_off, N, I, dd, rows,
-                                       dadu, cu, s),
-             "down backward (dh) launch");
-    }
-    ZC_LAUNCH(ZC_PH_BWD_DOWN_DW, zc::launch_bwd_down_dw<T>(dyg, h, r->offsets, N, I, dd, dwd, cu, s),
-           "down weight-gradient launch");
-    if (Tn > 0) {
-      ZC_LAUNCH(ZC_PH_BWD_GATE_UP_DX, zc::launch_bwd_gateup_dx<T>(dadu, wg, wu, r->offsets, w.tile_off, N, I, dd, rows, dxp,
-                                         cu, s),
-             "gate/up backward (dx) launch");
-    }
-    ZC_LAUNCH(ZC_PH_BWD_GATE_UP_DW, zc::launch_bwd_gateup_dw<T>(dadu, x, r->offsets, r->perm, N, I, dd, K, dwg, dwu, cu, s),
-           "gate/up weight-gradient launch");
+    if (Tn > 0)
+      ZC_LAUNCH(ZC_PH_BWD_DOWN_DH,
+                zc::launch_bwd_down_dh<T>(dout, r->perm, K, w.gs, wd, sv.a, sv.u, r->offsets,
+                                          w.tile_off, N, I, dd, rows, w.dadu, cu, s),
+                "down backward (dh) launch");
+    ZC_LAUNCH(ZC_PH_BWD_DOWN_DW,
+              zc::launch_bwd_down_dw<T>(dout, r->perm, K, sv.h, w.gs, r->offsets, N, I, dd, dwd, cu,
+                                        s),
+              "down weight-gradient launch");
+    if (Tn > 0)
+      ZC_LAUNCH(ZC_PH_BWD_GATE_UP_DX,
+                zc::launch_bwd_gateup_dx<T>(w.dadu, wg, wu, r->offsets, w.tile_off, N, I, dd, rows,
+                                            w.dxp, cu, s),
+                "gate/up backward (dx) launch");
+    ZC_LAUNCH(ZC_PH_BWD_GATE_UP_DW,
+              zc::launch_bwd_gateup_dw<T>(w.dadu, x, r->offsets, r->perm, N, I, dd, K, dwg, dwu, cu,
+                                          s),
+              "gate/up weight-gradient launch");
   }
-  ZC_LAUNCH(ZC_PH_BWD_ROUTER_DW, zc::launch_router_dw<T>(dl, ldl, x, Tn, E, dd, dwr, cu, s), "router weight-gradient launch");
+  ZC_LAUNCH(ZC_PH_BWD_ROUTER_DW, zc::launch_router_dw<T>(w.dl, ldl, x, Tn, E, dd, dwr, cu, s),
+            "router weight-gradient launch");
   if (Tn > 0) {
-    ZC_LAUNCH(ZC_PH_BWD_ROUTER_DX, zc::launch_router_dx<T>(dl, ldl, wr, Tn, E, dd, dxr, cu, s), "router dx launch");
-    ZC_LAUNCH(ZC_PH_BWD_DX_GATHER, zc::launch_dx_gather<T>(dout, dxp, dxr, r->topk_idx, r->topk_gate, r->inv, Tn, dd, N, K,
-                                   d->out_scale, dx, s),
-           "dx gather launch");
+    ZC_LAUNCH(ZC_PH_BWD_ROUTER_DX, zc::launch_router_dx<T>(w.dl, ldl, wr, Tn, E, dd, w.dxr, cu, s),
+              "router dx launch");
+    ZC_LAUNCH(ZC_PH_BWD_DX_GATHER,
+              zc::launch_dx_gather<T>(dout, w.dxp, w.dxr, r->topk_idx, r->topk_gate, r->inv, Tn, dd,
+                                      N, K, d->out_scale, dx, s),
+              "dx gather launch");
   }
   return ZC_OK;
 }
@@ -369,9 +379,9 @@ zc_status zc_moe_route(const zc_moe_desc* desc, const void* x, const void* w_rou
                        const float* bias, zc_route_buf* r, void* ws, size_t ws_bytes,
                        void* stream) {
   ZC_CHECK(check_desc(desc));
-  ZC_CHECK(check_route(r));
+  ZC_CHECK(check_route(r, desc->T == 0));
   ZC_CHECK(check_ptr(bias, "bias"));
-  if ((x == nullptr) != (w_router == nullptr))
+  if ((x == nullptr) != (w_router == nullptr) && desc->T > 0)
     return fail(ZC_ERR_INVALID, "x and w_router must both be set or both be NULL");
   ZC_CHECK(check_ptr(x, "x", true));
   ZC_CHECK(check_ptr(w_router, "w_router", true));
@@ -390,12 +400,13 @@ zc_status zc_moe_forward(const zc_moe_desc* desc, const void* x, const void* w_r
                          const void* w_down, void* out, zc_route_buf* r, void* saved, void* ws,
                          size_t ws_bytes, void* stream) {
   ZC_CHECK(check_desc(desc));
-  ZC_CHECK(check_route(r));
-  ZC_CHECK(check_ptr(x, "x"));
+  const bool none = desc->T == 0;
+  ZC_CHECK(check_route(r, none));
+  ZC_CHECK(check_ptr(x, "x", none));
   ZC_CHECK(check_ptr(w_router, "w_router"));
   ZC_CHECK(check_ptr(bias, "bias"));
   ZC_CHECK(check_weights(desc, w_gate, w_up, w_down));
-  ZC_CHECK(check_ptr(out, "out"));
+  ZC_CHECK(check_ptr(out, "out", none));
   ZC_CHECK(check_ptr(saved, "saved", true));
   ZC_CHECK(check_ws(ws, ws_bytes, fwd_ws_bytes(desc)));
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -418,13 +429,14 @@ zc_status zc_moe_backward(const zc_moe_desc* desc, const void* x, const void* w_
                           void* dw_router, void* dw_gate, void* dw_up, void* dw_down, void* ws,
                           size_t ws_bytes, void* stream) {
   ZC_CHECK(check_desc(desc));
-  ZC_CHECK(check_route(r));
-  ZC_CHECK(check_ptr(x, "x"));
+  const bool none = desc->T == 0;
+  ZC_CHECK(check_route(r, none));
+  ZC_CHECK(check_ptr(x, "x", none));
   ZC_CHECK(check_ptr(w_router, "w_router"));
   ZC_CHECK(check_weights(desc, w_gate, w_up, w_down));
   ZC_CHECK(check_ptr(saved, "saved"));
-  ZC_CHECK(check_ptr(dout, "dout"));
-  ZC_CHECK(check_ptr(dx, "dx"));
+  ZC_CHECK(check_ptr(dout, "dout", none));
+  ZC_CHECK(check_ptr(dx, "dx", none));
   ZC_CHECK(check_ptr(dw_router, "dw_router"));
   ZC_CHECK(check_weights(desc, dw_gate, dw_up, dw_down));
   ZC_CHECK(check_ws(ws, ws_bytes, bwd_ws_bytes(desc)));

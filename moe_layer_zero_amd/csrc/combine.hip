@@ -49,6 +49,17 @@ template <> struct V16<float> {
   }
 };
 
+// V consecutive fp32 values (V = 4 or 8, 16-byte aligned).
+template <int V>
+__device__ __forceinline__ void load_f32_n(const float* p, float* f) {
+#pragma unroll
+  for (int c = 0; c < V / 4; ++c) {
+    const f32x4_t v = reinterpret_cast<const f32x4_t*>(p)[c];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[4 * c + e] = v[e];
+  }
+}
+
 // Token's picks into LDS; returns c_t (sum of zero-computation gates).
 __device__ __forceinline__ float load_picks(const int32_t* topk_idx, const float* gate,
                                             const int32_t* inv, int64_t t, int N, int K,
@@ -111,13 +122,20 @@ __device__ __forceinline__ float block_sum(float v, float* s_red) {
   return ((s_red[0] + s_red[1]) + s_red[2]) + s_red[3];
 }
 
+// Backward of the combine for one token (one workgroup):
+//   dg_r = <out_scale * dout_t, y_r> for FFN picks, <out_scale * dout_t, x_t>
+//          for zero-computation picks (fixed-order block sums);
+//   gs[inv] = out_scale * g_r, the row scale the expert GEMMs apply;
+//   dl = gradient of the router scores through the gates: the softmax
+//        Jacobian restricted to the picks (renormalised gates) or over all
+//        experts (Eq.(1) gates), written as one fp32 row of width ldl.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
     const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ dout,
     const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
     const float* __restrict__ gate, const int32_t* __restrict__ inv, int d, int N, int E, int K,
-    int gate_norm, float out_scale, T* __restrict__ dyg, float* __restrict__ dg_out,
-    T* __restrict__ dl, int ldl) {
+    int gate_norm, float out_scale, float* __restrict__ gs, float* __restrict__ dg_out,
+    float* __restrict__ dl, int ldl) {
   __shared__ float s_g[kMaxK];
   __shared__ int32_t s_inv[kMaxK];
   __shared__ int32_t s_e[kMaxK];
@@ -127,39 +145,31 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
   const int64_t t = blockIdx.x;
   if (threadIdx.x < K) s_e[threadIdx.x] = topk_idx[t * K + threadIdx.x];
   load_picks(topk_idx, gate, inv, t, N, K, s_g, s_inv, &s_c);
+  if (threadIdx.x < K && s_inv[threadIdx.x] >= 0) gs[s_inv[threadIdx.x]] = out_scale * s_g[threadIdx.x];
   constexpr int V = V16<T>::n;
-  // dg_r = <out_scale*dout_t, y_r or x_t>; gated dy rows in dispatch order
   for (int r = 0; r < K; ++r) {
     const int q = s_inv[r];
+    const T* src = q >= 0 ? y + static_cast<int64_t>(q) * d : x + t * d;
     float part = 0.f;
     for (int j = threadIdx.x * V; j < d; j += kThreads * V) {
       float dv[V], v[V];
       V16<T>::load(dout + t * d + j, dv);
+      V16<T>::load(src + j, v);
 #pragma unroll
-      for (int e = 0; e < V; ++e) dv[e] *= out_scale;
-      V16<T>::load(q >= 0 ? y + static_cast<int64_t>(q) * d + j : x + t * d + j, v);
-#pragma unroll
-      for (int e = 0; e < V; ++e) part += dv[e] * v[e];
-      if (q >= 0) {
-        const float g = s_g[r];
-#pragma unroll
-        for (int e = 0; e < V; ++e) dv[e] *= g;
-        V16<T>::store(dyg + static_cast<int64_t>(q) * d + j, dv);
-      }
+      for (int e = 0; e < V; ++e) part += (out_scale * dv[e]) * v[e];
     }
     const float tot = block_sum(part, s_red);
     if (threadIdx.x == 0) s_dg[r] = tot;
   }
   __syncthreads();
   if (threadIdx.x < K) dg_out[t * K + threadIdx.x] = s_dg[threadIdx.x];
-  // router: softmax Jacobian, restricted to the picks (gate_norm 1) or full
   float sgd = 0.f;
   for (int r = 0; r < K; ++r) sgd += s_g[r] * s_dg[r];
-  T* dlr = dl + t * ldl;
+  float* dlr = dl + t * ldl;
   if (gate_norm) {
-    for (int j = threadIdx.x; j < ldl; j += kThreads) Elem<T>::st(dlr + j, 0.f);
+    for (int j = threadIdx.x; j < ldl; j += kThreads) dlr[j] = 0.f;
     __syncthreads();
-    if (threadIdx.x < K) Elem<T>::st(dlr + s_e[threadIdx.x], s_g[threadIdx.x] * (s_dg[threadIdx.x] - sgd));
+    if (threadIdx.x < K) dlr[s_e[threadIdx.x]] = s_g[threadIdx.x] * (s_dg[threadIdx.x] - sgd);
   } else {
     const float* l = logits + t * E;
     float m = -INFINITY;
@@ -182,14 +192,14 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
           if (s_e[r] == j) dgj = s_dg[r];
         v = pj * (dgj - sgd);
       }
-      Elem<T>::st(dlr + j, v);
+      dlr[j] = v;
     }
   }
 }
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void dx_gather_kernel(
-    const T* __restrict__ dout, const T* __restrict__ dxp, const T* __restrict__ dxr,
+    const T* __restrict__ dout, const float* __restrict__ dxp, const float* __restrict__ dxr,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ gate,
     const int32_t* __restrict__ inv, int d, int N, int K, float out_scale, T* __restrict__ dx) {
   __shared__ float s_g[kMaxK];
@@ -198,6 +208,7 @@ __global__ __launch_bounds__(kThreads) void dx_gather_kernel(
   const int64_t t = blockIdx.x;
   const float c = load_picks(topk_idx, gate, inv, t, N, K, s_g, s_inv, &s_c) * out_scale;
   constexpr int V = V16<T>::n;
+  auto load_f32 = [](const float* p, float* f) { load_f32_n<V>(p, f); };
   for (int j = threadIdx.x * V; j < d; j += kThreads * V) {
     float acc[V], v[V];
     V16<T>::load(dout + t * d + j, v);
@@ -206,11 +217,11 @@ __global__ __launch_bounds__(kThreads) void dx_gather_kernel(
     for (int r = 0; r < K; ++r) {
       const int q = s_inv[r];
       if (q < 0) continue;
-      V16<T>::load(dxp + static_cast<int64_t>(q) * d + j, v);
+      load_f32(dxp + static_cast<int64_t>(q) * d + j, v);
 #pragma unroll
       for (int e = 0; e < V; ++e) acc[e] += v[e];
     }
-    V16<T>::load(dxr + t * d + j, v);
+    load_f32(dxr + t * d + j, v);
 #pragma unroll
     for (int e = 0; e < V; ++e) acc[e] += v[e];
     V16<T>::store(dx + t * d + j, acc);
@@ -233,15 +244,15 @@ template <typename T>
 hipError_t launch_combine_bwd(const T* x, const T* y, const T* dout, const float* logits,
                               const int32_t* topk_idx, const float* gate, const int32_t* inv,
                               int Tn, int d, int N, int E, int K, int gate_norm, float out_scale,
-                              T* dyg, float* dg, T* dl, int ldl, hipStream_t s) {
+                              float* gs, float* dg, float* dl, int ldl, hipStream_t s) {
   if (Tn == 0) return hipSuccess;
   hipLaunchKernelGGL(combine_bwd_kernel<T>, dim3(Tn), dim3(kThreads), 0, s, x, y, dout, logits,
-                     topk_idx, gate, inv, d, N, E, K, gate_norm, out_scale, dyg, dg, dl, ldl);
+                     topk_idx, gate, inv, d, N, E, K, gate_norm, out_scale, gs, dg, dl, ldl);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_dx_gather(const T* dout, const T* dxp, const T* dxr, const int32_t* topk_idx,
+hipError_t launch_dx_gather(const T* dout, const float* dxp, const float* dxr, const int32_t* topk_idx,
                             const float* gate, const int32_t* inv, int Tn, int d, int N, int K,
                             float out_scale, T* dx, hipStream_t s) {
   if (Tn == 0) return hipSuccess;
@@ -256,9 +267,9 @@ hipError_t launch_dx_gather(const T* dout, const T* dxp, const T* dxr, const int
                                         hipStream_t);                                           \
   template hipError_t launch_combine_bwd<T>(const T*, const T*, const T*, const float*,         \
                                             const int32_t*, const float*, const int32_t*, int,  \
-                                            int, int, int, int, int, float, T*, float*, T*,     \
-                                            int, hipStream_t);                                  \
-  template hipError_t launch_dx_gather<T>(const T*, const T*, const T*, const int32_t*,         \
+                                            int, int, int, int, int, float, float*, float*,     \
+                                            float*, int, hipStream_t);                          \
+  template hipError_t launch_dx_gather<T>(const T*, const float*, const float*, const int32_t*, \
                                           const float*, const int32_t*, int, int, int, int,     \
                                           float, T*, hipStream_t);
 ZC_INST(bf16_t)

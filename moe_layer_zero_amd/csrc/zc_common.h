@@ -46,16 +46,16 @@ constexpr int kGemmBM = 128;
 // ---------------------------------------------------------------- launchers
 // Every launcher queues work on `s` and returns the hipError_t of the launch.
 
-// F1: logits[T][E] = x[T][d] * wr[E][d]^T (fp32 out).
+// Router scores: logits[T][E] = x[T][d] * wr[E][d]^T (fp32 out).
 template <typename T>
 hipError_t launch_router_gemm(const T* x, const T* wr, float* logits, int Tn, int E, int d,
                               int cu_count, hipStream_t s);
 
-// F2: routing keys, biased top-K, gates (one wavefront per token).
+// Routing keys, biased top-K, gates (one wavefront per token).
 hipError_t launch_topk(const float* logits, const float* bias, int Tn, int E, int K,
                        int gate_norm, int32_t* topk_idx, float* topk_gate, hipStream_t s);
 
-// F3: per-expert counts, offsets, canonical permutation and its inverse.
+// Dispatch: per-expert counts, offsets, canonical permutation and its inverse.
 // Scratch: dispatch_scratch_bytes(T, E, N).  Also writes the per-expert
 // m-tile prefix tile_off[N+1] for the grouped GEMMs (tile height `bm`).
 size_t dispatch_scratch_bytes(int64_t Tn, int64_t E, int64_t N);
@@ -68,58 +68,62 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int Tn, int E, int N, int K,
 hipError_t launch_tile_offsets(const int32_t* offsets, int N, int bm, int32_t* tile_off,
                                hipStream_t s);
 
-// Grouped / dense GEMMs (gemm.hip).  See the mode list there.
+// Grouped / dense GEMMs (gemm.hip); the backward's fp32 intermediates enter
+// bf16 GEMMs as exact hi+lo bf16 pairs.
 template <typename T>
 hipError_t launch_ffn_gateup(const T* x, const T* wg, const T* wu, const int32_t* offsets,
                              const int32_t* perm, const int32_t* tile_off, int N, int I, int d,
-                             int K, int64_t max_rows, T* h, T* save_a, T* save_u, int cu_count,
-                             hipStream_t s);
+                             int K, int64_t max_rows, T* h, float* save_a, float* save_u,
+                             float* save_h, int cu_count, hipStream_t s);
 template <typename T>
 hipError_t launch_ffn_down(const T* h, const T* wd, const int32_t* offsets,
                            const int32_t* tile_off, int N, int I, int d, int64_t max_rows, T* y,
                            int cu_count, hipStream_t s);
 template <typename T>
-hipError_t launch_bwd_down_dh(const T* dyg, const T* wd, const T* sa, const T* su,
+hipError_t launch_bwd_down_dh(const T* dout, const int32_t* perm, int K, const float* gs,
+                              const T* wd, const float* sa, const float* su,
                               const int32_t* offsets, const int32_t* tile_off, int N, int I,
-                              int d, int64_t max_rows, T* dadu, int cu_count, hipStream_t s);
+                              int d, int64_t max_rows, float* dadu, int cu_count, hipStream_t s);
 template <typename T>
-hipError_t launch_bwd_down_dw(const T* dyg, const T* h, const int32_t* offsets, int N, int I,
-                              int d, T* dwd, int cu_count, hipStream_t s);
+hipError_t launch_bwd_down_dw(const T* dout, const int32_t* perm, int K, const float* hsave,
+                              const float* gs, const int32_t* offsets, int N, int I, int d,
+                              T* dwd, int cu_count, hipStream_t s);
 template <typename T>
-hipError_t launch_bwd_gateup_dx(const T* dadu, const T* wg, const T* wu, const int32_t* offsets,
-                                const int32_t* tile_off, int N, int I, int d, int64_t max_rows,
-                                T* dxp, int cu_count, hipStream_t s);
+hipError_t launch_bwd_gateup_dx(const float* dadu, const T* wg, const T* wu,
+                                const int32_t* offsets, const int32_t* tile_off, int N, int I,
+                                int d, int64_t max_rows, float* dxp, int cu_count, hipStream_t s);
 template <typename T>
-hipError_t launch_bwd_gateup_dw(const T* dadu, const T* x, const int32_t* offsets,
+hipError_t launch_bwd_gateup_dw(const float* dadu, const T* x, const int32_t* offsets,
                                 const int32_t* perm, int N, int I, int d, int K, T* dwg, T* dwu,
                                 int cu_count, hipStream_t s);
 template <typename T>
-hipError_t launch_router_dw(const T* dl, int ldl, const T* x, int Tn, int E, int d, T* dwr,
+hipError_t launch_router_dw(const float* dl, int ldl, const T* x, int Tn, int E, int d, T* dwr,
                             int cu_count, hipStream_t s);
 template <typename T>
-hipError_t launch_router_dx(const T* dl, int ldl, const T* wr, int Tn, int E, int d, T* dxr,
-                            int cu_count, hipStream_t s);
+hipError_t launch_router_dx(const float* dl, int ldl, const T* wr, int Tn, int E, int d,
+                            float* dxr, int cu_count, hipStream_t s);
 
-// F6: out = out_scale * (c_t x_t + sum_r g_r y[inv]).
+// Combine: out = out_scale * (c_t x_t + sum_r g_r y[inv]).
 template <typename T>
 hipError_t launch_combine(const T* x, const T* y, const int32_t* topk_idx, const float* gate,
                           const int32_t* inv, int Tn, int d, int N, int K, float out_scale,
                           T* out, hipStream_t s);
 
-// B1 + router part of B5: dg, gated dy in dispatch order, dl [T][ldl].
+// Combine backward: dg per slot, out_scale * gate of every FFN pick in
+// dispatch order (gs), and the router-score gradient dl [T][ldl] (fp32).
 template <typename T>
 hipError_t launch_combine_bwd(const T* x, const T* y, const T* dout, const float* logits,
                               const int32_t* topk_idx, const float* gate, const int32_t* inv,
                               int Tn, int d, int N, int E, int K, int gate_norm, float out_scale,
-                              T* dyg, float* dg, T* dl, int ldl, hipStream_t s);
+                              float* gs, float* dg, float* dl, int ldl, hipStream_t s);
 
-// B6: dx = out_scale * c_t * dout_t + sum_r dxp[inv] + dxr_t.
+// dx gather: dx = out_scale * c_t * dout_t + sum_r dxp[inv] + dxr_t.
 template <typename T>
-hipError_t launch_dx_gather(const T* dout, const T* dxp, const T* dxr, const int32_t* topk_idx,
+hipError_t launch_dx_gather(const T* dout, const float* dxp, const float* dxr, const int32_t* topk_idx,
                             const float* gate, const int32_t* inv, int Tn, int d, int N, int K,
                             float out_scale, T* dx, hipStream_t s);
 
-// P1: Eq.(2).
+// Bias update, Eq.(2) of section 2.1.1.
 hipError_t launch_pid(int N, int K, const int32_t* counts, int64_t T_all, double mu, double K_e,
                       float* bias, hipStream_t s);
 

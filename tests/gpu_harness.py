@@ -5,7 +5,13 @@ compare with the tolerances of the method:
   - routing (picked experts, counts, offsets, dispatch order, inverse):
     bit-exact when both sides route the same scores;
   - fp32 layers: max|gpu - oracle| / max|oracle| <= 1e-4;
-  - bf16 layers: max|gpu - oracle| <= 2e-2 * RMS(oracle).
+  - bf16 layers: |gpu - oracle| <= 2e-2 * RMS(oracle) + ulp_bf16(oracle)/2
+    element by element: the first term is the arithmetic budget, the second
+    the rounding that storing the oracle's own value as bf16 (the dtype the
+    layer's outputs and gradients have) would already cost.  Without it the
+    bound would be out of reach of any bf16 result: an output near 5x its
+    RMS (an N(0,1) input tail passed through a zero-computation expert) has
+    a half-ulp of 2^-9 * 5 RMS ~ 1% of RMS at best and ~2% at worst.
 When the GPU routes its own fp32 scores and the oracle its own fp64 scores,
 a token whose top-K boundary is closer than the score tolerance allows may
 legitimately pick differently; such tokens are checked for validity (the
@@ -85,8 +91,18 @@ def assert_close(gpu, orc: np.ndarray, dtype, what: str):
         assert err <= F32_RTOL * max(ref, 1e-30), f"{what}: max err {err:.3e}, max|ref| {ref:.3e}"
         return err / max(ref, 1e-30)
     rms = float(np.sqrt(np.mean(orc * orc))) if orc.size else 0.0
-    assert err <= BF16_RMS_TOL * max(rms, 1e-30), f"{what}: max err {err:.3e}, rms {rms:.3e}"
+    allowed = BF16_RMS_TOL * rms + 0.5 * bf16_ulp(orc)
+    excess = (np.abs(g - orc) - allowed).max() if g.size else 0.0
+    assert excess <= 0.0, (f"{what}: max err {err:.3e} (rms {rms:.3e}); exceeds "
+                           f"2e-2*rms + ulp/2 by {excess:.3e}")
     return err / max(rms, 1e-30)
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |v| (8 significant bits)."""
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.exp2(e - 7), 0.0)
 
 
 def routing_agreement(gpu_idx: np.ndarray, orc_keys: np.ndarray, orc_idx: np.ndarray, lg_orc,
