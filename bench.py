@@ -80,6 +80,29 @@ def layer_forward_bench(sh, steps, warmup):
     return Lg, ms, phases, p_real, touched, counts
 
 
+def gate_up_roofline(sh, p_real, touched, gu_ms):
+    """Roofline of the gate/up GEMM for one launch: algorithmic flop
+    (4 d I per FFN pick) and bytes (gate and up weights of every touched
+    expert once, the gathered x row and the h row of every pick), against
+    the vendor peaks; the binding roofline is the one with the higher floor."""
+    d, I = sh.d, sh.I
+    flops = 4.0 * d * I * p_real
+    nbytes = 2.0 * 2 * d * I * touched + 2.0 * d * p_real + 2.0 * I * p_real
+    t = gu_ms * 1e-3
+    tflops, gbs = flops / t / 1e12, nbytes / t / 1e9
+    hbm_floor = nbytes / (HBM_PEAK_GBS * 1e9)
+    mfma_floor = flops / (BF16_PEAK_TFLOPS * 1e12)
+    mfma = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+    hbm = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    roof = dict(hbm if hbm_floor > mfma_floor else mfma)
+    roof.update(kernel="gate_up_gemm", traffic=None,
+                algorithmic={"flop": flops, "bytes": nbytes, "hbm_floor_ms": hbm_floor * 1e3,
+                             "mfma_floor_ms": mfma_floor * 1e3})
+    return roof, mfma, hbm
+
+
 def prefill(steps, warmup):
     sh = synth.CONFIGS["prefill_bf16"]
     Lg, ms, ph, p_real, touched, counts = layer_forward_bench(sh, steps, warmup)
@@ -88,21 +111,23 @@ def prefill(steps, warmup):
     flops_dn = 2.0 * d * I * p_real
     gu_ms = ph["gate_up_gemm"][0]
     dn_ms = ph["down_gemm"][0]
+    roof, mfma, hbm = gate_up_roofline(sh, p_real, touched, gu_ms)
     res = {
         "ms_per_step": ms,
         "tokens_per_s": sh.T / (ms / 1e3),
         "p_real": p_real,
+        "touched_experts": touched,
         "zero_pick_fraction": 1.0 - p_real / (sh.T * sh.K),
         "tokens_per_ffn_expert_max_over_mean": float(counts[: sh.N].max() / counts[: sh.N].mean()),
         "kernels_ms": {k: round(v[0], 4) for k, v in ph.items()},
+        "gate_up_mfma_frac": mfma["frac"],
+        "gate_up_hbm_frac": hbm["frac"],
         "gate_up_tflops": flops_gu / (gu_ms * 1e-3) / 1e12,
         "down_tflops": flops_dn / (dn_ms * 1e-3) / 1e12,
         "expert_gemms_tflops": (flops_gu + flops_dn) / ((gu_ms + dn_ms) * 1e-3) / 1e12,
+        "expert_gemms_mfma_frac": (flops_gu + flops_dn) / ((gu_ms + dn_ms) * 1e-3) / 1e12
+        / BF16_PEAK_TFLOPS,
     }
-    roof = {"bound": "mfma", "kernel": "gate_up_gemm",
-            "achieved": round(res["gate_up_tflops"], 2), "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(res["gate_up_tflops"] / BF16_PEAK_TFLOPS, 4),
-            "traffic": None}
     del Lg
     torch.cuda.empty_cache()
     return sh, res, roof
@@ -171,43 +196,50 @@ def train(steps, warmup):
     return res
 
 
-def cpu_baseline(budget_experts=160, max_tokens=64):
+def cpu_baseline(target_s=12.0, max_tokens=4096):
     """The fp64 oracle on a bounded sample of the prefill workload: router
-    scores, routing and layer output for a few tokens (only their experts'
-    weights are copied to the host).  Returns tokens/s of that sample."""
+    scores, routing and layer output for the first n tokens of a seeded
+    random order, n sized so that the timed work takes about target_s
+    seconds.  Returns tokens/s of that sample."""
     from oracle import oracle
 
     sh = synth.CONFIGS["prefill_bf16"]
-    log("[bench] cpu baseline: regenerating the prefill layer")
+    log("[bench] cpu baseline: regenerating the prefill layer, copying it to the host")
     Lg = synth.make_layer(sh, "cuda")
     g = torch.Generator().manual_seed(2024)
-    order = torch.randperm(sh.T, generator=g).numpy()
-    xh_all = synth.to_np(Lg["x"][torch.from_numpy(order[:max_tokens]).cuda()])
+    order = torch.randperm(sh.T, generator=g)[:max_tokens].numpy()
+    xs = synth.to_np(Lg["x"][torch.from_numpy(order).cuda()])
     wr = synth.to_np(Lg["wr"])
     bias = Lg["bias"].cpu().numpy()
-    # pick the sample: tokens in random order while their experts fit the budget
-    lg0 = oracle.logits(xh_all, wr)
-    r0 = oracle.route(lg0, bias, sh.N, sh.K, want_keys=False)
-    experts, n = set(), 0
-    for i in range(max_tokens):
-        new = experts | {int(e) for e in r0.topk_idx[i] if e < sh.N}
-        if len(new) > budget_experts:
-            break
-        experts, n = new, i + 1
-    wg = {e: synth.to_np(Lg["wg"][e]) for e in experts}
-    wu = {e: synth.to_np(Lg["wu"][e]) for e in experts}
-    wd = {e: synth.to_np(Lg["wd"][e]) for e in experts}
-    xh = np.ascontiguousarray(xh_all[:n])
+    wg, wu, wd = (synth.to_np(Lg[k]) for k in ("wg", "wu", "wd"))
     del Lg
     torch.cuda.empty_cache()
-    t0 = time.perf_counter()
-    lg = oracle.logits(xh, wr)
-    r = oracle.route(lg, bias, sh.N, sh.K, want_keys=False)
-    oracle.forward(xh, wg, wu, wd, r.topk_idx, r.gates, sh.N)
-    dt = time.perf_counter() - t0
+
+    def run(n):
+        x = np.ascontiguousarray(xs[:n])
+        t0 = time.perf_counter()
+        lg = oracle.logits(x, wr)
+        r = oracle.route(lg, bias, sh.N, sh.K, want_keys=False)
+        oracle.forward(x, wg, wu, wd, r.topk_idx, r.gates, sh.N)
+        return time.perf_counter() - t0
+
+    t_probe = run(16)
+    n = int(min(max_tokens, max(16, 16 * target_s / max(t_probe, 1e-3))))
+    log(f"[bench] cpu baseline: 16 tokens in {t_probe:.2f} s, timing {n} tokens")
+    dt = run(n)
     return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{n} random tokens of the prefill workload (router scores, routing, "
-                      f"{len(experts)} FFN experts' outputs, combine), {dt:.1f} s"}
+            "sample": f"{n} tokens of the prefill workload (seeded random subset): router "
+                      f"scores, routing, SwiGLU experts and combine in fp64, {dt:.1f} s"}
+
+
+def copy_probe(nbytes: int):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "launches": 3}), flush=True)
 
 
 def main():
@@ -217,12 +249,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", choices=["prefill", "decode", "train"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer's benchmark has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     zcmoe.lib()
     extra = {}
     sh = synth.CONFIGS["prefill_bf16"]
