@@ -19,7 +19,8 @@ BUILD = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libzcmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["api.hip", "router.hip", "dispatch.hip", "gemm.hip", "combine.hip", "pid.hip"]
+SOURCES = ["api.hip", "router.hip", "dispatch.hip", "gemm.hip", "gemm_fwd.hip", "combine.hip",
+           "pid.hip"]
 STRICT_FP = {"router.hip", "pid.hip"}
 
 COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

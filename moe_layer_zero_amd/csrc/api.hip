@@ -7,6 +7,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/zc_moe.h"
@@ -166,16 +167,18 @@ zc_status check_route(const zc_route_buf* r, bool no_tokens) {
 
 // ---- workspace layouts (all pieces 256-byte aligned)
 struct RouteWs {
-  int32_t* tile_off;
+  int32_t* tile_off;   // row-tile prefix for the generic grouped GEMM
+  int32_t* tile_off2;  // row-tile prefix for the bf16 forward expert GEMMs
   void* dispatch;
 };
 int64_t route_ws_bytes(const zc_moe_desc* d) {
-  return a256(4 * (d->N + 1)) + a256(zc::dispatch_scratch_bytes(d->T, d->N + d->Z, d->N));
+  return 2 * a256(4 * (d->N + 1)) + a256(zc::dispatch_scratch_bytes(d->T, d->N + d->Z, d->N));
 }
 RouteWs carve_route(char* p, const zc_moe_desc* d) {
   RouteWs w;
   w.tile_off = reinterpret_cast<int32_t*>(p);
-  w.dispatch = p + a256(4 * (d->N + 1));
+  w.tile_off2 = reinterpret_cast<int32_t*>(p + a256(4 * (d->N + 1)));
+  w.dispatch = p + 2 * a256(4 * (d->N + 1));
   return w;
 }
 
@@ -242,6 +245,19 @@ zc_status check_ws(const void* ws, size_t ws_bytes, int64_t need) {
   return ZC_OK;
 }
 
+// The 256 x 256 forward kernels: bf16 layers, no activations saved for a
+// backward pass, 32-bit element offsets (rows * columns < 2^31), and on
+// average at least 64 rows per FFN expert (T*K/N, known on the host without
+// reading the counts back); decode-sized batches keep the 128 x 128 kernel,
+// whose larger grid streams a few rows' worth of weights per expert better.
+template <typename T>
+bool use_fwd_kernels(const zc_moe_desc* d, const void* saved) {
+  if (!std::is_same<T, bf16_t>::value || saved) return false;
+  if (d->N == 0 || d->T * d->K < 64 * d->N) return false;
+  const int64_t rows = d->T * d->K, cols = d->I > d->d ? d->I : d->d;
+  return rows * cols < (int64_t(1) << 31) && d->T * d->d < (int64_t(1) << 31);
+}
+
 // Router + dispatch on an already validated call.
 template <typename T>
 zc_status do_route(const zc_moe_desc* d, const T* x, const T* wr, const float* bias,
@@ -254,8 +270,9 @@ zc_status do_route(const zc_moe_desc* d, const T* x, const T* wr, const float* b
            "router GEMM launch");
   ZC_LAUNCH(ZC_PH_TOPK, zc::launch_topk(r->logits, bias, Tn, E, K, d->gate_norm, r->topk_idx, r->topk_gate, s),
          "top-K launch");
-  ZC_LAUNCH(ZC_PH_DISPATCH, zc::launch_dispatch(r->topk_idx, Tn, E, N, K, zc::kGemmBM, r->counts, r->offsets,
-                             r->perm, r->inv, w.tile_off, w.dispatch, s),
+  ZC_LAUNCH(ZC_PH_DISPATCH, zc::launch_dispatch(r->topk_idx, Tn, E, N, K, zc::kGemmBM, zc::kFwdBM,
+                                                r->counts, r->offsets, r->perm, r->inv, w.tile_off,
+                                                w.tile_off2, w.dispatch, s),
          "dispatch launch");
   return ZC_OK;
 }
@@ -282,12 +299,28 @@ zc_status do_forward(const zc_moe_desc* d, const T* x, const T* wr, const float*
   }
   if (N > 0 && Tn > 0) {
     const int cu = cu_count();
-    ZC_LAUNCH(ZC_PH_GATE_UP, zc::launch_ffn_gateup<T>(x, wg, wu, r->offsets, r->perm, rw.tile_off, N,
-                                                      I, dd, K, rows, h, sa, su, sh, cu, s),
-              "gate/up GEMM launch");
-    ZC_LAUNCH(ZC_PH_DOWN, zc::launch_ffn_down<T>(h, wd, r->offsets, rw.tile_off, N, I, dd, rows, y,
-                                                 cu, s),
-              "down GEMM launch");
+    if (use_fwd_kernels<T>(d, saved)) {
+      // bf16 inference: 256 x 256 tiles, weights streamed once per expert
+      ZC_LAUNCH(ZC_PH_GATE_UP,
+                zc::launch_fwd_gateup(reinterpret_cast<const bf16_t*>(x),
+                                      reinterpret_cast<const bf16_t*>(wg),
+                                      reinterpret_cast<const bf16_t*>(wu), r->offsets, r->perm,
+                                      rw.tile_off2, N, I, dd, K, reinterpret_cast<bf16_t*>(h),
+                                      nullptr, nullptr, nullptr, cu, s),
+                "gate/up GEMM launch");
+      ZC_LAUNCH(ZC_PH_DOWN,
+                zc::launch_fwd_down(reinterpret_cast<const bf16_t*>(h),
+                                    reinterpret_cast<const bf16_t*>(wd), r->offsets, rw.tile_off2, N,
+                                    I, dd, reinterpret_cast<bf16_t*>(y), cu, s),
+                "down GEMM launch");
+    } else {
+      ZC_LAUNCH(ZC_PH_GATE_UP, zc::launch_ffn_gateup<T>(x, wg, wu, r->offsets, r->perm, rw.tile_off,
+                                                        N, I, dd, K, rows, h, sa, su, sh, cu, s),
+                "gate/up GEMM launch");
+      ZC_LAUNCH(ZC_PH_DOWN, zc::launch_ffn_down<T>(h, wd, r->offsets, rw.tile_off, N, I, dd, rows,
+                                                   y, cu, s),
+                "down GEMM launch");
+    }
   }
   ZC_LAUNCH(ZC_PH_COMBINE, zc::launch_combine<T>(x, y, r->topk_idx, r->topk_gate, r->inv, Tn, dd, N, K, d->out_scale,
                                out, s),

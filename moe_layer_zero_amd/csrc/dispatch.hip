@@ -60,11 +60,13 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restric
 // One block of 1024 threads (E <= 1024): counts, offsets, tile prefix and
 // per-(block, expert) bases.
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ cnt, int nblk,
-                                                    int E, int N, int bm, int32_t* counts,
-                                                    int32_t* offsets, int32_t* tile_off,
+                                                    int E, int N, int bm, int bm2,
+                                                    int32_t* counts, int32_t* offsets,
+                                                    int32_t* tile_off, int32_t* tile_off2,
                                                     int32_t* base) {
   __shared__ int32_t s_off[1024];
   __shared__ int32_t s_til[1024];
+  __shared__ int32_t s_til2[1024];
   const int e = threadIdx.x;
   int32_t tot = 0;
   if (e < E)
@@ -73,23 +75,28 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   // inclusive scans over FFN experts (Hillis-Steele; integer, order-free)
   s_off[e] = (e < N) ? tot : 0;
   s_til[e] = (e < N) ? (tot + bm - 1) / bm : 0;
+  s_til2[e] = (e < N) ? (tot + bm2 - 1) / bm2 : 0;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
     const int32_t a = e >= o ? s_off[e - o] : 0;
     const int32_t c = e >= o ? s_til[e - o] : 0;
+    const int32_t c2 = e >= o ? s_til2[e - o] : 0;
     __syncthreads();
     s_off[e] += a;
     s_til[e] += c;
+    s_til2[e] += c2;
     __syncthreads();
   }
   const int32_t excl = (e > 0 && e <= N) ? s_off[e - 1] : 0;
   if (e < N) {
     offsets[e] = excl;
     tile_off[e] = e > 0 ? s_til[e - 1] : 0;
+    tile_off2[e] = e > 0 ? s_til2[e - 1] : 0;
   }
   if (e == 0) {
     offsets[N] = N > 0 ? s_off[N - 1] : 0;
     tile_off[N] = N > 0 ? s_til[N - 1] : 0;
+    tile_off2[N] = N > 0 ? s_til2[N - 1] : 0;
   }
   if (e < N) {
     int32_t run = excl;
@@ -160,9 +167,9 @@ size_t dispatch_scratch_bytes(int64_t Tn, int64_t E, int64_t N) {
                              align256(nblk * E * 4));
 }
 
-hipError_t launch_dispatch(const int32_t* topk_idx, int Tn, int E, int N, int K, int bm,
+hipError_t launch_dispatch(const int32_t* topk_idx, int Tn, int E, int N, int K, int bm, int bm2,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                           int32_t* tile_off, void* scratch, hipStream_t s) {
+                           int32_t* tile_off, int32_t* tile_off2, void* scratch, hipStream_t s) {
   const int nblk = (Tn + kTokPerBlk - 1) / kTokPerBlk;
   Scratch sc = carve(scratch, nblk, E);
   if (nblk > 0) {
@@ -171,8 +178,8 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int Tn, int E, int N, int K,
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, sc.cnt, nblk, E, N, bm, counts,
-                     offsets, tile_off, sc.base);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, sc.cnt, nblk, E, N, bm, bm2, counts,
+                     offsets, tile_off, tile_off2, sc.base);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nblk == 0) return err;
   hipLaunchKernelGGL(scatter_kernel, dim3(nblk), dim3(kThreads), E * sizeof(uint64_t), s,

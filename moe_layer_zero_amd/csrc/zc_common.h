@@ -42,6 +42,8 @@ template <> struct Elem<bf16_t> {
 // Row-tile height of the grouped GEMMs; the dispatch step publishes the
 // per-expert prefix of ceil(rows / kGemmBM) tiles for them.
 constexpr int kGemmBM = 128;
+// Row-tile height of the bf16 forward expert GEMMs (gemm_fwd.hip).
+constexpr int kFwdBM = 256;
 
 // ---------------------------------------------------------------- launchers
 // Every launcher queues work on `s` and returns the hipError_t of the launch.
@@ -57,11 +59,12 @@ hipError_t launch_topk(const float* logits, const float* bias, int Tn, int E, in
 
 // Dispatch: per-expert counts, offsets, canonical permutation and its inverse.
 // Scratch: dispatch_scratch_bytes(T, E, N).  Also writes the per-expert
-// m-tile prefix tile_off[N+1] for the grouped GEMMs (tile height `bm`).
+// row-tile prefixes tile_off[N+1] and tile_off2[N+1] for the grouped GEMMs
+// (tile heights bm and bm2).
 size_t dispatch_scratch_bytes(int64_t Tn, int64_t E, int64_t N);
-hipError_t launch_dispatch(const int32_t* topk_idx, int Tn, int E, int N, int K, int bm,
+hipError_t launch_dispatch(const int32_t* topk_idx, int Tn, int E, int N, int K, int bm, int bm2,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                           int32_t* tile_off, void* scratch, hipStream_t s);
+                           int32_t* tile_off, int32_t* tile_off2, void* scratch, hipStream_t s);
 
 // tile_off[N+1] from offsets[N+1] (for a backward call that only has the
 // routing of its forward call).
@@ -102,6 +105,16 @@ hipError_t launch_router_dw(const float* dl, int ldl, const T* x, int Tn, int E,
 template <typename T>
 hipError_t launch_router_dx(const float* dl, int ldl, const T* wr, int Tn, int E, int d,
                             float* dxr, int cu_count, hipStream_t s);
+
+// bf16 forward expert GEMMs with 256 x 256 tiles (gemm_fwd.hip); mt_off is
+// the kFwdBM row-tile prefix from the dispatch step.
+hipError_t launch_fwd_gateup(const bf16_t* x, const bf16_t* wg, const bf16_t* wu,
+                             const int32_t* offsets, const int32_t* perm, const int32_t* mt_off,
+                             int N, int I, int d, int K, bf16_t* h, float* save_a, float* save_u,
+                             float* save_h, int cu, hipStream_t s);
+hipError_t launch_fwd_down(const bf16_t* h, const bf16_t* wd, const int32_t* offsets,
+                           const int32_t* mt_off, int N, int I, int d, bf16_t* y, int cu,
+                           hipStream_t s);
 
 // Combine: out = out_scale * (c_t x_t + sum_r g_r y[inv]).
 template <typename T>
