@@ -71,7 +71,16 @@ typedef struct {
                      /*    the picked scores; the picked R_i rescaled to sum  */
                      /*    to 1);  0: gate = R_i exactly as Eq.(1) prints it  */
   float out_scale;   /* scalar on the layer output (1.0 = none)               */
+  int32_t weight_layout; /* zc_weight_layout of w_gate, w_up and w_down       */
 } zc_moe_desc;
+
+/* Layouts of the FFN expert weights.
+ *  ZC_WEIGHTS_ROWMAJOR: the row-major layouts listed above.
+ *  ZC_WEIGHTS_PACKED:   the output of zc_moe_pack_weights.  Accepted by
+ *      zc_moe_forward for bf16 layers with d and I multiples of 256, when no
+ *      activations are saved (saved == NULL): the inference forward.  The
+ *      backward and the saving forward need row-major weights. */
+typedef enum { ZC_WEIGHTS_ROWMAJOR = 0, ZC_WEIGHTS_PACKED = 1 } zc_weight_layout;
 
 /* Routing state: written by zc_moe_route / zc_moe_forward, read by
  * zc_moe_backward.  All device buffers owned by the caller. */
@@ -159,6 +168,24 @@ zc_status zc_moe_backward(const zc_moe_desc* desc, const void* x,
 zc_status zc_moe_pid_update(int64_t N, int64_t Z, int64_t K,
                             const int32_t* counts, int64_t T_all, double mu,
                             double K_e, float* bias, void* stream);
+
+/* Rearranges one set of FFN expert weights (bf16) from the row-major layout
+ * into ZC_WEIGHTS_PACKED, for the bf16 inference forward, which then streams
+ * every weight panel from HBM in whole 1 KB pieces straight into the matrix
+ * cores' operand registers ("LongCat-Flash Technical Report", section 2.1:
+ * the FFN experts' weights are the bulk of the layer's memory traffic).
+ *   which = ZC_PACK_GATE_UP: src is w_gate or w_up, [N][I][d];
+ *   which = ZC_PACK_DOWN:    src is w_down, [N][d][I].
+ * Each expert's [R][C] matrix (R output columns, C reduction length) is
+ * stored as consecutive 1 KB blocks, block (r/32, c/16) at index
+ * (r/32)*(C/16) + c/16, and inside a block element (r, c) at
+ * (r%32 + 32*((c/8)%2))*8 + c%8: the B operand of one 32x32x16 MFMA step for
+ * 32 output columns, lane by lane.  dst has src's size and must not overlap
+ * it.  Needs dtype bf16 and d, I multiples of 256 (the desc's weight_layout
+ * is ignored).  Queued on `stream` like every call. */
+enum { ZC_PACK_GATE_UP = 0, ZC_PACK_DOWN = 1 };
+zc_status zc_moe_pack_weights(const zc_moe_desc* desc, int which, const void* src, void* dst,
+                              void* stream);
 
 /* Kernel timing for benchmarks.  While profiling is on, every entry point
  * brackets each of its kernel launches with a pair of HIP events recorded on

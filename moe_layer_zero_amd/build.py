@@ -19,7 +19,8 @@ BUILD = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libzcmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["api.hip", "router.hip", "dispatch.hip", "gemm.hip", "gemm_fwd.hip", "combine.hip",
+SOURCES = ["api.hip", "router.hip", "dispatch.hip", "gemm.hip", "gemm_fwd.hip", "gemm_fwdp.hip",
+           "combine.hip",
            "pid.hip"]
 STRICT_FP = {"router.hip", "pid.hip"}
 

@@ -114,6 +114,25 @@ int64_t a256(int64_t b) { return (b + 255) & ~int64_t(255); }
 int64_t esize(const zc_moe_desc* d) { return d->dtype == ZC_F32 ? 4 : 2; }
 int64_t ldl_of(int64_t E) { return (E + 7) / 8 * 8; }
 
+#define ZC_CHECK(x)                   \
+  do {                                \
+    zc_status s_ = (x);               \
+    if (s_ != ZC_OK) return s_;       \
+  } while (0)
+
+// Shapes the packed layout and its forward kernels handle: bf16, d and I
+// multiples of 256, activation buffers (x [T][d], h [T*K][I]) addressable
+// with 32-bit byte offsets.
+zc_status check_packable(const zc_moe_desc* d) {
+  if (d->dtype != ZC_BF16) return fail(ZC_ERR_UNSUPPORTED, "packed weights need a bf16 layer");
+  if (d->d % 256 || d->I % 256)
+    return fail(ZC_ERR_UNSUPPORTED, "packed weights need d and I multiples of 256 (d=%lld I=%lld)",
+                (long long)d->d, (long long)d->I);
+  if (d->T * d->d * 2 >= (int64_t(1) << 31) || d->T * d->K * d->I * 2 >= (int64_t(1) << 31))
+    return fail(ZC_ERR_UNSUPPORTED, "packed-weight forward needs T*d and T*K*I below 2^30");
+  return ZC_OK;
+}
+
 zc_status check_desc(const zc_moe_desc* d) {
   if (!d) return fail(ZC_ERR_INVALID, "desc is NULL");
   const int64_t E = d->N + d->Z;
@@ -128,6 +147,8 @@ zc_status check_desc(const zc_moe_desc* d) {
   if (d->gate_norm != 0 && d->gate_norm != 1)
     return fail(ZC_ERR_INVALID, "gate_norm %d is neither 0 nor 1", d->gate_norm);
   if (!std::isfinite(d->out_scale)) return fail(ZC_ERR_INVALID, "out_scale is not finite");
+  if (d->weight_layout != ZC_WEIGHTS_ROWMAJOR && d->weight_layout != ZC_WEIGHTS_PACKED)
+    return fail(ZC_ERR_INVALID, "weight_layout %d is neither ROWMAJOR nor PACKED", d->weight_layout);
   if (d->T * d->K >= (int64_t(1) << 31) || d->d >= (int64_t(1) << 24) || d->I >= (int64_t(1) << 24))
     return fail(ZC_ERR_UNSUPPORTED, "T*K, d or I too large for 32-bit indexing");
   const int64_t mult = d->dtype == ZC_BF16 ? 64 : 32;
@@ -135,6 +156,7 @@ zc_status check_desc(const zc_moe_desc* d) {
     return fail(ZC_ERR_UNSUPPORTED, "%s layers need d and I multiples of %lld (d=%lld I=%lld)",
                 d->dtype == ZC_BF16 ? "bf16" : "fp32", (long long)mult, (long long)d->d,
                 (long long)d->I);
+  if (d->weight_layout == ZC_WEIGHTS_PACKED) ZC_CHECK(check_packable(d));
   return ZC_OK;
 }
 
@@ -145,12 +167,6 @@ zc_status check_ptr(const void* p, const char* name, bool nullable = false) {
   if (!aligned(p)) return fail(ZC_ERR_INVALID, "%s is not 16-byte aligned", name);
   return ZC_OK;
 }
-
-#define ZC_CHECK(x)                   \
-  do {                                \
-    zc_status s_ = (x);               \
-    if (s_ != ZC_OK) return s_;       \
-  } while (0)
 
 // Per-token buffers may be NULL when there are no tokens (T == 0).
 zc_status check_route(const zc_route_buf* r, bool no_tokens) {
@@ -259,6 +275,14 @@ bool use_fwd_kernels(const zc_moe_desc* d, const void* saved) {
 }
 
 // Router + dispatch on an already validated call.
+// Row-tile height of the second tile prefix (tile_off2): the packed-weight
+// forward picks it from the average rows per FFN expert; the row-major bf16
+// forward kernels use 256.
+int fwd_rows_per_tile(const zc_moe_desc* d) {
+  if (d->weight_layout != ZC_WEIGHTS_PACKED || d->N == 0) return zc::kFwdBM;
+  return zc::fwdp_rows_per_tile(d->T * d->K / d->N);
+}
+
 template <typename T>
 zc_status do_route(const zc_moe_desc* d, const T* x, const T* wr, const float* bias,
                    zc_route_buf* r, const RouteWs& w, hipStream_t s) {
@@ -270,7 +294,8 @@ zc_status do_route(const zc_moe_desc* d, const T* x, const T* wr, const float* b
            "router GEMM launch");
   ZC_LAUNCH(ZC_PH_TOPK, zc::launch_topk(r->logits, bias, Tn, E, K, d->gate_norm, r->topk_idx, r->topk_gate, s),
          "top-K launch");
-  ZC_LAUNCH(ZC_PH_DISPATCH, zc::launch_dispatch(r->topk_idx, Tn, E, N, K, zc::kGemmBM, zc::kFwdBM,
+  ZC_LAUNCH(ZC_PH_DISPATCH, zc::launch_dispatch(r->topk_idx, Tn, E, N, K, zc::kGemmBM,
+                                                fwd_rows_per_tile(d),
                                                 r->counts, r->offsets, r->perm, r->inv, w.tile_off,
                                                 w.tile_off2, w.dispatch, s),
          "dispatch launch");
@@ -299,7 +324,22 @@ zc_status do_forward(const zc_moe_desc* d, const T* x, const T* wr, const float*
   }
   if (N > 0 && Tn > 0) {
     const int cu = cu_count();
-    if (use_fwd_kernels<T>(d, saved)) {
+    if (d->weight_layout == ZC_WEIGHTS_PACKED) {
+      // bf16 inference on packed weights (validated: bf16, no saved buffer)
+      const bf16_t* hx = reinterpret_cast<const bf16_t*>(x);
+      bf16_t* hh = reinterpret_cast<bf16_t*>(h);
+      ZC_LAUNCH(ZC_PH_GATE_UP,
+                zc::launch_fwdp_gateup(hx, d->T * d->d, reinterpret_cast<const bf16_t*>(wg),
+                                       reinterpret_cast<const bf16_t*>(wu), r->offsets, r->perm,
+                                       rw.tile_off2, fwd_rows_per_tile(d), N, I, dd, K, hh, cu,
+                                       s),
+                "gate/up GEMM launch");
+      ZC_LAUNCH(ZC_PH_DOWN,
+                zc::launch_fwdp_down(hh, rows * d->I, reinterpret_cast<const bf16_t*>(wd),
+                                     r->offsets, rw.tile_off2, fwd_rows_per_tile(d), N, I, dd,
+                                     reinterpret_cast<bf16_t*>(y), cu, s),
+                "down GEMM launch");
+    } else if (use_fwd_kernels<T>(d, saved)) {
       // bf16 inference: 256 x 256 tiles, weights streamed once per expert
       ZC_LAUNCH(ZC_PH_GATE_UP,
                 zc::launch_fwd_gateup(reinterpret_cast<const bf16_t*>(x),
@@ -441,6 +481,8 @@ zc_status zc_moe_forward(const zc_moe_desc* desc, const void* x, const void* w_r
   ZC_CHECK(check_weights(desc, w_gate, w_up, w_down));
   ZC_CHECK(check_ptr(out, "out", none));
   ZC_CHECK(check_ptr(saved, "saved", true));
+  if (saved && desc->weight_layout == ZC_WEIGHTS_PACKED)
+    return fail(ZC_ERR_UNSUPPORTED, "a forward that saves activations needs row-major weights");
   ZC_CHECK(check_ws(ws, ws_bytes, fwd_ws_bytes(desc)));
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
@@ -462,6 +504,8 @@ zc_status zc_moe_backward(const zc_moe_desc* desc, const void* x, const void* w_
                           void* dw_router, void* dw_gate, void* dw_up, void* dw_down, void* ws,
                           size_t ws_bytes, void* stream) {
   ZC_CHECK(check_desc(desc));
+  if (desc->weight_layout != ZC_WEIGHTS_ROWMAJOR)
+    return fail(ZC_ERR_UNSUPPORTED, "the backward needs row-major weights");
   const bool none = desc->T == 0;
   ZC_CHECK(check_route(r, none));
   ZC_CHECK(check_ptr(x, "x", none));
@@ -488,6 +532,32 @@ zc_status zc_moe_backward(const zc_moe_desc* desc, const void* x, const void* w_
                             static_cast<const float*>(dout), static_cast<float*>(dx),
                             static_cast<float*>(dw_router), static_cast<float*>(dw_gate),
                             static_cast<float*>(dw_up), static_cast<float*>(dw_down), w, s);
+}
+
+zc_status zc_moe_pack_weights(const zc_moe_desc* desc, int which, const void* src, void* dst,
+                              void* stream) {
+  ZC_CHECK(check_desc(desc));
+  if (desc->dtype != ZC_BF16) return fail(ZC_ERR_UNSUPPORTED, "packed weights need a bf16 layer");
+  if (desc->d % 256 || desc->I % 256)
+    return fail(ZC_ERR_UNSUPPORTED, "packed weights need d and I multiples of 256 (d=%lld I=%lld)",
+                (long long)desc->d, (long long)desc->I);
+  if (which != ZC_PACK_GATE_UP && which != ZC_PACK_DOWN)
+    return fail(ZC_ERR_INVALID, "which=%d is neither ZC_PACK_GATE_UP nor ZC_PACK_DOWN", which);
+  const bool opt = desc->N == 0;
+  ZC_CHECK(check_ptr(src, "src", opt));
+  ZC_CHECK(check_ptr(dst, "dst", opt));
+  const int64_t bytes = desc->N * desc->I * desc->d * 2;
+  const char* a = static_cast<const char*>(src);
+  const char* b = static_cast<const char*>(dst);
+  if (bytes > 0 && a < b + bytes && b < a + bytes)
+    return fail(ZC_ERR_INVALID, "src and dst overlap");
+  if (desc->N == 0) return ZC_OK;
+  const int R = static_cast<int>(which == ZC_PACK_GATE_UP ? desc->I : desc->d);
+  const int C = static_cast<int>(which == ZC_PACK_GATE_UP ? desc->d : desc->I);
+  hipError_t e = zc::launch_pack_weights(static_cast<const bf16_t*>(src), static_cast<bf16_t*>(dst),
+                                         desc->N, R, C, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "weight packing launch");
+  return ZC_OK;
 }
 
 zc_status zc_moe_pid_update(int64_t N, int64_t Z, int64_t K, const int32_t* counts, int64_t T_all,

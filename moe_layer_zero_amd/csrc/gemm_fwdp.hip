@@ -1,0 +1,422 @@
+// Forward expert GEMMs of bf16 inference layers on packed expert weights.
+//
+// "LongCat-Flash Technical Report", section 2.1: each FFN expert runs only on
+// the tokens routed to it; zero-computation experts never reach this file.
+//
+//   gate/up: h[p][n] = silu(x[tok(p)] . W_g[e][n]) * (x[tok(p)] . W_u[e][n])
+//   down:    y[p][n] = h[p] . W_d[e][n]
+// for the rows p of expert e's segment of the dispatch order.
+//
+// At the LongCat-Flash shape (d = 6144, I = 2048, 512 experts, section 2.4)
+// an expert gets a few hundred rows, so each weight panel is streamed from
+// HBM about once and the GEMMs sit at the HBM/matrix-core balance point.
+// Two properties of the memory system shape this kernel:
+//  - a compute unit returns its loads in issue order, so loads that hit L2
+//    (the gathered activations) wait behind loads that miss to HBM (the
+//    weights): both streams get the same prefetch distance;
+//  - HBM delivers full speed only for whole 128-byte lines: every request
+//    here covers whole lines.
+//
+// Weights are used in the packed layout of zc_moe_pack_weights: for each 32
+// output columns and 16 reduction steps, the 1 KB that a wave's 64 lanes feed
+// to one v_mfma_f32_32x32x16_bf16 as its B operand (lane l: column l % 32,
+// reduction steps 8 (l / 32) .. + 7).  Weights therefore go straight from
+// global memory into registers with 1 KB contiguous loads: no LDS, no barrier.
+//
+// Tile: 256 rows x 256 MFMA columns per 256-thread workgroup (gate/up: 128
+// gate + 128 up columns = 128 columns of h).  Wave w owns all 256 rows and 64
+// columns (gate/up: 32 gate + the matching 32 up columns, so SwiGLU is done
+// in registers): 8 x 2 blocks of 32 x 32 fp32 accumulators (256 registers).
+// Activation rows are staged through a 4-slot LDS ring, 64 reduction steps
+// (one 128-byte row piece) per slot, filled by buffer_load ... lds; rows past
+// the expert's segment load from outside the buffer (no traffic, never
+// stored).  Chunk c (16 bytes) of LDS row r sits in slot c ^ ((r >> 1) & 7),
+// which keeps every 16-lane phase of a fragment read on distinct banks.
+// Three slabs (A and B) are in flight while one is multiplied.
+// Tile order: expert-major; inside an expert, groups of up to 8 row tiles,
+// row tile fastest.  Workgroup b takes logical tiles (b mod 8) * G/8 + b/8 +
+// i * G, so each XCD (blocks are dealt to the 8 XCDs round-robin) works on
+// consecutive tiles: the row tiles sharing a weight panel read it from the
+// same L2.
+#include "zc_common.h"
+
+namespace zc {
+namespace {
+
+constexpr int BK = 64;      // reduction steps per slab
+constexpr int NST = 4;      // LDS ring slots
+constexpr int NTHR = 256;
+constexpr int GMV = 8;      // row tiles per group inside an expert
+
+enum { P_SWIGLU = 0, P_STORE = 1 };
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+struct PParams {
+  int N;                    // experts
+  int ncols;                // output columns (I for gate/up, d for down)
+  int K;                    // reduction length (d for gate/up, I for down)
+  const int32_t* offsets;   // [N+1] rows of each expert in dispatch order
+  const int32_t* mt_off;    // [N+1] prefix of ceil(rows / TM)
+  const bf16_t* A;          // gate/up: x [T][d] gathered through perm; down: h [P][I]
+  uint32_t a_bytes;         // bytes of A (buffer range; offsets past it load nothing)
+  const int32_t* perm;      // gate/up only
+  int kdiv;                 // K of the layer (slot -> token)
+  const bf16_t* B;          // packed W_g or W_d
+  const bf16_t* B2;         // packed W_u (gate/up)
+  bf16_t* C;                // h [P][I] or y [P][d]
+};
+
+__device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
+
+// One 16-byte-per-lane buffer load straight into LDS (64 lanes -> 1 KB at
+// dst).  Kept out of the kernel templates: the host pass drops template
+// kernels that use this builtin in a dependent context.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff,
+                                          int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+}
+
+// s_waitcnt immediate for "vmcnt <= n" (expcnt and lgkmcnt not waited)
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// TM: rows per tile (32, 64, 128 or 256).  LOADS_FIRST: a slab's loads are
+// issued right after its barrier; otherwise they are spread over the first
+// half of its MFMAs (256-row tiles only).
+template <int EPI, int TM, bool LOADS_FIRST>
+__global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
+  constexpr int RB = TM / 32;       // 32-row blocks per tile = A loads per wave per slab
+  constexpr int SLOT = TM * BK;     // bf16 per ring slot
+  constexpr int V = RB + 8;         // loads per wave per slab (A rows + 8 B blocks)
+  static_assert(TM == 32 || TM == 64 || TM == 128 || TM == 256, "tile height");
+  static_assert(LOADS_FIRST || TM == 256, "interleaved issue is laid out for 256-row tiles");
+  __shared__ __align__(16) bf16_t ring[NST * SLOT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  constexpr int OUTN = EPI == P_SWIGLU ? 128 : 256;  // output columns per tile
+  const int NT = p.ncols / OUTN;
+  const int64_t total = static_cast<int64_t>(p.mt_off[p.N]) * NT;
+  const int G = gridDim.x;
+  const int first = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  const int nk = p.K / BK;
+  const int kblk = p.K / 16;  // packed 1 KB blocks per 32 output columns
+
+  // A buffer resource: raw, range-checked against a_bytes
+  const __amdgpu_buffer_rsrc_t arsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(p.A), (short)0, p.a_bytes, 0x00020000);
+
+  // Slab copy of A: instruction i of wave w fills the 1 KB block b = RB w + i
+  // of a slot, i.e. rows 8b + lane/8, slot lane%8, which holds logical chunk
+  // (lane%8) ^ ((row >> 1) & 7) = (lane%8) ^ ((4b + lane/16) & 7).
+  // Fragment reads: rows 32 rb + lane%32 all have (row >> 1) & 7 = (lane >> 1) & 7.
+  const int s7 = (lane >> 1) & 7;
+  const int khalf = lane >> 5;
+  const int frag_lane = (lane & 31) * BK;
+
+  for (int64_t L = first; L < total; L += G) {
+    // ---- which expert, row tile and column tile
+    const int lmt = static_cast<int>(L / NT);
+    int lo = 0, hi = p.N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.mt_off[mid] <= lmt) lo = mid;
+      else hi = mid - 1;
+    }
+    const int e = lo;
+    const int mte = p.mt_off[e + 1] - p.mt_off[e];
+    const int q = static_cast<int>(L - static_cast<int64_t>(p.mt_off[e]) * NT);
+    const int grp = q / (GMV * NT);
+    const int fm = grp * GMV;
+    const int gsz = min(GMV, mte - fm);
+    const int rr = q - grp * GMV * NT;
+    const int mt = fm + rr % gsz;
+    const int nt = rr / gsz;
+    const int m0 = p.offsets[e] + mt * TM;
+    const int mcount = min(TM, p.offsets[e + 1] - m0);
+    const int n0 = nt * OUTN;
+
+    // ---- byte offsets of the RB A row pieces this lane copies per slab
+    uint32_t aoff[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int b = RB * wave + i;
+      const int row = 8 * b + (lane >> 3);
+      const int chunk = (lane & 7) ^ ((4 * b + (lane >> 4)) & 7);
+      if (row < mcount) {
+        const int gm = m0 + row;
+        const int src = EPI == P_SWIGLU ? p.perm[gm] / p.kdiv : gm;
+        aoff[i] = (static_cast<uint32_t>(src) * static_cast<uint32_t>(p.K) + chunk * 8) * 2u;
+      } else {
+        aoff[i] = p.a_bytes;  // out of range: the load returns zeros, reads nothing
+      }
+    }
+    // ---- packed B: this wave's two column groups of 32
+    const int64_t mat = static_cast<int64_t>(p.ncols) * p.K;
+    const bf16_t* b0;
+    const bf16_t* b1;
+    if constexpr (EPI == P_SWIGLU) {
+      const int g = n0 / 32 + wave;
+      b0 = p.B + e * mat + static_cast<int64_t>(g) * kblk * 512 + lane * 8;
+      b1 = p.B2 + e * mat + static_cast<int64_t>(g) * kblk * 512 + lane * 8;
+    } else {
+      const int g = n0 / 32 + 2 * wave;
+      b0 = p.B + e * mat + static_cast<int64_t>(g) * kblk * 512 + lane * 8;
+      b1 = b0 + static_cast<int64_t>(kblk) * 512;
+    }
+
+    bf16x8_t bq[NST][2][4];  // B fragments of the slabs in flight
+    auto issue = [&](int kt, int slot, bf16x8_t (&bf)[2][4]) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        lds_void* dst = (lds_void*)(ring + slot * SLOT + (RB * wave + i) * 8 * BK);
+        lds_dma16(arsrc, dst, aoff[i], kt * BK * 2);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bf[0][t] = *reinterpret_cast<const bf16x8_t*>(b0 + (4 * kt + t) * 512);
+        bf[1][t] = *reinterpret_cast<const bf16x8_t*>(b1 + (4 * kt + t) * 512);
+      }
+    };
+
+    f32x16_t acc[RB][2];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    auto compute = [&](int slot, const bf16x8_t (&bf)[2][4]) {
+      const bf16_t* a_s = ring + slot * SLOT + frag_lane;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int co = ((2 * t + khalf) ^ s7) << 3;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(a_s + rb * 32 * BK + co);
+          acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[0][t], acc[rb][0], 0, 0, 0);
+          acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[1][t], acc[rb][1], 0, 0, 0);
+        }
+      }
+    };
+
+    // Issue order inside a slab (4 RB fragment reads, 8 RB MFMAs, V loads):
+    // loads first, or spread over the first MFMAs; fragment reads run up to
+    // three ahead of the MFMAs that use them.
+    constexpr int NDS = 4 * RB;
+    constexpr int DS0 = NDS < 3 ? NDS : 3;
+    auto sched = [&](bool with_loads) {
+      if (with_loads && LOADS_FIRST) __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
+      if (with_loads && !LOADS_FIRST) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int g = 0; g < 14; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        return;
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, DS0, 0);
+#pragma unroll
+      for (int g = 0; g < NDS - DS0; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * DS0, 0);
+    };
+
+    // Slab kt: wait until at most the loads of the two younger slabs in
+    // flight are outstanding (V per slab per wave), barrier (slab kt visible
+    // to every wave, slot of slab kt-1 free), refill that slot with slab
+    // kt+3, multiply slab kt.  K is a multiple of 4 BK, so the loop runs in
+    // groups of four slabs with static buffer indexes.  The wait counts
+    // assume the loads of different slabs are never interleaved: scheduling
+    // barriers keep each slab's loads together, in slab order.
+    __builtin_amdgcn_sched_barrier(0);
+    issue(0, 0, bq[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(1, 1, bq[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(2, 2, bq[2]);
+    __builtin_amdgcn_sched_barrier(0);
+    int kt = 0;
+    for (; kt < nk - 4; kt += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
+        __builtin_amdgcn_s_barrier();
+        issue(kt + u + 3, (u + 3) & 3, bq[(u + 3) & 3]);
+        compute(u, bq[u]);
+        sched(true);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // last four slabs: slab nk-1 is issued at nk-4, then the pipeline drains
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
+    __builtin_amdgcn_s_barrier();
+    issue(kt + 3, 3, bq[3]);
+    compute(0, bq[0]);
+    sched(true);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
+    __builtin_amdgcn_s_barrier();
+    compute(1, bq[1]);
+    sched(false);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(V));
+    __builtin_amdgcn_s_barrier();
+    compute(2, bq[2]);
+    sched(false);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_barrier();
+    compute(3, bq[3]);
+    sched(false);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- epilogue: lane holds column lane%32 of its column group and rows
+    // 32 rb + 8 (v/4) + 4 (lane/32) + v%4.  The bf16 tile is staged in the
+    // ring (free once every wave has passed the barrier below; TM x OUTN
+    // bf16 fit in its 4 TM x 64), then written out with 16-byte
+    // row-contiguous stores; the last barrier keeps the next tile's loads
+    // from refilling the ring before the staging is read.
+    __syncthreads();  // every wave done reading the ring
+    bf16_t* st = ring;  // OUTN columns per row
+    const int rbase = 4 * khalf;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rl = rbase + 32 * rb + 8 * (v >> 2) + (v & 3);
+        if constexpr (EPI == P_SWIGLU) {
+          st[rl * OUTN + 32 * wave + (lane & 31)] = f2bf(silu_f(acc[rb][0][v]) * acc[rb][1][v]);
+        } else {
+          st[rl * OUTN + 64 * wave + (lane & 31)] = f2bf(acc[rb][0][v]);
+          st[rl * OUTN + 64 * wave + 32 + (lane & 31)] = f2bf(acc[rb][1][v]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    constexpr int RC = OUTN / 8;  // 16-byte chunks per row
+    for (int c = tid; c < mcount * RC; c += NTHR) {
+      const int rl = c / RC, cc = (c % RC) * 8;
+      *reinterpret_cast<u32x4_t*>(p.C + static_cast<int64_t>(m0 + rl) * p.ncols + n0 + cc) =
+          *reinterpret_cast<const u32x4_t*>(st + rl * OUTN + cc);
+    }
+    __syncthreads();  // staging read before the next tile's loads refill the ring
+  }
+}
+
+// Packed layout of one [R][C] weight matrix (R output columns, C reduction
+// steps): element (r, c) sits at
+//   ((r / 32) * (C / 16) + c / 16) * 512 + (r % 32 + 32 * ((c / 8) % 2)) * 8 + c % 8.
+// One thread writes one 16-byte chunk (8 consecutive c of one r).
+__global__ __launch_bounds__(256) void pack_kernel(const bf16_t* __restrict__ src,
+                                                   bf16_t* __restrict__ dst, int64_t nchunks,
+                                                   int R, int C) {
+  const int64_t per_mat = static_cast<int64_t>(R) * C / 8;
+  const int kb = C / 16;
+  for (int64_t q = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; q < nchunks;
+       q += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t m = q / per_mat;
+    const int64_t o = q - m * per_mat;
+    const int64_t blk = o >> 6;
+    const int l = static_cast<int>(o & 63);
+    const int64_t r = (blk / kb) * 32 + (l & 31);
+    const int64_t c = (blk % kb) * 16 + (l >> 5) * 8;
+    const int64_t base = m * R * static_cast<int64_t>(C);
+    *reinterpret_cast<u32x4_t*>(dst + base + o * 8) =
+        *reinterpret_cast<const u32x4_t*>(src + base + r * C + c);
+  }
+}
+
+// Kernel of each (epilogue, tile height); tiles of up to 64 rows leave room
+// for two workgroups per CU.
+typedef void (*fwdp_fn)(PParams);
+fwdp_fn pick_kernel(int epi, int tm, int* per_cu) {
+  *per_cu = tm <= 64 ? 2 : 1;
+  if (epi == P_SWIGLU) {
+    switch (tm) {
+      case 32: return fwdp_kernel<P_SWIGLU, 32, true>;
+      case 64: return fwdp_kernel<P_SWIGLU, 64, true>;
+      case 128: return fwdp_kernel<P_SWIGLU, 128, true>;
+      case 256: return fwdp_kernel<P_SWIGLU, 256, true>;
+    }
+  } else {
+    switch (tm) {
+      case 32: return fwdp_kernel<P_STORE, 32, true>;
+      case 64: return fwdp_kernel<P_STORE, 64, true>;
+      case 128: return fwdp_kernel<P_STORE, 128, true>;
+      case 256: return fwdp_kernel<P_STORE, 256, false>;
+    }
+  }
+  return nullptr;
+}
+
+hipError_t launch_tm(int epi, int tm, const PParams& p, int cu, hipStream_t s) {
+  int per_cu = 1;
+  fwdp_fn k = pick_kernel(epi, tm, &per_cu);
+  if (!k) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k, dim3(per_cu * cu), dim3(NTHR), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Rows per tile for a layer whose FFN experts average `avg_rows` rows: the
+// smallest of 32, 64, 128, 256 that covers the average (few rows: the GEMMs
+// only stream weights, so padding rows cost matrix-core time and power for
+// nothing; many rows: 256-row tiles read each weight panel least often).
+int fwdp_rows_per_tile(int64_t avg_rows) {
+  if (avg_rows <= 32) return 32;
+  if (avg_rows <= 64) return 64;
+  if (avg_rows <= 128) return 128;
+  return 256;
+}
+
+hipError_t launch_fwdp_gateup(const bf16_t* x, int64_t x_elems, const bf16_t* wg_p,
+                              const bf16_t* wu_p, const int32_t* offsets, const int32_t* perm,
+                              const int32_t* mt_off, int tm, int N, int I, int d, int K, bf16_t* h,
+                              int cu, hipStream_t s) {
+  PParams p{};
+  p.N = N; p.ncols = I; p.K = d;
+  p.offsets = offsets; p.mt_off = mt_off;
+  p.A = x; p.a_bytes = static_cast<uint32_t>(x_elems * 2); p.perm = perm; p.kdiv = K;
+  p.B = wg_p; p.B2 = wu_p; p.C = h;
+  return launch_tm(P_SWIGLU, tm, p, cu, s);
+}
+
+hipError_t launch_fwdp_down(const bf16_t* h, int64_t h_elems, const bf16_t* wd_p,
+                            const int32_t* offsets, const int32_t* mt_off, int tm, int N, int I,
+                            int d, bf16_t* y, int cu, hipStream_t s) {
+  PParams p{};
+  p.N = N; p.ncols = d; p.K = I;
+  p.offsets = offsets; p.mt_off = mt_off;
+  p.A = h; p.a_bytes = static_cast<uint32_t>(h_elems * 2);
+  p.B = wd_p; p.C = y;
+  return launch_tm(P_STORE, tm, p, cu, s);
+}
+
+hipError_t launch_pack_weights(const bf16_t* src, bf16_t* dst, int64_t nmat, int R, int C,
+                               hipStream_t s) {
+  const int64_t nchunks = nmat * R * static_cast<int64_t>(C) / 8;
+  if (nchunks == 0) return hipSuccess;
+  const int64_t want = (nchunks + 255) / 256;
+  const int grid = static_cast<int>(want < 16384 ? want : 16384);
+  hipLaunchKernelGGL(pack_kernel, dim3(grid), dim3(256), 0, s, src, dst, nchunks, R, C);
+  return hipGetLastError();
+}
+
+}  // namespace zc

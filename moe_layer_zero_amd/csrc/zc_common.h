@@ -116,6 +116,22 @@ hipError_t launch_fwd_down(const bf16_t* h, const bf16_t* wd, const int32_t* off
                            const int32_t* mt_off, int N, int I, int d, bf16_t* y, int cu,
                            hipStream_t s);
 
+// bf16 forward expert GEMMs on packed weights (gemm_fwdp.hip): x_elems /
+// h_elems bound the activation buffer (loads past it read nothing); tm is
+// the row-tile height, fwdp_rows_per_tile(T*K/N), and mt_off the prefix of
+// ceil(rows / tm) from the dispatch step.
+int fwdp_rows_per_tile(int64_t avg_rows);
+hipError_t launch_fwdp_gateup(const bf16_t* x, int64_t x_elems, const bf16_t* wg_p,
+                              const bf16_t* wu_p, const int32_t* offsets, const int32_t* perm,
+                              const int32_t* mt_off, int tm, int N, int I, int d, int K, bf16_t* h,
+                              int cu, hipStream_t s);
+hipError_t launch_fwdp_down(const bf16_t* h, int64_t h_elems, const bf16_t* wd_p,
+                            const int32_t* offsets, const int32_t* mt_off, int tm, int N, int I,
+                            int d, bf16_t* y, int cu, hipStream_t s);
+// nmat row-major [R][C] bf16 matrices -> packed layout (R % 32 == 0, C % 16 == 0).
+hipError_t launch_pack_weights(const bf16_t* src, bf16_t* dst, int64_t nmat, int R, int C,
+                               hipStream_t s);
+
 // Combine: out = out_scale * (c_t x_t + sum_r g_r y[inv]).
 template <typename T>
 hipError_t launch_combine(const T* x, const T* y, const int32_t* topk_idx, const float* gate,

@@ -20,10 +20,13 @@ LIB_PATH = os.path.join(HERE, "libzcmoe.so")
 ZC_OK, ZC_ERR_INVALID, ZC_ERR_UNSUPPORTED, ZC_ERR_WORKSPACE, ZC_ERR_HIP = range(5)
 ZC_F32, ZC_BF16 = 0, 1
 ZC_OP_ROUTE, ZC_OP_FORWARD, ZC_OP_BACKWARD = 0, 1, 2
+ZC_WEIGHTS_ROWMAJOR, ZC_WEIGHTS_PACKED = 0, 1
+ZC_PACK_GATE_UP, ZC_PACK_DOWN = 0, 1
 
 # Every symbol include/zc_moe.h declares.
 EXPORTS = ("zc_moe_workspace_size", "zc_moe_saved_size", "zc_moe_route", "zc_moe_forward",
-           "zc_moe_backward", "zc_moe_pid_update", "zc_moe_profile", "zc_moe_profile_read",
+           "zc_moe_backward", "zc_moe_pid_update", "zc_moe_pack_weights", "zc_moe_profile",
+           "zc_moe_profile_read",
            "zc_moe_phase_name", "zc_status_string", "zc_last_error")
 ZC_NUM_PHASES = 16
 
@@ -37,7 +40,8 @@ class ZcError(RuntimeError):
 class zc_moe_desc(C.Structure):
     _fields_ = [("T", C.c_int64), ("d", C.c_int64), ("N", C.c_int64), ("Z", C.c_int64),
                 ("I", C.c_int64), ("K", C.c_int64), ("dtype", C.c_int32),
-                ("gate_norm", C.c_int32), ("out_scale", C.c_float)]
+                ("gate_norm", C.c_int32), ("out_scale", C.c_float),
+                ("weight_layout", C.c_int32)]
 
 
 class zc_route_buf(C.Structure):
@@ -67,7 +71,9 @@ def lib() -> C.CDLL:
         L.zc_moe_forward.argtypes = [P, v, v, v, v, v, v, v, D, v, v, sz, v]
         L.zc_moe_backward.argtypes = [P, v, v, v, v, v, D, v, v, v, v, v, v, v, v, sz, v]
         L.zc_moe_pid_update.argtypes = [i64, i64, i64, v, i64, C.c_double, C.c_double, v, v]
-        for f in ("zc_moe_route", "zc_moe_forward", "zc_moe_backward", "zc_moe_pid_update"):
+        L.zc_moe_pack_weights.argtypes = [P, C.c_int, v, v, v]
+        for f in ("zc_moe_route", "zc_moe_forward", "zc_moe_backward", "zc_moe_pid_update",
+                  "zc_moe_pack_weights"):
             getattr(L, f).restype = C.c_int
         L.zc_moe_profile.argtypes = [C.c_int]
         L.zc_moe_profile.restype = C.c_int
@@ -117,6 +123,7 @@ class LayerDesc:
     dtype: torch.dtype = torch.bfloat16
     gate_norm: int = 1
     out_scale: float = 1.0
+    weight_layout: int = ZC_WEIGHTS_ROWMAJOR
 
     @property
     def E(self) -> int:
@@ -127,7 +134,7 @@ class LayerDesc:
             raise ValueError("layer dtype must be float32 or bfloat16")
         return zc_moe_desc(self.T, self.d, self.N, self.Z, self.I, self.K,
                            ZC_F32 if self.dtype == torch.float32 else ZC_BF16,
-                           self.gate_norm, self.out_scale)
+                           self.gate_norm, self.out_scale, self.weight_layout)
 
 
 class RouteBuffers:
@@ -231,6 +238,28 @@ def zc_moe_pid_update(N: int, Z: int, K: int, counts, T_all: int, mu: float, K_e
     _check_layer_tensor(bias, (N + Z,), torch.float32, "bias")
     _check(lib().zc_moe_pid_update(N, Z, K, _ptr(counts), T_all, float(mu), float(K_e),
                                    _ptr(bias), _stream(stream)), "zc_moe_pid_update")
+
+
+def zc_moe_pack_weights(desc: LayerDesc, which: int, src, dst, stream=None):
+    """Packs w_gate or w_up (which = ZC_PACK_GATE_UP, [N][I][d]) or w_down
+    (ZC_PACK_DOWN, [N][d][I]) into dst, a tensor of the same shape and dtype
+    whose bytes then hold the packed layout."""
+    shape = (desc.N, desc.I, desc.d) if which == ZC_PACK_GATE_UP else (desc.N, desc.d, desc.I)
+    _check_layer_tensor(src, shape, desc.dtype, "src")
+    _check_layer_tensor(dst, shape, desc.dtype, "dst")
+    d = desc.c()
+    _check(lib().zc_moe_pack_weights(C.byref(d), which, _ptr(src), _ptr(dst), _stream(stream)),
+           "zc_moe_pack_weights")
+
+
+def pack_expert_weights(desc: LayerDesc, w_gate, w_up, w_down, stream=None):
+    """Packed copies (new tensors) of the three expert weight tensors."""
+    out = []
+    for w, which in ((w_gate, ZC_PACK_GATE_UP), (w_up, ZC_PACK_GATE_UP), (w_down, ZC_PACK_DOWN)):
+        p = torch.empty_like(w)
+        zc_moe_pack_weights(desc, which, w, p, stream)
+        out.append(p)
+    return tuple(out)
 
 
 def zc_moe_profile(on: bool) -> None:

@@ -20,6 +20,8 @@ out of the element-wise output comparison.
 """
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import torch
 
@@ -44,12 +46,24 @@ def host(t: torch.Tensor) -> np.ndarray:
     return synth.to_np(t)
 
 
-def run_forward(desc, Lg, saved=False):
+def pack_ref(w: np.ndarray) -> np.ndarray:
+    """The packed weight layout of include/zc_moe.h as a numpy permutation of
+    [N][R][C] (R output columns, C reduction length): element (r, c) moves to
+    block (r/32)*(C/16) + c/16, lane r%32 + 32*((c/8)%2), position c%8."""
+    n, r, c = w.shape
+    return np.ascontiguousarray(
+        w.reshape(n, r // 32, 32, c // 16, 2, 8).transpose(0, 1, 3, 4, 2, 5)).reshape(n, r, c)
+
+
+def run_forward(desc, Lg, saved=False, packed=False):
     route = zcmoe.RouteBuffers(desc)
     out = torch.empty((desc.T, desc.d), dtype=desc.dtype, device="cuda")
     sv = zcmoe.saved_buffer(desc) if saved else None
-    zcmoe.zc_moe_forward(desc, Lg["x"], Lg["wr"], Lg["bias"], Lg.get("wg"), Lg.get("wu"),
-                         Lg.get("wd"), out, route, sv)
+    wg, wu, wd = Lg.get("wg"), Lg.get("wu"), Lg.get("wd")
+    if packed:
+        wg, wu, wd = zcmoe.pack_expert_weights(desc, wg, wu, wd)
+        desc = dataclasses.replace(desc, weight_layout=zcmoe.ZC_WEIGHTS_PACKED)
+    zcmoe.zc_moe_forward(desc, Lg["x"], Lg["wr"], Lg["bias"], wg, wu, wd, out, route, sv)
     torch.cuda.synchronize()
     return route, out, sv
 

@@ -135,3 +135,37 @@ def test_binding_rejects_host_tensors():
     with pytest.raises((ValueError, zcmoe.ZcError)):
         zcmoe.zc_moe_route(d, x, torch.zeros(12, 128), torch.zeros(12),
                            zcmoe.RouteBuffers(d, device="cpu"), ws=x)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(weight_layout=2), zcmoe.ZC_ERR_INVALID),
+    (dict(weight_layout=zcmoe.ZC_WEIGHTS_PACKED), zcmoe.ZC_ERR_UNSUPPORTED),   # fp32 layer
+    (dict(weight_layout=zcmoe.ZC_WEIGHTS_PACKED, dtype=torch.bfloat16), zcmoe.ZC_ERR_UNSUPPORTED),
+    (dict(weight_layout=zcmoe.ZC_WEIGHTS_PACKED, dtype=torch.bfloat16, d=256, I=128),
+     zcmoe.ZC_ERR_UNSUPPORTED),
+])
+def test_bad_weight_layouts(L, bad, code):
+    assert call_route(L, desc(**bad)) == code
+
+
+def test_packed_weight_argument_checks(L):
+    d = desc(dtype=torch.bfloat16, d=256, I=256, weight_layout=zcmoe.ZC_WEIGHTS_PACKED)
+    dd = d.c()
+    r = route_buf()
+    big = 1 << 40
+    # packed weights serve the inference forward only
+    st = L.zc_moe_forward(C.byref(dd), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, C.byref(r), FAKE,
+                          FAKE, big, None)
+    assert st == zcmoe.ZC_ERR_UNSUPPORTED and "row-major" in L.zc_last_error().decode()
+    st = L.zc_moe_backward(C.byref(dd), FAKE, FAKE, FAKE, FAKE, FAKE, C.byref(r), FAKE, FAKE, FAKE,
+                           FAKE, FAKE, FAKE, FAKE, FAKE, big, None)
+    assert st == zcmoe.ZC_ERR_UNSUPPORTED and "row-major" in L.zc_last_error().decode()
+    # the packing call itself
+    other = C.c_void_p(1 << 40)
+    assert L.zc_moe_pack_weights(C.byref(dd), 5, FAKE, other, None) == zcmoe.ZC_ERR_INVALID
+    assert L.zc_moe_pack_weights(C.byref(dd), 0, FAKE, FAKE, None) == zcmoe.ZC_ERR_INVALID
+    assert "overlap" in L.zc_last_error().decode()
+    f32 = desc(d=256, I=256).c()
+    assert L.zc_moe_pack_weights(C.byref(f32), 0, FAKE, other, None) == zcmoe.ZC_ERR_UNSUPPORTED
+    odd = desc(dtype=torch.bfloat16, d=256, I=192).c()
+    assert L.zc_moe_pack_weights(C.byref(odd), 1, FAKE, other, None) == zcmoe.ZC_ERR_UNSUPPORTED

@@ -121,14 +121,14 @@ def test_pid_update_is_bit_exact(N, Z, K, T, mu, Ke):
 
 
 # ------------------------------------------------------------ forward, small layers
-def forward_case(sh, gate_norm=1, out_scale=1.0, bias=None, toks=None):
+def forward_case(sh, gate_norm=1, out_scale=1.0, bias=None, toks=None, packed=False):
     L = synth.make_layer(sh, "cpu")
     if bias is not None:
         L["bias"] = bias
     Lg = H.to_dev(L)
     desc = H.desc_of(sh, gate_norm, out_scale)
-    print(f"[forward] {sh.name} T={sh.T} gate_norm={gate_norm}", flush=True)
-    route, out, _ = H.run_forward(desc, Lg)
+    print(f"[forward] {sh.name} T={sh.T} gate_norm={gate_norm} packed={packed}", flush=True)
+    route, out, _ = H.run_forward(desc, Lg, packed=packed)
     xh, wrh = H.host(L["x"]), H.host(L["wr"])
     lg = oracle.logits(xh, wrh)
     H.assert_logits(route.logits, lg)
@@ -190,11 +190,11 @@ def test_forward_is_deterministic():
 
 
 # ------------------------------------------------------------ forward, LongCat-Flash shapes
-def big_case(sh, n_logit_tok=256, n_out_tok=8):
-    print(f"[forward-big] {sh.name} T={sh.T}", flush=True)
+def big_case(sh, n_logit_tok=256, n_out_tok=8, packed=False):
+    print(f"[forward-big] {sh.name} T={sh.T} packed={packed}", flush=True)
     Lg = synth.make_layer(sh, "cuda")
     desc = H.desc_of(sh)
-    route, out, _ = H.run_forward(desc, Lg)
+    route, out, _ = H.run_forward(desc, Lg, packed=packed)
     g = torch.Generator().manual_seed(123)
     toks = torch.randperm(sh.T, generator=g)[: min(n_logit_tok, sh.T)].sort().values.numpy()
     xh = H.host(Lg["x"][torch.from_numpy(toks).cuda()])
@@ -224,6 +224,63 @@ def test_forward_decode_full_size():
 
 def test_forward_prefill_full_size():
     big_case(CF["prefill_bf16"])
+
+
+# ------------------------------------------------------------ packed expert weights
+def test_pack_weights_is_the_documented_permutation():
+    g = torch.Generator(device="cuda").manual_seed(5)
+    for which, shape in ((zcmoe.ZC_PACK_GATE_UP, (3, 512, 256)), (zcmoe.ZC_PACK_DOWN, (3, 256, 512))):
+        desc = zcmoe.LayerDesc(64, 256, 3, 1, 512, 2, torch.bfloat16)
+        w = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+        p = torch.empty_like(w)
+        zcmoe.zc_moe_pack_weights(desc, which, w, p)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(H.host(p), H.pack_ref(H.host(w)))
+
+
+def test_forward_packed_small_bf16():
+    forward_case(CF["small_bf16"], packed=True)
+
+
+def test_forward_packed_ragged_and_literal_gates():
+    sh = CF["small_bf16"].with_T(1000)
+    forward_case(sh, gate_norm=0, out_scale=0.7, bias=torch.zeros(sh.E), packed=True)
+
+
+def test_forward_packed_few_rows_per_expert():
+    # decode-like: most experts get a handful of rows, most of every row tile
+    # reads outside the activation buffer
+    forward_case(CF["small_bf16"].with_T(40), packed=True)
+
+
+def test_forward_packed_single_expert_mlp():
+    sh = synth.LayerShape("mlp256", 9, 600, 256, 1, 0, 256, 1, "bf16", 0.05, "zero")
+    forward_case(sh, packed=True)
+
+
+def test_forward_packed_all_zero_computation_picks():
+    sh = CF["small_bf16"].with_T(300)
+    b = torch.zeros(sh.E)
+    b[sh.N:] = 1.0
+    L, Lg, desc, route, out, o = forward_case(sh, bias=b, packed=True)
+    assert route.offsets[-1].item() == 0
+
+
+def test_forward_packed_is_deterministic():
+    sh = CF["small_bf16"]
+    Lg = H.to_dev(synth.make_layer(sh, "cpu"))
+    desc = H.desc_of(sh)
+    _, a, _ = H.run_forward(desc, Lg, packed=True)
+    _, b, _ = H.run_forward(desc, Lg, packed=True)
+    assert torch.equal(a, b)
+
+
+def test_forward_packed_decode_full_size():
+    big_case(CF["decode_bf16"], packed=True)
+
+
+def test_forward_packed_prefill_full_size():
+    big_case(CF["prefill_bf16"], packed=True)
 
 
 # ------------------------------------------------------------ backward
