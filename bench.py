@@ -14,6 +14,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill]
 from __future__ import annotations
 
 import argparse
+import dataclasses
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +31,24 @@ from moe_layer_zero_amd import synth, zcmoe  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
+
+# HBM bytes of one prefill gate/up launch read from rocprofv3 counters
+# (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a plain copy of known
+# size gives), valid for the kernel source they were measured on: reported
+# as roofline.traffic only while that source is unchanged.
+GATE_UP_TRAFFIC = {"source": "moe_layer_zero_amd/csrc/gemm_fwdp.hip",
+                   "sha256": "27bc6658c92d26eb0d71166ee6b442b33d441e821f0c9ca759be744daf84f582",
+                   "fetch_bytes": 32217948885, "write_bytes": 594657280}
+
+
+def measured_traffic():
+    path = os.path.join(ROOT, GATE_UP_TRAFFIC["source"])
+    if GATE_UP_TRAFFIC["sha256"] is None or not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(path, "rb").read()).hexdigest()
+    if sha != GATE_UP_TRAFFIC["sha256"]:
+        return None
+    return GATE_UP_TRAFFIC["fetch_bytes"] + GATE_UP_TRAFFIC["write_bytes"]
 
 
 def log(*a):
@@ -61,10 +81,19 @@ def timed(fn, steps, warmup):
     return a.elapsed_time(b) / steps, phases
 
 
-def layer_forward_bench(sh, steps, warmup):
+def layer_forward_bench(sh, steps, warmup, packed=True):
+    """Inference forward of one layer.  packed: the expert weights are
+    rearranged once (untimed, like loading a model) into the packed layout
+    the bf16 inference kernels stream; the row-major copies are dropped."""
     log(f"[bench] generating {sh.name} layer on the GPU")
     Lg = synth.make_layer(sh, "cuda")
     desc = desc_of(sh)
+    if packed:
+        Lg["wg"], Lg["wu"], Lg["wd"] = zcmoe.pack_expert_weights(desc, Lg["wg"], Lg["wu"],
+                                                                 Lg["wd"])
+        desc = dataclasses.replace(desc, weight_layout=zcmoe.ZC_WEIGHTS_PACKED)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     route = zcmoe.RouteBuffers(desc)
     out = torch.empty((sh.T, sh.d), dtype=sh.torch_dtype, device="cuda")
     ws = zcmoe.workspace(desc, zcmoe.ZC_OP_FORWARD)
@@ -97,15 +126,15 @@ def gate_up_roofline(sh, p_real, touched, gu_ms):
     hbm = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(gbs / HBM_PEAK_GBS, 4)}
     roof = dict(hbm if hbm_floor > mfma_floor else mfma)
-    roof.update(kernel="gate_up_gemm", traffic=None,
+    roof.update(kernel="gate_up_gemm", traffic=measured_traffic(),
                 algorithmic={"flop": flops, "bytes": nbytes, "hbm_floor_ms": hbm_floor * 1e3,
                              "mfma_floor_ms": mfma_floor * 1e3})
     return roof, mfma, hbm
 
 
-def prefill(steps, warmup):
+def prefill(steps, warmup, packed=True):
     sh = synth.CONFIGS["prefill_bf16"]
-    Lg, ms, ph, p_real, touched, counts = layer_forward_bench(sh, steps, warmup)
+    Lg, ms, ph, p_real, touched, counts = layer_forward_bench(sh, steps, warmup, packed)
     d, I = sh.d, sh.I
     flops_gu = 4.0 * d * I * p_real          # gate and up projections of every FFN pick
     flops_dn = 2.0 * d * I * p_real
@@ -133,9 +162,9 @@ def prefill(steps, warmup):
     return sh, res, roof
 
 
-def decode(steps, warmup):
+def decode(steps, warmup, packed=True):
     sh = synth.CONFIGS["decode_bf16"]
-    Lg, ms, ph, p_real, touched, counts = layer_forward_bench(sh, steps, warmup)
+    Lg, ms, ph, p_real, touched, counts = layer_forward_bench(sh, steps, warmup, packed)
     d, I, E = sh.d, sh.I, sh.E
     w_bytes = 2.0 * 3 * d * I * touched       # every touched expert's weights once (bf16)
     layer_bytes = w_bytes + 2.0 * d * E + 2 * 2.0 * sh.T * d + 4.0 * E + 8.0 * sh.T * sh.K
@@ -196,7 +225,7 @@ def train(steps, warmup):
     return res
 
 
-def cpu_baseline(target_s=12.0, max_tokens=4096):
+def cpu_baseline(target_s=15.0, max_tokens=4096):
     """The fp64 oracle on a bounded sample of the prefill workload: router
     scores, routing and layer output for the first n tokens of a seeded
     random order, n sized so that the timed work takes about target_s
@@ -249,6 +278,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", choices=["prefill", "decode", "train"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rowmajor", action="store_true",
+                    help="inference on row-major expert weights instead of the packed layout")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -265,10 +296,10 @@ def main():
     sh = synth.CONFIGS["prefill_bf16"]
     res = roof = None
     if args.only in (None, "prefill"):
-        sh, res, roof = prefill(args.steps, args.warmup)
+        sh, res, roof = prefill(args.steps, args.warmup, not args.rowmajor)
         log(f"[bench] prefill {res['ms_per_step']:.3f} ms/step")
     if args.only in (None, "decode"):
-        extra["decode"] = decode(args.steps, args.warmup)
+        extra["decode"] = decode(args.steps, args.warmup, not args.rowmajor)
         log(f"[bench] decode {extra['decode']['ms_per_step']:.3f} ms/step")
     if args.only in (None, "train"):
         extra["train"] = train(args.steps, args.warmup)
@@ -294,7 +325,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) inputs, N(0,std) weights, random init)",
         "config": {"workload": sh.name, "T": sh.T, "d": sh.d, "N": sh.N, "Z": sh.Z, "I": sh.I,
-                   "K": sh.K, "bias": sh.bias},
+                   "K": sh.K, "bias": sh.bias,
+                   "expert_weights": "row-major" if args.rowmajor else "packed"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": res,
