@@ -38,6 +38,8 @@
 // i * G, so each XCD (blocks are dealt to the 8 XCDs round-robin) works on
 // consecutive tiles: the row tiles sharing a weight panel read it from the
 // same L2.
+#include <type_traits>
+
 #include "zc_common.h"
 
 namespace zc {
@@ -167,155 +169,174 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
       b1 = b0 + static_cast<int64_t>(kblk) * 512;
     }
 
-    bf16x8_t bq[NST][2][4];  // B fragments of the slabs in flight
-    auto issue = [&](int kt, int slot, bf16x8_t (&bf)[2][4]) {
+    // The tile's pipeline, specialised on the number of 32-row blocks that
+    // hold rows (NRB): a ragged last tile of an expert multiplies and reads
+    // only those, instead of all TM rows.
+    const int nrb = (mcount + 31) >> 5;
+    auto run = [&](auto nrb_c) {
+      constexpr int NRB = decltype(nrb_c)::value;
+      // interleaved issue is laid out for a full 256-row tile
+      constexpr bool LF = LOADS_FIRST || NRB != 8;
+      bf16x8_t bq[NST][2][4];  // B fragments of the slabs in flight
+      auto issue = [&](int kt, int slot, bf16x8_t (&bf)[2][4]) {
 #pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        lds_void* dst = (lds_void*)(ring + slot * SLOT + (RB * wave + i) * 8 * BK);
-        lds_dma16(arsrc, dst, aoff[i], kt * BK * 2);
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        bf[0][t] = *reinterpret_cast<const bf16x8_t*>(b0 + (4 * kt + t) * 512);
-        bf[1][t] = *reinterpret_cast<const bf16x8_t*>(b1 + (4 * kt + t) * 512);
-      }
-    };
-
-    f32x16_t acc[RB][2];
-#pragma unroll
-    for (int i = 0; i < RB; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    auto compute = [&](int slot, const bf16x8_t (&bf)[2][4]) {
-      const bf16_t* a_s = ring + slot * SLOT + frag_lane;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int co = ((2 * t + khalf) ^ s7) << 3;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(a_s + rb * 32 * BK + co);
-          acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[0][t], acc[rb][0], 0, 0, 0);
-          acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[1][t], acc[rb][1], 0, 0, 0);
-        }
-      }
-    };
-
-    // Issue order inside a slab (4 RB fragment reads, 8 RB MFMAs, V loads):
-    // loads first, or spread over the first MFMAs; fragment reads run up to
-    // three ahead of the MFMAs that use them.
-    constexpr int NDS = 4 * RB;
-    constexpr int DS0 = NDS < 3 ? NDS : 3;
-    auto sched = [&](bool with_loads) {
-      if (with_loads && LOADS_FIRST) __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
-      if (with_loads && !LOADS_FIRST) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int i = 0; i < RB; ++i) {
+          lds_void* dst = (lds_void*)(ring + slot * SLOT + (RB * wave + i) * 8 * BK);
+          lds_dma16(arsrc, dst, aoff[i], kt * BK * 2);
         }
 #pragma unroll
-        for (int g = 0; g < 14; ++g) {
+        for (int t = 0; t < 4; ++t) {
+          bf[0][t] = *reinterpret_cast<const bf16x8_t*>(b0 + (4 * kt + t) * 512);
+          bf[1][t] = *reinterpret_cast<const bf16x8_t*>(b1 + (4 * kt + t) * 512);
+        }
+      };
+
+      f32x16_t acc[NRB][2];
+#pragma unroll
+      for (int i = 0; i < NRB; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+      auto compute = [&](int slot, const bf16x8_t (&bf)[2][4]) {
+        const bf16_t* a_s = ring + slot * SLOT + frag_lane;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int co = ((2 * t + khalf) ^ s7) << 3;
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(a_s + rb * 32 * BK + co);
+            acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[0][t], acc[rb][0], 0, 0, 0);
+            acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[1][t], acc[rb][1], 0, 0, 0);
+          }
+        }
+      };
+
+      // Issue order inside a slab (4 NRB fragment reads, 8 NRB MFMAs, V loads):
+      // loads first, or spread over the first MFMAs; fragment reads run up to
+      // three ahead of the MFMAs that use them.
+      constexpr int NDS = 4 * NRB;
+      constexpr int DS0 = NDS < 3 ? NDS : 3;
+      auto sched = [&](bool with_loads) {
+        if (with_loads && LF) __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
+        if (with_loads && !LF) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+          for (int g = 0; g < 16; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+#pragma unroll
+          for (int g = 0; g < 14; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          return;
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, DS0, 0);
+#pragma unroll
+        for (int g = 0; g < NDS - DS0; ++g) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        return;
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, DS0, 0);
-#pragma unroll
-      for (int g = 0; g < NDS - DS0; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * DS0, 0);
-    };
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * DS0, 0);
+      };
 
-    // Slab kt: wait until at most the loads of the two younger slabs in
-    // flight are outstanding (V per slab per wave), barrier (slab kt visible
-    // to every wave, slot of slab kt-1 free), refill that slot with slab
-    // kt+3, multiply slab kt.  K is a multiple of 4 BK, so the loop runs in
-    // groups of four slabs with static buffer indexes.  The wait counts
-    // assume the loads of different slabs are never interleaved: scheduling
-    // barriers keep each slab's loads together, in slab order.
-    __builtin_amdgcn_sched_barrier(0);
-    issue(0, 0, bq[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(1, 1, bq[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(2, 2, bq[2]);
-    __builtin_amdgcn_sched_barrier(0);
-    int kt = 0;
-    for (; kt < nk - 4; kt += 4) {
+      // Slab kt: wait until at most the loads of the two younger slabs in
+      // flight are outstanding (V per slab per wave), barrier (slab kt visible
+      // to every wave, slot of slab kt-1 free), refill that slot with slab
+      // kt+3, multiply slab kt.  K is a multiple of 4 BK, so the loop runs in
+      // groups of four slabs with static buffer indexes.  The wait counts
+      // assume the loads of different slabs are never interleaved: scheduling
+      // barriers keep each slab's loads together, in slab order.
+      __builtin_amdgcn_sched_barrier(0);
+      issue(0, 0, bq[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(1, 1, bq[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(2, 2, bq[2]);
+      __builtin_amdgcn_sched_barrier(0);
+      int kt = 0;
+      for (; kt < nk - 4; kt += 4) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
-        __builtin_amdgcn_s_barrier();
-        issue(kt + u + 3, (u + 3) & 3, bq[(u + 3) & 3]);
-        compute(u, bq[u]);
-        sched(true);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // last four slabs: slab nk-1 is issued at nk-4, then the pipeline drains
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
-    __builtin_amdgcn_s_barrier();
-    issue(kt + 3, 3, bq[3]);
-    compute(0, bq[0]);
-    sched(true);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
-    __builtin_amdgcn_s_barrier();
-    compute(1, bq[1]);
-    sched(false);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(V));
-    __builtin_amdgcn_s_barrier();
-    compute(2, bq[2]);
-    sched(false);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __builtin_amdgcn_s_barrier();
-    compute(3, bq[3]);
-    sched(false);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- epilogue: lane holds column lane%32 of its column group and rows
-    // 32 rb + 8 (v/4) + 4 (lane/32) + v%4.  The bf16 tile is staged in the
-    // ring (free once every wave has passed the barrier below; TM x OUTN
-    // bf16 fit in its 4 TM x 64), then written out with 16-byte
-    // row-contiguous stores; the last barrier keeps the next tile's loads
-    // from refilling the ring before the staging is read.
-    __syncthreads();  // every wave done reading the ring
-    bf16_t* st = ring;  // OUTN columns per row
-    const int rbase = 4 * khalf;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rl = rbase + 32 * rb + 8 * (v >> 2) + (v & 3);
-        if constexpr (EPI == P_SWIGLU) {
-          st[rl * OUTN + 32 * wave + (lane & 31)] = f2bf(silu_f(acc[rb][0][v]) * acc[rb][1][v]);
-        } else {
-          st[rl * OUTN + 64 * wave + (lane & 31)] = f2bf(acc[rb][0][v]);
-          st[rl * OUTN + 64 * wave + 32 + (lane & 31)] = f2bf(acc[rb][1][v]);
+        for (int u = 0; u < 4; ++u) {
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
+          __builtin_amdgcn_s_barrier();
+          issue(kt + u + 3, (u + 3) & 3, bq[(u + 3) & 3]);
+          compute(u, bq[u]);
+          sched(true);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
+      // last four slabs: slab nk-1 is issued at nk-4, then the pipeline drains
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
+      __builtin_amdgcn_s_barrier();
+      issue(kt + 3, 3, bq[3]);
+      compute(0, bq[0]);
+      sched(true);
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
+      __builtin_amdgcn_s_barrier();
+      compute(1, bq[1]);
+      sched(false);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(V));
+      __builtin_amdgcn_s_barrier();
+      compute(2, bq[2]);
+      sched(false);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __builtin_amdgcn_s_barrier();
+      compute(3, bq[3]);
+      sched(false);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- epilogue: lane holds column lane%32 of its column group and rows
+      // 32 rb + 8 (v/4) + 4 (lane/32) + v%4.  The bf16 tile is staged in the
+      // ring (free once every wave has passed the barrier below; TM x OUTN
+      // bf16 fit in its 4 TM x 64), then written out with 16-byte
+      // row-contiguous stores; the last barrier keeps the next tile's loads
+      // from refilling the ring before the staging is read.
+      __syncthreads();  // every wave done reading the ring
+      bf16_t* st = ring;  // OUTN columns per row
+      const int rbase = 4 * khalf;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rl = rbase + 32 * rb + 8 * (v >> 2) + (v & 3);
+          if constexpr (EPI == P_SWIGLU) {
+            st[rl * OUTN + 32 * wave + (lane & 31)] = f2bf(silu_f(acc[rb][0][v]) * acc[rb][1][v]);
+          } else {
+            st[rl * OUTN + 64 * wave + (lane & 31)] = f2bf(acc[rb][0][v]);
+            st[rl * OUTN + 64 * wave + 32 + (lane & 31)] = f2bf(acc[rb][1][v]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
+      constexpr int RC = OUTN / 8;  // 16-byte chunks per row
+      for (int c = tid; c < mcount * RC; c += NTHR) {
+        const int rl = c / RC, cc = (c % RC) * 8;
+        *reinterpret_cast<u32x4_t*>(p.C + static_cast<int64_t>(m0 + rl) * p.ncols + n0 + cc) =
+            *reinterpret_cast<const u32x4_t*>(st + rl * OUTN + cc);
+      }
+      __syncthreads();  // staging read before the next tile's loads refill the ring
+    };
+    switch (nrb) {
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: if constexpr (RB >= 2) run(std::integral_constant<int, 2>{}); break;
+      case 3: if constexpr (RB >= 4) run(std::integral_constant<int, 3>{}); break;
+      case 4: if constexpr (RB >= 4) run(std::integral_constant<int, 4>{}); break;
+      case 5: if constexpr (RB >= 8) run(std::integral_constant<int, 5>{}); break;
+      case 6: if constexpr (RB >= 8) run(std::integral_constant<int, 6>{}); break;
+      case 7: if constexpr (RB >= 8) run(std::integral_constant<int, 7>{}); break;
+      default: if constexpr (RB >= 8) run(std::integral_constant<int, 8>{}); break;
     }
-    __syncthreads();
-    constexpr int RC = OUTN / 8;  // 16-byte chunks per row
-    for (int c = tid; c < mcount * RC; c += NTHR) {
-      const int rl = c / RC, cc = (c % RC) * 8;
-      *reinterpret_cast<u32x4_t*>(p.C + static_cast<int64_t>(m0 + rl) * p.ncols + n0 + cc) =
-          *reinterpret_cast<const u32x4_t*>(st + rl * OUTN + cc);
-    }
-    __syncthreads();  // staging read before the next tile's loads refill the ring
   }
 }
 
