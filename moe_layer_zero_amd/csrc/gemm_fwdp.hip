@@ -61,6 +61,7 @@ struct PParams {
   int K;                    // reduction length (d for gate/up, I for down)
   const int32_t* offsets;   // [N+1] rows of each expert in dispatch order
   const int32_t* mt_off;    // [N+1] prefix of ceil(rows / TM)
+  const int32_t* tile_exp;  // [mt_off[N]] expert of each row tile
   const bf16_t* A;          // gate/up: x [T][d] gathered through perm; down: h [P][I]
   uint32_t a_bytes;         // bytes of A (buffer range; offsets past it load nothing)
   const int32_t* perm;      // gate/up only
@@ -121,13 +122,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   for (int64_t L = first; L < total; L += G) {
     // ---- which expert, row tile and column tile
     const int lmt = static_cast<int>(L / NT);
-    int lo = 0, hi = p.N - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.mt_off[mid] <= lmt) lo = mid;
-      else hi = mid - 1;
-    }
-    const int e = lo;
+    const int e = p.tile_exp[lmt];
     const int mte = p.mt_off[e + 1] - p.mt_off[e];
     const int q = static_cast<int>(L - static_cast<int64_t>(p.mt_off[e]) * NT);
     const int grp = q / (GMV * NT);
@@ -409,22 +404,22 @@ int fwdp_rows_per_tile(int64_t avg_rows) {
 
 hipError_t launch_fwdp_gateup(const bf16_t* x, int64_t x_elems, const bf16_t* wg_p,
                               const bf16_t* wu_p, const int32_t* offsets, const int32_t* perm,
-                              const int32_t* mt_off, int tm, int N, int I, int d, int K, bf16_t* h,
-                              int cu, hipStream_t s) {
+                              const int32_t* mt_off, const int32_t* tile_exp, int tm, int N, int I,
+                              int d, int K, bf16_t* h, int cu, hipStream_t s) {
   PParams p{};
   p.N = N; p.ncols = I; p.K = d;
-  p.offsets = offsets; p.mt_off = mt_off;
+  p.offsets = offsets; p.mt_off = mt_off; p.tile_exp = tile_exp;
   p.A = x; p.a_bytes = static_cast<uint32_t>(x_elems * 2); p.perm = perm; p.kdiv = K;
   p.B = wg_p; p.B2 = wu_p; p.C = h;
   return launch_tm(P_SWIGLU, tm, p, cu, s);
 }
 
 hipError_t launch_fwdp_down(const bf16_t* h, int64_t h_elems, const bf16_t* wd_p,
-                            const int32_t* offsets, const int32_t* mt_off, int tm, int N, int I,
-                            int d, bf16_t* y, int cu, hipStream_t s) {
+                            const int32_t* offsets, const int32_t* mt_off, const int32_t* tile_exp,
+                            int tm, int N, int I, int d, bf16_t* y, int cu, hipStream_t s) {
   PParams p{};
   p.N = N; p.ncols = d; p.K = I;
-  p.offsets = offsets; p.mt_off = mt_off;
+  p.offsets = offsets; p.mt_off = mt_off; p.tile_exp = tile_exp;
   p.A = h; p.a_bytes = static_cast<uint32_t>(h_elems * 2);
   p.B = wd_p; p.C = y;
   return launch_tm(P_STORE, tm, p, cu, s);
