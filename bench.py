@@ -37,8 +37,8 @@ BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
 # size gives), valid for the kernel source they were measured on: reported
 # as roofline.traffic only while that source is unchanged.
 GATE_UP_TRAFFIC = {"source": "moe_layer_zero_amd/csrc/gemm_fwdp.hip",
-                   "sha256": "27bc6658c92d26eb0d71166ee6b442b33d441e821f0c9ca759be744daf84f582",
-                   "fetch_bytes": 32217948885, "write_bytes": 594657280}
+                   "sha256": "7424b66f11288e0dffb2daac59e7ba0bb1b344d18b26be455eb2a469b0758b7a",
+                   "fetch_bytes": 34972781525, "write_bytes": 593608704}
 
 
 def measured_traffic():
