@@ -186,21 +186,26 @@ struct RouteWs {
   int32_t* tile_off;   // row-tile prefix for the generic grouped GEMM
   int32_t* tile_off2;  // row-tile prefix for the bf16 forward expert GEMMs
   int32_t* tile_exp;   // expert of each of those row tiles
+  int32_t* sched;      // tile counters of the packed-weight GEMMs
   void* dispatch;
 };
 // Row tiles of the second prefix, at most: every FFN pick in a tile of its
 // own expert, tiles at least 32 rows high.
 int64_t max_tiles2(const zc_moe_desc* d) { return d->T * d->K / 32 + d->N + 1; }
 int64_t route_ws_bytes(const zc_moe_desc* d) {
-  return 2 * a256(4 * (d->N + 1)) + a256(4 * max_tiles2(d)) +
+  return 2 * a256(4 * (d->N + 1)) + a256(4 * max_tiles2(d)) + a256(4 * zc::kSchedInts) +
          a256(zc::dispatch_scratch_bytes(d->T, d->N + d->Z, d->N));
 }
 RouteWs carve_route(char* p, const zc_moe_desc* d) {
   RouteWs w;
   w.tile_off = reinterpret_cast<int32_t*>(p);
   w.tile_off2 = reinterpret_cast<int32_t*>(p + a256(4 * (d->N + 1)));
-  w.tile_exp = reinterpret_cast<int32_t*>(p + 2 * a256(4 * (d->N + 1)));
-  w.dispatch = p + 2 * a256(4 * (d->N + 1)) + a256(4 * max_tiles2(d));
+  char* q = p + 2 * a256(4 * (d->N + 1));
+  w.tile_exp = reinterpret_cast<int32_t*>(q);
+  q += a256(4 * max_tiles2(d));
+  w.sched = reinterpret_cast<int32_t*>(q);
+  q += a256(4 * zc::kSchedInts);
+  w.dispatch = q;
   return w;
 }
 
@@ -303,7 +308,7 @@ zc_status do_route(const zc_moe_desc* d, const T* x, const T* wr, const float* b
   ZC_LAUNCH(ZC_PH_DISPATCH, zc::launch_dispatch(r->topk_idx, Tn, E, N, K, zc::kGemmBM,
                                                 fwd_rows_per_tile(d),
                                                 r->counts, r->offsets, r->perm, r->inv, w.tile_off,
-                                                w.tile_off2, w.tile_exp, w.dispatch, s),
+                                                w.tile_off2, w.tile_exp, w.sched, w.dispatch, s),
          "dispatch launch");
   return ZC_OK;
 }
@@ -337,13 +342,14 @@ zc_status do_forward(const zc_moe_desc* d, const T* x, const T* wr, const float*
       ZC_LAUNCH(ZC_PH_GATE_UP,
                 zc::launch_fwdp_gateup(hx, d->T * d->d, reinterpret_cast<const bf16_t*>(wg),
                                        reinterpret_cast<const bf16_t*>(wu), r->offsets, r->perm,
-                                       rw.tile_off2, rw.tile_exp, fwd_rows_per_tile(d), N, I, dd,
-                                       K, hh, cu, s),
+                                       rw.tile_off2, rw.tile_exp, rw.sched, fwd_rows_per_tile(d), N,
+                                       I, dd, K, hh, cu, s),
                 "gate/up GEMM launch");
       ZC_LAUNCH(ZC_PH_DOWN,
                 zc::launch_fwdp_down(hh, rows * d->I, reinterpret_cast<const bf16_t*>(wd),
-                                     r->offsets, rw.tile_off2, rw.tile_exp, fwd_rows_per_tile(d),
-                                     N, I, dd, reinterpret_cast<bf16_t*>(y), cu, s),
+                                     r->offsets, rw.tile_off2, rw.tile_exp, rw.sched + 8,
+                                     fwd_rows_per_tile(d), N, I, dd, reinterpret_cast<bf16_t*>(y),
+                                     cu, s),
                 "down GEMM launch");
     } else if (use_fwd_kernels<T>(d, saved)) {
       // bf16 inference: 256 x 256 tiles, weights streamed once per expert

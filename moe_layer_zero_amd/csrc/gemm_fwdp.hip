@@ -34,10 +34,9 @@
 // which keeps every 16-lane phase of a fragment read on distinct banks.
 // Three slabs (A and B) are in flight while one is multiplied.
 // Tile order: expert-major; inside an expert, groups of up to 8 row tiles,
-// row tile fastest.  Workgroup b takes logical tiles (b mod 8) * G/8 + b/8 +
-// i * G, so each XCD (blocks are dealt to the 8 XCDs round-robin) works on
-// consecutive tiles: the row tiles sharing a weight panel read it from the
-// same L2.
+// row tile fastest.  The tiles are dealt to the 8 XCDs in chunks of
+// consecutive tiles, so the row tiles sharing a weight panel read it from
+// the same L2, and an XCD's workgroups claim its tiles from a counter.
 #include <type_traits>
 
 #include "zc_common.h"
@@ -62,6 +61,7 @@ struct PParams {
   const int32_t* offsets;   // [N+1] rows of each expert in dispatch order
   const int32_t* mt_off;    // [N+1] prefix of ceil(rows / TM)
   const int32_t* tile_exp;  // [mt_off[N]] expert of each row tile
+  int32_t* sched;           // [8] per-XCD tile counters, zero at launch
   const bf16_t* A;          // gate/up: x [T][d] gathered through perm; down: h [P][I]
   uint32_t a_bytes;         // bytes of A (buffer range; offsets past it load nothing)
   const int32_t* perm;      // gate/up only
@@ -94,7 +94,10 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   constexpr int V = RB + 8;         // loads per wave per slab (A rows + 8 B blocks)
   static_assert(TM == 32 || TM == 64 || TM == 128 || TM == 256, "tile height");
   static_assert(LOADS_FIRST || TM == 256, "interleaved issue is laid out for 256-row tiles");
-  __shared__ __align__(16) bf16_t ring[NST * SLOT];
+  // the ring, then one int: the next tile index claimed by thread 0 (kept in
+  // the same LDS object, see the note on the tables of the decode)
+  __shared__ __align__(16) bf16_t ring[NST * SLOT + 16];
+  int32_t* const s_claim = reinterpret_cast<int32_t*>(ring + NST * SLOT);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,7 +106,21 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   const int NT = p.ncols / OUTN;
   const int64_t total = static_cast<int64_t>(p.mt_off[p.N]) * NT;
   const int G = gridDim.x;
-  const int first = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+  // Tiles are dealt to the 8 XCDs in chunks of G/8 consecutive tiles, round
+  // robin (blocks are dealt to the XCDs round robin, so block b runs on XCD
+  // b mod 8): the row tiles sharing a weight panel meet in one L2.  Inside an
+  // XCD the workgroups claim the XCD's tiles in order from a counter, so a
+  // workgroup that drew cheap (ragged) tiles takes more of them and all
+  // finish together.  Tile n of XCD x is (n / C) * 8C + x C + n % C.
+  const int xcd = blockIdx.x % 8;
+  const int C = G / 8;
+  int32_t* const claim = p.sched + xcd;
+  auto tile_of = [&](int n) -> int64_t {
+    return static_cast<int64_t>(n / C) * 8 * C + xcd * C + n % C;
+  };
+  if (tid == 0) s_claim[0] = atomicAdd(claim, 1);
+  __syncthreads();
+  int cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
   const int nk = p.K / BK;
   const int kblk = p.K / 16;  // packed 1 KB blocks per 32 output columns
 
@@ -119,7 +136,10 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   const int khalf = lane >> 5;
   const int frag_lane = (lane & 31) * BK;
 
-  for (int64_t L = first; L < total; L += G) {
+  for (int64_t L = tile_of(cur_n); L < total; L = tile_of(cur_n)) {
+    // claim the next tile now; its index is published in the epilogue
+    int32_t next_n = 0;
+    if (tid == 0) next_n = atomicAdd(claim, 1);
     // ---- which expert, row tile and column tile
     const int lmt = static_cast<int>(L / NT);
     const int e = p.tile_exp[lmt];
@@ -320,6 +340,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
         *reinterpret_cast<u32x4_t*>(p.C + static_cast<int64_t>(m0 + rl) * p.ncols + n0 + cc) =
             *reinterpret_cast<const u32x4_t*>(st + rl * OUTN + cc);
       }
+      if (tid == 0) s_claim[0] = next_n;
       __syncthreads();  // staging read before the next tile's loads refill the ring
     };
     switch (nrb) {
@@ -332,6 +353,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
       case 7: if constexpr (RB >= 8) run(std::integral_constant<int, 7>{}); break;
       default: if constexpr (RB >= 8) run(std::integral_constant<int, 8>{}); break;
     }
+    cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
   }
 }
 
@@ -404,11 +426,12 @@ int fwdp_rows_per_tile(int64_t avg_rows) {
 
 hipError_t launch_fwdp_gateup(const bf16_t* x, int64_t x_elems, const bf16_t* wg_p,
                               const bf16_t* wu_p, const int32_t* offsets, const int32_t* perm,
-                              const int32_t* mt_off, const int32_t* tile_exp, int tm, int N, int I,
-                              int d, int K, bf16_t* h, int cu, hipStream_t s) {
+                              const int32_t* mt_off, const int32_t* tile_exp, int32_t* sched,
+                              int tm, int N, int I, int d, int K, bf16_t* h, int cu,
+                              hipStream_t s) {
   PParams p{};
   p.N = N; p.ncols = I; p.K = d;
-  p.offsets = offsets; p.mt_off = mt_off; p.tile_exp = tile_exp;
+  p.offsets = offsets; p.mt_off = mt_off; p.tile_exp = tile_exp; p.sched = sched;
   p.A = x; p.a_bytes = static_cast<uint32_t>(x_elems * 2); p.perm = perm; p.kdiv = K;
   p.B = wg_p; p.B2 = wu_p; p.C = h;
   return launch_tm(P_SWIGLU, tm, p, cu, s);
@@ -416,10 +439,11 @@ hipError_t launch_fwdp_gateup(const bf16_t* x, int64_t x_elems, const bf16_t* wg
 
 hipError_t launch_fwdp_down(const bf16_t* h, int64_t h_elems, const bf16_t* wd_p,
                             const int32_t* offsets, const int32_t* mt_off, const int32_t* tile_exp,
-                            int tm, int N, int I, int d, bf16_t* y, int cu, hipStream_t s) {
+                            int32_t* sched, int tm, int N, int I, int d, bf16_t* y, int cu,
+                            hipStream_t s) {
   PParams p{};
   p.N = N; p.ncols = d; p.K = I;
-  p.offsets = offsets; p.mt_off = mt_off; p.tile_exp = tile_exp;
+  p.offsets = offsets; p.mt_off = mt_off; p.tile_exp = tile_exp; p.sched = sched;
   p.A = h; p.a_bytes = static_cast<uint32_t>(h_elems * 2);
   p.B = wd_p; p.C = y;
   return launch_tm(P_STORE, tm, p, cu, s);

@@ -62,13 +62,15 @@ hipError_t launch_topk(const float* logits, const float* bias, int Tn, int E, in
 // Dispatch: per-expert counts, offsets, canonical permutation and its inverse.
 // Scratch: dispatch_scratch_bytes(T, E, N).  Also writes the per-expert
 // row-tile prefixes tile_off[N+1] and tile_off2[N+1] for the grouped GEMMs
-// (tile heights bm and bm2) and, if tile_exp is not NULL, the expert of each
-// of the tile_off2[N] bm2-row tiles.
+// (tile heights bm and bm2), if tile_exp is not NULL the expert of each of
+// the tile_off2[N] bm2-row tiles, and if sched is not NULL zeroes its
+// kSchedInts tile counters (for the packed-weight GEMMs of the same call).
 size_t dispatch_scratch_bytes(int64_t Tn, int64_t E, int64_t N);
 hipError_t launch_dispatch(const int32_t* topk_idx, int Tn, int E, int N, int K, int bm, int bm2,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                            int32_t* tile_off, int32_t* tile_off2, int32_t* tile_exp,
-                           void* scratch, hipStream_t s);
+                           int32_t* sched, void* scratch, hipStream_t s);
+constexpr int kSchedInts = 16;  // 8 XCD counters for gate/up, 8 for down
 
 // tile_off[N+1] from offsets[N+1] (for a backward call that only has the
 // routing of its forward call).
@@ -122,16 +124,19 @@ hipError_t launch_fwd_down(const bf16_t* h, const bf16_t* wd, const int32_t* off
 
 // bf16 forward expert GEMMs on packed weights (gemm_fwdp.hip): x_elems /
 // h_elems bound the activation buffer (loads past it read nothing); tm is
-// the row-tile height, fwdp_rows_per_tile(T*K/N), and mt_off the prefix of
-// ceil(rows / tm) from the dispatch step.
+// the row-tile height, fwdp_rows_per_tile(T*K/N), mt_off the prefix of
+// ceil(rows / tm) and tile_exp the expert of each tile from the dispatch
+// step; sched: 8 tile counters, zero at launch (the dispatch zeroes them).
 int fwdp_rows_per_tile(int64_t avg_rows);
 hipError_t launch_fwdp_gateup(const bf16_t* x, int64_t x_elems, const bf16_t* wg_p,
                               const bf16_t* wu_p, const int32_t* offsets, const int32_t* perm,
-                              const int32_t* mt_off, const int32_t* tile_exp, int tm, int N, int I,
-                              int d, int K, bf16_t* h, int cu, hipStream_t s);
+                              const int32_t* mt_off, const int32_t* tile_exp, int32_t* sched,
+                              int tm, int N, int I, int d, int K, bf16_t* h, int cu,
+                              hipStream_t s);
 hipError_t launch_fwdp_down(const bf16_t* h, int64_t h_elems, const bf16_t* wd_p,
                             const int32_t* offsets, const int32_t* mt_off, const int32_t* tile_exp,
-                            int tm, int N, int I, int d, bf16_t* y, int cu, hipStream_t s);
+                            int32_t* sched, int tm, int N, int I, int d, bf16_t* y, int cu,
+                            hipStream_t s);
 // nmat row-major [R][C] bf16 matrices -> packed layout (R % 32 == 0, C % 16 == 0).
 hipError_t launch_pack_weights(const bf16_t* src, bf16_t* dst, int64_t nmat, int R, int C,
                                hipStream_t s);
