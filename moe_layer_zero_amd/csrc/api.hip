@@ -236,13 +236,19 @@ int64_t fwd_ws_bytes(const zc_moe_desc* d) {
 
 struct BwdWs {
   int32_t* tile_off;
-  float *gs, *dg, *dl, *dadu, *dxp, *dxr;
+  float *gs, *dg, *dl, *dadu, *dxp, *dxr, *rdw;
 };
+// fp32 partials of the router weight gradient (token chunks), 0 when unsplit
+int64_t rdw_bytes(const zc_moe_desc* d) {
+  const int64_t E = d->N + d->Z;
+  const int s = zc::router_dw_splits(d->T, E, d->d);
+  return s > 1 ? 4 * s * E * d->d : 0;
+}
 int64_t bwd_ws_bytes(const zc_moe_desc* d) {
   const int64_t rows = d->T * d->K, E = d->N + d->Z;
   return a256(4 * (d->N + 1)) + a256(4 * rows) + a256(4 * d->T * d->K) +
          a256(4 * d->T * ldl_of(E)) + a256(4 * rows * 2 * d->I) + a256(4 * rows * d->d) +
-         a256(4 * d->T * d->d);
+         a256(4 * d->T * d->d) + a256(rdw_bytes(d));
 }
 BwdWs carve_bwd(char* p, const zc_moe_desc* d) {
   const int64_t rows = d->T * d->K, E = d->N + d->Z;
@@ -260,6 +266,7 @@ BwdWs carve_bwd(char* p, const zc_moe_desc* d) {
   w.dadu = take(4 * rows * 2 * d->I);
   w.dxp = take(4 * rows * d->d);
   w.dxr = take(4 * d->T * d->d);
+  w.rdw = rdw_bytes(d) > 0 ? take(rdw_bytes(d)) : nullptr;
   return w;
 }
 
@@ -420,7 +427,7 @@ zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg
                                           s),
               "gate/up weight-gradient launch");
   }
-  ZC_LAUNCH(ZC_PH_BWD_ROUTER_DW, zc::launch_router_dw<T>(w.dl, ldl, x, Tn, E, dd, dwr, cu, s),
+  ZC_LAUNCH(ZC_PH_BWD_ROUTER_DW, zc::launch_router_dw<T>(w.dl, ldl, x, Tn, E, dd, dwr, w.rdw, cu, s),
             "router weight-gradient launch");
   if (Tn > 0) {
     ZC_LAUNCH(ZC_PH_BWD_ROUTER_DX, zc::launch_router_dx<T>(w.dl, ldl, wr, Tn, E, dd, w.dxr, cu, s),

@@ -67,6 +67,7 @@ struct Params {
   int M, N, K;  // DENSE: all three; MGROUP: N, K; KGROUP: M, N
   int ngroups;
   const int32_t* goff;      // [ngroups+1] segment bounds (MGROUP rows / KGROUP k)
+  int kchunk;               // KGROUP without goff: segment g is k in [g kchunk, (g+1) kchunk)
   const int32_t* tile_off;  // MGROUP: [ngroups+1] prefix of m-tiles per segment
   // A: KC -> A[g*a_gs + row(m)*lda + k]; MN -> A[g*a_gs + row(k)*lda + m]
   const void* A;
@@ -215,8 +216,13 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(Params p) {
       m0 = mt * BM;
       mcount = min(BM, p.M - m0);
       if constexpr (GRP == KGROUP) {
-        kbeg = p.goff[g];
-        kend = p.goff[g + 1];
+        if (p.goff) {
+          kbeg = p.goff[g];
+          kend = p.goff[g + 1];
+        } else {
+          kbeg = g * p.kchunk;
+          kend = min(p.K, kbeg + p.kchunk);
+        }
       }
     }
     const int n0 = nt * BNOUT;
@@ -583,20 +589,72 @@ hipError_t launch_bwd_gateup_dw(const float* dadu, const T* x, const int32_t* of
   return hipSuccess;
 }
 
-// dW_r = dl^T x   (dl [T][ldl] fp32, zero-padded columns E..ldl).
+// dW_r = dl^T x   (dl [T][ldl] fp32, zero-padded columns E..ldl).  The
+// output is small (E x d) and the reduction long (T), so with splits > 1 the
+// tokens are cut into `splits` chunks, each chunk's product goes to its own
+// fp32 partial in `part` ([splits][E][d]), and a second kernel adds the
+// partials in chunk order (a fixed order: reproducible).
+__global__ __launch_bounds__(256) void add_partials_kernel_f32(const float* __restrict__ part,
+                                                               int splits, int64_t n, float* out) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    float acc = 0.f;
+    for (int g = 0; g < splits; ++g) acc += part[g * n + i];
+    out[i] = acc;
+  }
+}
+__global__ __launch_bounds__(256) void add_partials_kernel_bf16(const float* __restrict__ part,
+                                                                int splits, int64_t n,
+                                                                bf16_t* out) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    float acc = 0.f;
+    for (int g = 0; g < splits; ++g) acc += part[g * n + i];
+    out[i] = f2bf(acc);
+  }
+}
+
+int router_dw_splits(int64_t Tn, int64_t E, int64_t d) {
+  const int64_t tiles = cdiv(E, BM) * cdiv(d, BN);
+  int64_t s = 256 / (tiles > 0 ? tiles : 1);
+  if (s > Tn / 256) s = Tn / 256;
+  if (s > 32) s = 32;
+  return s < 1 ? 1 : static_cast<int>(s);
+}
+
 template <typename T>
 hipError_t launch_router_dw(const float* dl, int ldl, const T* x, int Tn, int E, int d, T* dwr,
-                            int cu, hipStream_t s) {
+                            float* part, int cu, hipStream_t s) {
   Params p = blank();
   p.M = E; p.N = d; p.K = Tn;
   p.A = dl; p.lda = ldl; p.a_ext = ldl;
   p.B = x; p.ldb = d; p.b_ext = d;
   p.C = dwr; p.ldc = d;
-  const int64_t tot = cdiv(E, BM) * cdiv(d, BN);
+  const int splits = router_dw_splits(Tn, E, d);
+  if (splits <= 1 || !part) {
+    const int64_t tot = cdiv(E, BM) * cdiv(d, BN);
+    if constexpr (is_bf16<T>())
+      return run<T, OP_SPLIT_MN, OP_DUP_MN, DENSE, EPI_STORE, false, false, false>(p, tot, cu, s);
+    else
+      return run<T, OP_MN, OP_MN, DENSE, EPI_STORE, false, false, false>(p, tot, cu, s);
+  }
+  p.ngroups = splits;
+  p.kchunk = static_cast<int>(cdiv(Tn, splits));
+  p.C = part; p.c_gs = static_cast<int64_t>(E) * d;
+  const int64_t tot = cdiv(E, BM) * cdiv(d, BN) * splits;
+  hipError_t e;
   if constexpr (is_bf16<T>())
-    return run<T, OP_SPLIT_MN, OP_DUP_MN, DENSE, EPI_STORE, false, false, false>(p, tot, cu, s);
+    e = run<T, OP_SPLIT_MN, OP_DUP_MN, KGROUP, EPI_F32, false, false, false>(p, tot, cu, s);
   else
-    return run<T, OP_MN, OP_MN, DENSE, EPI_STORE, false, false, false>(p, tot, cu, s);
+    e = run<T, OP_MN, OP_MN, KGROUP, EPI_F32, false, false, false>(p, tot, cu, s);
+  if (e != hipSuccess) return e;
+  const int64_t n = static_cast<int64_t>(E) * d;
+  const int grid = static_cast<int>(std::min<int64_t>(cdiv(n, 256), 4096));
+  if constexpr (is_bf16<T>())
+    hipLaunchKernelGGL(add_partials_kernel_bf16, dim3(grid), dim3(256), 0, s, part, splits, n, dwr);
+  else
+    hipLaunchKernelGGL(add_partials_kernel_f32, dim3(grid), dim3(256), 0, s, part, splits, n, dwr);
+  return hipGetLastError();
 }
 
 // Router part of dx: dxr = dl W_r (fp32 out).
@@ -637,8 +695,8 @@ hipError_t launch_router_dx(const float* dl, int ldl, const T* wr, int Tn, int E
   template hipError_t launch_bwd_gateup_dw<T>(const float*, const T*, const int32_t*,            \
                                               const int32_t*, int, int, int, int, T*, T*, int,   \
                                               hipStream_t);                                      \
-  template hipError_t launch_router_dw<T>(const float*, int, const T*, int, int, int, T*, int,   \
-                                          hipStream_t);                                          \
+  template hipError_t launch_router_dw<T>(const float*, int, const T*, int, int, int, T*,        \
+                                          float*, int, hipStream_t);                             \
   template hipError_t launch_router_dx<T>(const float*, int, const T*, int, int, int, float*,    \
                                           int, hipStream_t);
 ZC_INST(bf16_t)

@@ -107,7 +107,10 @@ hipError_t launch_bwd_gateup_dw(const float* dadu, const T* x, const int32_t* of
                                 int cu_count, hipStream_t s);
 template <typename T>
 hipError_t launch_router_dw(const float* dl, int ldl, const T* x, int Tn, int E, int d, T* dwr,
-                            int cu_count, hipStream_t s);
+                            float* part, int cu_count, hipStream_t s);
+// Token chunks of the router weight gradient (1: no split); part of
+// launch_router_dw needs splits * E * d floats when splits > 1.
+int router_dw_splits(int64_t Tn, int64_t E, int64_t d);
 template <typename T>
 hipError_t launch_router_dx(const float* dl, int ldl, const T* wr, int Tn, int E, int d,
                             float* dxr, int cu_count, hipStream_t s);

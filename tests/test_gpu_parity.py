@@ -319,6 +319,12 @@ def test_backward_tiny_fp32_literal_gates():
     backward_case(CF["tiny_fp32"], gate_norm=0, out_scale=0.5)
 
 
+def test_backward_fp32_long_batch_splits_router_gradient():
+    # T = 1024 tokens: the router weight gradient is computed in 4 token chunks
+    # whose fp32 partials are added in chunk order
+    backward_case(CF["tiny_fp32"].with_T(1024))
+
+
 def test_backward_train_shape_bf16():
     # the training layer's shapes with fewer tokens, so the fp64 oracle
     # finishes in seconds; all 128 experts' gradients compared
