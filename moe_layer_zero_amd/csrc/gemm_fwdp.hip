@@ -73,6 +73,18 @@ struct PParams {
 
 __device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
 
+// fp32 -> bf16, round to nearest even (NaN stays NaN), one conversion
+// instruction per value, for the down projection's epilogue.  Written as an
+// opaque instruction: as a plain cast the compiler pairs and hoists the
+// conversions, and the 256-row kernel then spills inside its k loop.  (The
+// gate/up epilogue keeps f2bf: with any branch-free rounding there the
+// register allocator spills inside the k loop as well.)
+__device__ __forceinline__ bf16_t cvt_bf16(float f) {
+  uint32_t r;
+  asm volatile("v_cvt_pk_bf16_f32 %0, %1, 0" : "=v"(r) : "v"(f));
+  return static_cast<bf16_t>(r);
+}
+
 // One 16-byte-per-lane buffer load straight into LDS (64 lanes -> 1 KB at
 // dst).  Kept out of the kernel templates: the host pass drops template
 // kernels that use this builtin in a dependent context.
@@ -327,8 +339,8 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
           if constexpr (EPI == P_SWIGLU) {
             st[rl * OUTN + 32 * wave + (lane & 31)] = f2bf(silu_f(acc[rb][0][v]) * acc[rb][1][v]);
           } else {
-            st[rl * OUTN + 64 * wave + (lane & 31)] = f2bf(acc[rb][0][v]);
-            st[rl * OUTN + 64 * wave + 32 + (lane & 31)] = f2bf(acc[rb][1][v]);
+            st[rl * OUTN + 64 * wave + (lane & 31)] = cvt_bf16(acc[rb][0][v]);
+            st[rl * OUTN + 64 * wave + 32 + (lane & 31)] = cvt_bf16(acc[rb][1][v]);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
