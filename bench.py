@@ -37,8 +37,8 @@ BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
 # size gives), valid for the kernel source they were measured on: reported
 # as roofline.traffic only while that source is unchanged.
 GATE_UP_TRAFFIC = {"source": "moe_layer_zero_amd/csrc/gemm_fwdp.hip",
-                   "sha256": "7424b66f11288e0dffb2daac59e7ba0bb1b344d18b26be455eb2a469b0758b7a",
-                   "fetch_bytes": 34972781525, "write_bytes": 593608704}
+                   "sha256": "f535174affbe7da4c7f07f6a6d511d3468eac1b264a8aefe71978794baaba5b7",
+                   "fetch_bytes": 35377913088, "write_bytes": 594221056}
 
 
 def measured_traffic():

@@ -187,14 +187,20 @@ struct RouteWs {
   int32_t* tile_off2;  // row-tile prefix for the bf16 forward expert GEMMs
   int32_t* tile_exp;   // expert of each of those row tiles
   int32_t* sched;      // tile counters of the packed-weight GEMMs
+  float* rpart;        // fp32 partials of a split router GEMM (nullptr: unsplit)
   void* dispatch;
 };
 // Row tiles of the second prefix, at most: every FFN pick in a tile of its
 // own expert, tiles at least 32 rows high.
 int64_t max_tiles2(const zc_moe_desc* d) { return d->T * d->K / 32 + d->N + 1; }
+int64_t rpart_bytes(const zc_moe_desc* d) {
+  const int64_t E = d->N + d->Z;
+  const int s = zc::router_gemm_splits(d->T, E, d->d);
+  return s > 1 ? 4 * s * d->T * E : 0;
+}
 int64_t route_ws_bytes(const zc_moe_desc* d) {
   return 2 * a256(4 * (d->N + 1)) + a256(4 * max_tiles2(d)) + a256(4 * zc::kSchedInts) +
-         a256(zc::dispatch_scratch_bytes(d->T, d->N + d->Z, d->N));
+         a256(rpart_bytes(d)) + a256(zc::dispatch_scratch_bytes(d->T, d->N + d->Z, d->N));
 }
 RouteWs carve_route(char* p, const zc_moe_desc* d) {
   RouteWs w;
@@ -205,6 +211,8 @@ RouteWs carve_route(char* p, const zc_moe_desc* d) {
   q += a256(4 * max_tiles2(d));
   w.sched = reinterpret_cast<int32_t*>(q);
   q += a256(4 * zc::kSchedInts);
+  w.rpart = rpart_bytes(d) > 0 ? reinterpret_cast<float*>(q) : nullptr;
+  q += a256(rpart_bytes(d));
   w.dispatch = q;
   return w;
 }
@@ -307,7 +315,7 @@ zc_status do_route(const zc_moe_desc* d, const T* x, const T* wr, const float* b
   const int Tn = static_cast<int>(d->T), E = static_cast<int>(d->N + d->Z);
   const int N = static_cast<int>(d->N), K = static_cast<int>(d->K);
   if (x && Tn > 0)
-    ZC_LAUNCH(ZC_PH_ROUTER_GEMM, zc::launch_router_gemm<T>(x, wr, r->logits, Tn, E, static_cast<int>(d->d), cu_count(),
+    ZC_LAUNCH(ZC_PH_ROUTER_GEMM, zc::launch_router_gemm<T>(x, wr, r->logits, Tn, E, static_cast<int>(d->d), w.rpart, cu_count(),
                                      s),
            "router GEMM launch");
   ZC_LAUNCH(ZC_PH_TOPK, zc::launch_topk(r->logits, bias, Tn, E, K, d->gate_norm, r->topk_idx, r->topk_gate, s),

@@ -469,17 +469,70 @@ constexpr bool is_bf16() {
 
 }  // namespace
 
+// Partial sums of a GEMM whose reduction was cut into chunks: out[i] = sum
+// over chunks g = 0, 1, ... of part[g][i], added in chunk order (a fixed
+// order: reproducible).
+__global__ __launch_bounds__(256) void add_partials_kernel_f32(const float* __restrict__ part,
+                                                               int splits, int64_t n, float* out) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    float acc = 0.f;
+    for (int g = 0; g < splits; ++g) acc += part[g * n + i];
+    out[i] = acc;
+  }
+}
+__global__ __launch_bounds__(256) void add_partials_kernel_bf16(const float* __restrict__ part,
+                                                                int splits, int64_t n,
+                                                                bf16_t* out) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    float acc = 0.f;
+    for (int g = 0; g < splits; ++g) acc += part[g * n + i];
+    out[i] = f2bf(acc);
+  }
+}
+
+int router_dw_splits(int64_t Tn, int64_t E, int64_t d) {
+  const int64_t tiles = cdiv(E, BM) * cdiv(d, BN);
+  int64_t s = 256 / (tiles > 0 ? tiles : 1);
+  if (s > Tn / 256) s = Tn / 256;
+  if (s > 32) s = 32;
+  return s < 1 ? 1 : static_cast<int>(s);
+}
+
+int router_gemm_splits(int64_t Tn, int64_t E, int64_t d) {
+  const int64_t tiles = cdiv(Tn, BM) * cdiv(E, BN);
+  int64_t s = 256 / (tiles > 0 ? tiles : 1);
+  if (s > d / 512) s = d / 512;  // at least 512 reduction steps per chunk
+  if (s > 32) s = 32;
+  return s < 1 ? 1 : static_cast<int>(s);
+}
+
 // Router scores: logits[T][E] = x[T][d] * wr[E][d]^T.
 template <typename T>
 hipError_t launch_router_gemm(const T* x, const T* wr, float* logits, int Tn, int E, int d,
-                              int cu, hipStream_t s) {
+                              float* part, int cu, hipStream_t s) {
   Params p = blank();
   p.M = Tn; p.N = E; p.K = d;
   p.A = x; p.lda = d;
   p.B = wr; p.ldb = d;
   p.C = logits; p.ldc = E;
-  return run<T, OP_KC, OP_KC, DENSE, EPI_F32, false, false, false>(p, cdiv(Tn, BM) * cdiv(E, BN),
-                                                                   cu, s);
+  const int splits = router_gemm_splits(Tn, E, d);
+  if (splits <= 1 || !part)
+    return run<T, OP_KC, OP_KC, DENSE, EPI_F32, false, false, false>(
+        p, cdiv(Tn, BM) * cdiv(E, BN), cu, s);
+  // few tokens (decode): too few output tiles to fill the GPU, so the
+  // hidden dimension is cut into chunks whose fp32 partials are then added
+  p.ngroups = splits;
+  p.kchunk = static_cast<int>(cdiv(cdiv(d, splits), 64) * 64);
+  p.C = part; p.c_gs = static_cast<int64_t>(Tn) * E;
+  hipError_t e = run<T, OP_KC, OP_KC, KGROUP, EPI_F32, false, false, false>(
+      p, cdiv(Tn, BM) * cdiv(E, BN) * splits, cu, s);
+  if (e != hipSuccess) return e;
+  const int64_t n = static_cast<int64_t>(Tn) * E;
+  const int grid = static_cast<int>(std::min<int64_t>(cdiv(n, 256), 4096));
+  hipLaunchKernelGGL(add_partials_kernel_f32, dim3(grid), dim3(256), 0, s, part, splits, n, logits);
+  return hipGetLastError();
 }
 
 // h = silu(x_e W_g[e]^T) * (x_e W_u[e]^T) over each expert's rows; a, u, h
@@ -594,34 +647,6 @@ hipError_t launch_bwd_gateup_dw(const float* dadu, const T* x, const int32_t* of
 // tokens are cut into `splits` chunks, each chunk's product goes to its own
 // fp32 partial in `part` ([splits][E][d]), and a second kernel adds the
 // partials in chunk order (a fixed order: reproducible).
-__global__ __launch_bounds__(256) void add_partials_kernel_f32(const float* __restrict__ part,
-                                                               int splits, int64_t n, float* out) {
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    float acc = 0.f;
-    for (int g = 0; g < splits; ++g) acc += part[g * n + i];
-    out[i] = acc;
-  }
-}
-__global__ __launch_bounds__(256) void add_partials_kernel_bf16(const float* __restrict__ part,
-                                                                int splits, int64_t n,
-                                                                bf16_t* out) {
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    float acc = 0.f;
-    for (int g = 0; g < splits; ++g) acc += part[g * n + i];
-    out[i] = f2bf(acc);
-  }
-}
-
-int router_dw_splits(int64_t Tn, int64_t E, int64_t d) {
-  const int64_t tiles = cdiv(E, BM) * cdiv(d, BN);
-  int64_t s = 256 / (tiles > 0 ? tiles : 1);
-  if (s > Tn / 256) s = Tn / 256;
-  if (s > 32) s = 32;
-  return s < 1 ? 1 : static_cast<int>(s);
-}
-
 template <typename T>
 hipError_t launch_router_dw(const float* dl, int ldl, const T* x, int Tn, int E, int d, T* dwr,
                             float* part, int cu, hipStream_t s) {
@@ -674,8 +699,8 @@ hipError_t launch_router_dx(const float* dl, int ldl, const T* wr, int Tn, int E
 }
 
 #define ZC_INST(T)                                                                               \
-  template hipError_t launch_router_gemm<T>(const T*, const T*, float*, int, int, int, int,      \
-                                            hipStream_t);                                        \
+  template hipError_t launch_router_gemm<T>(const T*, const T*, float*, int, int, int, float*,   \
+                                            int, hipStream_t);                                   \
   template hipError_t launch_ffn_gateup<T>(const T*, const T*, const T*, const int32_t*,         \
                                            const int32_t*, const int32_t*, int, int, int, int,   \
                                            int64_t, T*, float*, float*, float*, int,             \

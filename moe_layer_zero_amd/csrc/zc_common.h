@@ -50,10 +50,14 @@ constexpr int kFwdBM = 256;
 // ---------------------------------------------------------------- launchers
 // Every launcher queues work on `s` and returns the hipError_t of the launch.
 
-// Router scores: logits[T][E] = x[T][d] * wr[E][d]^T (fp32 out).
+// Router scores: logits[T][E] = x[T][d] * wr[E][d]^T (fp32 out).  With
+// router_gemm_splits(T, E, d) > 1 the hidden dimension is cut into that many
+// chunks whose fp32 partials (part: splits * T * E floats) are added in
+// chunk order.
+int router_gemm_splits(int64_t Tn, int64_t E, int64_t d);
 template <typename T>
 hipError_t launch_router_gemm(const T* x, const T* wr, float* logits, int Tn, int E, int d,
-                              int cu_count, hipStream_t s);
+                              float* part, int cu_count, hipStream_t s);
 
 // Routing keys, biased top-K, gates (one wavefront per token).
 hipError_t launch_topk(const float* logits, const float* bias, int Tn, int E, int K,
