@@ -37,11 +37,14 @@ def lib():
         L.orc_forward.argtypes = [_i64, _i64, _i64, _i64, _i64, _i32, _f64, _p, _p, _p, _p,
                                   _p, _p, _i64, _p, _p, _p]
         L.orc_backward.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i32, _i32, _f64, _p, _p,
-                                   _p, _p, _p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _p]
+                                   _p, _p, _p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _p,
+                                   _p]
+        L.orc_lb_loss.argtypes = [_i64, _i64, _i64, _i64, _i64, _f64, _f64, _p, _p, _p, _p]
         L.orc_num_threads.restype = C.c_int
         L.orc_num_threads.argtypes = []
         L.orc_pid_update.argtypes = [_i64, _i64, _i64, _p, _i64, _f64, _f64, _p]
-        for f in ("orc_logits", "orc_route", "orc_forward", "orc_backward", "orc_pid_update"):
+        for f in ("orc_logits", "orc_route", "orc_forward", "orc_backward", "orc_pid_update",
+                  "orc_lb_loss"):
             getattr(L, f).restype = C.c_int
         _LIB = L
     return _LIB
@@ -162,9 +165,10 @@ def forward(x, wg, wu, wd, topk_idx, gates, N, out_scale=1.0, toks=None, want_y=
 
 
 def backward(x, wr, wg, wu, wd, lg, topk_idx, gates, dY, N, Z, gate_norm=1, out_scale=1.0,
-             toks=None, want_experts=None, want_dwr=True):
+             toks=None, want_experts=None, want_dwr=True, dl_extra=None):
     """O9.  Returns dict with dx [n,d], dwr [E,d] (or None), dwg/dwu/dwd as
-    {e: array} for experts in want_experts (all N when None)."""
+    {e: array} for experts in want_experts (all N when None).  dl_extra
+    ([T,E], e.g. lb_loss's dlogits) is added to the router-score gradient."""
     x, wr, dY = _c(x), _c(wr), _c(dY)
     T, d = x.shape
     E = N + Z
@@ -178,6 +182,9 @@ def backward(x, wr, wg, wu, wd, lg, topk_idx, gates, dY, N, Z, gate_norm=1, out_
     ti = _c(topk_idx, np.int32)
     gg = _c(gates, np.float64)
     tk = None if toks is None else _c(np.asarray(toks), np.int64)
+    ex = None if dl_extra is None else _c(dl_extra, np.float64)
+    if ex is not None:
+        assert ex.shape == (T, E)
     n = T if tk is None else len(tk)
     dx = np.empty((n, d), np.float64)
     dwr = np.zeros((E, d), np.float64) if want_dwr else None
@@ -190,7 +197,7 @@ def backward(x, wr, wg, wu, wd, lg, topk_idx, gates, dY, N, Z, gate_norm=1, out_
     pd, qd = _table(dwd, N)
     rc = lib().orc_backward(T, d, N, Z, I, K, _dt(x), int(gate_norm), float(out_scale), _ptr(x),
                             _ptr(wr), tg, tu, td, _ptr(lg), _ptr(ti), _ptr(gg), _ptr(dY), n,
-                            _ptr(tk), _ptr(dx), _ptr(dwr), pg, pu, pd)
+                            _ptr(tk), _ptr(ex), _ptr(dx), _ptr(dwr), pg, pu, pd)
     assert rc == 0, f"oracle backward failed rc={rc}"
     del kg, ku, kd, qg, qu, qd
     return {"dx": dx, "dwr": dwr, "dwg": dwg, "dwu": dwu, "dwd": dwd}
@@ -203,3 +210,19 @@ def pid_update(counts, T_all, bias, N, Z, K, mu, K_e) -> np.ndarray:
     rc = lib().orc_pid_update(N, Z, K, _ptr(c), int(T_all), float(mu), float(K_e), _ptr(b))
     assert rc == 0
     return b
+
+
+def lb_loss(lg, topk_idx, N, D, K_e, alpha, want_grad=True):
+    """O10: device-level load-balance loss (section 2.1.2, Eq.(4)-(5)).
+    Returns (L, f [D+1], P [D+1], dlogits [T,E] or None)."""
+    lg = _c(lg, np.float64)
+    ti = _c(topk_idx, np.int32)
+    T, E = lg.shape
+    K = ti.shape[1]
+    out = np.zeros(1 + 2 * (D + 1), np.float64)
+    dl = np.empty((T, E), np.float64) if want_grad else None
+    rc = lib().orc_lb_loss(T, E, N, K, D, float(K_e), float(alpha), _ptr(lg), _ptr(ti),
+                           _ptr(out), _ptr(dl))
+    if rc != 0:
+        raise ValueError(f"oracle lb_loss rejected its arguments (rc={rc})")
+    return float(out[0]), out[1:D + 2].copy(), out[D + 2:].copy(), dl

@@ -9,8 +9,9 @@
  *
  * Source: "LongCat-Flash Technical Report" (Chinese translation on
  * 171host.com), section 2.1 "Zero-computation experts", Eq.(1) and the
- * expert definition E_i that follows it, and section 2.1.1 "Computation
- * budget control", Eq.(2).  The FFN expert form (SwiGLU without biases) and
+ * expert definition E_i that follows it, section 2.1.1 "Computation
+ * budget control", Eq.(2), and section 2.1.2 "Load balance control" (the
+ * device-level loss L_LB with Eq.(4) and Eq.(5)).  The FFN expert form (SwiGLU without biases) and
  * the linear softmax router are readings of points the page leaves open.
  *
  * Every floating-point step runs in binary64 on the exact values of the
@@ -309,15 +310,19 @@ int orc_forward(int64_t T, int64_t d, int64_t N, int64_t I, int64_t K, int dt,
  * Weight gradients are accumulated (+=) over the listed tokens in ascending
  * list order; expert tables dwg/dwu/dwd may hold NULL for experts whose
  * gradient is not wanted; dwr may be NULL.  dx is [n_tok][d], overwritten.
- * gates must be the gates of the same gate_norm mode. */
+ * gates must be the gates of the same gate_norm mode.
+ * dl_extra (nullable, [T][E]) is a further gradient of the objective with
+ * respect to the router scores (the load-balance loss's, from
+ * orc_lb_loss); it is added to dl above before dWr and the dx term. */
 int orc_backward(int64_t T, int64_t d, int64_t N, int64_t Z, int64_t I,
                  int64_t K, int dt, int gate_norm, double out_scale,
                  const void* x, const void* wr, const void* const* wg,
                  const void* const* wu, const void* const* wd,
                  const double* logits, const int32_t* topk_idx,
                  const double* gates, const void* dY, int64_t n_tok,
-                 const int64_t* toks, double* dx, double* dwr,
-                 double* const* dwg, double* const* dwu, double* const* dwd) {
+                 const int64_t* toks, const double* dl_extra, double* dx,
+                 double* dwr, double* const* dwg, double* const* dwu,
+                 double* const* dwd) {
   const int64_t E = N + Z;
   if (!x || !wr || !wg || !wu || !wd || !logits || !topk_idx || !gates || !dY || !dx)
     return 1;
@@ -418,6 +423,8 @@ int orc_backward(int64_t T, int64_t d, int64_t N, int64_t Z, int64_t I,
           dl[j] += (ex[j] / Ssum) * dg[r];
         }
       }
+      if (dl_extra)
+        for (int64_t j = 0; j < E; ++j) dl[j] += dl_extra[t * E + j];
       for (int64_t k = 0; k < d; ++k) {
         double acc = 0.0;
         for (int64_t j = 0; j < E; ++j) acc += dl[j] * ld(wr, dt, j * d + k);
@@ -478,5 +485,93 @@ int orc_pid_update(int64_t N, int64_t Z, int64_t K, const int32_t* counts,
     double obs = (double)counts[i] / ((double)K * (double)T_all);
     bias[i] = (float)((double)bias[i] + mu * (tgt - obs));
   }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O10 -- device-level load-balance loss of section 2.1.2 ("Load balance
+ * control"): the L_LB formula there with P_j of Eq.(4) and f_j of Eq.(5):
+ *   L = alpha * sum_{j=1}^{D+1} f_j P_j.
+ * Groups: the N FFN experts split into D groups of G = N/D consecutive
+ * indices (Group_j = experts (j-1)G .. jG-1, the experts one device holds
+ * under expert parallelism); every zero-computation expert belongs to the
+ * extra group D+1.
+ *   P_j = (1/T) sum over i in Group_j, t of R_{t,i}, with R the unbiased
+ *         softmax of the token's scores (orc_exp, orc_sum64 as in O2);
+ *   f_j = D/(K_e T) * (picks of all tokens that fall in Group_j), j <= D;
+ *   f_{D+1} = 1/((K-K_e) T) * (picks of zero-computation experts).
+ * The indicator counts picks: a token with two picks in one group counts
+ * twice, so that every f_j is 1 when the FFN picks spread evenly over the
+ * groups and the layer takes K_e FFN experts per token on average.  With
+ * Z = 0 the extra group is empty and its term is left out.
+ * Gradient with respect to the scores (f is a count of discrete picks and
+ * is held constant): with c_j = alpha f_{g(j)} / T for the group g(j) of j,
+ *   dL/dl_{t,i} = R_{t,i} ( c_{g(i)} - sum_k R_{t,k} c_{g(k)} ).
+ * out: [1 + 2(D+1)] = L, f_1..f_{D+1}, P_1..P_{D+1} (slots of the extra
+ * group are 0 when Z = 0); dlogits: [T][E] or NULL.  T = 0 gives zeros.
+ * Needs N >= 1, 1 <= D <= N, N % D == 0, 0 < K_e <= K, and K_e < K when
+ * Z > 0. */
+int orc_lb_loss(int64_t T, int64_t E, int64_t N, int64_t K, int64_t D,
+                double K_e, double alpha, const double* logits,
+                const int32_t* topk_idx, double* out, double* dlogits) {
+  const int64_t Z = E - N;
+  if (T < 0 || N < 1 || Z < 0 || K < 1 || K > E || D < 1 || D > N || N % D != 0 ||
+      !(K_e > 0.0) || K_e > (double)K || (Z > 0 && !(K_e < (double)K)) || !out ||
+      (T > 0 && (!logits || !topk_idx)))
+    return 1;
+  const int64_t G = N / D, ng = D + 1;
+  for (int64_t j = 0; j < 1 + 2 * ng; ++j) out[j] = 0.0;
+  if (T == 0) return 0;
+  /* f from the picks */
+  double* picks = (double*)calloc((size_t)ng, sizeof(double));
+  for (int64_t i = 0; i < T * K; ++i) {
+    int32_t e = topk_idx[i];
+    if (e < 0 || e >= E) { free(picks); return 1; }
+    picks[e < N ? e / G : D] += 1.0;
+  }
+  double* f = out + 1;
+  double* P = out + 1 + ng;
+  for (int64_t j = 0; j < D; ++j) f[j] = (double)D / (K_e * (double)T) * picks[j];
+  if (Z > 0) f[D] = 1.0 / (((double)K - K_e) * (double)T) * picks[D];
+  free(picks);
+  /* R per token, then P_j as the group sum of the per-expert token sums */
+  double* R = (double*)malloc(sizeof(double) * (size_t)(T * E));
+#pragma omp parallel
+  {
+    double* e = (double*)malloc(sizeof(double) * (size_t)E);
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      const double* l = logits + t * E;
+      double m = l[0];
+      for (int64_t j = 1; j < E; ++j)
+        if (l[j] > m) m = l[j];
+      for (int64_t j = 0; j < E; ++j) e[j] = orc_exp(l[j] - m);
+      double S = orc_sum64(e, E);
+      for (int64_t j = 0; j < E; ++j) R[t * E + j] = e[j] / S;
+    }
+    free(e);
+  }
+  for (int64_t i = 0; i < E; ++i) {
+    double col = 0.0;
+    for (int64_t t = 0; t < T; ++t) col += R[t * E + i];
+    P[i < N ? i / G : D] += col;
+  }
+  for (int64_t j = 0; j < ng; ++j) P[j] /= (double)T;
+  double L = 0.0;
+  for (int64_t j = 0; j < ng; ++j) L += f[j] * P[j];
+  out[0] = alpha * L;
+  if (dlogits) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      const double* r = R + t * E;
+      double mean = 0.0;
+      for (int64_t k = 0; k < E; ++k) mean += r[k] * (alpha * f[k < N ? k / G : D] / (double)T);
+      for (int64_t i = 0; i < E; ++i) {
+        double ci = alpha * f[i < N ? i / G : D] / (double)T;
+        dlogits[t * E + i] = r[i] * (ci - mean);
+      }
+    }
+  }
+  free(R);
   return 0;
 }
