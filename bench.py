@@ -200,6 +200,9 @@ def train(steps, warmup):
     xs = [synth.step_x(sh, s, "cuda") for s in range(n)]
     dys = [synth.step_dy(sh, s, "cuda") for s in range(n)]
     bias = torch.zeros(sh.E, device="cuda")
+    lb = zcmoe.LoadBalance(synth.TRAIN_LB_D, synth.TRAIN_K_E, synth.TRAIN_LB_ALPHA)
+    wsl = zcmoe.workspace(desc, zcmoe.ZC_OP_LB_LOSS)
+    lb_out = torch.empty(1 + 2 * (lb.D + 1), dtype=torch.float64, device="cuda")
     it = [0]
 
     def step():
@@ -208,9 +211,10 @@ def train(steps, warmup):
         x = xs[s]
         zcmoe.zc_moe_forward(desc, x, L["wr"], bias, L["wg"], L["wu"], L["wd"], out, route, saved,
                              wsf)
+        zcmoe.zc_moe_lb_loss(desc, lb, route, lb_out, wsl)
         zcmoe.zc_moe_backward(desc, x, L["wr"], L["wg"], L["wu"], L["wd"], route, saved, dys[s],
                               grads["dx"], grads["dwr"], grads["dwg"], grads["dwu"], grads["dwd"],
-                              wsb)
+                              wsb, lb=lb)
         zcmoe.zc_moe_pid_update(sh.N, sh.Z, sh.K, route.counts, sh.T, synth.TRAIN_MU,
                                 synth.TRAIN_K_E, bias)
 
@@ -219,6 +223,7 @@ def train(steps, warmup):
     flops = 18.0 * sh.d * sh.I * p_real + 6.0 * sh.T * sh.d * sh.E
     res = {"ms_per_step": ms, "tokens_per_s": sh.T / (ms / 1e3), "p_real_last": p_real,
            "mean_real_experts_last": p_real / sh.T, "tflops": flops / (ms * 1e-3) / 1e12,
+           "lb_loss_last": float(lb_out[0].item()),
            "kernels_ms": {k: round(v[0], 4) for k, v in ph.items()}}
     del L, xs, dys, saved
     torch.cuda.empty_cache()
@@ -326,7 +331,8 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs, N(0,std) weights, random init)",
         "config": {"workload": sh.name, "T": sh.T, "d": sh.d, "N": sh.N, "Z": sh.Z, "I": sh.I,
                    "K": sh.K, "bias": sh.bias,
-                   "expert_weights": "row-major" if args.rowmajor else "packed"},
+                   "expert_weights": "row-major" if args.rowmajor or sh.name == "train_bf16"
+                   else "packed"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": res,

@@ -8,7 +8,8 @@
  * which K experts are picked, gates taken from the unbiased softmax, FFN
  * experts evaluated on the tokens routed to them, and zero-computation
  * experts returning their input x_t.  The bias follows Eq.(2) of section
- * 2.1.1 ("Computation budget control").
+ * 2.1.1 ("Computation budget control").  The device-level load-balance
+ * loss is the one of section 2.1.2 ("Load balance control").
  *
  * Conventions shared by every call:
  *  - Pointers are DEVICE pointers unless a comment says "host".  The caller
@@ -96,7 +97,19 @@ typedef struct {
                      /*        zero-computation pick                          */
 } zc_route_buf;
 
-enum { ZC_OP_ROUTE = 0, ZC_OP_FORWARD = 1, ZC_OP_BACKWARD = 2 };
+enum { ZC_OP_ROUTE = 0, ZC_OP_FORWARD = 1, ZC_OP_BACKWARD = 2, ZC_OP_LB_LOSS = 3 };
+
+/* Device-level load-balance loss settings ("LongCat-Flash Technical
+ * Report", section 2.1.2; host struct, passed by pointer).  The N FFN
+ * experts form D groups of G = N/D consecutive indices (group j holds
+ * experts (j-1)G .. jG-1: the experts one device holds under expert
+ * parallelism); every zero-computation expert is in the extra group D+1. */
+typedef struct {
+  int64_t D;    /* groups, 1 <= D <= N, N % D == 0                          */
+  double K_e;   /* expected FFN experts per token: 0 < K_e <= K, and        */
+                /* K_e < K when Z > 0                                       */
+  double alpha; /* balance factor (finite)                                  */
+} zc_lb_cfg;
 
 /* Bytes of scratch memory `op` needs for this layer (0 for an invalid
  * description).  The bound depends only on the description, never on the
@@ -148,6 +161,11 @@ zc_status zc_moe_forward(const zc_moe_desc* desc, const void* x,
  *   router: dl_j = g_j (dg_j - sum_picks g dg) on the picks (gate_norm 1),
  *           dl_j = p_j (dg_j [pick] - sum_picks p dg) (gate_norm 0);
  *   dx = out_scale*(identity gates)*dout + expert dx + dl W_r.
+ * With lb (host, nullable) the objective also holds the device-level
+ * load-balance loss of zc_moe_lb_loss on the same routing, and dl above
+ * takes its score gradient (f held fixed, it counts discrete picks):
+ *   dl_j += p_j (c_j - sum_k p_k c_k),  c_j = alpha f_{g(j)} / T,
+ * with p the fp32 softmax of the token's scores and g(j) the group of j.
  * Every gradient buffer is overwritten (not accumulated).  r and saved must
  * come from the zc_moe_forward call being differentiated. */
 zc_status zc_moe_backward(const zc_moe_desc* desc, const void* x,
@@ -155,8 +173,28 @@ zc_status zc_moe_backward(const zc_moe_desc* desc, const void* x,
                           const void* w_up, const void* w_down,
                           const zc_route_buf* r, const void* saved,
                           const void* dout, void* dx, void* dw_router,
-                          void* dw_gate, void* dw_up, void* dw_down, void* ws,
-                          size_t ws_bytes, void* stream);
+                          void* dw_gate, void* dw_up, void* dw_down,
+                          const zc_lb_cfg* lb, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* Device-level load-balance loss, section 2.1.2 of the report:
+ *   L = alpha * sum_{j=1}^{D+1} f_j P_j,
+ *   P_j = (1/T) sum over i in group j and all tokens t of R_{t,i}  (Eq.(4)),
+ *   f_j = D/(K_e T) * (picks of all tokens in group j),  j <= D    (Eq.(5)),
+ *   f_{D+1} = 1/((K-K_e) T) * (zero-computation picks)             (Eq.(5)),
+ * a pick counting once for each expert of the group it lands on, so every
+ * f_j is 1 when the FFN picks spread evenly and K_e FFN experts are picked
+ * per token on average; with Z = 0 the extra group's term is left out.
+ * R is the unbiased softmax of r->logits, computed in binary64 exactly as
+ * for the routing keys (see zc_moe_route); the picks come from r->counts.
+ * r is the route buffer of the zc_moe_route / zc_moe_forward call of this
+ * micro-batch (only logits and counts are read).  out (device, 1 + 2(D+1)
+ * doubles): L, then f_1..f_{D+1}, then P_1..P_{D+1} (the extra group's
+ * slots 0 when Z = 0); all zero when T = 0.  Sums run in a fixed order.
+ * Scratch: zc_moe_workspace_size(desc, ZC_OP_LB_LOSS) bytes. */
+zc_status zc_moe_lb_loss(const zc_moe_desc* desc, const zc_lb_cfg* lb,
+                         const zc_route_buf* r, double* out, void* ws,
+                         size_t ws_bytes, void* stream);
 
 /* Eq.(2) bias update, in place on bias [N+Z] (fp32), for FFN experts i < N:
  *   b_i += mu * ( K_e/(K*N) - T_i/(K*T_all) ),  T_i = counts[i],
@@ -199,7 +237,7 @@ enum {
   ZC_PH_ROUTER_GEMM = 0, ZC_PH_TOPK, ZC_PH_DISPATCH, ZC_PH_GATE_UP, ZC_PH_DOWN, ZC_PH_COMBINE,
   ZC_PH_BWD_COMBINE, ZC_PH_BWD_DOWN_DH, ZC_PH_BWD_DOWN_DW, ZC_PH_BWD_GATE_UP_DX,
   ZC_PH_BWD_GATE_UP_DW, ZC_PH_BWD_ROUTER_DW, ZC_PH_BWD_ROUTER_DX, ZC_PH_BWD_DX_GATHER,
-  ZC_PH_BIAS_UPDATE, ZC_PH_TILE_OFFSETS, ZC_NUM_PHASES
+  ZC_PH_BIAS_UPDATE, ZC_PH_TILE_OFFSETS, ZC_PH_LB_LOSS, ZC_PH_LB_COEF, ZC_NUM_PHASES
 };
 zc_status zc_moe_profile(int on);
 zc_status zc_moe_profile_read(double* total_ms, int32_t* count);

@@ -244,7 +244,7 @@ int64_t fwd_ws_bytes(const zc_moe_desc* d) {
 
 struct BwdWs {
   int32_t* tile_off;
-  float *gs, *dg, *dl, *dadu, *dxp, *dxr, *rdw;
+  float *gs, *dg, *dl, *dadu, *dxp, *dxr, *rdw, *lbc;
 };
 // fp32 partials of the router weight gradient (token chunks), 0 when unsplit
 int64_t rdw_bytes(const zc_moe_desc* d) {
@@ -256,7 +256,7 @@ int64_t bwd_ws_bytes(const zc_moe_desc* d) {
   const int64_t rows = d->T * d->K, E = d->N + d->Z;
   return a256(4 * (d->N + 1)) + a256(4 * rows) + a256(4 * d->T * d->K) +
          a256(4 * d->T * ldl_of(E)) + a256(4 * rows * 2 * d->I) + a256(4 * rows * d->d) +
-         a256(4 * d->T * d->d) + a256(rdw_bytes(d));
+         a256(4 * d->T * d->d) + a256(rdw_bytes(d)) + a256(4 * E);
 }
 BwdWs carve_bwd(char* p, const zc_moe_desc* d) {
   const int64_t rows = d->T * d->K, E = d->N + d->Z;
@@ -275,6 +275,7 @@ BwdWs carve_bwd(char* p, const zc_moe_desc* d) {
   w.dxp = take(4 * rows * d->d);
   w.dxr = take(4 * d->T * d->d);
   w.rdw = rdw_bytes(d) > 0 ? take(rdw_bytes(d)) : nullptr;
+  w.lbc = take(4 * E);
   return w;
 }
 
@@ -285,6 +286,26 @@ zc_status check_ws(const void* ws, size_t ws_bytes, int64_t need) {
   if (ws && (reinterpret_cast<uintptr_t>(ws) & 255u))
     return fail(ZC_ERR_INVALID, "workspace is not 256-byte aligned");
   return ZC_OK;
+}
+
+// Load-balance loss settings against the layer: D groups of N/D FFN
+// experts, 0 < K_e <= K (K_e < K when there are zero-computation experts,
+// whose pick frequency divides by K - K_e), finite alpha.
+zc_status check_lb(const zc_moe_desc* d, const zc_lb_cfg* lb) {
+  if (!lb) return fail(ZC_ERR_INVALID, "load-balance settings are NULL");
+  if (d->N < 1) return fail(ZC_ERR_INVALID, "the load-balance loss needs FFN experts (N >= 1)");
+  if (lb->D < 1 || lb->D > d->N || d->N % lb->D)
+    return fail(ZC_ERR_INVALID, "D=%lld does not split N=%lld into equal groups",
+                (long long)lb->D, (long long)d->N);
+  if (!std::isfinite(lb->K_e) || !(lb->K_e > 0.0) || lb->K_e > static_cast<double>(d->K) ||
+      (d->Z > 0 && !(lb->K_e < static_cast<double>(d->K))))
+    return fail(ZC_ERR_INVALID, "K_e=%g outside (0, K=%lld%s", lb->K_e, (long long)d->K,
+                d->Z > 0 ? ")" : "]");
+  if (!std::isfinite(lb->alpha)) return fail(ZC_ERR_INVALID, "alpha is not finite");
+  return ZC_OK;
+}
+int64_t lb_ws_bytes(const zc_moe_desc* d) {
+  return a256(static_cast<int64_t>(zc::lb_scratch_bytes(d->T, d->N + d->Z)));
 }
 
 // The 256 x 256 forward kernels: bf16 layers, no activations saved for a
@@ -398,7 +419,8 @@ zc_status do_forward(const zc_moe_desc* d, const T* x, const T* wr, const float*
 template <typename T>
 zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg, const T* wu,
                       const T* wd, const zc_route_buf* r, const void* saved, const T* dout, T* dx,
-                      T* dwr, T* dwg, T* dwu, T* dwd, char* ws, hipStream_t s) {
+                      T* dwr, T* dwg, T* dwu, T* dwd, const zc_lb_cfg* lb, char* ws,
+                      hipStream_t s) {
   const int Tn = static_cast<int>(d->T), N = static_cast<int>(d->N), K = static_cast<int>(d->K);
   const int E = static_cast<int>(d->N + d->Z), dd = static_cast<int>(d->d);
   const int I = static_cast<int>(d->I), ldl = static_cast<int>(ldl_of(E));
@@ -410,10 +432,15 @@ zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg
   if (N > 0)
     ZC_LAUNCH(ZC_PH_TILE_OFFSETS, zc::launch_tile_offsets(r->offsets, N, zc::kGemmBM, w.tile_off, s),
               "tile offsets");
+  if (lb)
+    ZC_LAUNCH(ZC_PH_LB_COEF,
+              zc::launch_lb_coef(r->counts, Tn, N, E, K, static_cast<int>(lb->D), lb->K_e,
+                                 lb->alpha, w.lbc, s),
+              "load-balance coefficient launch");
   ZC_LAUNCH(ZC_PH_BWD_COMBINE,
             zc::launch_combine_bwd<T>(x, y, dout, r->logits, r->topk_idx, r->topk_gate, r->inv, Tn,
-                                      dd, N, E, K, d->gate_norm, d->out_scale, w.gs, w.dg, w.dl,
-                                      ldl, s),
+                                      dd, N, E, K, d->gate_norm, d->out_scale,
+                                      lb ? w.lbc : nullptr, w.gs, w.dg, w.dl, ldl, s),
             "combine backward launch");
   if (N > 0) {
     if (Tn > 0)
@@ -466,6 +493,7 @@ size_t zc_moe_workspace_size(const zc_moe_desc* desc, int op) {
     case ZC_OP_ROUTE: return static_cast<size_t>(route_ws_bytes(desc));
     case ZC_OP_FORWARD: return static_cast<size_t>(fwd_ws_bytes(desc));
     case ZC_OP_BACKWARD: return static_cast<size_t>(bwd_ws_bytes(desc));
+    case ZC_OP_LB_LOSS: return static_cast<size_t>(lb_ws_bytes(desc));
     default: return 0;
   }
 }
@@ -528,8 +556,8 @@ zc_status zc_moe_forward(const zc_moe_desc* desc, const void* x, const void* w_r
 zc_status zc_moe_backward(const zc_moe_desc* desc, const void* x, const void* w_router,
                           const void* w_gate, const void* w_up, const void* w_down,
                           const zc_route_buf* r, const void* saved, const void* dout, void* dx,
-                          void* dw_router, void* dw_gate, void* dw_up, void* dw_down, void* ws,
-                          size_t ws_bytes, void* stream) {
+                          void* dw_router, void* dw_gate, void* dw_up, void* dw_down,
+                          const zc_lb_cfg* lb, void* ws, size_t ws_bytes, void* stream) {
   ZC_CHECK(check_desc(desc));
   if (desc->weight_layout != ZC_WEIGHTS_ROWMAJOR)
     return fail(ZC_ERR_UNSUPPORTED, "the backward needs row-major weights");
@@ -543,6 +571,7 @@ zc_status zc_moe_backward(const zc_moe_desc* desc, const void* x, const void* w_
   ZC_CHECK(check_ptr(dx, "dx", none));
   ZC_CHECK(check_ptr(dw_router, "dw_router"));
   ZC_CHECK(check_weights(desc, dw_gate, dw_up, dw_down));
+  if (lb) ZC_CHECK(check_lb(desc, lb));
   ZC_CHECK(check_ws(ws, ws_bytes, bwd_ws_bytes(desc)));
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
@@ -552,13 +581,32 @@ zc_status zc_moe_backward(const zc_moe_desc* desc, const void* x, const void* w_
         static_cast<const bf16_t*>(w_gate), static_cast<const bf16_t*>(w_up),
         static_cast<const bf16_t*>(w_down), r, saved, static_cast<const bf16_t*>(dout),
         static_cast<bf16_t*>(dx), static_cast<bf16_t*>(dw_router), static_cast<bf16_t*>(dw_gate),
-        static_cast<bf16_t*>(dw_up), static_cast<bf16_t*>(dw_down), w, s);
+        static_cast<bf16_t*>(dw_up), static_cast<bf16_t*>(dw_down), lb, w, s);
   return do_backward<float>(desc, static_cast<const float*>(x), static_cast<const float*>(w_router),
                             static_cast<const float*>(w_gate), static_cast<const float*>(w_up),
                             static_cast<const float*>(w_down), r, saved,
                             static_cast<const float*>(dout), static_cast<float*>(dx),
                             static_cast<float*>(dw_router), static_cast<float*>(dw_gate),
-                            static_cast<float*>(dw_up), static_cast<float*>(dw_down), w, s);
+                            static_cast<float*>(dw_up), static_cast<float*>(dw_down), lb, w, s);
+}
+
+zc_status zc_moe_lb_loss(const zc_moe_desc* desc, const zc_lb_cfg* lb, const zc_route_buf* r,
+                         double* out, void* ws, size_t ws_bytes, void* stream) {
+  ZC_CHECK(check_desc(desc));
+  ZC_CHECK(check_lb(desc, lb));
+  if (!r) return fail(ZC_ERR_INVALID, "route buffer is NULL");
+  ZC_CHECK(check_ptr(r->logits, "r->logits", desc->T == 0));
+  ZC_CHECK(check_ptr(r->counts, "r->counts"));
+  ZC_CHECK(check_ptr(out, "out"));
+  ZC_CHECK(check_ws(ws, ws_bytes, lb_ws_bytes(desc)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int E = static_cast<int>(desc->N + desc->Z);
+  ZC_LAUNCH(ZC_PH_LB_LOSS,
+            zc::launch_lb_loss(r->logits, r->counts, static_cast<int>(desc->T),
+                               static_cast<int>(desc->N), E, static_cast<int>(desc->K),
+                               static_cast<int>(lb->D), lb->K_e, lb->alpha, out, ws, s),
+            "load-balance loss launch");
+  return ZC_OK;
 }
 
 zc_status zc_moe_pack_weights(const zc_moe_desc* desc, int which, const void* src, void* dst,
@@ -636,7 +684,8 @@ const char* zc_moe_phase_name(int phase) {
   static const char* names[ZC_NUM_PHASES] = {
       "router_gemm", "topk", "dispatch", "gate_up_gemm", "down_gemm", "combine",
       "bwd_combine", "bwd_down_dh", "bwd_down_dw", "bwd_gate_up_dx", "bwd_gate_up_dw",
-      "bwd_router_dw", "bwd_router_dx", "bwd_dx_gather", "bias_update", "tile_offsets"};
+      "bwd_router_dw", "bwd_router_dx", "bwd_dx_gather", "bias_update", "tile_offsets",
+      "lb_loss", "lb_coef"};
   return (phase >= 0 && phase < ZC_NUM_PHASES) ? names[phase] : "";
 }
 

@@ -128,14 +128,16 @@ __device__ __forceinline__ float block_sum(float v, float* s_red) {
 //   gs[inv] = out_scale * g_r, the row scale the expert GEMMs apply;
 //   dl = gradient of the router scores through the gates: the softmax
 //        Jacobian restricted to the picks (renormalised gates) or over all
-//        experts (Eq.(1) gates), written as one fp32 row of width ldl.
+//        experts (Eq.(1) gates), written as one fp32 row of width ldl;
+//        with lbc, plus the device-level load-balance loss's gradient
+//        p_j (lbc_j - sum_k p_k lbc_k) (section 2.1.2, f held fixed).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
     const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ dout,
     const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
     const float* __restrict__ gate, const int32_t* __restrict__ inv, int d, int N, int E, int K,
-    int gate_norm, float out_scale, float* __restrict__ gs, float* __restrict__ dg_out,
-    float* __restrict__ dl, int ldl) {
+    int gate_norm, float out_scale, const float* __restrict__ lbc, float* __restrict__ gs,
+    float* __restrict__ dg_out, float* __restrict__ dl, int ldl) {
   __shared__ float s_g[kMaxK];
   __shared__ int32_t s_inv[kMaxK];
   __shared__ int32_t s_e[kMaxK];
@@ -166,34 +168,45 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
   float sgd = 0.f;
   for (int r = 0; r < K; ++r) sgd += s_g[r] * s_dg[r];
   float* dlr = dl + t * ldl;
-  if (gate_norm) {
+  if (gate_norm && !lbc) {
     for (int j = threadIdx.x; j < ldl; j += kThreads) dlr[j] = 0.f;
     __syncthreads();
     if (threadIdx.x < K) dlr[s_e[threadIdx.x]] = s_g[threadIdx.x] * (s_dg[threadIdx.x] - sgd);
-  } else {
-    const float* l = logits + t * E;
-    float m = -INFINITY;
-    for (int j = threadIdx.x; j < E; j += kThreads) m = fmaxf(m, l[j]);
+    return;
+  }
+  // the full softmax p of the token's scores
+  const float* l = logits + t * E;
+  float m = -INFINITY;
+  for (int j = threadIdx.x; j < E; j += kThreads) m = fmaxf(m, l[j]);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    float part = 0.f;
-    for (int j = threadIdx.x; j < E; j += kThreads) part += __expf(l[j] - m);
-    const float S = block_sum(part, s_red);
-    for (int j = threadIdx.x; j < ldl; j += kThreads) {
-      float v = 0.f;
-      if (j < E) {
-        const float pj = __expf(l[j] - m) / S;
-        float dgj = 0.f;
-        for (int r = 0; r < K; ++r)
-          if (s_e[r] == j) dgj = s_dg[r];
-        v = pj * (dgj - sgd);
-      }
-      dlr[j] = v;
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  float part = 0.f;
+  for (int j = threadIdx.x; j < E; j += kThreads) part += __expf(l[j] - m);
+  const float S = block_sum(part, s_red);
+  float sc = 0.f;
+  if (lbc) {
+    part = 0.f;
+    for (int j = threadIdx.x; j < E; j += kThreads) part += (__expf(l[j] - m) / S) * lbc[j];
+    sc = block_sum(part, s_red);
+  }
+  for (int j = threadIdx.x; j < ldl; j += kThreads) {
+    float v = 0.f;
+    if (j < E) {
+      const float pj = __expf(l[j] - m) / S;
+      int r = -1;
+      for (int q = 0; q < K; ++q)
+        if (s_e[q] == j) r = q;
+      if (gate_norm)
+        v = r >= 0 ? s_g[r] * (s_dg[r] - sgd) : 0.f;
+      else
+        v = pj * ((r >= 0 ? s_dg[r] : 0.f) - sgd);
+      if (lbc) v += pj * (lbc[j] - sc);
     }
+    dlr[j] = v;
   }
 }
 
@@ -244,10 +257,12 @@ template <typename T>
 hipError_t launch_combine_bwd(const T* x, const T* y, const T* dout, const float* logits,
                               const int32_t* topk_idx, const float* gate, const int32_t* inv,
                               int Tn, int d, int N, int E, int K, int gate_norm, float out_scale,
-                              float* gs, float* dg, float* dl, int ldl, hipStream_t s) {
+                              const float* lb_coef, float* gs, float* dg, float* dl, int ldl,
+                              hipStream_t s) {
   if (Tn == 0) return hipSuccess;
   hipLaunchKernelGGL(combine_bwd_kernel<T>, dim3(Tn), dim3(kThreads), 0, s, x, y, dout, logits,
-                     topk_idx, gate, inv, d, N, E, K, gate_norm, out_scale, gs, dg, dl, ldl);
+                     topk_idx, gate, inv, d, N, E, K, gate_norm, out_scale, lb_coef, gs, dg, dl,
+                     ldl);
   return hipGetLastError();
 }
 
@@ -267,8 +282,8 @@ hipError_t launch_dx_gather(const T* dout, const float* dxp, const float* dxr, c
                                         hipStream_t);                                           \
   template hipError_t launch_combine_bwd<T>(const T*, const T*, const T*, const float*,         \
                                             const int32_t*, const float*, const int32_t*, int,  \
-                                            int, int, int, int, int, float, float*, float*,     \
-                                            float*, int, hipStream_t);                          \
+                                            int, int, int, int, int, float, const float*,       \
+                                            float*, float*, float*, int, hipStream_t);          \
   template hipError_t launch_dx_gather<T>(const T*, const float*, const float*, const int32_t*, \
                                           const float*, const int32_t*, int, int, int, int,     \
                                           float, T*, hipStream_t);

@@ -62,17 +62,11 @@ __device__ __forceinline__ bool ahead(double ka, int ja, double kb, int jb) {
 
 constexpr int kWavesPerBlock = 4;
 
-// One wavefront per token; NPER = register slots per lane (E <= 64*NPER).
+// The routing exponentials of one token for one wavefront: lane L holds
+// e_j = key_exp(l_j - m) for j = L + 64 i (0 past E), and every lane gets S.
 template <int NPER>
-__global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(
-    const float* __restrict__ logits, const float* __restrict__ bias, int Tn, int E, int K,
-    int gate_norm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (t >= Tn) return;
-  const float* l = logits + static_cast<int64_t>(t) * E;
-
-  double ev[NPER], kv[NPER];
+__device__ __forceinline__ void token_exps(const float* __restrict__ l, int E, int lane,
+                                           double (&ev)[NPER], double& S) {
   float lv[NPER];
   float m = -INFINITY;
 #pragma unroll
@@ -84,7 +78,6 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   const double md = static_cast<double>(m);
-
   double part = 0.0;
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
@@ -94,7 +87,21 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) part = part + __shfl_xor(part, o);
-  const double S = part;
+  S = part;
+}
+
+// One wavefront per token; NPER = register slots per lane (E <= 64*NPER).
+template <int NPER>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int Tn, int E, int K,
+    int gate_norm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const float* l = logits + static_cast<int64_t>(t) * E;
+
+  double ev[NPER], kv[NPER], S;
+  token_exps<NPER>(l, E, lane, ev, S);
 
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
@@ -143,6 +150,114 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(
   }
 }
 
+
+// ------------------------------------------------------------------------
+// Device-level load-balance loss, "LongCat-Flash Technical Report", section
+// 2.1.2: L = alpha * sum_j f_j P_j over D groups of G = N/D consecutive FFN
+// experts plus one group holding every zero-computation expert.  P_j
+// (Eq.(4)) is the group's softmax mass averaged over the T tokens, f_j
+// (Eq.(5)) the number of picks that land in the group times D/(K_e T), or
+// 1/((K-K_e) T) for the extra group (left out when Z = 0).  The softmax is
+// the routing one above (binary64), so P follows the same R the picks saw.
+//
+// lb_colsum_kernel: wave w of block b walks tokens b*4+w, b*4+w+4*nblk, ...
+//   ascending, adding each token's e_j / S to a binary64 register per
+//   expert; the block adds its four waves in wave order into part[b][E].
+// lb_reduce_kernel: col[j] = part[0..nblk)[j], four consecutive quarters
+//   of b (one per wave, ascending) added in wave order.
+// lb_finish_kernel: per group, col and counts summed over ascending j;
+//   out = [L, f_1..f_{D+1}, P_1..P_{D+1}]; L summed over the groups in a
+//   fixed tree.  Every order is fixed, so the result is reproducible.
+template <int NPER>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void lb_colsum_kernel(
+    const float* __restrict__ logits, int Tn, int E, double* __restrict__ part) {
+  __shared__ double s_col[kWavesPerBlock][64 * NPER];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  double col[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) col[i] = 0.0;
+  for (int t = blockIdx.x * kWavesPerBlock + w; t < Tn; t += gridDim.x * kWavesPerBlock) {
+    double ev[NPER], S;
+    token_exps<NPER>(logits + static_cast<int64_t>(t) * E, E, lane, ev, S);
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) col[i] = col[i] + ev[i] / S;
+  }
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) s_col[w][lane + 64 * i] = col[i];
+  __syncthreads();
+  for (int j = threadIdx.x; j < E; j += 64 * kWavesPerBlock)
+    part[static_cast<int64_t>(blockIdx.x) * E + j] =
+        ((s_col[0][j] + s_col[1][j]) + s_col[2][j]) + s_col[3][j];
+}
+
+__global__ __launch_bounds__(64 * kWavesPerBlock) void lb_reduce_kernel(
+    const double* __restrict__ part, int nblk, int E, double* __restrict__ col) {
+  __shared__ double s_r[kWavesPerBlock][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + lane;
+  const int q = (nblk + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int b1 = min(nblk, (w + 1) * q);
+  double v = 0.0;
+  if (j < E)
+    for (int b = w * q; b < b1; ++b) v = v + part[static_cast<int64_t>(b) * E + j];
+  s_r[w][lane] = v;
+  __syncthreads();
+  if (w == 0 && j < E) col[j] = ((s_r[0][lane] + s_r[1][lane]) + s_r[2][lane]) + s_r[3][lane];
+}
+
+// Pick frequency f_g of group g (D/(K_e T) or 1/((K-K_e) T) times the
+// group's picks), from the per-expert pick counts.
+__device__ __forceinline__ double lb_freq(const int32_t* __restrict__ counts, int g, int G, int N,
+                                          int E, int D, int K, double K_e, int Tn) {
+  const int lo = g < D ? g * G : N, hi = g < D ? lo + G : E;
+  int64_t c = 0;
+  for (int j = lo; j < hi; ++j) c += counts[j];
+  if (g < D) return static_cast<double>(D) / (K_e * static_cast<double>(Tn)) * static_cast<double>(c);
+  if (E == N) return 0.0;
+  return 1.0 / ((static_cast<double>(K) - K_e) * static_cast<double>(Tn)) * static_cast<double>(c);
+}
+
+__global__ __launch_bounds__(64 * kWavesPerBlock) void lb_finish_kernel(
+    const double* __restrict__ col, const int32_t* __restrict__ counts, int Tn, int N, int E,
+    int K, int D, double K_e, double alpha, double* __restrict__ out) {
+  __shared__ double s_red[kWavesPerBlock];
+  const int ng = D + 1, G = N / D;
+  double acc = 0.0;
+  for (int g = threadIdx.x; g < ng; g += 64 * kWavesPerBlock) {
+    double f = 0.0, P = 0.0;
+    if (Tn > 0) {
+      const int lo = g < D ? g * G : N, hi = g < D ? lo + G : E;
+      double p = 0.0;
+      for (int j = lo; j < hi; ++j) p = p + col[j];
+      P = p / static_cast<double>(Tn);
+      f = lb_freq(counts, g, G, N, E, D, K, K_e, Tn);
+    }
+    out[1 + g] = f;
+    out[1 + ng + g] = P;
+    acc = acc + f * P;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) out[0] = alpha * (((s_red[0] + s_red[1]) + s_red[2]) + s_red[3]);
+}
+
+// Per-expert coefficient of the loss's score gradient,
+// c_j = (float)(alpha * f_{g(j)} / T): dL/dl_{t,j} = R_{t,j} (c_j - sum_k R_{t,k} c_k).
+__global__ __launch_bounds__(64 * kWavesPerBlock) void lb_coef_kernel(
+    const int32_t* __restrict__ counts, int Tn, int N, int E, int K, int D, double K_e,
+    double alpha, float* __restrict__ coef) {
+  __shared__ double s_f[kMaxExperts + 1];
+  const int ng = D + 1, G = N / D;
+  for (int g = threadIdx.x; g < ng; g += 64 * kWavesPerBlock)
+    s_f[g] = Tn > 0 ? lb_freq(counts, g, G, N, E, D, K, K_e, Tn) : 0.0;
+  __syncthreads();
+  for (int j = threadIdx.x; j < E; j += 64 * kWavesPerBlock) {
+    const double f = s_f[j < N ? j / G : D];
+    coef[j] = Tn > 0 ? static_cast<float>(alpha * f / static_cast<double>(Tn)) : 0.f;
+  }
+}
 }  // namespace
 
 hipError_t launch_topk(const float* logits, const float* bias, int Tn, int E, int K,
@@ -160,6 +275,51 @@ hipError_t launch_topk(const float* logits, const float* bias, int Tn, int E, in
   else if (nper <= 12) ZC_TOPK(12);
   else ZC_TOPK(16);
 #undef ZC_TOPK
+  return hipGetLastError();
+}
+
+int lb_blocks(int64_t Tn) {
+  const int64_t b = (Tn + 31) / 32;
+  return static_cast<int>(b < 1 ? 1 : (b > 256 ? 256 : b));
+}
+
+size_t lb_scratch_bytes(int64_t Tn, int64_t E) {
+  return static_cast<size_t>(lb_blocks(Tn) + 1) * static_cast<size_t>(E) * sizeof(double);
+}
+
+hipError_t launch_lb_loss(const float* logits, const int32_t* counts, int Tn, int N, int E, int K,
+                          int D, double K_e, double alpha, double* out, void* scratch,
+                          hipStream_t s) {
+  const int nblk = lb_blocks(Tn);
+  double* part = static_cast<double*>(scratch);
+  double* col = part + static_cast<int64_t>(nblk) * E;
+  const dim3 block(64 * kWavesPerBlock);
+  if (Tn > 0) {
+    const int nper = (E + 63) / 64;
+#define ZC_LBC(NP) \
+  hipLaunchKernelGGL((lb_colsum_kernel<NP>), dim3(nblk), block, 0, s, logits, Tn, E, part)
+    if (nper <= 1) ZC_LBC(1);
+    else if (nper <= 2) ZC_LBC(2);
+    else if (nper <= 4) ZC_LBC(4);
+    else if (nper <= 8) ZC_LBC(8);
+    else if (nper <= 12) ZC_LBC(12);
+    else ZC_LBC(16);
+#undef ZC_LBC
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(lb_reduce_kernel, dim3((E + 63) / 64), block, 0, s, part, nblk, E, col);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(lb_finish_kernel, dim3(1), block, 0, s, col, counts, Tn, N, E, K, D, K_e,
+                     alpha, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_lb_coef(const int32_t* counts, int Tn, int N, int E, int K, int D, double K_e,
+                          double alpha, float* coef, hipStream_t s) {
+  hipLaunchKernelGGL(lb_coef_kernel, dim3(1), dim3(64 * kWavesPerBlock), 0, s, counts, Tn, N, E, K,
+                     D, K_e, alpha, coef);
   return hipGetLastError();
 }
 

@@ -63,6 +63,18 @@ hipError_t launch_router_gemm(const T* x, const T* wr, float* logits, int Tn, in
 hipError_t launch_topk(const float* logits, const float* bias, int Tn, int E, int K,
                        int gate_norm, int32_t* topk_idx, float* topk_gate, hipStream_t s);
 
+// Device-level load-balance loss of section 2.1.2 (Eq.(4)-(5)) from the
+// scores and the per-expert pick counts: out = [L, f_1..f_{D+1},
+// P_1..P_{D+1}] (binary64).  Scratch: lb_scratch_bytes(T, E).
+size_t lb_scratch_bytes(int64_t Tn, int64_t E);
+hipError_t launch_lb_loss(const float* logits, const int32_t* counts, int Tn, int N, int E, int K,
+                          int D, double K_e, double alpha, double* out, void* scratch,
+                          hipStream_t s);
+// coef[j] = alpha * f_{g(j)} / T (fp32, [E]): the loss's score gradient is
+// R_j (coef_j - sum_k R_k coef_k) for each token.
+hipError_t launch_lb_coef(const int32_t* counts, int Tn, int N, int E, int K, int D, double K_e,
+                          double alpha, float* coef, hipStream_t s);
+
 // Dispatch: per-expert counts, offsets, canonical permutation and its inverse.
 // Scratch: dispatch_scratch_bytes(T, E, N).  Also writes the per-expert
 // row-tile prefixes tile_off[N+1] and tile_off2[N+1] for the grouped GEMMs
@@ -155,12 +167,15 @@ hipError_t launch_combine(const T* x, const T* y, const int32_t* topk_idx, const
                           T* out, hipStream_t s);
 
 // Combine backward: dg per slot, out_scale * gate of every FFN pick in
-// dispatch order (gs), and the router-score gradient dl [T][ldl] (fp32).
+// dispatch order (gs), and the router-score gradient dl [T][ldl] (fp32);
+// with lb_coef (from launch_lb_coef, else NULL) dl also takes the
+// load-balance loss's score gradient.
 template <typename T>
 hipError_t launch_combine_bwd(const T* x, const T* y, const T* dout, const float* logits,
                               const int32_t* topk_idx, const float* gate, const int32_t* inv,
                               int Tn, int d, int N, int E, int K, int gate_norm, float out_scale,
-                              float* gs, float* dg, float* dl, int ldl, hipStream_t s);
+                              const float* lb_coef, float* gs, float* dg, float* dl, int ldl,
+                              hipStream_t s);
 
 // dx gather: dx = out_scale * c_t * dout_t + sum_r dxp[inv] + dxr_t.
 template <typename T>

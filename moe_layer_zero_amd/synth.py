@@ -75,6 +75,12 @@ ZIPF_S = 1.1
 TRAIN_K_E = 6.0
 TRAIN_MU = 1.0
 TRAIN_STEPS = 50
+# Device-level load-balance loss of the training layer: its 128 FFN experts
+# in 8 groups of 16 (one group per device of an 8-way expert-parallel
+# placement); the balance factor is not printed with the loss, 1e-3 is a
+# stated choice.
+TRAIN_LB_D = 8
+TRAIN_LB_ALPHA = 1e-3
 
 X, WR, WG, WU, WD, BIAS, DY, RANK = 1, 2, 3, 4, 5, 6, 7, 8
 

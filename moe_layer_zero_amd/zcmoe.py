@@ -19,16 +19,17 @@ LIB_PATH = os.path.join(HERE, "libzcmoe.so")
 
 ZC_OK, ZC_ERR_INVALID, ZC_ERR_UNSUPPORTED, ZC_ERR_WORKSPACE, ZC_ERR_HIP = range(5)
 ZC_F32, ZC_BF16 = 0, 1
-ZC_OP_ROUTE, ZC_OP_FORWARD, ZC_OP_BACKWARD = 0, 1, 2
+ZC_OP_ROUTE, ZC_OP_FORWARD, ZC_OP_BACKWARD, ZC_OP_LB_LOSS = 0, 1, 2, 3
 ZC_WEIGHTS_ROWMAJOR, ZC_WEIGHTS_PACKED = 0, 1
 ZC_PACK_GATE_UP, ZC_PACK_DOWN = 0, 1
 
 # Every symbol include/zc_moe.h declares.
 EXPORTS = ("zc_moe_workspace_size", "zc_moe_saved_size", "zc_moe_route", "zc_moe_forward",
-           "zc_moe_backward", "zc_moe_pid_update", "zc_moe_pack_weights", "zc_moe_profile",
+           "zc_moe_backward", "zc_moe_lb_loss", "zc_moe_pid_update", "zc_moe_pack_weights",
+           "zc_moe_profile",
            "zc_moe_profile_read",
            "zc_moe_phase_name", "zc_status_string", "zc_last_error")
-ZC_NUM_PHASES = 16
+ZC_NUM_PHASES = 18
 
 
 class ZcError(RuntimeError):
@@ -42,6 +43,10 @@ class zc_moe_desc(C.Structure):
                 ("I", C.c_int64), ("K", C.c_int64), ("dtype", C.c_int32),
                 ("gate_norm", C.c_int32), ("out_scale", C.c_float),
                 ("weight_layout", C.c_int32)]
+
+
+class zc_lb_cfg(C.Structure):
+    _fields_ = [("D", C.c_int64), ("K_e", C.c_double), ("alpha", C.c_double)]
 
 
 class zc_route_buf(C.Structure):
@@ -69,11 +74,13 @@ def lib() -> C.CDLL:
         L.zc_moe_saved_size.restype = sz
         L.zc_moe_route.argtypes = [P, v, v, v, D, v, sz, v]
         L.zc_moe_forward.argtypes = [P, v, v, v, v, v, v, v, D, v, v, sz, v]
-        L.zc_moe_backward.argtypes = [P, v, v, v, v, v, D, v, v, v, v, v, v, v, v, sz, v]
+        LB = C.POINTER(zc_lb_cfg)
+        L.zc_moe_backward.argtypes = [P, v, v, v, v, v, D, v, v, v, v, v, v, v, LB, v, sz, v]
+        L.zc_moe_lb_loss.argtypes = [P, LB, D, v, v, sz, v]
         L.zc_moe_pid_update.argtypes = [i64, i64, i64, v, i64, C.c_double, C.c_double, v, v]
         L.zc_moe_pack_weights.argtypes = [P, C.c_int, v, v, v]
-        for f in ("zc_moe_route", "zc_moe_forward", "zc_moe_backward", "zc_moe_pid_update",
-                  "zc_moe_pack_weights"):
+        for f in ("zc_moe_route", "zc_moe_forward", "zc_moe_backward", "zc_moe_lb_loss",
+                  "zc_moe_pid_update", "zc_moe_pack_weights"):
             getattr(L, f).restype = C.c_int
         L.zc_moe_profile.argtypes = [C.c_int]
         L.zc_moe_profile.restype = C.c_int
@@ -217,8 +224,21 @@ def zc_moe_forward(desc: LayerDesc, x, w_router, bias, w_gate, w_up, w_down, out
                                 _ptr(ws), ws.numel(), _stream(stream)), "zc_moe_forward")
 
 
+@dataclass
+class LoadBalance:
+    """Device-level load-balance loss settings: D groups of N/D consecutive
+    FFN experts, expected FFN experts per token K_e, balance factor alpha."""
+    D: int
+    K_e: float
+    alpha: float
+
+    def c(self) -> zc_lb_cfg:
+        return zc_lb_cfg(int(self.D), float(self.K_e), float(self.alpha))
+
+
 def zc_moe_backward(desc: LayerDesc, x, w_router, w_gate, w_up, w_down, route: RouteBuffers,
-                    saved, dout, dx, dw_router, dw_gate, dw_up, dw_down, ws=None, stream=None):
+                    saved, dout, dx, dw_router, dw_gate, dw_up, dw_down, ws=None, stream=None,
+                    lb: "LoadBalance | None" = None):
     for t, n in ((x, "x"), (dout, "dout"), (dx, "dx")):
         _check_layer_tensor(t, (desc.T, desc.d), desc.dtype, n)
     _check_weights(desc, w_router, w_gate, w_up, w_down)
@@ -226,10 +246,26 @@ def zc_moe_backward(desc: LayerDesc, x, w_router, w_gate, w_up, w_down, route: R
     if ws is None:
         ws = workspace(desc, ZC_OP_BACKWARD, x.device)
     d, r = desc.c(), route.c()
+    lbc = None if lb is None else C.byref(lb.c())
     _check(lib().zc_moe_backward(C.byref(d), _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up),
                                  _ptr(w_down), C.byref(r), _ptr(saved), _ptr(dout), _ptr(dx),
                                  _ptr(dw_router), _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down),
-                                 _ptr(ws), ws.numel(), _stream(stream)), "zc_moe_backward")
+                                 lbc, _ptr(ws), ws.numel(), _stream(stream)), "zc_moe_backward")
+
+
+def zc_moe_lb_loss(desc: LayerDesc, lb: LoadBalance, route: RouteBuffers, out=None, ws=None,
+                   stream=None):
+    """Queues the device-level load-balance loss of the routed batch; returns
+    out, a float64 GPU tensor [1 + 2(D+1)]: L, f_1..f_{D+1}, P_1..P_{D+1}."""
+    if out is None:
+        out = torch.empty(1 + 2 * (lb.D + 1), dtype=torch.float64, device=route.counts.device)
+    _check_layer_tensor(out, (1 + 2 * (lb.D + 1),), torch.float64, "out")
+    if ws is None:
+        ws = workspace(desc, ZC_OP_LB_LOSS, route.counts.device)
+    d, r, c = desc.c(), route.c(), lb.c()
+    _check(lib().zc_moe_lb_loss(C.byref(d), C.byref(c), C.byref(r), _ptr(out), _ptr(ws),
+                                ws.numel(), _stream(stream)), "zc_moe_lb_loss")
+    return out
 
 
 def zc_moe_pid_update(N: int, Z: int, K: int, counts, T_all: int, mu: float, K_e: float, bias,

@@ -45,7 +45,8 @@ def test_sizes_are_positive_and_grow_with_T():
     for dt in (torch.float32, torch.bfloat16):
         a = desc(dtype=dt)
         b = desc(dtype=dt, T=4096)
-        for op in (zcmoe.ZC_OP_ROUTE, zcmoe.ZC_OP_FORWARD, zcmoe.ZC_OP_BACKWARD):
+        for op in (zcmoe.ZC_OP_ROUTE, zcmoe.ZC_OP_FORWARD, zcmoe.ZC_OP_BACKWARD,
+                   zcmoe.ZC_OP_LB_LOSS):
             assert 0 < zcmoe.zc_moe_workspace_size(a, op) < zcmoe.zc_moe_workspace_size(b, op)
         assert 0 < zcmoe.zc_moe_saved_size(a) < zcmoe.zc_moe_saved_size(b)
     # an invalid description sizes to 0
@@ -116,7 +117,7 @@ def test_forward_backward_argument_checks(L):
     assert st == zcmoe.ZC_ERR_WORKSPACE
     # backward needs the saved activations
     st = L.zc_moe_backward(C.byref(dd), FAKE, FAKE, FAKE, FAKE, FAKE, C.byref(r), None, FAKE, FAKE,
-                           FAKE, FAKE, FAKE, FAKE, FAKE, big, None)
+                           FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None)
     assert st == zcmoe.ZC_ERR_INVALID and "saved" in L.zc_last_error().decode()
     # Eq.(2) update: T_all >= 1
     st = L.zc_moe_pid_update(8, 4, 2, FAKE, 0, 1.0, 1.5, FAKE, None)
@@ -158,7 +159,7 @@ def test_packed_weight_argument_checks(L):
                           FAKE, big, None)
     assert st == zcmoe.ZC_ERR_UNSUPPORTED and "row-major" in L.zc_last_error().decode()
     st = L.zc_moe_backward(C.byref(dd), FAKE, FAKE, FAKE, FAKE, FAKE, C.byref(r), FAKE, FAKE, FAKE,
-                           FAKE, FAKE, FAKE, FAKE, FAKE, big, None)
+                           FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None)
     assert st == zcmoe.ZC_ERR_UNSUPPORTED and "row-major" in L.zc_last_error().decode()
     # the packing call itself
     other = C.c_void_p(1 << 40)
@@ -169,3 +170,36 @@ def test_packed_weight_argument_checks(L):
     assert L.zc_moe_pack_weights(C.byref(f32), 0, FAKE, other, None) == zcmoe.ZC_ERR_UNSUPPORTED
     odd = desc(dtype=torch.bfloat16, d=256, I=192).c()
     assert L.zc_moe_pack_weights(C.byref(odd), 1, FAKE, other, None) == zcmoe.ZC_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("cfg,kw", [
+    (dict(D=3, K_e=1.5, alpha=0.1), {}),              # 3 does not divide N = 8
+    (dict(D=0, K_e=1.5, alpha=0.1), {}),
+    (dict(D=16, K_e=1.5, alpha=0.1), {}),             # more groups than experts
+    (dict(D=2, K_e=2.0, alpha=0.1), {}),              # K_e = K with Z > 0
+    (dict(D=2, K_e=0.0, alpha=0.1), {}),
+    (dict(D=2, K_e=float("nan"), alpha=0.1), {}),
+    (dict(D=2, K_e=1.5, alpha=float("inf")), {}),
+    (dict(D=1, K_e=1.0, alpha=0.1), dict(N=0, Z=4)),  # no FFN experts
+])
+def test_lb_loss_argument_checks(L, cfg, kw):
+    d = desc(**kw).c()
+    c = zcmoe.zc_lb_cfg(cfg["D"], cfg["K_e"], cfg["alpha"])
+    r = route_buf()
+    st = L.zc_moe_lb_loss(C.byref(d), C.byref(c), C.byref(r), FAKE, FAKE, 1 << 40, None)
+    assert st == zcmoe.ZC_ERR_INVALID, L.zc_last_error()
+    # the backward checks the same settings before anything else is queued
+    st = L.zc_moe_backward(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, C.byref(r), FAKE, FAKE, FAKE,
+                           FAKE, FAKE, FAKE, FAKE, C.byref(c), FAKE, 1 << 40, None)
+    assert st == zcmoe.ZC_ERR_INVALID
+
+
+def test_lb_loss_accepts_k_e_equal_k_without_zero_experts(L):
+    d = desc(Z=0).c()
+    c = zcmoe.zc_lb_cfg(4, 2.0, 0.1)
+    r = route_buf()
+    # valid settings: fails only on the workspace
+    st = L.zc_moe_lb_loss(C.byref(d), C.byref(c), C.byref(r), FAKE, FAKE, 8, None)
+    assert st == zcmoe.ZC_ERR_WORKSPACE
+    st = L.zc_moe_lb_loss(C.byref(d), C.byref(c), C.byref(r), None, FAKE, 1 << 40, None)
+    assert st == zcmoe.ZC_ERR_INVALID and "out" in L.zc_last_error().decode()
