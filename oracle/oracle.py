@@ -40,11 +40,12 @@ def lib():
                                    _p, _p, _p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _p,
                                    _p]
         L.orc_lb_loss.argtypes = [_i64, _i64, _i64, _i64, _i64, _f64, _f64, _p, _p, _p, _p]
+        L.orc_route_stats.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p]
         L.orc_num_threads.restype = C.c_int
         L.orc_num_threads.argtypes = []
         L.orc_pid_update.argtypes = [_i64, _i64, _i64, _p, _i64, _f64, _f64, _p]
         for f in ("orc_logits", "orc_route", "orc_forward", "orc_backward", "orc_pid_update",
-                  "orc_lb_loss"):
+                  "orc_lb_loss", "orc_route_stats"):
             getattr(L, f).restype = C.c_int
         _LIB = L
     return _LIB
@@ -226,3 +227,14 @@ def lb_loss(lg, topk_idx, N, D, K_e, alpha, want_grad=True):
     if rc != 0:
         raise ValueError(f"oracle lb_loss rejected its arguments (rc={rc})")
     return float(out[0]), out[1:D + 2].copy(), out[D + 2:].copy(), dl
+
+
+def route_stats(topk_idx, N):
+    """O11: FFN experts per token -> (hist [K+1] int32, mean, std)."""
+    ti = _c(topk_idx, np.int32)
+    T, K = ti.shape
+    hist = np.zeros(K + 1, np.int32)
+    m, s = C.c_double(), C.c_double()
+    rc = lib().orc_route_stats(T, N, K, _ptr(ti), _ptr(hist), C.byref(m), C.byref(s))
+    assert rc == 0, f"oracle route_stats failed rc={rc}"
+    return hist, m.value, s.value

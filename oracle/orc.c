@@ -11,7 +11,8 @@
  * 171host.com), section 2.1 "Zero-computation experts", Eq.(1) and the
  * expert definition E_i that follows it, section 2.1.1 "Computation
  * budget control", Eq.(2), and section 2.1.2 "Load balance control" (the
- * device-level loss L_LB with Eq.(4) and Eq.(5)).  The FFN expert form (SwiGLU without biases) and
+ * device-level loss L_LB with Eq.(4) and Eq.(5)); the routing telemetry
+ * follows the statistics section 2.1.1 records (Fig.3b/3c).  The FFN expert form (SwiGLU without biases) and
  * the linear softmax router are readings of points the page leaves open.
  *
  * Every floating-point step runs in binary64 on the exact values of the
@@ -573,5 +574,39 @@ int orc_lb_loss(int64_t T, int64_t E, int64_t N, int64_t K, int64_t D,
     }
   }
   free(R);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O11 -- budget-control telemetry of section 2.1.1 (the mean and the
+ * standard deviation of the FFN experts each token activates, plotted in
+ * Fig.3b/3c):
+ *   n_t = number of the token's K picks that are FFN experts (index < N);
+ *   hist[k] = number of tokens with n_t = k, k = 0..K;
+ *   mean = (1/T) sum_t n_t;  std = sqrt((1/T) sum_t (n_t - mean)^2)
+ * (the population deviation over the batch's tokens, t ascending).
+ * T = 0 gives an all-zero histogram and mean = std = 0. */
+int orc_route_stats(int64_t T, int64_t N, int64_t K, const int32_t* topk_idx,
+                    int32_t* hist, double* mean, double* std) {
+  if (T < 0 || N < 0 || K < 1 || !hist || !mean || !std || (T > 0 && !topk_idx)) return 1;
+  for (int64_t k = 0; k <= K; ++k) hist[k] = 0;
+  *mean = 0.0;
+  *std = 0.0;
+  if (T == 0) return 0;
+  int32_t* n = (int32_t*)malloc(sizeof(int32_t) * (size_t)T);
+  for (int64_t t = 0; t < T; ++t) {
+    int32_t c = 0;
+    for (int64_t r = 0; r < K; ++r) c += topk_idx[t * K + r] < N ? 1 : 0;
+    n[t] = c;
+    hist[c] += 1;
+  }
+  double s = 0.0;
+  for (int64_t t = 0; t < T; ++t) s += (double)n[t];
+  double m = s / (double)T;
+  double v = 0.0;
+  for (int64_t t = 0; t < T; ++t) v += ((double)n[t] - m) * ((double)n[t] - m);
+  *mean = m;
+  *std = sqrt(v / (double)T);
+  free(n);
   return 0;
 }

@@ -193,3 +193,56 @@ def test_backward_with_lb_gradient_against_autograd(orc):
     g0 = orc.backward(L["x"], L["wr"], L["wg"], L["wu"], L["wd"], lg, ro.topk_idx, ro.gates,
                       dY, N, Z)
     assert np.abs(g["dwr"] - g0["dwr"]).max() > 1e-4
+
+
+# ------------------------------------------------- budget-control telemetry
+def test_route_stats_closed_forms(orc):
+    """All picks FFN: every token activates K, mean K, std 0.  Tokens whose
+    FFN-pick count cycles through 0..K: the discrete uniform law, mean K/2,
+    variance ((K+1)^2 - 1)/12."""
+    N, Z, K, T = 6, 6, 4, 5 * 7
+    idx = np.tile(np.arange(K, dtype=np.int32), (T, 1))
+    hist, m, s = orc.route_stats(idx, N)
+    assert hist.tolist() == [0] * K + [T] and m == K and s == 0.0
+    rows = []
+    for t in range(T):
+        k = t % (K + 1)
+        rows.append(list(range(k)) + list(range(N, N + K - k)))
+    hist, m, s = orc.route_stats(np.array(rows, np.int32), N)
+    assert hist.tolist() == [T // (K + 1)] * (K + 1)
+    assert abs(m - K / 2) < 1e-15
+    assert abs(s - np.sqrt(((K + 1) ** 2 - 1) / 12)) < 1e-15
+
+
+def test_route_stats_against_numpy_and_counts(orc):
+    """Random routing: numpy's bincount / mean / std (population) of the
+    per-token FFN-pick counts, and sum_k k hist[k] = sum of the FFN experts'
+    token counts from the routing."""
+    r = rng(9)
+    N, Z, K, T = 24, 12, 6, 500
+    lg = r.standard_normal((T, N + Z))
+    ro = orc.route(lg, np.zeros(N + Z, np.float32), N, K)
+    hist, m, s = orc.route_stats(ro.topk_idx, N)
+    n_t = (ro.topk_idx < N).sum(1)
+    np.testing.assert_array_equal(hist, np.bincount(n_t, minlength=K + 1))
+    assert abs(m - n_t.mean()) < 1e-14 and abs(s - n_t.std()) < 1e-14
+    assert int((np.arange(K + 1) * hist).sum()) == int(ro.counts[:N].sum())
+    h0, m0, s0 = orc.route_stats(np.zeros((0, K), np.int32), N)
+    assert not h0.any() and m0 == 0.0 and s0 == 0.0
+
+
+def test_global_batch_counts_are_micro_batch_sums(orc):
+    """Routing is per token, so the T_i of Eq.(2) over a global batch equal
+    the sums of the micro-batches' counts, and one bias update on the summed
+    counts with T_all = sum of T equals the update on the whole batch."""
+    r = rng(10)
+    N, Z, K = 16, 8, 4
+    bias = r.uniform(-0.05, 0.05, N + Z).astype(np.float32)
+    parts = [r.standard_normal((T, N + Z)) for T in (37, 64, 5)]
+    whole = orc.route(np.concatenate(parts), bias, N, K)
+    acc = sum(orc.route(p, bias, N, K).counts.astype(np.int64) for p in parts)
+    np.testing.assert_array_equal(acc, whole.counts)
+    T_all = sum(p.shape[0] for p in parts)
+    b1 = orc.pid_update(acc.astype(np.int32), T_all, bias, N, Z, K, 0.7, 2.5)
+    b2 = orc.pid_update(whole.counts, T_all, bias, N, Z, K, 0.7, 2.5)
+    np.testing.assert_array_equal(b1, b2)
