@@ -97,7 +97,10 @@ typedef struct {
                      /*        zero-computation pick                          */
 } zc_route_buf;
 
-enum { ZC_OP_ROUTE = 0, ZC_OP_FORWARD = 1, ZC_OP_BACKWARD = 2, ZC_OP_LB_LOSS = 3 };
+enum {
+  ZC_OP_ROUTE = 0, ZC_OP_FORWARD = 1, ZC_OP_BACKWARD = 2, ZC_OP_LB_LOSS = 3,
+  ZC_OP_ROUTE_STATS = 4
+};
 
 /* Device-level load-balance loss settings ("LongCat-Flash Technical
  * Report", section 2.1.2; host struct, passed by pointer).  The N FFN
@@ -207,6 +210,28 @@ zc_status zc_moe_pid_update(int64_t N, int64_t Z, int64_t K,
                             const int32_t* counts, int64_t T_all, double mu,
                             double K_e, float* bias, void* stream);
 
+/* Budget-control telemetry ("LongCat-Flash Technical Report", section
+ * 2.1.1, which tracks the mean and the spread of the FFN experts each token
+ * activates, Fig.3b/3c).  From r->topk_idx of a routed batch:
+ *   n_t      = number of token t's K picks that are FFN experts (< N);
+ *   hist[k]  = tokens with n_t = k, k = 0..K   (device, K+1 int32);
+ *   moments  = [mean of n_t, population standard deviation of n_t]
+ *              (device, 2 doubles; mean from the exact integer sum; both 0
+ *              when T = 0).
+ * Scratch: zc_moe_workspace_size(desc, ZC_OP_ROUTE_STATS) bytes. */
+zc_status zc_moe_route_stats(const zc_moe_desc* desc, const zc_route_buf* r,
+                             int32_t* hist, double* moments, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* acc[i] += counts[i] for i < E (device int32 arrays, distinct): sums the
+ * per-expert counts T_i of several micro-batches (or steps), so that one
+ * zc_moe_pid_update over acc with T_all = their total tokens applies
+ * Eq.(2) over a global batch, or at a lower update frequency, as section
+ * 2.1.1 advises for small batches.  The caller zeroes acc before the first
+ * micro-batch and keeps the total below 2^31 picks per expert. */
+zc_status zc_moe_accumulate_counts(int64_t E, const int32_t* counts,
+                                   int32_t* acc, void* stream);
+
 /* Rearranges one set of FFN expert weights (bf16) from the row-major layout
  * into ZC_WEIGHTS_PACKED, for the bf16 inference forward, which then streams
  * every weight panel from HBM in whole 1 KB pieces straight into the matrix
@@ -237,7 +262,8 @@ enum {
   ZC_PH_ROUTER_GEMM = 0, ZC_PH_TOPK, ZC_PH_DISPATCH, ZC_PH_GATE_UP, ZC_PH_DOWN, ZC_PH_COMBINE,
   ZC_PH_BWD_COMBINE, ZC_PH_BWD_DOWN_DH, ZC_PH_BWD_DOWN_DW, ZC_PH_BWD_GATE_UP_DX,
   ZC_PH_BWD_GATE_UP_DW, ZC_PH_BWD_ROUTER_DW, ZC_PH_BWD_ROUTER_DX, ZC_PH_BWD_DX_GATHER,
-  ZC_PH_BIAS_UPDATE, ZC_PH_TILE_OFFSETS, ZC_PH_LB_LOSS, ZC_PH_LB_COEF, ZC_NUM_PHASES
+  ZC_PH_BIAS_UPDATE, ZC_PH_TILE_OFFSETS, ZC_PH_LB_LOSS, ZC_PH_LB_COEF, ZC_PH_ROUTE_STATS,
+  ZC_PH_ACCUMULATE, ZC_NUM_PHASES
 };
 zc_status zc_moe_profile(int on);
 zc_status zc_moe_profile_read(double* total_ms, int32_t* count);

@@ -304,6 +304,9 @@ zc_status check_lb(const zc_moe_desc* d, const zc_lb_cfg* lb) {
   if (!std::isfinite(lb->alpha)) return fail(ZC_ERR_INVALID, "alpha is not finite");
   return ZC_OK;
 }
+int64_t stats_ws_bytes(const zc_moe_desc* d) {
+  return a256(static_cast<int64_t>(zc::stats_scratch_bytes(d->T, d->K)));
+}
 int64_t lb_ws_bytes(const zc_moe_desc* d) {
   return a256(static_cast<int64_t>(zc::lb_scratch_bytes(d->T, d->N + d->Z)));
 }
@@ -494,6 +497,7 @@ size_t zc_moe_workspace_size(const zc_moe_desc* desc, int op) {
     case ZC_OP_FORWARD: return static_cast<size_t>(fwd_ws_bytes(desc));
     case ZC_OP_BACKWARD: return static_cast<size_t>(bwd_ws_bytes(desc));
     case ZC_OP_LB_LOSS: return static_cast<size_t>(lb_ws_bytes(desc));
+    case ZC_OP_ROUTE_STATS: return static_cast<size_t>(stats_ws_bytes(desc));
     default: return 0;
   }
 }
@@ -609,6 +613,34 @@ zc_status zc_moe_lb_loss(const zc_moe_desc* desc, const zc_lb_cfg* lb, const zc_
   return ZC_OK;
 }
 
+zc_status zc_moe_route_stats(const zc_moe_desc* desc, const zc_route_buf* r, int32_t* hist,
+                             double* moments, void* ws, size_t ws_bytes, void* stream) {
+  ZC_CHECK(check_desc(desc));
+  if (!r) return fail(ZC_ERR_INVALID, "route buffer is NULL");
+  ZC_CHECK(check_ptr(r->topk_idx, "r->topk_idx", desc->T == 0));
+  ZC_CHECK(check_ptr(hist, "hist"));
+  ZC_CHECK(check_ptr(moments, "moments"));
+  ZC_CHECK(check_ws(ws, ws_bytes, stats_ws_bytes(desc)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ZC_LAUNCH(ZC_PH_ROUTE_STATS,
+            zc::launch_route_stats(r->topk_idx, static_cast<int>(desc->T),
+                                   static_cast<int>(desc->N), static_cast<int>(desc->K), hist,
+                                   moments, ws, s),
+            "routing statistics launch");
+  return ZC_OK;
+}
+
+zc_status zc_moe_accumulate_counts(int64_t E, const int32_t* counts, int32_t* acc, void* stream) {
+  if (E < 1 || E > 1024) return fail(ZC_ERR_INVALID, "E=%lld outside 1..1024", (long long)E);
+  ZC_CHECK(check_ptr(counts, "counts"));
+  ZC_CHECK(check_ptr(acc, "acc"));
+  if (counts == acc) return fail(ZC_ERR_INVALID, "counts and acc are the same buffer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ZC_LAUNCH(ZC_PH_ACCUMULATE, zc::launch_accumulate_counts(counts, static_cast<int>(E), acc, s),
+            "count accumulation launch");
+  return ZC_OK;
+}
+
 zc_status zc_moe_pack_weights(const zc_moe_desc* desc, int which, const void* src, void* dst,
                               void* stream) {
   ZC_CHECK(check_desc(desc));
@@ -685,7 +717,7 @@ const char* zc_moe_phase_name(int phase) {
       "router_gemm", "topk", "dispatch", "gate_up_gemm", "down_gemm", "combine",
       "bwd_combine", "bwd_down_dh", "bwd_down_dw", "bwd_gate_up_dx", "bwd_gate_up_dw",
       "bwd_router_dw", "bwd_router_dx", "bwd_dx_gather", "bias_update", "tile_offsets",
-      "lb_loss", "lb_coef"};
+      "lb_loss", "lb_coef", "route_stats", "accumulate_counts"};
   return (phase >= 0 && phase < ZC_NUM_PHASES) ? names[phase] : "";
 }
 

@@ -163,7 +163,96 @@ __global__ __launch_bounds__(1024) void tile_off_kernel(const int32_t* __restric
   if (e == 0) tile_off[N] = N > 0 ? s_til[N - 1] : 0;
 }
 
+
+// Budget-control telemetry (section 2.1.1 of the report tracks the mean and
+// the standard deviation of the FFN experts each token activates, Fig.3b/c).
+// stats_partial_kernel: each block histograms n_t = (FFN picks of token t)
+// over its grid-stride share of the tokens (LDS integer atomics: the
+// counts do not depend on their order) into part[b][K+1].
+// stats_finish_kernel: hist[k] = sum over blocks; mean = sum_k k hist[k] / T
+// (an exact integer sum, one division); std = sqrt(sum_k hist[k] (k - mean)^2 / T).
+__global__ __launch_bounds__(kThreads) void stats_partial_kernel(
+    const int32_t* __restrict__ topk_idx, int Tn, int N, int K, int32_t* __restrict__ part) {
+  __shared__ int32_t s_h[33];
+  if (threadIdx.x <= K) s_h[threadIdx.x] = 0;
+  __syncthreads();
+  for (int t = blockIdx.x * kThreads + threadIdx.x; t < Tn; t += gridDim.x * kThreads) {
+    const int32_t* row = topk_idx + static_cast<int64_t>(t) * K;
+    int c = 0;
+    for (int r = 0; r < K; ++r) c += row[r] < N ? 1 : 0;
+    atomicAdd(&s_h[c], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x <= K) part[blockIdx.x * (K + 1) + threadIdx.x] = s_h[threadIdx.x];
+}
+
+__global__ __launch_bounds__(64) void stats_finish_kernel(const int32_t* __restrict__ part,
+                                                          int nblk, int Tn, int K,
+                                                          int32_t* __restrict__ hist,
+                                                          double* __restrict__ moments) {
+  __shared__ int32_t s_h[33];
+  const int k = threadIdx.x;
+  if (k <= K) {
+    int32_t h = 0;
+    for (int b = 0; b < nblk; ++b) h += part[b * (K + 1) + k];
+    s_h[k] = h;
+    hist[k] = h;
+  }
+  __syncthreads();
+  if (k == 0) {
+    double mean = 0.0, var = 0.0;
+    if (Tn > 0) {
+      int64_t sum = 0;
+      for (int j = 0; j <= K; ++j) sum += static_cast<int64_t>(j) * s_h[j];
+      mean = static_cast<double>(sum) / static_cast<double>(Tn);
+      for (int j = 0; j <= K; ++j) {
+        const double dv = static_cast<double>(j) - mean;
+        var += static_cast<double>(s_h[j]) * (dv * dv);
+      }
+      var /= static_cast<double>(Tn);
+    }
+    moments[0] = mean;
+    moments[1] = sqrt(var);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void accumulate_kernel(const int32_t* __restrict__ counts,
+                                                              int E, int32_t* __restrict__ acc) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < E) acc[i] += counts[i];
+}
+
 }  // namespace
+
+int stats_blocks(int64_t Tn) {
+  const int64_t b = (Tn + kThreads - 1) / kThreads;
+  return static_cast<int>(b < 1 ? 1 : (b > 256 ? 256 : b));
+}
+
+size_t stats_scratch_bytes(int64_t Tn, int64_t K) {
+  return static_cast<size_t>(stats_blocks(Tn)) * static_cast<size_t>(K + 1) * sizeof(int32_t);
+}
+
+hipError_t launch_route_stats(const int32_t* topk_idx, int Tn, int N, int K, int32_t* hist,
+                              double* moments, void* scratch, hipStream_t s) {
+  const int nblk = Tn > 0 ? stats_blocks(Tn) : 0;
+  int32_t* part = static_cast<int32_t*>(scratch);
+  if (nblk > 0) {
+    hipLaunchKernelGGL(stats_partial_kernel, dim3(nblk), dim3(kThreads), 0, s, topk_idx, Tn, N, K,
+                       part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(stats_finish_kernel, dim3(1), dim3(64), 0, s, part, nblk, Tn, K, hist,
+                     moments);
+  return hipGetLastError();
+}
+
+hipError_t launch_accumulate_counts(const int32_t* counts, int E, int32_t* acc, hipStream_t s) {
+  hipLaunchKernelGGL(accumulate_kernel, dim3((E + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
+                     counts, E, acc);
+  return hipGetLastError();
+}
 
 hipError_t launch_tile_offsets(const int32_t* offsets, int N, int bm, int32_t* tile_off,
                                hipStream_t s) {

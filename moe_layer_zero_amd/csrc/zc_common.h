@@ -88,6 +88,14 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int Tn, int E, int N, int K,
                            int32_t* sched, void* scratch, hipStream_t s);
 constexpr int kSchedInts = 16;  // 8 XCD counters for gate/up, 8 for down
 
+// FFN picks per token (budget-control telemetry): hist[K+1] and moments
+// [mean, population std], from topk_idx.  Scratch: stats_scratch_bytes(T, K).
+size_t stats_scratch_bytes(int64_t Tn, int64_t K);
+hipError_t launch_route_stats(const int32_t* topk_idx, int Tn, int N, int K, int32_t* hist,
+                              double* moments, void* scratch, hipStream_t s);
+// acc[i] += counts[i] for i < E (int32).
+hipError_t launch_accumulate_counts(const int32_t* counts, int E, int32_t* acc, hipStream_t s);
+
 // tile_off[N+1] from offsets[N+1] (for a backward call that only has the
 // routing of its forward call).
 hipError_t launch_tile_offsets(const int32_t* offsets, int N, int bm, int32_t* tile_off,

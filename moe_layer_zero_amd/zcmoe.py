@@ -19,17 +19,18 @@ LIB_PATH = os.path.join(HERE, "libzcmoe.so")
 
 ZC_OK, ZC_ERR_INVALID, ZC_ERR_UNSUPPORTED, ZC_ERR_WORKSPACE, ZC_ERR_HIP = range(5)
 ZC_F32, ZC_BF16 = 0, 1
-ZC_OP_ROUTE, ZC_OP_FORWARD, ZC_OP_BACKWARD, ZC_OP_LB_LOSS = 0, 1, 2, 3
+ZC_OP_ROUTE, ZC_OP_FORWARD, ZC_OP_BACKWARD, ZC_OP_LB_LOSS, ZC_OP_ROUTE_STATS = 0, 1, 2, 3, 4
 ZC_WEIGHTS_ROWMAJOR, ZC_WEIGHTS_PACKED = 0, 1
 ZC_PACK_GATE_UP, ZC_PACK_DOWN = 0, 1
 
 # Every symbol include/zc_moe.h declares.
 EXPORTS = ("zc_moe_workspace_size", "zc_moe_saved_size", "zc_moe_route", "zc_moe_forward",
-           "zc_moe_backward", "zc_moe_lb_loss", "zc_moe_pid_update", "zc_moe_pack_weights",
+           "zc_moe_backward", "zc_moe_lb_loss", "zc_moe_route_stats", "zc_moe_accumulate_counts",
+           "zc_moe_pid_update", "zc_moe_pack_weights",
            "zc_moe_profile",
            "zc_moe_profile_read",
            "zc_moe_phase_name", "zc_status_string", "zc_last_error")
-ZC_NUM_PHASES = 18
+ZC_NUM_PHASES = 20
 
 
 class ZcError(RuntimeError):
@@ -77,10 +78,13 @@ def lib() -> C.CDLL:
         LB = C.POINTER(zc_lb_cfg)
         L.zc_moe_backward.argtypes = [P, v, v, v, v, v, D, v, v, v, v, v, v, v, LB, v, sz, v]
         L.zc_moe_lb_loss.argtypes = [P, LB, D, v, v, sz, v]
+        L.zc_moe_route_stats.argtypes = [P, D, v, v, v, sz, v]
+        L.zc_moe_accumulate_counts.argtypes = [i64, v, v, v]
         L.zc_moe_pid_update.argtypes = [i64, i64, i64, v, i64, C.c_double, C.c_double, v, v]
         L.zc_moe_pack_weights.argtypes = [P, C.c_int, v, v, v]
         for f in ("zc_moe_route", "zc_moe_forward", "zc_moe_backward", "zc_moe_lb_loss",
-                  "zc_moe_pid_update", "zc_moe_pack_weights"):
+                  "zc_moe_route_stats", "zc_moe_accumulate_counts", "zc_moe_pid_update",
+                  "zc_moe_pack_weights"):
             getattr(L, f).restype = C.c_int
         L.zc_moe_profile.argtypes = [C.c_int]
         L.zc_moe_profile.restype = C.c_int
@@ -266,6 +270,35 @@ def zc_moe_lb_loss(desc: LayerDesc, lb: LoadBalance, route: RouteBuffers, out=No
     _check(lib().zc_moe_lb_loss(C.byref(d), C.byref(c), C.byref(r), _ptr(out), _ptr(ws),
                                 ws.numel(), _stream(stream)), "zc_moe_lb_loss")
     return out
+
+
+def zc_moe_route_stats(desc: LayerDesc, route: RouteBuffers, hist=None, moments=None, ws=None,
+                       stream=None):
+    """Queues the FFN-experts-per-token statistics of a routed batch; returns
+    (hist [K+1] int32, moments [2] float64 = mean, std), both on the GPU."""
+    dev = route.counts.device
+    if hist is None:
+        hist = torch.empty(desc.K + 1, dtype=torch.int32, device=dev)
+    if moments is None:
+        moments = torch.empty(2, dtype=torch.float64, device=dev)
+    _check_layer_tensor(hist, (desc.K + 1,), torch.int32, "hist")
+    _check_layer_tensor(moments, (2,), torch.float64, "moments")
+    if ws is None:
+        ws = workspace(desc, ZC_OP_ROUTE_STATS, dev)
+    d, r = desc.c(), route.c()
+    _check(lib().zc_moe_route_stats(C.byref(d), C.byref(r), _ptr(hist), _ptr(moments), _ptr(ws),
+                                    ws.numel(), _stream(stream)), "zc_moe_route_stats")
+    return hist, moments
+
+
+def zc_moe_accumulate_counts(counts, acc, stream=None):
+    """acc += counts (int32 [E] GPU tensors): per-expert token counts over
+    several micro-batches, for one Eq.(2) update with T_all = their tokens."""
+    E = counts.numel()
+    _check_layer_tensor(counts, (E,), torch.int32, "counts")
+    _check_layer_tensor(acc, (E,), torch.int32, "acc")
+    _check(lib().zc_moe_accumulate_counts(E, _ptr(counts), _ptr(acc), _stream(stream)),
+           "zc_moe_accumulate_counts")
 
 
 def zc_moe_pid_update(N: int, Z: int, K: int, counts, T_all: int, mu: float, K_e: float, bias,

@@ -48,6 +48,9 @@ def test_sizes_are_positive_and_grow_with_T():
         for op in (zcmoe.ZC_OP_ROUTE, zcmoe.ZC_OP_FORWARD, zcmoe.ZC_OP_BACKWARD,
                    zcmoe.ZC_OP_LB_LOSS):
             assert 0 < zcmoe.zc_moe_workspace_size(a, op) < zcmoe.zc_moe_workspace_size(b, op)
+        # the statistics' scratch is one small histogram per block of 256 tokens
+        op = zcmoe.ZC_OP_ROUTE_STATS
+        assert 0 < zcmoe.zc_moe_workspace_size(a, op) <= zcmoe.zc_moe_workspace_size(b, op)
         assert 0 < zcmoe.zc_moe_saved_size(a) < zcmoe.zc_moe_saved_size(b)
     # an invalid description sizes to 0
     assert zcmoe.zc_moe_workspace_size(desc(K=0), zcmoe.ZC_OP_FORWARD) == 0
@@ -203,3 +206,20 @@ def test_lb_loss_accepts_k_e_equal_k_without_zero_experts(L):
     assert st == zcmoe.ZC_ERR_WORKSPACE
     st = L.zc_moe_lb_loss(C.byref(d), C.byref(c), C.byref(r), None, FAKE, 1 << 40, None)
     assert st == zcmoe.ZC_ERR_INVALID and "out" in L.zc_last_error().decode()
+
+
+def test_route_stats_and_accumulate_argument_checks(L):
+    d = desc().c()
+    r = route_buf()
+    big = 1 << 40
+    assert L.zc_moe_route_stats(C.byref(d), None, FAKE, FAKE, FAKE, big, None) == \
+        zcmoe.ZC_ERR_INVALID
+    assert L.zc_moe_route_stats(C.byref(d), C.byref(r), None, FAKE, FAKE, big, None) == \
+        zcmoe.ZC_ERR_INVALID
+    assert L.zc_moe_route_stats(C.byref(d), C.byref(r), FAKE, FAKE, FAKE, 4, None) == \
+        zcmoe.ZC_ERR_WORKSPACE
+    other = C.c_void_p(1 << 40)
+    assert L.zc_moe_accumulate_counts(0, FAKE, other, None) == zcmoe.ZC_ERR_INVALID
+    assert L.zc_moe_accumulate_counts(1025, FAKE, other, None) == zcmoe.ZC_ERR_INVALID
+    assert L.zc_moe_accumulate_counts(12, FAKE, FAKE, None) == zcmoe.ZC_ERR_INVALID
+    assert L.zc_moe_accumulate_counts(12, None, other, None) == zcmoe.ZC_ERR_INVALID
