@@ -41,11 +41,20 @@ def lib():
                                    _p]
         L.orc_lb_loss.argtypes = [_i64, _i64, _i64, _i64, _i64, _f64, _f64, _p, _p, _p, _p]
         L.orc_route_stats.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p]
+        L.orc_e4m3_value.restype = C.c_double
+        L.orc_e4m3_value.argtypes = [_i32]
+        L.orc_e4m3_encode.restype = C.c_int
+        L.orc_e4m3_encode.argtypes = [C.c_double]
+        L.orc_mx_quantize.argtypes = [_i64, _i64, _i32, _p, _p, _p]
+        L.orc_mx_dequantize.argtypes = [_i64, _i64, _p, _p, _p]
+        L.orc_forward_mx.argtypes = [_i64, _i64, _i64, _i64, _i64, _i32, _f64, _p, _p, _p, _p,
+                                     _p, _p, _i64, _p, _p, _p]
         L.orc_num_threads.restype = C.c_int
         L.orc_num_threads.argtypes = []
         L.orc_pid_update.argtypes = [_i64, _i64, _i64, _p, _i64, _f64, _f64, _p]
         for f in ("orc_logits", "orc_route", "orc_forward", "orc_backward", "orc_pid_update",
-                  "orc_lb_loss", "orc_route_stats"):
+                  "orc_lb_loss", "orc_route_stats", "orc_mx_quantize", "orc_mx_dequantize",
+                  "orc_forward_mx"):
             getattr(L, f).restype = C.c_int
         _LIB = L
     return _LIB
@@ -238,3 +247,70 @@ def route_stats(topk_idx, N):
     rc = lib().orc_route_stats(T, N, K, _ptr(ti), _ptr(hist), C.byref(m), C.byref(s))
     assert rc == 0, f"oracle route_stats failed rc={rc}"
     return hist, m.value, s.value
+
+
+def e4m3_value(code: int) -> float:
+    """O12: value of an OCP FP8 E4M3 code."""
+    return lib().orc_e4m3_value(int(code))
+
+
+def e4m3_encode(v: float) -> int:
+    """O12: nearest E4M3 code (ties to even, saturating at 448)."""
+    return int(lib().orc_e4m3_encode(float(v)))
+
+
+def mx_quantize(a: np.ndarray):
+    """O12: MXFP8 (E4M3 codes, E8M0 scale per 32 along the last axis) of a 2-D
+    fp32 / bf16-bits / float64 array.  Returns (codes uint8, scales uint8)."""
+    if a.dtype == np.float64:
+        dt = 2
+    else:
+        dt = _dt(a)
+    a = _c(a)
+    rows, cols = a.shape
+    codes = np.empty((rows, cols), np.uint8)
+    scales = np.empty((rows, cols // 32), np.uint8)
+    rc = lib().orc_mx_quantize(rows, cols, dt, _ptr(a), _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError("oracle mx_quantize rejected its arguments")
+    return codes, scales
+
+
+def mx_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    codes, scales = _c(codes, np.uint8), _c(scales, np.uint8)
+    rows, cols = codes.shape
+    out = np.empty((rows, cols), np.float64)
+    rc = lib().orc_mx_dequantize(rows, cols, _ptr(codes), _ptr(scales), _ptr(out))
+    assert rc == 0
+    return out
+
+
+def mx_weights(w: np.ndarray) -> np.ndarray:
+    """Dequantized binary64 MXFP8 image of one expert weight [R][C] (blocks
+    of 32 along C, the reduction dimension)."""
+    return mx_dequantize(*mx_quantize(w))
+
+
+def forward_mx(x, wgq, wuq, wdq, topk_idx, gates, N, out_scale=1.0, toks=None, want_y=False):
+    """O13: the layer forward with MXFP8 expert operands.  wgq / wuq / wdq:
+    {expert: dequantized binary64 weight} (mx_weights) for every FFN expert
+    the listed tokens pick."""
+    x = _c(x)
+    T, d = x.shape
+    K = topk_idx.shape[1]
+    e0 = next(iter(wgq.values()))
+    I = e0.shape[0]
+    tg, kg = _table({e: _c(v, np.float64) for e, v in wgq.items()}, N)
+    tu, ku = _table({e: _c(v, np.float64) for e, v in wuq.items()}, N)
+    td, kd = _table({e: _c(v, np.float64) for e, v in wdq.items()}, N)
+    ti = _c(topk_idx, np.int32)
+    gg = _c(gates, np.float64)
+    tk = None if toks is None else _c(np.asarray(toks), np.int64)
+    n = T if tk is None else len(tk)
+    out = np.empty((n, d), np.float64)
+    y = np.empty((n * K, d), np.float64) if want_y else None
+    rc = lib().orc_forward_mx(T, d, N, I, K, _dt(x), float(out_scale), _ptr(x), tg, tu, td,
+                              _ptr(ti), _ptr(gg), n, _ptr(tk), _ptr(out), _ptr(y))
+    assert rc == 0, f"oracle forward_mx failed rc={rc}"
+    del kg, ku, kd
+    return (out, y) if want_y else out

@@ -610,3 +610,172 @@ int orc_route_stats(int64_t T, int64_t N, int64_t K, const int32_t* topk_idx,
   free(n);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* O12 -- FP8 blockwise quantization of expert operands (the deployment path
+ * of the LongCat pages quantizes blockwise to FP8 and keeps sensitive parts
+ * in higher precision).  Block format: the OCP Microscaling (MX) format
+ * MXFP8-E4M3, i.e. 32 consecutive values along the reduction dimension
+ * share one power-of-two scale X = 2^(S-127) stored as an 8-bit exponent S
+ * (E8M0), and each value is stored as an FP8 E4M3 code of v / X.
+ *
+ * E4M3 (OCP): sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent
+ * field 0 holds subnormals m/8 * 2^-6; the largest finite magnitude is 448
+ * (field 1111, mantissa 110); 1111/111 is NaN; no infinities.
+ *
+ * Scale of a block: amax = max |v_i|; if amax = 0, S = 0; otherwise
+ * S = floor(log2 amax) - 8 + 127 (8 = exponent of the largest E4M3 power of
+ * two), clamped to 0..254.  Codes: v_i / X rounded to the nearest E4M3
+ * value, ties to the even mantissa code, magnitudes above 448 saturated to
+ * 448.  Dequantized value: decode(code) * X. */
+double orc_e4m3_value(int code) {
+  code &= 0xff;
+  const double s = (code & 0x80) ? -1.0 : 1.0;
+  const int e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) return s * ldexp((double)m, -9);          /* m/8 * 2^-6 */
+  return s * ldexp((double)(8 + m), e - 10);             /* (1 + m/8) 2^(e-7) */
+}
+
+/* Nearest E4M3 code of a finite v (exact binary64 arithmetic: v times a
+ * power of two is exact, rint rounds ties to even). */
+int orc_e4m3_encode(double v) {
+  const int neg = signbit(v) ? 0x80 : 0;
+  double a = fabs(v);
+  if (a >= 448.0) return neg | 0x7e;
+  int ex;
+  frexp(a, &ex);                      /* a = f 2^ex, f in [0.5, 1) */
+  int E = ex - 1;                     /* floor(log2 a) for a > 0 */
+  if (a == 0.0 || E < -6) E = -6;     /* subnormal quantum 2^-9 */
+  double q = rint(ldexp(a, 3 - E));   /* units of 2^(E-3) */
+  if (q == 16.0) {                    /* rounded up into the next binade */
+    q = 8.0;
+    E += 1;
+  }
+  if (E > 8 || (E == 8 && q > 14.0)) return neg | 0x7e;
+  if (q < 8.0) return neg | (int)q;   /* subnormal (E = -6) or zero */
+  return neg | ((E + 7) << 3) | ((int)q - 8);
+}
+
+/* Quantize rows x cols values (dt: ORC_F32 / ORC_BF16 storage, or 2 for
+ * binary64) in blocks of 32 along each row: codes [rows][cols], scales
+ * [rows][cols/32] (E8M0, plain block order).  cols % 32 == 0. */
+int orc_mx_quantize(int64_t rows, int64_t cols, int dt, const void* src, uint8_t* codes,
+                    uint8_t* scales) {
+  if (rows < 0 || cols <= 0 || cols % 32 || !src || !codes || !scales) return 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < cols / 32; ++b) {
+      double v[32], amax = 0.0;
+      for (int i = 0; i < 32; ++i) {
+        const int64_t o = r * cols + b * 32 + i;
+        v[i] = dt == 2 ? ((const double*)src)[o] : ld(src, dt, o);
+        if (fabs(v[i]) > amax) amax = fabs(v[i]);
+      }
+      int S = 0;
+      if (amax > 0.0) {
+        int ex;
+        frexp(amax, &ex);
+        S = (ex - 1) - 8 + 127;
+        if (S < 0) S = 0;
+        if (S > 254) S = 254;
+      }
+      scales[r * (cols / 32) + b] = (uint8_t)S;
+      for (int i = 0; i < 32; ++i)
+        codes[r * cols + b * 32 + i] = (uint8_t)orc_e4m3_encode(ldexp(v[i], 127 - S));
+    }
+  }
+  return 0;
+}
+
+/* Dequantized values decode(code) * 2^(S-127), binary64. */
+int orc_mx_dequantize(int64_t rows, int64_t cols, const uint8_t* codes, const uint8_t* scales,
+                      double* out) {
+  if (rows < 0 || cols <= 0 || cols % 32 || !codes || !scales || !out) return 1;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c)
+      out[r * cols + c] = ldexp(orc_e4m3_value(codes[r * cols + c]),
+                                (int)scales[r * (cols / 32) + c / 32] - 127);
+  return 0;
+}
+
+/* O13 -- the layer forward with MXFP8 expert operands (O12):
+ *   x'  = MX(x_t) along d (per token);  W' = MX(W) along each weight's
+ *         reduction dimension (given here already dequantized, binary64);
+ *   a = W'_g x',  u = W'_u x',  h = silu(a) * u, rounded to fp32 (the
+ *         precision in which the GPU takes the quantization decision);
+ *   h' = MX(h) along I;  y = W'_d h';
+ *   out_t = out_scale * ( c_t x_t + sum over FFN picks of g_r y_r ), with
+ *         the zero-computation term on the unquantized x_t.
+ * Weight tables as in orc_forward, binary64 [I][d] / [d][I] per expert.
+ * y_out (nullable) receives y per listed (token, slot) [n_tok*K][d] (0 for
+ * identity picks). */
+int orc_forward_mx(int64_t T, int64_t d, int64_t N, int64_t I, int64_t K, int dt,
+                   double out_scale, const void* x, const double* const* wg,
+                   const double* const* wu, const double* const* wd, const int32_t* topk_idx,
+                   const double* gates, int64_t n_tok, const int64_t* toks, double* out,
+                   double* y_out) {
+  if (T < 0 || d <= 0 || d % 32 || I <= 0 || I % 32 || K < 1 || !x || !wg || !wu || !wd ||
+      !topk_idx || !gates || !out)
+    return 1;
+  if (!toks) n_tok = T;
+  int bad = 0;
+#pragma omp parallel
+  {
+    double* xq = (double*)malloc(sizeof(double) * (size_t)d);
+    uint8_t* qc = (uint8_t*)malloc((size_t)(d > I ? d : I));
+    uint8_t* qs = (uint8_t*)malloc((size_t)(d > I ? d : I) / 32);
+    double* h = (double*)malloc(sizeof(double) * (size_t)I);
+    double* hq = (double*)malloc(sizeof(double) * (size_t)I);
+    double* y = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t q = 0; q < n_tok; ++q) {
+      const int64_t t = toks ? toks[q] : q;
+      if (t < 0 || t >= T) {
+#pragma omp atomic write
+        bad = 1;
+        continue;
+      }
+      if (dt == ORC_BF16) {
+        orc_mx_quantize(1, d, ORC_BF16, (const uint16_t*)x + t * d, qc, qs);
+      } else {
+        orc_mx_quantize(1, d, ORC_F32, (const float*)x + t * d, qc, qs);
+      }
+      orc_mx_dequantize(1, d, qc, qs, xq);
+      double* o = out + q * d;
+      double c = 0.0;
+      for (int64_t n = 0; n < d; ++n) o[n] = 0.0;
+      for (int64_t r = 0; r < K; ++r) {
+        const int64_t e = topk_idx[t * K + r];
+        const double g = gates[t * K + r];
+        double* yo = y_out ? y_out + (q * K + r) * d : NULL;
+        if (e >= N) {
+          c += g;
+          if (yo)
+            for (int64_t n = 0; n < d; ++n) yo[n] = 0.0;
+          continue;
+        }
+        for (int64_t i = 0; i < I; ++i) {
+          double a = 0.0, u = 0.0;
+          for (int64_t k = 0; k < d; ++k) {
+            a += wg[e][i * d + k] * xq[k];
+            u += wu[e][i * d + k] * xq[k];
+          }
+          h[i] = (double)(float)(silu(a) * u);
+        }
+        orc_mx_quantize(1, I, 2, h, qc, qs);
+        orc_mx_dequantize(1, I, qc, qs, hq);
+        for (int64_t n = 0; n < d; ++n) {
+          double acc = 0.0;
+          for (int64_t i = 0; i < I; ++i) acc += wd[e][n * I + i] * hq[i];
+          y[n] = acc;
+          if (yo) yo[n] = acc;
+        }
+        for (int64_t n = 0; n < d; ++n) o[n] += g * y[n];
+      }
+      for (int64_t n = 0; n < d; ++n) o[n] = out_scale * (c * ld(x, dt, t * d + n) + o[n]);
+    }
+    free(xq); free(qc); free(qs); free(h); free(hq); free(y);
+  }
+  return bad;
+}
