@@ -80,8 +80,14 @@ typedef struct {
  *  ZC_WEIGHTS_PACKED:   the output of zc_moe_pack_weights.  Accepted by
  *      zc_moe_forward for bf16 layers with d and I multiples of 256, when no
  *      activations are saved (saved == NULL): the inference forward.  The
- *      backward and the saving forward need row-major weights. */
-typedef enum { ZC_WEIGHTS_ROWMAJOR = 0, ZC_WEIGHTS_PACKED = 1 } zc_weight_layout;
+ *      backward and the saving forward need row-major weights.
+ *  ZC_WEIGHTS_MXFP8:    the output of zc_moe_quantize_weights: FP8
+ *      blockwise-quantized expert weights (see there).  Accepted by
+ *      zc_moe_forward for bf16 layers with d and I multiples of 512 and no
+ *      saved buffer: the FP8 inference forward. */
+typedef enum {
+  ZC_WEIGHTS_ROWMAJOR = 0, ZC_WEIGHTS_PACKED = 1, ZC_WEIGHTS_MXFP8 = 2
+} zc_weight_layout;
 
 /* Routing state: written by zc_moe_route / zc_moe_forward, read by
  * zc_moe_backward.  All device buffers owned by the caller. */
@@ -250,6 +256,30 @@ enum { ZC_PACK_GATE_UP = 0, ZC_PACK_DOWN = 1 };
 zc_status zc_moe_pack_weights(const zc_moe_desc* desc, int which, const void* src, void* dst,
                               void* stream);
 
+/* FP8 blockwise quantization of one set of FFN expert weights (bf16) for
+ * the FP8 inference forward (the LongCat deployment runs its expert GEMMs
+ * blockwise in FP8, keeping sensitive parts in higher precision).  Format:
+ * OCP Microscaling MXFP8 -- each run of 32 consecutive values along a
+ * weight row's reduction dimension shares one power-of-two scale
+ * 2^(S-127), S an 8-bit exponent (E8M0), and each value is stored as an
+ * FP8 E4M3 code of value / 2^(S-127):
+ *   S = floor(log2 max|v|) - 8 + 127 (at least 0; 0 for an all-zero run);
+ *   code = nearest E4M3 value, ties to even, magnitudes above 448 clamped.
+ * A forward with desc->weight_layout = ZC_WEIGHTS_MXFP8 quantizes x the
+ * same way per token (runs of 32 along d) and h per pick (runs of 32 along
+ * I, from h rounded to fp32), multiplies on the scaled FP8 matrix cores with
+ * fp32 accumulation, and keeps the router, gates, combine and the
+ * zero-computation experts (which return the unquantized x) in bf16/fp32.
+ *   which = ZC_PACK_GATE_UP: src is w_gate or w_up, [N][I][d];
+ *   which = ZC_PACK_DOWN:    src is w_down, [N][d][I].
+ * dst (zc_moe_quantized_weight_bytes(desc) bytes, not overlapping src)
+ * receives the codes of all N experts in the matrix cores' operand order,
+ * then their scales; its layout is private to this library.  Needs dtype
+ * bf16 and d, I multiples of 512 (desc->weight_layout is ignored). */
+size_t zc_moe_quantized_weight_bytes(const zc_moe_desc* desc);
+zc_status zc_moe_quantize_weights(const zc_moe_desc* desc, int which,
+                                  const void* src, void* dst, void* stream);
+
 /* Kernel timing for benchmarks.  While profiling is on, every entry point
  * brackets each of its kernel launches with a pair of HIP events recorded on
  * the call's own stream, tagged with one of the phases below.  The events
@@ -263,7 +293,7 @@ enum {
   ZC_PH_BWD_COMBINE, ZC_PH_BWD_DOWN_DH, ZC_PH_BWD_DOWN_DW, ZC_PH_BWD_GATE_UP_DX,
   ZC_PH_BWD_GATE_UP_DW, ZC_PH_BWD_ROUTER_DW, ZC_PH_BWD_ROUTER_DX, ZC_PH_BWD_DX_GATHER,
   ZC_PH_BIAS_UPDATE, ZC_PH_TILE_OFFSETS, ZC_PH_LB_LOSS, ZC_PH_LB_COEF, ZC_PH_ROUTE_STATS,
-  ZC_PH_ACCUMULATE, ZC_NUM_PHASES
+  ZC_PH_ACCUMULATE, ZC_PH_QUANTIZE, ZC_NUM_PHASES
 };
 zc_status zc_moe_profile(int on);
 zc_status zc_moe_profile_read(double* total_ms, int32_t* count);

@@ -133,6 +133,18 @@ zc_status check_packable(const zc_moe_desc* d) {
   return ZC_OK;
 }
 
+// Shapes the MXFP8 forward handles: bf16 layer, d and I multiples of 512
+// (whole groups of four 128-step slabs), 32-bit byte offsets into x' and h'.
+zc_status check_mxfp8(const zc_moe_desc* d) {
+  if (d->dtype != ZC_BF16) return fail(ZC_ERR_UNSUPPORTED, "MXFP8 weights need a bf16 layer");
+  if (d->d % 512 || d->I % 512)
+    return fail(ZC_ERR_UNSUPPORTED, "MXFP8 weights need d and I multiples of 512 (d=%lld I=%lld)",
+                (long long)d->d, (long long)d->I);
+  if (d->T * d->d >= (int64_t(1) << 31) || d->T * d->K * d->I >= (int64_t(1) << 31))
+    return fail(ZC_ERR_UNSUPPORTED, "MXFP8 forward needs T*d and T*K*I below 2^31");
+  return ZC_OK;
+}
+
 zc_status check_desc(const zc_moe_desc* d) {
   if (!d) return fail(ZC_ERR_INVALID, "desc is NULL");
   const int64_t E = d->N + d->Z;
@@ -147,8 +159,10 @@ zc_status check_desc(const zc_moe_desc* d) {
   if (d->gate_norm != 0 && d->gate_norm != 1)
     return fail(ZC_ERR_INVALID, "gate_norm %d is neither 0 nor 1", d->gate_norm);
   if (!std::isfinite(d->out_scale)) return fail(ZC_ERR_INVALID, "out_scale is not finite");
-  if (d->weight_layout != ZC_WEIGHTS_ROWMAJOR && d->weight_layout != ZC_WEIGHTS_PACKED)
-    return fail(ZC_ERR_INVALID, "weight_layout %d is neither ROWMAJOR nor PACKED", d->weight_layout);
+  if (d->weight_layout != ZC_WEIGHTS_ROWMAJOR && d->weight_layout != ZC_WEIGHTS_PACKED &&
+      d->weight_layout != ZC_WEIGHTS_MXFP8)
+    return fail(ZC_ERR_INVALID, "weight_layout %d is not ROWMAJOR, PACKED or MXFP8",
+                d->weight_layout);
   if (d->T * d->K >= (int64_t(1) << 31) || d->d >= (int64_t(1) << 24) || d->I >= (int64_t(1) << 24))
     return fail(ZC_ERR_UNSUPPORTED, "T*K, d or I too large for 32-bit indexing");
   const int64_t mult = d->dtype == ZC_BF16 ? 64 : 32;
@@ -157,6 +171,7 @@ zc_status check_desc(const zc_moe_desc* d) {
                 d->dtype == ZC_BF16 ? "bf16" : "fp32", (long long)mult, (long long)d->d,
                 (long long)d->I);
   if (d->weight_layout == ZC_WEIGHTS_PACKED) ZC_CHECK(check_packable(d));
+  if (d->weight_layout == ZC_WEIGHTS_MXFP8) ZC_CHECK(check_mxfp8(d));
   return ZC_OK;
 }
 
@@ -237,9 +252,13 @@ Saved carve_saved(char* p, const zc_moe_desc* d) {
 
 // Forward scratch: routing scratch, h in the layer dtype (operand of the
 // down GEMM) and y when no saved buffer takes it.
+// MXFP8 layers add x' (codes T*d, scales T*d/32); h' (codes and scales)
+// fits in the h piece.
 int64_t fwd_ws_bytes(const zc_moe_desc* d) {
   const int64_t rows = d->T * d->K, es = esize(d);
-  return route_ws_bytes(d) + a256(rows * d->I * es) + a256(rows * d->d * es);
+  int64_t b = route_ws_bytes(d) + a256(rows * d->I * es) + a256(rows * d->d * es);
+  if (d->weight_layout == ZC_WEIGHTS_MXFP8) b += a256(d->T * d->d) + a256(d->T * d->d / 32);
+  return b;
 }
 
 struct BwdWs {
@@ -329,8 +348,12 @@ bool use_fwd_kernels(const zc_moe_desc* d, const void* saved) {
 // forward picks it from the average rows per FFN expert; the row-major bf16
 // forward kernels use 256.
 int fwd_rows_per_tile(const zc_moe_desc* d) {
-  if (d->weight_layout != ZC_WEIGHTS_PACKED || d->N == 0) return zc::kFwdBM;
-  return zc::fwdp_rows_per_tile(d->T * d->K / d->N);
+  if (d->weight_layout == ZC_WEIGHTS_ROWMAJOR || d->N == 0) return zc::kFwdBM;
+  const int tm = zc::fwdp_rows_per_tile(d->T * d->K / d->N);
+  // the MXFP8 kernels stop at 128-row tiles: their 256-row variants exceed
+  // the register file, and spill traffic in flight breaks the per-slab
+  // load counts their waits rely on
+  return d->weight_layout == ZC_WEIGHTS_MXFP8 && tm > 128 ? 128 : tm;
 }
 
 template <typename T>
@@ -374,7 +397,29 @@ zc_status do_forward(const zc_moe_desc* d, const T* x, const T* wr, const float*
   }
   if (N > 0 && Tn > 0) {
     const int cu = cu_count();
-    if (d->weight_layout == ZC_WEIGHTS_PACKED) {
+    if (d->weight_layout == ZC_WEIGHTS_MXFP8) {
+      // MXFP8 inference: x quantized once, h quantized in the gate/up
+      // epilogue (validated: bf16, no saved buffer)
+      uint8_t* xq = reinterpret_cast<uint8_t*>(ws + fwd_ws_bytes(d) - a256(d->T * d->d) -
+                                               a256(d->T * d->d / 32));
+      uint8_t* xs = xq + a256(d->T * d->d);
+      uint8_t* hq = reinterpret_cast<uint8_t*>(h);
+      uint8_t* hs = hq + a256(rows * d->I);
+      ZC_LAUNCH(ZC_PH_QUANTIZE,
+                zc::launch_mxq_rows(reinterpret_cast<const bf16_t*>(x), d->T, dd, xq, xs, s),
+                "activation quantization launch");
+      ZC_LAUNCH(ZC_PH_GATE_UP,
+                zc::launch_fwdq_gateup(xq, xs, d->T, reinterpret_cast<const uint8_t*>(wg),
+                                       reinterpret_cast<const uint8_t*>(wu), r->offsets, r->perm,
+                                       rw.tile_off2, rw.tile_exp, rw.sched, fwd_rows_per_tile(d), N,
+                                       I, dd, K, hq, hs, cu, s),
+                "gate/up GEMM launch");
+      ZC_LAUNCH(ZC_PH_DOWN,
+                zc::launch_fwdq_down(hq, hs, rows, reinterpret_cast<const uint8_t*>(wd), r->offsets,
+                                     rw.tile_off2, rw.tile_exp, rw.sched + 8, fwd_rows_per_tile(d),
+                                     N, I, dd, reinterpret_cast<bf16_t*>(y), cu, s),
+                "down GEMM launch");
+    } else if (d->weight_layout == ZC_WEIGHTS_PACKED) {
       // bf16 inference on packed weights (validated: bf16, no saved buffer)
       const bf16_t* hx = reinterpret_cast<const bf16_t*>(x);
       bf16_t* hh = reinterpret_cast<bf16_t*>(h);
@@ -540,7 +585,7 @@ zc_status zc_moe_forward(const zc_moe_desc* desc, const void* x, const void* w_r
   ZC_CHECK(check_weights(desc, w_gate, w_up, w_down));
   ZC_CHECK(check_ptr(out, "out", none));
   ZC_CHECK(check_ptr(saved, "saved", true));
-  if (saved && desc->weight_layout == ZC_WEIGHTS_PACKED)
+  if (saved && desc->weight_layout != ZC_WEIGHTS_ROWMAJOR)
     return fail(ZC_ERR_UNSUPPORTED, "a forward that saves activations needs row-major weights");
   ZC_CHECK(check_ws(ws, ws_bytes, fwd_ws_bytes(desc)));
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -667,6 +712,36 @@ zc_status zc_moe_pack_weights(const zc_moe_desc* desc, int which, const void* sr
   return ZC_OK;
 }
 
+size_t zc_moe_quantized_weight_bytes(const zc_moe_desc* desc) {
+  if (check_desc(desc) != ZC_OK) return 0;
+  const int64_t n = desc->N * desc->I * desc->d;
+  return static_cast<size_t>(n + n / 32);
+}
+
+zc_status zc_moe_quantize_weights(const zc_moe_desc* desc, int which, const void* src, void* dst,
+                                  void* stream) {
+  ZC_CHECK(check_desc(desc));
+  ZC_CHECK(check_mxfp8(desc));
+  if (which != ZC_PACK_GATE_UP && which != ZC_PACK_DOWN)
+    return fail(ZC_ERR_INVALID, "which=%d is neither ZC_PACK_GATE_UP nor ZC_PACK_DOWN", which);
+  const bool opt = desc->N == 0;
+  ZC_CHECK(check_ptr(src, "src", opt));
+  ZC_CHECK(check_ptr(dst, "dst", opt));
+  const int64_t sbytes = desc->N * desc->I * desc->d * 2;
+  const int64_t dbytes = static_cast<int64_t>(zc_moe_quantized_weight_bytes(desc));
+  const char* a = static_cast<const char*>(src);
+  const char* b = static_cast<const char*>(dst);
+  if (sbytes > 0 && a < b + dbytes && b < a + sbytes)
+    return fail(ZC_ERR_INVALID, "src and dst overlap");
+  if (desc->N == 0) return ZC_OK;
+  const int R = static_cast<int>(which == ZC_PACK_GATE_UP ? desc->I : desc->d);
+  const int C = static_cast<int>(which == ZC_PACK_GATE_UP ? desc->d : desc->I);
+  hipError_t e = zc::launch_mxq_weights(static_cast<const bf16_t*>(src), static_cast<uint8_t*>(dst),
+                                        desc->N, R, C, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "weight quantization launch");
+  return ZC_OK;
+}
+
 zc_status zc_moe_pid_update(int64_t N, int64_t Z, int64_t K, const int32_t* counts, int64_t T_all,
                             double mu, double K_e, float* bias, void* stream) {
   if (N < 0 || Z < 0 || N + Z < 1 || N + Z > 1024)
@@ -717,7 +792,7 @@ const char* zc_moe_phase_name(int phase) {
       "router_gemm", "topk", "dispatch", "gate_up_gemm", "down_gemm", "combine",
       "bwd_combine", "bwd_down_dh", "bwd_down_dw", "bwd_gate_up_dx", "bwd_gate_up_dw",
       "bwd_router_dw", "bwd_router_dx", "bwd_dx_gather", "bias_update", "tile_offsets",
-      "lb_loss", "lb_coef", "route_stats", "accumulate_counts"};
+      "lb_loss", "lb_coef", "route_stats", "accumulate_counts", "quantize"};
   return (phase >= 0 && phase < ZC_NUM_PHASES) ? names[phase] : "";
 }
 

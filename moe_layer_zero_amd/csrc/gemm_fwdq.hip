@@ -1,0 +1,592 @@
+// Forward expert GEMMs with FP8 blockwise-quantized operands (MXFP8).
+//
+// The LongCat deployment quantizes the expert GEMMs blockwise to FP8 and
+// keeps sensitive parts in higher precision ("LongCat-Flash Technical
+// Report" series blog, deployment notes).  On gfx950 the matrix cores take
+// blockwise FP8 natively: v_mfma_scale_f32_32x32x64_f8f6f4 multiplies E4M3
+// operands and applies one power-of-two scale (E8M0) per 32 reduction
+// steps of every row and column, the OCP Microscaling format MXFP8.  So the
+// blocks here are 32 values along the reduction dimension with an E8M0
+// scale; weights are quantized once at load time, the gathered activations
+// x once per call, and h inside the gate/up epilogue.  The router, the
+// gates, the combine and the zero-computation experts (which return the
+// unquantized x) stay in bf16 / fp32.
+//
+// Quantization of a block of 32 values v (the same rule everywhere):
+//   S = biased exponent of max|v| minus 8, at least 0 (E8M0 of
+//       2^(floor(log2 max|v|) - 8), 0 for an all-zero block);
+//   code_i = E4M3 of v_i * 2^(127 - S), nearest with ties to even, after
+//            clamping to +-448 (the conversion instruction rounds to nearest
+//            even; without the clamp it returns NaN past 464).
+//
+// Matrix-core operand layout of one 32x32x64 step (measured on MI355X):
+// lane l feeds row (or column) l % 32; with h = l / 32, its bytes 0..15 are
+// reduction steps 16h .. 16h+15 and its bytes 16..31 are steps 32+16h ..
+// 32+16h+15; the scale operand of lane l is the E8M0 of its row and of the
+// 32-step block l / 32 of the step.
+//
+// Storage:
+//  - activations (x', h'): codes row-major [rows][K]; scales [rows][K/32]
+//    with each group of 4 blocks (one 128-step slab) stored in the order
+//    (0, 2, 1, 3), so that lane half h finds the scales of both 64-step
+//    MFMA steps of a slab in one 16-bit word at byte 2h of the group;
+//  - weights [R][C] (R output columns, C reduction steps): codes in 1 KB
+//    pieces [R/32][C/128][step 2][half 2][lane 64][16], lane l = column
+//    32g + l%32 with h = l/32, piece "half" holding bytes 16*half .. of the
+//    lane's 32-byte operand; then scales [R/32][C/128][lane 64] 16-bit words
+//    (block 4t + h, block 4t + 2 + h) of column 32g + l%32.  A quantized
+//    weight set is the N experts' codes followed by their scales.
+#include <type_traits>
+
+#include "zc_common.h"
+
+namespace zc {
+namespace {
+
+constexpr int BKQ = 128;      // reduction steps per slab (128 bytes per row)
+constexpr int NST = 4;        // LDS ring slots
+constexpr int NTHR = 256;
+constexpr int GMV = 8;        // row tiles per group inside an expert
+constexpr int SC_BYTES = 1024;  // per-slot activation-scale area (256 rows)
+
+enum { Q_SWIGLU = 0, Q_STORE = 1 };
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+struct QParams {
+  int N;                     // experts
+  int ncols;                 // output columns (I for gate/up, d for down)
+  int K;                     // reduction length (d for gate/up, I for down)
+  const int32_t* offsets;    // [N+1] rows of each expert in dispatch order
+  const int32_t* mt_off;     // [N+1] prefix of ceil(rows / TM)
+  const int32_t* tile_exp;   // [mt_off[N]] expert of each row tile
+  int32_t* sched;            // [8] per-XCD tile counters, zero at launch
+  const uint8_t* A;          // codes: x' [T][d] gathered through perm, or h' [P][I]
+  uint32_t a_bytes;
+  const uint8_t* As;         // activation scales [rows][K/32]
+  uint32_t as_bytes;
+  const int32_t* perm;       // gate/up only
+  int kdiv;                  // K of the layer (slot -> token)
+  const uint8_t* B;          // quantized W_g or W_d (codes, then scales)
+  const uint8_t* B2;         // quantized W_u (gate/up)
+  uint8_t* Cq;               // gate/up: h' codes [P][I]
+  uint8_t* Cs;               // gate/up: h' scales [P][I/32]
+  bf16_t* Cb;                // down: y [P][d]
+};
+
+__device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
+
+__device__ __forceinline__ bf16_t cvt_bf16(float f) {
+  uint32_t r;
+  asm volatile("v_cvt_pk_bf16_f32 %0, %1, 0" : "=v"(r) : "v"(f));
+  return static_cast<bf16_t>(r);
+}
+
+// E8M0 scale of a block whose largest magnitude is amax (finite, >= 0).
+__device__ __forceinline__ int mx_scale(float amax) {
+  const int be = static_cast<int>((__float_as_uint(amax) >> 23) & 0xff);
+  return be > 8 ? be - 8 : 0;
+}
+
+// E4M3 code of v at scale S.
+__device__ __forceinline__ uint32_t mx_code(float v, int S) {
+  float q = __builtin_ldexpf(v, 127 - S);
+  q = fminf(fmaxf(q, -448.f), 448.f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q, 0.f, 0, false)) & 0xffu;
+}
+
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff,
+                                          int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff,
+                                         int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, voff, soff, 0, 0);
+}
+
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// TM rows x 256 MFMA columns per workgroup (gate/up: 128 gate + 128 up
+// columns), wave w owning all TM rows and 64 columns, as in the bf16 kernel;
+// one slab = 128 reduction steps = two MFMA steps.
+template <int EPI, int TM>
+__global__ __launch_bounds__(NTHR, 1) void fwdq_kernel(QParams p) {
+  constexpr int RB = TM / 32;
+  constexpr int SLOT = TM * BKQ + SC_BYTES;  // bytes per ring slot: codes, then scales
+  constexpr int V = RB + 11;                 // loads per wave per slab
+  static_assert(TM == 32 || TM == 64 || TM == 128, "tile height");
+  __shared__ __align__(16) uint8_t ring[NST * SLOT + 16];
+  int32_t* const s_claim = reinterpret_cast<int32_t*>(ring + NST * SLOT);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  constexpr int OUTN = EPI == Q_SWIGLU ? 128 : 256;
+  const int NT = p.ncols / OUTN;
+  const int64_t total = static_cast<int64_t>(p.mt_off[p.N]) * NT;
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % 8;
+  const int C = G / 8;
+  int32_t* const claim = p.sched + xcd;
+  auto tile_of = [&](int n) -> int64_t {
+    return static_cast<int64_t>(n / C) * 8 * C + xcd * C + n % C;
+  };
+  if (tid == 0) s_claim[0] = atomicAdd(claim, 1);
+  __syncthreads();
+  int cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
+  const int nk = p.K / BKQ;
+  const int kb32 = p.K / 32;
+
+  const __amdgpu_buffer_rsrc_t arsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.A), (short)0, p.a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.As), (short)0, p.as_bytes, 0x00020000);
+
+  const int s7 = (lane >> 1) & 7;
+  const int khalf = lane >> 5;
+  const int frag_lane = (lane & 31) * BKQ;
+
+  for (int64_t L = tile_of(cur_n); L < total; L = tile_of(cur_n)) {
+    int32_t next_n = 0;
+    if (tid == 0) next_n = atomicAdd(claim, 1);
+    const int lmt = static_cast<int>(L / NT);
+    const int e = p.tile_exp[lmt];
+    const int mte = p.mt_off[e + 1] - p.mt_off[e];
+    const int q = static_cast<int>(L - static_cast<int64_t>(p.mt_off[e]) * NT);
+    const int grp = q / (GMV * NT);
+    const int fm = grp * GMV;
+    const int gsz = min(GMV, mte - fm);
+    const int rr = q - grp * GMV * NT;
+    const int mt = fm + rr % gsz;
+    const int nt = rr / gsz;
+    const int m0 = p.offsets[e] + mt * TM;
+    const int mcount = min(TM, p.offsets[e + 1] - m0);
+    const int n0 = nt * OUTN;
+
+    // ---- A code pieces (RB per wave per slab) and this wave's scale rows
+    uint32_t aoff[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int b = RB * wave + i;
+      const int row = 8 * b + (lane >> 3);
+      const int chunk = (lane & 7) ^ ((4 * b + (lane >> 4)) & 7);
+      if (row < mcount) {
+        const int gm = m0 + row;
+        const int src = EPI == Q_SWIGLU ? p.perm[gm] / p.kdiv : gm;
+        aoff[i] = static_cast<uint32_t>(src) * static_cast<uint32_t>(p.K) + chunk * 16;
+      } else {
+        aoff[i] = p.a_bytes;
+      }
+    }
+    uint32_t soff;
+    {
+      const int row = 64 * wave + lane;
+      if (row < mcount) {
+        const int gm = m0 + row;
+        const int src = EPI == Q_SWIGLU ? p.perm[gm] / p.kdiv : gm;
+        soff = static_cast<uint32_t>(src) * static_cast<uint32_t>(kb32);
+      } else {
+        soff = p.as_bytes;
+      }
+    }
+    // ---- quantized B: this wave's two column groups of 32
+    const int64_t mat = static_cast<int64_t>(p.ncols) * p.K;
+    const int gA = EPI == Q_SWIGLU ? n0 / 32 + wave : n0 / 32 + 2 * wave;
+    const int gB = EPI == Q_SWIGLU ? gA : gA + 1;
+    const uint8_t* Bsrc1 = EPI == Q_SWIGLU ? p.B2 : p.B;
+    const uint8_t* b0 = p.B + e * mat + static_cast<int64_t>(gA) * nk * 4096 + lane * 16;
+    const uint8_t* b1 = Bsrc1 + e * mat + static_cast<int64_t>(gB) * nk * 4096 + lane * 16;
+    const int64_t nexp = static_cast<int64_t>(p.N) * mat;  // scales follow all codes
+    const uint16_t* bs0 = reinterpret_cast<const uint16_t*>(p.B + nexp + e * (mat / 32)) +
+                          static_cast<int64_t>(gA) * nk * 64 + lane;
+    const uint16_t* bs1 = reinterpret_cast<const uint16_t*>(Bsrc1 + nexp + e * (mat / 32)) +
+                          static_cast<int64_t>(gB) * nk * 64 + lane;
+
+    const int nrb = (mcount + 31) >> 5;
+    auto run = [&](auto nrb_c) {
+      constexpr int NRB = decltype(nrb_c)::value;
+      i32x8_t bq[NST][2][2];   // B operands in flight: [slot][column group][step]
+      uint32_t bsc[NST][2];    // B scales in flight
+      auto issue = [&](int kt, int slot) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          lds_void* dst = (lds_void*)(ring + slot * SLOT + (RB * wave + i) * 8 * BKQ);
+          lds_dma16(arsrc, dst, aoff[i], kt * BKQ);
+        }
+        lds_dma4(srsrc, (lds_void*)(ring + slot * SLOT + TM * BKQ + 256 * wave), soff, kt * 4);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          bq[slot][0][st].lo = *reinterpret_cast<const i32x4_t*>(b0 + (4 * kt + 2 * st) * 1024);
+          bq[slot][0][st].hi = *reinterpret_cast<const i32x4_t*>(b0 + (4 * kt + 2 * st + 1) * 1024);
+          bq[slot][1][st].lo = *reinterpret_cast<const i32x4_t*>(b1 + (4 * kt + 2 * st) * 1024);
+          bq[slot][1][st].hi = *reinterpret_cast<const i32x4_t*>(b1 + (4 * kt + 2 * st + 1) * 1024);
+        }
+        bsc[slot][0] = bs0[kt * 64];
+        bsc[slot][1] = bs1[kt * 64];
+      };
+
+      f32x16_t acc[NRB][2];
+#pragma unroll
+      for (int i = 0; i < NRB; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+      auto compute = [&](int slot) {
+        const uint8_t* a_s = ring + slot * SLOT + frag_lane;
+        const uint8_t* a_sc = ring + slot * SLOT + TM * BKQ + (lane & 31) * 4 + 2 * khalf;
+        const uint32_t sb0 = bsc[slot][0], sb1 = bsc[slot][1];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int c0 = ((4 * s + khalf) ^ s7) << 4;
+          const int c1 = ((4 * s + 2 + khalf) ^ s7) << 4;
+          const uint32_t b0s = s == 0 ? (sb0 & 0xffu) : (sb0 >> 8);
+          const uint32_t b1s = s == 0 ? (sb1 & 0xffu) : (sb1 >> 8);
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) {
+            i32x8_t a;
+            a.lo = *reinterpret_cast<const i32x4_t*>(a_s + rb * 32 * BKQ + c0);
+            a.hi = *reinterpret_cast<const i32x4_t*>(a_s + rb * 32 * BKQ + c1);
+            const uint32_t asw = *reinterpret_cast<const uint16_t*>(a_sc + rb * 32 * 4);
+            const uint32_t as = s == 0 ? (asw & 0xffu) : (asw >> 8);
+            acc[rb][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                a, bq[slot][0][s], acc[rb][0], 0, 0, 0, static_cast<int>(as), 0,
+                static_cast<int>(b0s));
+            acc[rb][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                a, bq[slot][1][s], acc[rb][1], 0, 0, 0, static_cast<int>(as), 0,
+                static_cast<int>(b1s));
+          }
+        }
+      };
+
+      // Issue order inside a slab: the slab's loads first (with_loads), then
+      // fragment reads (two 16-byte code reads and one scale read per 32
+      // rows and MFMA step) one fragment ahead of its two MFMAs.
+      constexpr int NFR = 2 * NRB;  // fragments per slab
+      auto sched = [&](bool with_loads) {
+        if (with_loads) __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+        for (int g = 0; g < NFR - 1; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      };
+
+      // same slab pipeline as the bf16 kernel: three slabs in flight, the
+      // wait before slab kt leaves the loads of the two younger slabs
+      // outstanding (V per slab per wave, never interleaved across slabs)
+      __builtin_amdgcn_sched_barrier(0);
+      issue(0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(2, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      int kt = 0;
+      for (; kt < nk - 4; kt += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
+          __builtin_amdgcn_s_barrier();
+          issue(kt + u + 3, (u + 3) & 3);
+          compute(u);
+          sched(true);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
+      __builtin_amdgcn_s_barrier();
+      issue(kt + 3, 3);
+      compute(0);
+      sched(true);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
+      __builtin_amdgcn_s_barrier();
+      compute(1);
+      sched(false);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(V));
+      __builtin_amdgcn_s_barrier();
+      compute(2);
+      sched(false);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __builtin_amdgcn_s_barrier();
+      compute(3);
+      sched(false);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- epilogue.  Lane: column lane%32 of its group, rows
+      // 32 rb + 8 (v/4) + 4 (lane/32) + v%4.
+      __syncthreads();
+      const int rbase = 4 * khalf;
+      if constexpr (EPI == Q_SWIGLU) {
+        // h = silu(gate) * up staged as fp32 rows of 132 (128 columns + 4 of
+        // padding against bank conflicts); then one thread per (row, block
+        // of 32 columns) takes the block's scale and writes its 32 codes and
+        // its scale byte (slab order 0, 2, 1, 3).
+        constexpr int HS = 132;
+        float* sth = reinterpret_cast<float*>(ring);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int rl = rbase + 32 * rb + 8 * (v >> 2) + (v & 3);
+            sth[rl * HS + 32 * wave + (lane & 31)] = silu_f(acc[rb][0][v]) * acc[rb][1][v];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+        for (int c = tid; c < mcount * 4; c += NTHR) {
+          const int rl = c >> 2, j = c & 3;
+          const float* src = sth + rl * HS + 32 * j;
+          float v[32];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(src + 4 * i);
+            v[4 * i] = w4[0];
+            v[4 * i + 1] = w4[1];
+            v[4 * i + 2] = w4[2];
+            v[4 * i + 3] = w4[3];
+          }
+          float m = 0.f;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
+          const int S = mx_scale(m);
+          u32x4_t q0, q1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            q0[i] = mx_code(v[4 * i], S) | (mx_code(v[4 * i + 1], S) << 8) |
+                    (mx_code(v[4 * i + 2], S) << 16) | (mx_code(v[4 * i + 3], S) << 24);
+            q1[i] = mx_code(v[16 + 4 * i], S) | (mx_code(v[16 + 4 * i + 1], S) << 8) |
+                    (mx_code(v[16 + 4 * i + 2], S) << 16) | (mx_code(v[16 + 4 * i + 3], S) << 24);
+          }
+          uint8_t* dq = p.Cq + static_cast<int64_t>(m0 + rl) * p.ncols + n0 + 32 * j;
+          *reinterpret_cast<u32x4_t*>(dq) = q0;
+          *reinterpret_cast<u32x4_t*>(dq + 16) = q1;
+          p.Cs[static_cast<int64_t>(m0 + rl) * (p.ncols / 32) + n0 / 32 + 2 * (j & 1) + (j >> 1)] =
+              static_cast<uint8_t>(S);
+        }
+      } else {
+        bf16_t* st = reinterpret_cast<bf16_t*>(ring);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int rl = rbase + 32 * rb + 8 * (v >> 2) + (v & 3);
+            st[rl * OUTN + 64 * wave + (lane & 31)] = cvt_bf16(acc[rb][0][v]);
+            st[rl * OUTN + 64 * wave + 32 + (lane & 31)] = cvt_bf16(acc[rb][1][v]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+        constexpr int RC = OUTN / 8;
+        for (int c = tid; c < mcount * RC; c += NTHR) {
+          const int rl = c / RC, cc = (c % RC) * 8;
+          *reinterpret_cast<u32x4_t*>(p.Cb + static_cast<int64_t>(m0 + rl) * p.ncols + n0 + cc) =
+              *reinterpret_cast<const u32x4_t*>(st + rl * OUTN + cc);
+        }
+      }
+      if (tid == 0) s_claim[0] = next_n;
+      __syncthreads();
+    };
+    switch (nrb) {
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: if constexpr (RB >= 2) run(std::integral_constant<int, 2>{}); break;
+      case 3: if constexpr (RB >= 4) run(std::integral_constant<int, 3>{}); break;
+      case 4: if constexpr (RB >= 4) run(std::integral_constant<int, 4>{}); break;
+      case 5: if constexpr (RB >= 8) run(std::integral_constant<int, 5>{}); break;
+      case 6: if constexpr (RB >= 8) run(std::integral_constant<int, 6>{}); break;
+      case 7: if constexpr (RB >= 8) run(std::integral_constant<int, 7>{}); break;
+      default: if constexpr (RB >= 8) run(std::integral_constant<int, 8>{}); break;
+    }
+    cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
+  }
+}
+
+// Activation quantizer: rows x K bf16 (row-major, rows gathered by nothing)
+// -> codes [rows][K] and scales [rows][K/32] in slab order (0, 2, 1, 3).
+// Four lanes per block, eight values per lane.
+__global__ __launch_bounds__(256) void mxq_rows_kernel(const bf16_t* __restrict__ src,
+                                                       int64_t nblocks, int K,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales) {
+  const int kb = K / 32;
+  for (int64_t g = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+       g < nblocks * 4; g += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t blk = g >> 2;           // block index = row * kb + j
+    const int part = static_cast<int>(g & 3);
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src + blk * 32 + part * 8);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    const int S = mx_scale(m);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= mx_code(v[i], S) << (8 * i);
+      hi |= mx_code(v[4 + i], S) << (8 * i);
+    }
+    *reinterpret_cast<uint2*>(codes + blk * 32 + part * 8) = make_uint2(lo, hi);
+    if (part == 0) {
+      const int64_t row = blk / kb;
+      const int j = static_cast<int>(blk - row * kb);
+      const int pos = (j & ~3) + 2 * (j & 1) + ((j >> 1) & 1);
+      scales[row * kb + pos] = static_cast<uint8_t>(S);
+    }
+  }
+}
+
+// Weight quantizer + packer: nmat matrices [R][C] bf16 -> codes in the
+// packed layout, then scales (see the header comment).
+__global__ __launch_bounds__(256) void mxq_weights_kernel(const bf16_t* __restrict__ src,
+                                                          int64_t nblocks, int R, int C,
+                                                          uint8_t* __restrict__ dst,
+                                                          int64_t nmat) {
+  const int kb = C / 32;
+  const int nk = C / 128;
+  const int64_t per_mat = static_cast<int64_t>(R) * C;
+  uint16_t* const sdst = reinterpret_cast<uint16_t*>(dst + nmat * per_mat);
+  for (int64_t g = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+       g < nblocks * 4; g += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t blk = g >> 2;
+    const int part = static_cast<int>(g & 3);
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src + blk * 32 + part * 8);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    const int S = mx_scale(m);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= mx_code(v[i], S) << (8 * i);
+      hi |= mx_code(v[4 + i], S) << (8 * i);
+    }
+    const int64_t mi = blk / (static_cast<int64_t>(R) * kb);
+    const int64_t rem = blk - mi * R * kb;
+    const int r = static_cast<int>(rem / kb);
+    const int jb = static_cast<int>(rem - static_cast<int64_t>(r) * kb);  // block along C
+    const int t = jb >> 2;               // slab
+    const int step = (jb >> 1) & 1;      // MFMA step in the slab
+    const int half = jb & 1;             // operand half (bytes 16 half ..)
+    const int h = part >> 1;             // lane half: values 16h .. 16h+15 of the block
+    const int lanei = (r & 31) + 32 * h;
+    const int64_t piece = ((static_cast<int64_t>(r >> 5) * nk + t) * 2 + step) * 2 + half;
+    uint8_t* o = dst + mi * per_mat + piece * 1024 + lanei * 16 + (part & 1) * 8;
+    *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+    if (part == 0) {
+      // 16-bit word (block 4t + hh, block 4t + 2 + hh) of lane (r%32) + 32 hh
+      const int j = jb & 3;
+      const int hh = j & 1, byte = j >> 1;
+      const int64_t wi = (static_cast<int64_t>(r >> 5) * nk + t) * 64 + (r & 31) + 32 * hh;
+      reinterpret_cast<uint8_t*>(sdst + mi * (per_mat / 64))[wi * 2 + byte] =
+          static_cast<uint8_t>(S);
+    }
+  }
+}
+
+typedef void (*fwdq_fn)(QParams);
+// Tile heights 32 .. 128 (a 256-row tile does not fit the register file
+// without spills, whose memory traffic would upset the per-slab wait counts).
+fwdq_fn pick_q(int epi, int tm, int* per_cu) {
+  *per_cu = tm <= 64 ? 2 : 1;
+  if (epi == Q_SWIGLU) {
+    switch (tm) {
+      case 32: return fwdq_kernel<Q_SWIGLU, 32>;
+      case 64: return fwdq_kernel<Q_SWIGLU, 64>;
+      case 128: return fwdq_kernel<Q_SWIGLU, 128>;
+    }
+  } else {
+    switch (tm) {
+      case 32: return fwdq_kernel<Q_STORE, 32>;
+      case 64: return fwdq_kernel<Q_STORE, 64>;
+      case 128: return fwdq_kernel<Q_STORE, 128>;
+    }
+  }
+  return nullptr;
+}
+
+hipError_t launch_q(int epi, int tm, const QParams& p, int cu, hipStream_t s) {
+  int per_cu = 1;
+  fwdq_fn k = pick_q(epi, tm, &per_cu);
+  if (!k) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k, dim3(per_cu * cu), dim3(NTHR), 0, s, p);
+  return hipGetLastError();
+}
+
+int grid_for(int64_t threads) {
+  const int64_t want = (threads + 255) / 256;
+  return static_cast<int>(want < 16384 ? want : 16384);
+}
+
+}  // namespace
+
+hipError_t launch_mxq_rows(const bf16_t* src, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
+                           hipStream_t s) {
+  const int64_t nblocks = rows * (K / 32);
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(mxq_rows_kernel, dim3(grid_for(nblocks * 4)), dim3(256), 0, s, src, nblocks,
+                     K, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxq_weights(const bf16_t* src, uint8_t* dst, int64_t nmat, int R, int C,
+                              hipStream_t s) {
+  const int64_t nblocks = nmat * R * static_cast<int64_t>(C / 32);
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(mxq_weights_kernel, dim3(grid_for(nblocks * 4)), dim3(256), 0, s, src,
+                     nblocks, R, C, dst, nmat);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwdq_gateup(const uint8_t* xq, const uint8_t* xs, int64_t T, const uint8_t* wg_q,
+                              const uint8_t* wu_q, const int32_t* offsets, const int32_t* perm,
+                              const int32_t* mt_off, const int32_t* tile_exp, int32_t* sched,
+                              int tm, int N, int I, int d, int K, uint8_t* hq, uint8_t* hs, int cu,
+                              hipStream_t s) {
+  QParams p{};
+  p.N = N; p.ncols = I; p.K = d;
+  p.offsets = offsets; p.mt_off = mt_off; p.tile_exp = tile_exp; p.sched = sched;
+  p.A = xq; p.a_bytes = static_cast<uint32_t>(T * d);
+  p.As = xs; p.as_bytes = static_cast<uint32_t>(T * (d / 32));
+  p.perm = perm; p.kdiv = K;
+  p.B = wg_q; p.B2 = wu_q; p.Cq = hq; p.Cs = hs;
+  return launch_q(Q_SWIGLU, tm, p, cu, s);
+}
+
+hipError_t launch_fwdq_down(const uint8_t* hq, const uint8_t* hs, int64_t rows,
+                            const uint8_t* wd_q, const int32_t* offsets, const int32_t* mt_off,
+                            const int32_t* tile_exp, int32_t* sched, int tm, int N, int I, int d,
+                            bf16_t* y, int cu, hipStream_t s) {
+  QParams p{};
+  p.N = N; p.ncols = d; p.K = I;
+  p.offsets = offsets; p.mt_off = mt_off; p.tile_exp = tile_exp; p.sched = sched;
+  p.A = hq; p.a_bytes = static_cast<uint32_t>(rows * I);
+  p.As = hs; p.as_bytes = static_cast<uint32_t>(rows * (I / 32));
+  p.B = wd_q; p.Cb = y;
+  return launch_q(Q_STORE, tm, p, cu, s);
+}
+
+}  // namespace zc

@@ -168,6 +168,25 @@ hipError_t launch_fwdp_down(const bf16_t* h, int64_t h_elems, const bf16_t* wd_p
 hipError_t launch_pack_weights(const bf16_t* src, bf16_t* dst, int64_t nmat, int R, int C,
                                hipStream_t s);
 
+// MXFP8 expert GEMMs (gemm_fwdq.hip): E4M3 codes with one E8M0 scale per
+// 32 reduction steps.  Activation quantizer (rows x K bf16 -> codes and
+// slab-ordered scales), weight quantizer + packer (nmat [R][C] matrices ->
+// packed codes followed by packed scales), and the two grouped GEMMs (tile
+// bookkeeping as for the packed bf16 GEMMs).
+hipError_t launch_mxq_rows(const bf16_t* src, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
+                           hipStream_t s);
+hipError_t launch_mxq_weights(const bf16_t* src, uint8_t* dst, int64_t nmat, int R, int C,
+                              hipStream_t s);
+hipError_t launch_fwdq_gateup(const uint8_t* xq, const uint8_t* xs, int64_t T, const uint8_t* wg_q,
+                              const uint8_t* wu_q, const int32_t* offsets, const int32_t* perm,
+                              const int32_t* mt_off, const int32_t* tile_exp, int32_t* sched,
+                              int tm, int N, int I, int d, int K, uint8_t* hq, uint8_t* hs, int cu,
+                              hipStream_t s);
+hipError_t launch_fwdq_down(const uint8_t* hq, const uint8_t* hs, int64_t rows,
+                            const uint8_t* wd_q, const int32_t* offsets, const int32_t* mt_off,
+                            const int32_t* tile_exp, int32_t* sched, int tm, int N, int I, int d,
+                            bf16_t* y, int cu, hipStream_t s);
+
 // Combine: out = out_scale * (c_t x_t + sum_r g_r y[inv]).
 template <typename T>
 hipError_t launch_combine(const T* x, const T* y, const int32_t* topk_idx, const float* gate,

@@ -20,17 +20,18 @@ LIB_PATH = os.path.join(HERE, "libzcmoe.so")
 ZC_OK, ZC_ERR_INVALID, ZC_ERR_UNSUPPORTED, ZC_ERR_WORKSPACE, ZC_ERR_HIP = range(5)
 ZC_F32, ZC_BF16 = 0, 1
 ZC_OP_ROUTE, ZC_OP_FORWARD, ZC_OP_BACKWARD, ZC_OP_LB_LOSS, ZC_OP_ROUTE_STATS = 0, 1, 2, 3, 4
-ZC_WEIGHTS_ROWMAJOR, ZC_WEIGHTS_PACKED = 0, 1
+ZC_WEIGHTS_ROWMAJOR, ZC_WEIGHTS_PACKED, ZC_WEIGHTS_MXFP8 = 0, 1, 2
 ZC_PACK_GATE_UP, ZC_PACK_DOWN = 0, 1
 
 # Every symbol include/zc_moe.h declares.
 EXPORTS = ("zc_moe_workspace_size", "zc_moe_saved_size", "zc_moe_route", "zc_moe_forward",
            "zc_moe_backward", "zc_moe_lb_loss", "zc_moe_route_stats", "zc_moe_accumulate_counts",
-           "zc_moe_pid_update", "zc_moe_pack_weights",
+           "zc_moe_pid_update", "zc_moe_pack_weights", "zc_moe_quantized_weight_bytes",
+           "zc_moe_quantize_weights",
            "zc_moe_profile",
            "zc_moe_profile_read",
            "zc_moe_phase_name", "zc_status_string", "zc_last_error")
-ZC_NUM_PHASES = 20
+ZC_NUM_PHASES = 21
 
 
 class ZcError(RuntimeError):
@@ -82,9 +83,12 @@ def lib() -> C.CDLL:
         L.zc_moe_accumulate_counts.argtypes = [i64, v, v, v]
         L.zc_moe_pid_update.argtypes = [i64, i64, i64, v, i64, C.c_double, C.c_double, v, v]
         L.zc_moe_pack_weights.argtypes = [P, C.c_int, v, v, v]
+        L.zc_moe_quantized_weight_bytes.argtypes = [P]
+        L.zc_moe_quantized_weight_bytes.restype = sz
+        L.zc_moe_quantize_weights.argtypes = [P, C.c_int, v, v, v]
         for f in ("zc_moe_route", "zc_moe_forward", "zc_moe_backward", "zc_moe_lb_loss",
                   "zc_moe_route_stats", "zc_moe_accumulate_counts", "zc_moe_pid_update",
-                  "zc_moe_pack_weights"):
+                  "zc_moe_pack_weights", "zc_moe_quantize_weights"):
             getattr(L, f).restype = C.c_int
         L.zc_moe_profile.argtypes = [C.c_int]
         L.zc_moe_profile.restype = C.c_int
@@ -195,6 +199,13 @@ def _check_layer_tensor(t, shape, dtype, name):
 def _check_weights(desc, w_router, w_gate, w_up, w_down):
     dt = desc.dtype
     _check_layer_tensor(w_router, (desc.E, desc.d), dt, "w_router")
+    if desc.weight_layout == ZC_WEIGHTS_MXFP8:
+        d = desc.c()
+        n = int(lib().zc_moe_quantized_weight_bytes(C.byref(d)))
+        for t, name in ((w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down")):
+            if t is not None and (t.dtype != torch.uint8 or t.numel() < n):
+                raise ValueError(f"{name}: expected a quantized weight set of {n} uint8")
+        return
     _check_layer_tensor(w_gate, (desc.N, desc.I, desc.d), dt, "w_gate")
     _check_layer_tensor(w_up, (desc.N, desc.I, desc.d), dt, "w_up")
     _check_layer_tensor(w_down, (desc.N, desc.d, desc.I), dt, "w_down")
@@ -343,3 +354,28 @@ def zc_moe_profile_read() -> dict:
     _check(lib().zc_moe_profile_read(tot, cnt), "zc_moe_profile_read")
     return {lib().zc_moe_phase_name(i).decode(): (tot[i], cnt[i])
             for i in range(ZC_NUM_PHASES) if cnt[i]}
+
+
+def zc_moe_quantize_weights(desc: LayerDesc, which: int, src, dst=None, stream=None):
+    """FP8 blockwise (MXFP8) quantization of w_gate or w_up (which =
+    ZC_PACK_GATE_UP, [N][I][d]) or w_down (ZC_PACK_DOWN, [N][d][I]) into dst,
+    a uint8 GPU tensor of zc_moe_quantized_weight_bytes(desc) bytes (allocated
+    when None).  Returns dst."""
+    shape = (desc.N, desc.I, desc.d) if which == ZC_PACK_GATE_UP else (desc.N, desc.d, desc.I)
+    _check_layer_tensor(src, shape, desc.dtype, "src")
+    d = desc.c()
+    n = int(lib().zc_moe_quantized_weight_bytes(C.byref(d)))
+    if dst is None:
+        dst = torch.empty(max(n, 16), dtype=torch.uint8, device=src.device)
+    if dst.dtype != torch.uint8 or dst.numel() < n:
+        raise ValueError(f"dst: expected at least {n} uint8, got {dst.numel()} {dst.dtype}")
+    _check(lib().zc_moe_quantize_weights(C.byref(d), which, _ptr(src), _ptr(dst), _stream(stream)),
+           "zc_moe_quantize_weights")
+    return dst
+
+
+def quantize_expert_weights(desc: LayerDesc, w_gate, w_up, w_down, stream=None):
+    """The three MXFP8 weight sets a ZC_WEIGHTS_MXFP8 forward takes."""
+    return (zc_moe_quantize_weights(desc, ZC_PACK_GATE_UP, w_gate, stream=stream),
+            zc_moe_quantize_weights(desc, ZC_PACK_GATE_UP, w_up, stream=stream),
+            zc_moe_quantize_weights(desc, ZC_PACK_DOWN, w_down, stream=stream))

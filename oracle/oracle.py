@@ -48,7 +48,7 @@ def lib():
         L.orc_mx_quantize.argtypes = [_i64, _i64, _i32, _p, _p, _p]
         L.orc_mx_dequantize.argtypes = [_i64, _i64, _p, _p, _p]
         L.orc_forward_mx.argtypes = [_i64, _i64, _i64, _i64, _i64, _i32, _f64, _p, _p, _p, _p,
-                                     _p, _p, _i64, _p, _p, _p]
+                                     _p, _p, _p, _p, _p, _i64, _p, _p, _p, _f64, _p]
         L.orc_num_threads.restype = C.c_int
         L.orc_num_threads.argtypes = []
         L.orc_pid_update.argtypes = [_i64, _i64, _i64, _p, _i64, _f64, _f64, _p]
@@ -285,32 +285,42 @@ def mx_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return out
 
 
-def mx_weights(w: np.ndarray) -> np.ndarray:
-    """Dequantized binary64 MXFP8 image of one expert weight [R][C] (blocks
-    of 32 along C, the reduction dimension)."""
-    return mx_dequantize(*mx_quantize(w))
+def mx_weights(w: np.ndarray):
+    """MXFP8 image (codes, scales) of one expert weight [R][C], blocks of 32
+    along C (the reduction dimension)."""
+    return mx_quantize(w)
 
 
-def forward_mx(x, wgq, wuq, wdq, topk_idx, gates, N, out_scale=1.0, toks=None, want_y=False):
+def forward_mx(x, wgq, wuq, wdq, topk_idx, gates, N, out_scale=1.0, toks=None, want_y=False,
+               flip_eps=None):
     """O13: the layer forward with MXFP8 expert operands.  wgq / wuq / wdq:
-    {expert: dequantized binary64 weight} (mx_weights) for every FFN expert
-    the listed tokens pick."""
+    {expert: (codes, scales)} (mx_weights) for every FFN expert the listed
+    tokens pick.  With flip_eps (the accuracy of fp32 dot products relative
+    to their sum of absolute products), also returns the per-element bound
+    of the output change from h codes that sit that close to a code or scale
+    boundary (see orc.c)."""
     x = _c(x)
     T, d = x.shape
     K = topk_idx.shape[1]
-    e0 = next(iter(wgq.values()))
-    I = e0.shape[0]
-    tg, kg = _table({e: _c(v, np.float64) for e, v in wgq.items()}, N)
-    tu, ku = _table({e: _c(v, np.float64) for e, v in wuq.items()}, N)
-    td, kd = _table({e: _c(v, np.float64) for e, v in wdq.items()}, N)
+    I = next(iter(wgq.values()))[0].shape[0] if wgq else 32  # no FFN pick: any I
+    tabs, keep = [], []
+    for src in (wgq, wuq, wdq):
+        for part in (0, 1):
+            arrs = {e: _c(v[part], np.uint8) for e, v in src.items()}
+            t, k = _table(arrs, N)
+            tabs.append(t)
+            keep.append((arrs, k))
     ti = _c(topk_idx, np.int32)
     gg = _c(gates, np.float64)
     tk = None if toks is None else _c(np.asarray(toks), np.int64)
     n = T if tk is None else len(tk)
     out = np.empty((n, d), np.float64)
     y = np.empty((n * K, d), np.float64) if want_y else None
-    rc = lib().orc_forward_mx(T, d, N, I, K, _dt(x), float(out_scale), _ptr(x), tg, tu, td,
-                              _ptr(ti), _ptr(gg), n, _ptr(tk), _ptr(out), _ptr(y))
+    fl = np.empty((n, d), np.float64) if flip_eps is not None else None
+    rc = lib().orc_forward_mx(T, d, N, I, K, _dt(x), float(out_scale), _ptr(x), *tabs,
+                              _ptr(ti), _ptr(gg), n, _ptr(tk), _ptr(out), _ptr(y),
+                              float(flip_eps or 0.0), _ptr(fl))
     assert rc == 0, f"oracle forward_mx failed rc={rc}"
-    del kg, ku, kd
-    return (out, y) if want_y else out
+    del keep
+    res = (out,) + ((y,) if want_y else ()) + ((fl,) if flip_eps is not None else ())
+    return res if len(res) > 1 else out

@@ -701,41 +701,69 @@ int orc_mx_dequantize(int64_t rows, int64_t cols, const uint8_t* codes, const ui
 
 /* O13 -- the layer forward with MXFP8 expert operands (O12):
  *   x'  = MX(x_t) along d (per token);  W' = MX(W) along each weight's
- *         reduction dimension (given here already dequantized, binary64);
+ *         reduction dimension (given as codes + scales per expert, the
+ *         output of orc_mx_quantize on [I][d] or [d][I]);
  *   a = W'_g x',  u = W'_u x',  h = silu(a) * u, rounded to fp32 (the
  *         precision in which the GPU takes the quantization decision);
  *   h' = MX(h) along I;  y = W'_d h';
  *   out_t = out_scale * ( c_t x_t + sum over FFN picks of g_r y_r ), with
  *         the zero-computation term on the unquantized x_t.
- * Weight tables as in orc_forward, binary64 [I][d] / [d][I] per expert.
- * y_out (nullable) receives y per listed (token, slot) [n_tok*K][d] (0 for
- * identity picks). */
+ * Weight tables: per expert e, codes (wgc/wuc [I][d], wdc [d][I]) and
+ * scales (wgs/wus [I][d/32], wds [d][I/32]); NULL for experts no listed
+ * token picks.  y_out (nullable) receives y per listed (token, slot)
+ * [n_tok*K][d] (0 for identity picks).
+ *
+ * h' is a quantization decision taken on an fp32 value that any other
+ * implementation computes in another summation order.  With a and u summed
+ * in fp32 to within eps times the sum of their absolute products (Sa, Su),
+ * h_i is known to within
+ *   tol_i = eps (|silu'(a) u| Sa + |silu(a)| Su) + 2^-21 |h_i|
+ * (the last term for the fp32 evaluation of silu and the product), so an
+ * h_i within tol_i of a rounding boundary of its code (or a block whose
+ * amax is that close to a power of two, which moves its scale) may
+ * legitimately come out one code apart.  flip (nullable, [n_tok][d])
+ * receives, per output element, the largest change such flips can cause:
+ * out_scale * sum over FFN picks of g * sum over those i of
+ * |W'_d[n][i]| * (largest distance between the dequantized candidates). */
+static void mx_candidates(const double* h, const double* tol, int64_t I, const uint8_t* qs,
+                          const double* hq, double* delta);
 int orc_forward_mx(int64_t T, int64_t d, int64_t N, int64_t I, int64_t K, int dt,
-                   double out_scale, const void* x, const double* const* wg,
-                   const double* const* wu, const double* const* wd, const int32_t* topk_idx,
-                   const double* gates, int64_t n_tok, const int64_t* toks, double* out,
-                   double* y_out) {
-  if (T < 0 || d <= 0 || d % 32 || I <= 0 || I % 32 || K < 1 || !x || !wg || !wu || !wd ||
-      !topk_idx || !gates || !out)
+                   double out_scale, const void* x, const uint8_t* const* wgc,
+                   const uint8_t* const* wgs, const uint8_t* const* wuc,
+                   const uint8_t* const* wus, const uint8_t* const* wdc,
+                   const uint8_t* const* wds, const int32_t* topk_idx, const double* gates,
+                   int64_t n_tok, const int64_t* toks, double* out, double* y_out, double eps,
+                   double* flip) {
+  if (T < 0 || d <= 0 || d % 32 || I <= 0 || I % 32 || K < 1 || !x || !wgc || !wgs || !wuc ||
+      !wus || !wdc || !wds || !topk_idx || !gates || !out)
     return 1;
   if (!toks) n_tok = T;
-  int bad = 0;
+  double val[256];
+  for (int c = 0; c < 256; ++c) val[c] = orc_e4m3_value(c);
+  for (int64_t q = 0; q < n_tok; ++q) {
+    const int64_t t = toks ? toks[q] : q;
+    if (t < 0 || t >= T) return 1;
+    for (int64_t r = 0; r < K; ++r) {
+      const int64_t e = topk_idx[t * K + r];
+      if (e < N && (!wgc[e] || !wgs[e] || !wuc[e] || !wus[e] || !wdc[e] || !wds[e])) return 1;
+    }
+  }
+  const int64_t wmax = d > I ? d : I;
 #pragma omp parallel
   {
     double* xq = (double*)malloc(sizeof(double) * (size_t)d);
-    uint8_t* qc = (uint8_t*)malloc((size_t)(d > I ? d : I));
-    uint8_t* qs = (uint8_t*)malloc((size_t)(d > I ? d : I) / 32);
+    uint8_t* qc = (uint8_t*)malloc((size_t)wmax);
+    uint8_t* qs = (uint8_t*)malloc((size_t)wmax / 32);
     double* h = (double*)malloc(sizeof(double) * (size_t)I);
     double* hq = (double*)malloc(sizeof(double) * (size_t)I);
     double* y = (double*)malloc(sizeof(double) * (size_t)d);
+    double* wrow = (double*)malloc(sizeof(double) * (size_t)wmax);
+    double* urow = (double*)malloc(sizeof(double) * (size_t)d);
+    double* dlt = (double*)malloc(sizeof(double) * (size_t)I);
+    double* tl = (double*)malloc(sizeof(double) * (size_t)I);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t q = 0; q < n_tok; ++q) {
       const int64_t t = toks ? toks[q] : q;
-      if (t < 0 || t >= T) {
-#pragma omp atomic write
-        bad = 1;
-        continue;
-      }
       if (dt == ORC_BF16) {
         orc_mx_quantize(1, d, ORC_BF16, (const uint16_t*)x + t * d, qc, qs);
       } else {
@@ -743,8 +771,11 @@ int orc_forward_mx(int64_t T, int64_t d, int64_t N, int64_t I, int64_t K, int dt
       }
       orc_mx_dequantize(1, d, qc, qs, xq);
       double* o = out + q * d;
+      double* fo = flip ? flip + q * d : NULL;
       double c = 0.0;
       for (int64_t n = 0; n < d; ++n) o[n] = 0.0;
+      if (fo)
+        for (int64_t n = 0; n < d; ++n) fo[n] = 0.0;
       for (int64_t r = 0; r < K; ++r) {
         const int64_t e = topk_idx[t * K + r];
         const double g = gates[t * K + r];
@@ -756,26 +787,90 @@ int orc_forward_mx(int64_t T, int64_t d, int64_t N, int64_t I, int64_t K, int dt
           continue;
         }
         for (int64_t i = 0; i < I; ++i) {
-          double a = 0.0, u = 0.0;
+          /* rows i of W'_g and W'_u, dequantized */
           for (int64_t k = 0; k < d; ++k) {
-            a += wg[e][i * d + k] * xq[k];
-            u += wu[e][i * d + k] * xq[k];
+            wrow[k] = ldexp(val[wgc[e][i * d + k]], (int)wgs[e][(i * d + k) / 32] - 127);
+            urow[k] = ldexp(val[wuc[e][i * d + k]], (int)wus[e][(i * d + k) / 32] - 127);
+          }
+          double a = 0.0, u = 0.0, sa = 0.0, su = 0.0;
+          for (int64_t k = 0; k < d; ++k) {
+            a += wrow[k] * xq[k];
+            u += urow[k] * xq[k];
+            sa += fabs(wrow[k] * xq[k]);
+            su += fabs(urow[k] * xq[k]);
           }
           h[i] = (double)(float)(silu(a) * u);
+          const double sg = 1.0 / (1.0 + exp(-a));
+          tl[i] = eps * (fabs(sg * (1.0 + a * (1.0 - sg)) * u) * sa + fabs(a * sg) * su) +
+                  ldexp(fabs(h[i]), -21);
         }
         orc_mx_quantize(1, I, 2, h, qc, qs);
         orc_mx_dequantize(1, I, qc, qs, hq);
+        if (fo) mx_candidates(h, tl, I, qs, hq, dlt);
         for (int64_t n = 0; n < d; ++n) {
+          for (int64_t i = 0; i < I; ++i)
+            wrow[i] = ldexp(val[wdc[e][n * I + i]], (int)wds[e][(n * I + i) / 32] - 127);
           double acc = 0.0;
-          for (int64_t i = 0; i < I; ++i) acc += wd[e][n * I + i] * hq[i];
+          for (int64_t i = 0; i < I; ++i) acc += wrow[i] * hq[i];
           y[n] = acc;
           if (yo) yo[n] = acc;
+          if (fo) {
+            double fl = 0.0;
+            for (int64_t i = 0; i < I; ++i)
+              if (dlt[i] > 0.0) fl += fabs(wrow[i]) * dlt[i];
+            fo[n] += fabs(out_scale * g) * fl;
+          }
         }
         for (int64_t n = 0; n < d; ++n) o[n] += g * y[n];
       }
       for (int64_t n = 0; n < d; ++n) o[n] = out_scale * (c * ld(x, dt, t * d + n) + o[n]);
     }
-    free(xq); free(qc); free(qs); free(h); free(hq); free(y);
+    free(xq); free(qc); free(qs); free(h); free(hq); free(y); free(wrow); free(urow); free(dlt);
+    free(tl);
   }
-  return bad;
+  return 0;
+}
+
+/* For each h_i: 0 when its code and scale are the same for every value in
+ * [h_i - tol_i, h_i + tol_i] (and for the block's amax moved the same way);
+ * otherwise the largest distance between hq_i and the dequantized value of
+ * any of those alternatives. */
+static void mx_candidates(const double* h, const double* tol, int64_t I, const uint8_t* qs,
+                          const double* hq, double* delta) {
+  for (int64_t b = 0; b < I / 32; ++b) {
+    double lo = 0.0, hi = 0.0;  /* range of the block's amax */
+    for (int i = 0; i < 32; ++i) {
+      const double m = fabs(h[b * 32 + i]), t = tol[b * 32 + i];
+      if (m + t > hi) hi = m + t;
+      if (m - t > lo) lo = m - t;
+    }
+    int Ss[3], ns = 0;
+    Ss[ns++] = qs[b];
+    const double ends[2] = {lo, hi};
+    for (int w = 0; w < 2; ++w) {
+      int S = 0;
+      if (ends[w] > 0.0) {
+        int ex;
+        frexp(ends[w], &ex);
+        S = (ex - 1) - 8 + 127;
+        if (S < 0) S = 0;
+        if (S > 254) S = 254;
+      }
+      int dup = 0;
+      for (int q = 0; q < ns; ++q) dup |= Ss[q] == S;
+      if (!dup) Ss[ns++] = S;
+    }
+    for (int i = 0; i < 32; ++i) {
+      const int64_t k = b * 32 + i;
+      double dm = 0.0;
+      for (int si = 0; si < ns; ++si)
+        for (int sgn = -1; sgn <= 1; ++sgn) {
+          const double v = h[k] + sgn * tol[k];
+          const int code = orc_e4m3_encode(ldexp(v, 127 - Ss[si]));
+          const double dv = ldexp(orc_e4m3_value(code), Ss[si] - 127);
+          if (fabs(dv - hq[k]) > dm) dm = fabs(dv - hq[k]);
+        }
+      delta[k] = dm;
+    }
+  }
 }

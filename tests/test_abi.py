@@ -142,7 +142,12 @@ def test_binding_rejects_host_tensors():
 
 
 @pytest.mark.parametrize("bad,code", [
-    (dict(weight_layout=2), zcmoe.ZC_ERR_INVALID),
+    (dict(weight_layout=3), zcmoe.ZC_ERR_INVALID),
+    (dict(weight_layout=zcmoe.ZC_WEIGHTS_MXFP8), zcmoe.ZC_ERR_UNSUPPORTED),    # fp32 layer
+    (dict(weight_layout=zcmoe.ZC_WEIGHTS_MXFP8, dtype=torch.bfloat16, d=256, I=512),
+     zcmoe.ZC_ERR_UNSUPPORTED),                                              # d % 512
+    (dict(weight_layout=zcmoe.ZC_WEIGHTS_MXFP8, dtype=torch.bfloat16, d=512, I=768),
+     zcmoe.ZC_ERR_UNSUPPORTED),                                              # I % 512
     (dict(weight_layout=zcmoe.ZC_WEIGHTS_PACKED), zcmoe.ZC_ERR_UNSUPPORTED),   # fp32 layer
     (dict(weight_layout=zcmoe.ZC_WEIGHTS_PACKED, dtype=torch.bfloat16), zcmoe.ZC_ERR_UNSUPPORTED),
     (dict(weight_layout=zcmoe.ZC_WEIGHTS_PACKED, dtype=torch.bfloat16, d=256, I=128),
@@ -223,3 +228,31 @@ def test_route_stats_and_accumulate_argument_checks(L):
     assert L.zc_moe_accumulate_counts(1025, FAKE, other, None) == zcmoe.ZC_ERR_INVALID
     assert L.zc_moe_accumulate_counts(12, FAKE, FAKE, None) == zcmoe.ZC_ERR_INVALID
     assert L.zc_moe_accumulate_counts(12, None, other, None) == zcmoe.ZC_ERR_INVALID
+
+
+def test_quantized_weight_argument_checks(L):
+    d = desc(dtype=torch.bfloat16, d=512, I=512)
+    dd = d.c()
+    n = L.zc_moe_quantized_weight_bytes(C.byref(dd))
+    assert n == 8 * 512 * 512 * 33 // 32
+    assert L.zc_moe_quantized_weight_bytes(C.byref(desc(K=0).c())) == 0
+    other = C.c_void_p(1 << 40)
+    assert L.zc_moe_quantize_weights(C.byref(dd), 2, FAKE, other, None) == zcmoe.ZC_ERR_INVALID
+    assert L.zc_moe_quantize_weights(C.byref(dd), 0, FAKE, FAKE, None) == zcmoe.ZC_ERR_INVALID
+    assert "overlap" in L.zc_last_error().decode()
+    f32 = desc(d=512, I=512).c()
+    assert L.zc_moe_quantize_weights(C.byref(f32), 0, FAKE, other, None) == \
+        zcmoe.ZC_ERR_UNSUPPORTED
+    # the MXFP8 forward serves inference only: no saved activations, no backward
+    mx = desc(dtype=torch.bfloat16, d=512, I=512, weight_layout=zcmoe.ZC_WEIGHTS_MXFP8).c()
+    r = route_buf()
+    st = L.zc_moe_forward(C.byref(mx), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, C.byref(r), FAKE,
+                          FAKE, 1 << 40, None)
+    assert st == zcmoe.ZC_ERR_UNSUPPORTED
+    st = L.zc_moe_backward(C.byref(mx), FAKE, FAKE, FAKE, FAKE, FAKE, C.byref(r), FAKE, FAKE, FAKE,
+                           FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
+    assert st == zcmoe.ZC_ERR_UNSUPPORTED
+    # its workspace holds the quantized activations on top of the bf16 forward's
+    bf = desc(dtype=torch.bfloat16, d=512, I=512).c()
+    assert L.zc_moe_workspace_size(C.byref(mx), zcmoe.ZC_OP_FORWARD) > \
+        L.zc_moe_workspace_size(C.byref(bf), zcmoe.ZC_OP_FORWARD)

@@ -151,8 +151,11 @@ def test_forward_mx_is_a_composition_of_quantized_matmuls(orc):
     T, d, N, Z, I, K = 12, 64, 3, 2, 64, 5
     x, wg, wu, wd, lg = _layer(T, d, N, Z, I, K, seed=4)
     ro = orc.route(lg, np.zeros(N + Z, np.float32), N, K)
-    G, U, D = _mxq(orc, wg), _mxq(orc, wu), _mxq(orc, wd)
-    out = orc.forward_mx(x, G, U, D, ro.topk_idx, ro.gates, N, out_scale=0.5)
+    Gq, Uq, Dq = _mxq(orc, wg), _mxq(orc, wu), _mxq(orc, wd)
+    out = orc.forward_mx(x, Gq, Uq, Dq, ro.topk_idx, ro.gates, N, out_scale=0.5)
+    G = {e: orc.mx_dequantize(*v) for e, v in Gq.items()}
+    U = {e: orc.mx_dequantize(*v) for e, v in Uq.items()}
+    D = {e: orc.mx_dequantize(*v) for e, v in Dq.items()}
     xq = orc.mx_dequantize(*orc.mx_quantize(x))
     want = np.zeros((T, d))
     for t in range(T):
@@ -190,3 +193,41 @@ def test_forward_mx_is_close_to_the_unquantized_forward(orc):
     out = orc.forward_mx(x, _mxq(orc, wg), _mxq(orc, wu), _mxq(orc, wd), ro.topk_idx, ro.gates, N)
     rel = np.sqrt(np.mean((out - ref) ** 2)) / np.sqrt(np.mean(ref ** 2))
     assert 1e-3 < rel < 0.06, rel
+
+
+def test_forward_mx_flip_bound_covers_perturbed_h(orc):
+    """The flip bound (largest output change from h codes within relative
+    eps of a boundary) is 0 for eps = 0 and covers the actual change when
+    every h_i is moved by a random factor within 1 +- eps (numpy composition
+    of the pinned quantizer), and is not vacuous."""
+    T, d, N, Z, I, K = 10, 64, 3, 2, 64, 4
+    x, wg, wu, wd, lg = _layer(T, d, N, Z, I, K, seed=7)
+    ro = orc.route(lg, np.zeros(N + Z, np.float32), N, K)
+    Gq, Uq, Dq = _mxq(orc, wg), _mxq(orc, wu), _mxq(orc, wd)
+    eps = 2.0 ** -7
+    out, fl = orc.forward_mx(x, Gq, Uq, Dq, ro.topk_idx, ro.gates, N, flip_eps=eps)
+    _, fl0 = orc.forward_mx(x, Gq, Uq, Dq, ro.topk_idx, ro.gates, N, flip_eps=0.0)
+    assert not fl0.any() and fl.max() > 0
+    G = {e: orc.mx_dequantize(*v) for e, v in Gq.items()}
+    U = {e: orc.mx_dequantize(*v) for e, v in Uq.items()}
+    D = {e: orc.mx_dequantize(*v) for e, v in Dq.items()}
+    xq = orc.mx_dequantize(*orc.mx_quantize(x))
+    r = rng(8)
+    moved = 0.0
+    for trial in range(6):
+        want = np.zeros((T, d))
+        for t in range(T):
+            for k in range(K):
+                e, g = ro.topk_idx[t, k], ro.gates[t, k]
+                if e >= N:
+                    want[t] += g * x[t].astype(np.float64)
+                    continue
+                a, u = G[e] @ xq[t], U[e] @ xq[t]
+                h = (a / (1 + np.exp(-a)) * u).astype(np.float32).astype(np.float64)
+                h = h * (1 + r.uniform(-eps, eps, I))
+                hq = orc.mx_dequantize(*orc.mx_quantize(h[None, :]))[0]
+                want[t] += g * (D[e] @ hq)
+        diff = np.abs(want - out)
+        moved = max(moved, diff.max())
+        assert (diff <= fl * (1 + 1e-9) + 1e-13).all()
+    assert moved > 0  # the perturbations did flip codes
