@@ -31,6 +31,7 @@ from moe_layer_zero_amd import synth, zcmoe  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, vendor figure
 
 # HBM bytes of one prefill gate/up launch read from rocprofv3 counters
 # (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a plain copy of known
@@ -81,14 +82,21 @@ def timed(fn, steps, warmup):
     return a.elapsed_time(b) / steps, phases
 
 
-def layer_forward_bench(sh, steps, warmup, packed=True):
+def layer_forward_bench(sh, steps, warmup, packed=True, fp8=False):
     """Inference forward of one layer.  packed: the expert weights are
     rearranged once (untimed, like loading a model) into the packed layout
-    the bf16 inference kernels stream; the row-major copies are dropped."""
+    the bf16 inference kernels stream; the row-major copies are dropped.
+    fp8: the expert weights are quantized once (untimed) to MXFP8 instead."""
     log(f"[bench] generating {sh.name} layer on the GPU")
     Lg = synth.make_layer(sh, "cuda")
     desc = desc_of(sh)
-    if packed:
+    if fp8:
+        Lg["wg"], Lg["wu"], Lg["wd"] = zcmoe.quantize_expert_weights(desc, Lg["wg"], Lg["wu"],
+                                                                     Lg["wd"])
+        desc = dataclasses.replace(desc, weight_layout=zcmoe.ZC_WEIGHTS_MXFP8)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    elif packed:
         Lg["wg"], Lg["wu"], Lg["wd"] = zcmoe.pack_expert_weights(desc, Lg["wg"], Lg["wu"],
                                                                  Lg["wd"])
         desc = dataclasses.replace(desc, weight_layout=zcmoe.ZC_WEIGHTS_PACKED)
@@ -230,6 +238,44 @@ def train(steps, warmup):
     return res
 
 
+def fp8_forward(name, steps, warmup):
+    """The MXFP8 inference forward (E4M3 codes, one E8M0 scale per 32
+    reduction steps) of the prefill or decode layer.  Algorithmic bytes of
+    the gate/up GEMM: W_g and W_u of every touched expert once at 33/32 bytes
+    per weight, the quantized x row and scales of every pick, and the
+    quantized h row and scales it writes; of the whole layer at decode: all
+    expert weights touched at 33/32 bytes, the router weights, x, out, and
+    the routing arrays."""
+    sh = synth.CONFIGS[name]
+    Lg, ms, ph, p_real, touched, counts = layer_forward_bench(sh, steps, warmup, fp8=True)
+    d, I, E = sh.d, sh.I, sh.E
+    q = 33.0 / 32.0
+    gu_ms, dn_ms = ph["gate_up_gemm"][0], ph["down_gemm"][0]
+    flops_gu = 4.0 * d * I * p_real
+    flops_dn = 2.0 * d * I * p_real
+    gu_bytes = q * 2 * d * I * touched + q * d * p_real + q * I * p_real
+    res = {
+        "ms_per_step": ms,
+        "tokens_per_s": sh.T / (ms / 1e3),
+        "p_real": p_real,
+        "touched_experts": touched,
+        "kernels_ms": {k: round(v[0], 4) for k, v in ph.items()},
+        "gate_up_tflops": flops_gu / (gu_ms * 1e-3) / 1e12,
+        "gate_up_fp8_mfma_frac": flops_gu / (gu_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
+        "gate_up_gbs": gu_bytes / (gu_ms * 1e-3) / 1e9,
+        "gate_up_hbm_frac": gu_bytes / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "down_tflops": flops_dn / (dn_ms * 1e-3) / 1e12,
+    }
+    if name == "decode_bf16":
+        layer_bytes = (q * 3 * d * I * touched + 2.0 * d * E + 2 * 2.0 * sh.T * d + 4.0 * E +
+                       8.0 * sh.T * sh.K)
+        res["layer_gbs"] = layer_bytes / (ms * 1e-3) / 1e9
+        res["layer_hbm_frac"] = res["layer_gbs"] / HBM_PEAK_GBS
+    del Lg
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(target_s=15.0, max_tokens=4096):
     """The fp64 oracle on a bounded sample of the prefill workload: router
     scores, routing and layer output for the first n tokens of a seeded
@@ -281,7 +327,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", choices=["prefill", "decode", "train"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "train", "fp8-prefill", "fp8-decode"],
+                    default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rowmajor", action="store_true",
                     help="inference on row-major expert weights instead of the packed layout")
@@ -309,11 +356,16 @@ def main():
     if args.only in (None, "train"):
         extra["train"] = train(args.steps, args.warmup)
         log(f"[bench] train {extra['train']['ms_per_step']:.3f} ms/step")
+    for key, name in (("fp8-prefill", "prefill_bf16"), ("fp8-decode", "decode_bf16")):
+        if args.only in (None, key):
+            extra[key.replace("-", "_")] = fp8_forward(name, args.steps, args.warmup)
+            log(f"[bench] {key} {extra[key.replace('-', '_')]['ms_per_step']:.3f} ms/step")
     cpu = None if args.no_cpu_baseline or args.only not in (None, "prefill") else cpu_baseline()
     if res is None:  # a secondary workload alone: report it as the line
         k = args.only
-        res = extra.pop(k)
-        sh = synth.CONFIGS["decode_bf16" if k == "decode" else "train_bf16"]
+        res = extra.pop(k.replace("-", "_"))
+        sh = synth.CONFIGS["train_bf16" if k == "train" else
+                           "prefill_bf16" if k == "fp8-prefill" else "decode_bf16"]
         roof = None
     line = {
         "metric": "MoE-layer tokens/s at 1 GPU (prefill forward; % bf16 MFMA peak of the "
@@ -331,8 +383,8 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs, N(0,std) weights, random init)",
         "config": {"workload": sh.name, "T": sh.T, "d": sh.d, "N": sh.N, "Z": sh.Z, "I": sh.I,
                    "K": sh.K, "bias": sh.bias,
-                   "expert_weights": "row-major" if args.rowmajor or sh.name == "train_bf16"
-                   else "packed"},
+                   "expert_weights": "mxfp8" if (args.only or "").startswith("fp8") else
+                   "row-major" if args.rowmajor or sh.name == "train_bf16" else "packed"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": res,

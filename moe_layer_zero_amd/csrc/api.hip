@@ -201,6 +201,7 @@ struct RouteWs {
   int32_t* tile_off;   // row-tile prefix for the generic grouped GEMM
   int32_t* tile_off2;  // row-tile prefix for the bf16 forward expert GEMMs
   int32_t* tile_exp;   // expert of each of those row tiles
+  int32_t* tile_exp1;  // expert of each row tile of the first prefix
   int32_t* sched;      // tile counters of the packed-weight GEMMs
   float* rpart;        // fp32 partials of a split router GEMM (nullptr: unsplit)
   void* dispatch;
@@ -214,7 +215,7 @@ int64_t rpart_bytes(const zc_moe_desc* d) {
   return s > 1 ? 4 * s * d->T * E : 0;
 }
 int64_t route_ws_bytes(const zc_moe_desc* d) {
-  return 2 * a256(4 * (d->N + 1)) + a256(4 * max_tiles2(d)) + a256(4 * zc::kSchedInts) +
+  return 2 * a256(4 * (d->N + 1)) + 2 * a256(4 * max_tiles2(d)) + a256(4 * zc::kSchedInts) +
          a256(rpart_bytes(d)) + a256(zc::dispatch_scratch_bytes(d->T, d->N + d->Z, d->N));
 }
 RouteWs carve_route(char* p, const zc_moe_desc* d) {
@@ -223,6 +224,8 @@ RouteWs carve_route(char* p, const zc_moe_desc* d) {
   w.tile_off2 = reinterpret_cast<int32_t*>(p + a256(4 * (d->N + 1)));
   char* q = p + 2 * a256(4 * (d->N + 1));
   w.tile_exp = reinterpret_cast<int32_t*>(q);
+  q += a256(4 * max_tiles2(d));
+  w.tile_exp1 = reinterpret_cast<int32_t*>(q);
   q += a256(4 * max_tiles2(d));
   w.sched = reinterpret_cast<int32_t*>(q);
   q += a256(4 * zc::kSchedInts);
@@ -349,11 +352,7 @@ bool use_fwd_kernels(const zc_moe_desc* d, const void* saved) {
 // forward kernels use 256.
 int fwd_rows_per_tile(const zc_moe_desc* d) {
   if (d->weight_layout == ZC_WEIGHTS_ROWMAJOR || d->N == 0) return zc::kFwdBM;
-  const int tm = zc::fwdp_rows_per_tile(d->T * d->K / d->N);
-  // the MXFP8 kernels stop at 128-row tiles: their 256-row variants exceed
-  // the register file, and spill traffic in flight breaks the per-slab
-  // load counts their waits rely on
-  return d->weight_layout == ZC_WEIGHTS_MXFP8 && tm > 128 ? 128 : tm;
+  return zc::fwdp_rows_per_tile(d->T * d->K / d->N);
 }
 
 template <typename T>
@@ -370,7 +369,8 @@ zc_status do_route(const zc_moe_desc* d, const T* x, const T* wr, const float* b
   ZC_LAUNCH(ZC_PH_DISPATCH, zc::launch_dispatch(r->topk_idx, Tn, E, N, K, zc::kGemmBM,
                                                 fwd_rows_per_tile(d),
                                                 r->counts, r->offsets, r->perm, r->inv, w.tile_off,
-                                                w.tile_off2, w.tile_exp, w.sched, w.dispatch, s),
+                                                w.tile_off2, w.tile_exp, w.tile_exp1, w.sched,
+                                                w.dispatch, s),
          "dispatch launch");
   return ZC_OK;
 }
@@ -414,10 +414,17 @@ zc_status do_forward(const zc_moe_desc* d, const T* x, const T* wr, const float*
                                        rw.tile_off2, rw.tile_exp, rw.sched, fwd_rows_per_tile(d), N,
                                        I, dd, K, hq, hs, cu, s),
                 "gate/up GEMM launch");
+      // the MXFP8 down GEMM stops at 128-row tiles (its 256-row variant
+      // would not fit the register file): there it runs on the kGemmBM-row
+      // tiling of the first prefix
+      const int tmu = fwd_rows_per_tile(d);
+      const bool split = tmu > zc::kGemmBM;
       ZC_LAUNCH(ZC_PH_DOWN,
                 zc::launch_fwdq_down(hq, hs, rows, reinterpret_cast<const uint8_t*>(wd), r->offsets,
-                                     rw.tile_off2, rw.tile_exp, rw.sched + 8, fwd_rows_per_tile(d),
-                                     N, I, dd, reinterpret_cast<bf16_t*>(y), cu, s),
+                                     split ? rw.tile_off : rw.tile_off2,
+                                     split ? rw.tile_exp1 : rw.tile_exp, rw.sched + 8,
+                                     split ? zc::kGemmBM : tmu, N, I, dd,
+                                     reinterpret_cast<bf16_t*>(y), cu, s),
                 "down GEMM launch");
     } else if (d->weight_layout == ZC_WEIGHTS_PACKED) {
       // bf16 inference on packed weights (validated: bf16, no saved buffer)

@@ -63,8 +63,8 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
                                                     int E, int N, int bm, int bm2,
                                                     int32_t* counts, int32_t* offsets,
                                                     int32_t* tile_off, int32_t* tile_off2,
-                                                    int32_t* tile_exp, int32_t* sched,
-                                                    int32_t* base) {
+                                                    int32_t* tile_exp, int32_t* tile_exp1,
+                                                    int32_t* sched, int32_t* base) {
   __shared__ int32_t s_off[1024];
   __shared__ int32_t s_til[1024];
   __shared__ int32_t s_til2[1024];
@@ -107,6 +107,11 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   if (tile_exp && e < N) {
     const int32_t t1 = s_til2[e], t0 = e > 0 ? s_til2[e - 1] : 0;
     for (int32_t t = t0; t < t1; ++t) tile_exp[t] = e;
+  }
+  // and of every bm-row tile
+  if (tile_exp1 && e < N) {
+    const int32_t t1 = s_til[e], t0 = e > 0 ? s_til[e - 1] : 0;
+    for (int32_t t = t0; t < t1; ++t) tile_exp1[t] = e;
   }
   if (e < N) {
     int32_t run = excl;
@@ -270,7 +275,7 @@ size_t dispatch_scratch_bytes(int64_t Tn, int64_t E, int64_t N) {
 hipError_t launch_dispatch(const int32_t* topk_idx, int Tn, int E, int N, int K, int bm, int bm2,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                            int32_t* tile_off, int32_t* tile_off2, int32_t* tile_exp,
-                           int32_t* sched, void* scratch, hipStream_t s) {
+                           int32_t* tile_exp1, int32_t* sched, void* scratch, hipStream_t s) {
   const int nblk = (Tn + kTokPerBlk - 1) / kTokPerBlk;
   Scratch sc = carve(scratch, nblk, E);
   if (nblk > 0) {
@@ -280,7 +285,7 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int Tn, int E, int N, int K,
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, sc.cnt, nblk, E, N, bm, bm2, counts,
-                     offsets, tile_off, tile_off2, tile_exp, sched, sc.base);
+                     offsets, tile_off, tile_off2, tile_exp, tile_exp1, sched, sc.base);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nblk == 0) return err;
   hipLaunchKernelGGL(scatter_kernel, dim3(nblk), dim3(kThreads), E * sizeof(uint64_t), s,

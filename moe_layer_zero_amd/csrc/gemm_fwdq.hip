@@ -47,7 +47,10 @@ constexpr int BKQ = 128;      // reduction steps per slab (128 bytes per row)
 constexpr int NST = 4;        // LDS ring slots
 constexpr int NTHR = 256;
 constexpr int GMV = 8;        // row tiles per group inside an expert
-constexpr int SC_BYTES = 1024;  // per-slot activation-scale area (256 rows)
+// per-slot scale area: activation scales of 256 rows (1 KB), then weight
+// scales of each wave's two column groups (4 waves x 2 x 256 B)
+constexpr int SC_A = 1024;
+constexpr int SC_BYTES = SC_A + 2048;
 
 enum { Q_SWIGLU = 0, Q_STORE = 1 };
 
@@ -117,13 +120,13 @@ __global__ __launch_bounds__(NTHR, 1) void fwdq_kernel(QParams p) {
   constexpr int RB = TM / 32;
   constexpr int SLOT = TM * BKQ + SC_BYTES;  // bytes per ring slot: codes, then scales
   constexpr int V = RB + 11;                 // loads per wave per slab
-  static_assert(TM == 32 || TM == 64 || TM == 128, "tile height");
+  static_assert(TM == 32 || TM == 64 || TM == 128 || TM == 256, "tile height");
   __shared__ __align__(16) uint8_t ring[NST * SLOT + 16];
   int32_t* const s_claim = reinterpret_cast<int32_t*>(ring + NST * SLOT);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
   constexpr int OUTN = EPI == Q_SWIGLU ? 128 : 256;
   const int NT = p.ncols / OUTN;
   const int64_t total = static_cast<int64_t>(p.mt_off[p.N]) * NT;
@@ -199,17 +202,24 @@ __global__ __launch_bounds__(NTHR, 1) void fwdq_kernel(QParams p) {
     const uint8_t* Bsrc1 = EPI == Q_SWIGLU ? p.B2 : p.B;
     const uint8_t* b0 = p.B + e * mat + static_cast<int64_t>(gA) * nk * 4096 + lane * 16;
     const uint8_t* b1 = Bsrc1 + e * mat + static_cast<int64_t>(gB) * nk * 4096 + lane * 16;
+    // weight scales: one 4-byte-per-lane copy per column group and slab into
+    // LDS (lanes 0..31 carry the group's 128 bytes, lanes 32..63 read nothing)
     const int64_t nexp = static_cast<int64_t>(p.N) * mat;  // scales follow all codes
-    const uint16_t* bs0 = reinterpret_cast<const uint16_t*>(p.B + nexp + e * (mat / 32)) +
-                          static_cast<int64_t>(gA) * nk * 64 + lane;
-    const uint16_t* bs1 = reinterpret_cast<const uint16_t*>(Bsrc1 + nexp + e * (mat / 32)) +
-                          static_cast<int64_t>(gB) * nk * 64 + lane;
+    const uint32_t sbytes = static_cast<uint32_t>(nexp / 32);
+    const __amdgpu_buffer_rsrc_t bsr0 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(p.B + nexp), (short)0, sbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t bsr1 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(Bsrc1 + nexp), (short)0, sbytes, 0x00020000);
+    const uint32_t ebase = static_cast<uint32_t>(e) * static_cast<uint32_t>(mat / 32);
+    const uint32_t bso0 = lane < 32 ? ebase + static_cast<uint32_t>(gA * nk * 128 + 4 * lane)
+                                    : sbytes;
+    const uint32_t bso1 = lane < 32 ? ebase + static_cast<uint32_t>(gB * nk * 128 + 4 * lane)
+                                    : sbytes;
 
     const int nrb = (mcount + 31) >> 5;
     auto run = [&](auto nrb_c) {
       constexpr int NRB = decltype(nrb_c)::value;
       i32x8_t bq[NST][2][2];   // B operands in flight: [slot][column group][step]
-      uint32_t bsc[NST][2];    // B scales in flight
       auto issue = [&](int kt, int slot) {
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
@@ -217,6 +227,9 @@ __global__ __launch_bounds__(NTHR, 1) void fwdq_kernel(QParams p) {
           lds_dma16(arsrc, dst, aoff[i], kt * BKQ);
         }
         lds_dma4(srsrc, (lds_void*)(ring + slot * SLOT + TM * BKQ + 256 * wave), soff, kt * 4);
+        uint8_t* const bsd = ring + slot * SLOT + TM * BKQ + SC_A + 512 * wave;
+        lds_dma4(bsr0, (lds_void*)bsd, bso0, kt * 128);
+        lds_dma4(bsr1, (lds_void*)(bsd + 256), bso1, kt * 128);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           bq[slot][0][st].lo = *reinterpret_cast<const i32x4_t*>(b0 + (4 * kt + 2 * st) * 1024);
@@ -224,8 +237,6 @@ __global__ __launch_bounds__(NTHR, 1) void fwdq_kernel(QParams p) {
           bq[slot][1][st].lo = *reinterpret_cast<const i32x4_t*>(b1 + (4 * kt + 2 * st) * 1024);
           bq[slot][1][st].hi = *reinterpret_cast<const i32x4_t*>(b1 + (4 * kt + 2 * st + 1) * 1024);
         }
-        bsc[slot][0] = bs0[kt * 64];
-        bsc[slot][1] = bs1[kt * 64];
       };
 
       f32x16_t acc[NRB][2];
@@ -239,7 +250,9 @@ __global__ __launch_bounds__(NTHR, 1) void fwdq_kernel(QParams p) {
       auto compute = [&](int slot) {
         const uint8_t* a_s = ring + slot * SLOT + frag_lane;
         const uint8_t* a_sc = ring + slot * SLOT + TM * BKQ + (lane & 31) * 4 + 2 * khalf;
-        const uint32_t sb0 = bsc[slot][0], sb1 = bsc[slot][1];
+        const uint8_t* bsl = ring + slot * SLOT + TM * BKQ + SC_A + 512 * wave + 2 * lane;
+        const uint32_t sb0 = *reinterpret_cast<const uint16_t*>(bsl);
+        const uint32_t sb1 = *reinterpret_cast<const uint16_t*>(bsl + 256);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           const int c0 = ((4 * s + khalf) ^ s7) << 4;
@@ -508,8 +521,9 @@ __global__ __launch_bounds__(256) void mxq_weights_kernel(const bf16_t* __restri
 }
 
 typedef void (*fwdq_fn)(QParams);
-// Tile heights 32 .. 128 (a 256-row tile does not fit the register file
-// without spills, whose memory traffic would upset the per-slab wait counts).
+// Tile heights 32 .. 256 for gate/up, 32 .. 128 for down (its 256-row tile
+// does not fit the register file without spills, whose memory traffic in
+// flight would upset the per-slab wait counts).
 fwdq_fn pick_q(int epi, int tm, int* per_cu) {
   *per_cu = tm <= 64 ? 2 : 1;
   if (epi == Q_SWIGLU) {
@@ -517,6 +531,7 @@ fwdq_fn pick_q(int epi, int tm, int* per_cu) {
       case 32: return fwdq_kernel<Q_SWIGLU, 32>;
       case 64: return fwdq_kernel<Q_SWIGLU, 64>;
       case 128: return fwdq_kernel<Q_SWIGLU, 128>;
+      case 256: return fwdq_kernel<Q_SWIGLU, 256>;
     }
   } else {
     switch (tm) {

@@ -78,14 +78,15 @@ hipError_t launch_lb_coef(const int32_t* counts, int Tn, int N, int E, int K, in
 // Dispatch: per-expert counts, offsets, canonical permutation and its inverse.
 // Scratch: dispatch_scratch_bytes(T, E, N).  Also writes the per-expert
 // row-tile prefixes tile_off[N+1] and tile_off2[N+1] for the grouped GEMMs
-// (tile heights bm and bm2), if tile_exp is not NULL the expert of each of
-// the tile_off2[N] bm2-row tiles, and if sched is not NULL zeroes its
-// kSchedInts tile counters (for the packed-weight GEMMs of the same call).
+// (tile heights bm and bm2), if tile_exp / tile_exp1 are not NULL the
+// expert of each of the tile_off2[N] bm2-row / tile_off[N] bm-row tiles,
+// and if sched is not NULL zeroes its kSchedInts tile counters (for the
+// packed-weight GEMMs of the same call).
 size_t dispatch_scratch_bytes(int64_t Tn, int64_t E, int64_t N);
 hipError_t launch_dispatch(const int32_t* topk_idx, int Tn, int E, int N, int K, int bm, int bm2,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                            int32_t* tile_off, int32_t* tile_off2, int32_t* tile_exp,
-                           int32_t* sched, void* scratch, hipStream_t s);
+                           int32_t* tile_exp1, int32_t* sched, void* scratch, hipStream_t s);
 constexpr int kSchedInts = 16;  // 8 XCD counters for gate/up, 8 for down
 
 // FFN picks per token (budget-control telemetry): hist[K+1] and moments
