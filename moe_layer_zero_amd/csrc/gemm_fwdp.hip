@@ -113,7 +113,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
   constexpr int OUTN = EPI == P_SWIGLU ? 128 : 256;  // output columns per tile
   const int NT = p.ncols / OUTN;
   const int64_t total = static_cast<int64_t>(p.mt_off[p.N]) * NT;
@@ -126,11 +126,15 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   // finish together.  Tile n of XCD x is (n / C) * 8C + x C + n % C.
   const int xcd = blockIdx.x % 8;
   const int C = G / 8;
-  int32_t* const claim = p.sched + xcd;
-  auto tile_of = [&](int n) -> int64_t {
-    return static_cast<int64_t>(n / C) * 8 * C + xcd * C + n % C;
+  // When its own XCD's tiles are all claimed, a workgroup goes on with the
+  // next XCD's counter, and so on round the 8: the XCDs finish together
+  // instead of waiting for the one that drew the most work.
+  int cx = xcd;
+  int hops = 0;
+  auto tile_of = [&](int x, int n) -> int64_t {
+    return static_cast<int64_t>(n / C) * 8 * C + x * C + n % C;
   };
-  if (tid == 0) s_claim[0] = atomicAdd(claim, 1);
+  if (tid == 0) s_claim[0] = atomicAdd(p.sched + cx, 1);
   __syncthreads();
   int cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
   const int nk = p.K / BK;
@@ -148,10 +152,20 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   const int khalf = lane >> 5;
   const int frag_lane = (lane & 31) * BK;
 
-  for (int64_t L = tile_of(cur_n); L < total; L = tile_of(cur_n)) {
+  for (;;) {
+    const int64_t L = tile_of(cx, cur_n);
+    if (L >= total) {
+      if (++hops == 8) break;
+      cx = (cx + 1) & 7;
+      __syncthreads();  // every thread has read the last claim
+      if (tid == 0) s_claim[0] = atomicAdd(p.sched + cx, 1);
+      __syncthreads();
+      cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
+      continue;
+    }
     // claim the next tile now; its index is published in the epilogue
     int32_t next_n = 0;
-    if (tid == 0) next_n = atomicAdd(claim, 1);
+    if (tid == 0) next_n = atomicAdd(p.sched + cx, 1);
     // ---- which expert, row tile and column tile
     const int lmt = static_cast<int>(L / NT);
     const int e = p.tile_exp[lmt];

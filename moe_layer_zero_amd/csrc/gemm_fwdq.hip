@@ -133,11 +133,15 @@ __global__ __launch_bounds__(NTHR, 1) void fwdq_kernel(QParams p) {
   const int G = gridDim.x;
   const int xcd = blockIdx.x % 8;
   const int C = G / 8;
-  int32_t* const claim = p.sched + xcd;
-  auto tile_of = [&](int n) -> int64_t {
-    return static_cast<int64_t>(n / C) * 8 * C + xcd * C + n % C;
+  // When its own XCD's tiles are all claimed, a workgroup goes on with the
+  // next XCD's counter, and so on round the 8: the XCDs finish together
+  // instead of waiting for the one that drew the most work.
+  int cx = xcd;
+  int hops = 0;
+  auto tile_of = [&](int x, int n) -> int64_t {
+    return static_cast<int64_t>(n / C) * 8 * C + x * C + n % C;
   };
-  if (tid == 0) s_claim[0] = atomicAdd(claim, 1);
+  if (tid == 0) s_claim[0] = atomicAdd(p.sched + cx, 1);
   __syncthreads();
   int cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
   const int nk = p.K / BKQ;
@@ -152,9 +156,20 @@ __global__ __launch_bounds__(NTHR, 1) void fwdq_kernel(QParams p) {
   const int khalf = lane >> 5;
   const int frag_lane = (lane & 31) * BKQ;
 
-  for (int64_t L = tile_of(cur_n); L < total; L = tile_of(cur_n)) {
+  for (;;) {
+    const int64_t L = tile_of(cx, cur_n);
+    if (L >= total) {
+      if (++hops == 8) break;
+      cx = (cx + 1) & 7;
+      __syncthreads();  // every thread has read the last claim
+      if (tid == 0) s_claim[0] = atomicAdd(p.sched + cx, 1);
+      __syncthreads();
+      cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
+      continue;
+    }
+    // claim the next tile now; its index is published in the epilogue
     int32_t next_n = 0;
-    if (tid == 0) next_n = atomicAdd(claim, 1);
+    if (tid == 0) next_n = atomicAdd(p.sched + cx, 1);
     const int lmt = static_cast<int>(L / NT);
     const int e = p.tile_exp[lmt];
     const int mte = p.mt_off[e + 1] - p.mt_off[e];
