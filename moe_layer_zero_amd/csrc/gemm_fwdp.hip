@@ -71,7 +71,13 @@ struct PParams {
   bf16_t* C;                // h [P][I] or y [P][d]
 };
 
-__device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
+// silu(a) = a / (1 + e^-a) with the hardware reciprocal (about 1 ulp) in
+// place of an IEEE division: the result is rounded to bf16 (or quantized to
+// FP8) right after, and the division's ten-instruction sequence per element
+// is the larger part of the gate/up epilogue.
+__device__ __forceinline__ float silu_f(float a) {
+  return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+}
 
 // fp32 -> bf16, round to nearest even (NaN stays NaN), one conversion
 // instruction per value, for the down projection's epilogue.  Written as an
