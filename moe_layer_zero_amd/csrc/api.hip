@@ -267,7 +267,29 @@ int64_t fwd_ws_bytes(const zc_moe_desc* d) {
 struct BwdWs {
   int32_t* tile_off;
   float *gs, *dg, *dl, *dadu, *dxp, *dxr, *rdw, *lbc;
+  // packed-weight backward (use_bwdp): tile prefix and experts, counters,
+  // transposed packed W_d, W_g, W_u, exact bf16 hi/lo pairs of da and du
+  int32_t *mt2, *texp2, *sched;
+  bf16_t *wdt, *wgt, *wut, *hilo;
 };
+// The backward's dh and expert-dx GEMMs run on transposed packed weights
+// (packed into the workspace by each call) for bf16 layers with d and I
+// multiples of 256 whose dout and hi/lo byte offsets fit 32 bits.
+bool use_bwdp(const zc_moe_desc* d) {
+  if (d->dtype != ZC_BF16 || d->N == 0 || d->d % 256 || d->I % 256) return false;
+  const int64_t rows = d->T * d->K;
+  return d->T * d->d * 2 < (int64_t(1) << 32) && rows * 4 * d->I * 2 < (int64_t(1) << 32);
+}
+int bwdp_rows_per_tile(const zc_moe_desc* d) {
+  const int tm = zc::fwdp_rows_per_tile(d->T * d->K / d->N);
+  return tm > zc::kGemmBM ? zc::kGemmBM : tm;
+}
+int64_t bwdp_bytes(const zc_moe_desc* d) {
+  if (!use_bwdp(d)) return 0;
+  const int64_t wbytes = d->N * d->I * d->d * 2;
+  return a256(4 * (d->N + 1)) + a256(4 * max_tiles2(d)) + a256(4 * zc::kSchedInts) +
+         3 * a256(wbytes) + a256(d->T * d->K * 4 * d->I * 2);
+}
 // fp32 partials of the router weight gradient (token chunks), 0 when unsplit
 int64_t rdw_bytes(const zc_moe_desc* d) {
   const int64_t E = d->N + d->Z;
@@ -278,7 +300,7 @@ int64_t bwd_ws_bytes(const zc_moe_desc* d) {
   const int64_t rows = d->T * d->K, E = d->N + d->Z;
   return a256(4 * (d->N + 1)) + a256(4 * rows) + a256(4 * d->T * d->K) +
          a256(4 * d->T * ldl_of(E)) + a256(4 * rows * 2 * d->I) + a256(4 * rows * d->d) +
-         a256(4 * d->T * d->d) + a256(rdw_bytes(d)) + a256(4 * E);
+         a256(4 * d->T * d->d) + a256(rdw_bytes(d)) + a256(4 * E) + bwdp_bytes(d);
 }
 BwdWs carve_bwd(char* p, const zc_moe_desc* d) {
   const int64_t rows = d->T * d->K, E = d->N + d->Z;
@@ -298,6 +320,23 @@ BwdWs carve_bwd(char* p, const zc_moe_desc* d) {
   w.dxr = take(4 * d->T * d->d);
   w.rdw = rdw_bytes(d) > 0 ? take(rdw_bytes(d)) : nullptr;
   w.lbc = take(4 * E);
+  w.mt2 = w.texp2 = w.sched = nullptr;
+  w.wdt = w.wgt = w.wut = w.hilo = nullptr;
+  if (use_bwdp(d)) {
+    auto takeb = [&p](int64_t bytes) {
+      char* q = p;
+      p += a256(bytes);
+      return q;
+    };
+    const int64_t wbytes = d->N * d->I * d->d * 2;
+    w.mt2 = reinterpret_cast<int32_t*>(takeb(4 * (d->N + 1)));
+    w.texp2 = reinterpret_cast<int32_t*>(takeb(4 * max_tiles2(d)));
+    w.sched = reinterpret_cast<int32_t*>(takeb(4 * zc::kSchedInts));
+    w.wdt = reinterpret_cast<bf16_t*>(takeb(wbytes));
+    w.wgt = reinterpret_cast<bf16_t*>(takeb(wbytes));
+    w.wut = reinterpret_cast<bf16_t*>(takeb(wbytes));
+    w.hilo = reinterpret_cast<bf16_t*>(takeb(rows * 4 * d->I * 2));
+  }
   return w;
 }
 
@@ -484,9 +523,22 @@ zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg
   BwdWs w = carve_bwd(ws, d);
   Saved sv = carve_saved(const_cast<char*>(static_cast<const char*>(saved)), d);
   const T* y = static_cast<const T*>(sv.y);
-  if (N > 0)
-    ZC_LAUNCH(ZC_PH_TILE_OFFSETS, zc::launch_tile_offsets(r->offsets, N, zc::kGemmBM, w.tile_off, s),
-              "tile offsets");
+  const bool bwdp = std::is_same<T, bf16_t>::value && use_bwdp(d);
+  const int tmb = bwdp ? bwdp_rows_per_tile(d) : 0;
+  if (N > 0) {
+    if (bwdp) {
+      ZC_LAUNCH(ZC_PH_TILE_OFFSETS,
+                zc::launch_tile_offsets2(r->offsets, N, zc::kGemmBM, w.tile_off, tmb, w.mt2,
+                                         w.texp2, w.sched, s),
+                "tile offsets");
+      ZC_LAUNCH(ZC_PH_BWD_PACK,
+                zc::launch_pack_weights_t(reinterpret_cast<const bf16_t*>(wd), w.wdt, N, dd, I, s),
+                "transposed weight packing launch");
+    } else {
+      ZC_LAUNCH(ZC_PH_TILE_OFFSETS,
+                zc::launch_tile_offsets(r->offsets, N, zc::kGemmBM, w.tile_off, s), "tile offsets");
+    }
+  }
   if (lb)
     ZC_LAUNCH(ZC_PH_LB_COEF,
               zc::launch_lb_coef(r->counts, Tn, N, E, K, static_cast<int>(lb->D), lb->K_e,
@@ -498,7 +550,13 @@ zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg
                                       lb ? w.lbc : nullptr, w.gs, w.dg, w.dl, ldl, s),
             "combine backward launch");
   if (N > 0) {
-    if (Tn > 0)
+    if (Tn > 0 && bwdp)
+      ZC_LAUNCH(ZC_PH_BWD_DOWN_DH,
+                zc::launch_bwdp_dh(reinterpret_cast<const bf16_t*>(dout), d->T * d->d, w.wdt,
+                                   r->offsets, r->perm, w.mt2, w.texp2, w.sched, tmb, N, I, dd, K,
+                                   w.gs, sv.a, sv.u, w.dadu, w.hilo, cu, s),
+                "down backward (dh) launch");
+    else if (Tn > 0)
       ZC_LAUNCH(ZC_PH_BWD_DOWN_DH,
                 zc::launch_bwd_down_dh<T>(dout, r->perm, K, w.gs, wd, sv.a, sv.u, r->offsets,
                                           w.tile_off, N, I, dd, rows, w.dadu, cu, s),
@@ -507,11 +565,23 @@ zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg
               zc::launch_bwd_down_dw<T>(dout, r->perm, K, sv.h, w.gs, r->offsets, N, I, dd, dwd, cu,
                                         s),
               "down weight-gradient launch");
-    if (Tn > 0)
+    if (Tn > 0 && bwdp) {
+      ZC_LAUNCH(ZC_PH_BWD_PACK,
+                zc::launch_pack_weights_t(reinterpret_cast<const bf16_t*>(wg), w.wgt, N, I, dd, s),
+                "transposed weight packing launch");
+      ZC_LAUNCH(ZC_PH_BWD_PACK,
+                zc::launch_pack_weights_t(reinterpret_cast<const bf16_t*>(wu), w.wut, N, I, dd, s),
+                "transposed weight packing launch");
+      ZC_LAUNCH(ZC_PH_BWD_GATE_UP_DX,
+                zc::launch_bwdp_dx(w.hilo, rows * 4 * d->I, w.wgt, w.wut, r->offsets, w.mt2,
+                                   w.texp2, w.sched + 8, tmb, N, I, dd, w.dxp, cu, s),
+                "gate/up backward (dx) launch");
+    } else if (Tn > 0) {
       ZC_LAUNCH(ZC_PH_BWD_GATE_UP_DX,
                 zc::launch_bwd_gateup_dx<T>(w.dadu, wg, wu, r->offsets, w.tile_off, N, I, dd, rows,
                                             w.dxp, cu, s),
                 "gate/up backward (dx) launch");
+    }
     ZC_LAUNCH(ZC_PH_BWD_GATE_UP_DW,
               zc::launch_bwd_gateup_dw<T>(w.dadu, x, r->offsets, r->perm, N, I, dd, K, dwg, dwu, cu,
                                           s),
@@ -799,7 +869,7 @@ const char* zc_moe_phase_name(int phase) {
       "router_gemm", "topk", "dispatch", "gate_up_gemm", "down_gemm", "combine",
       "bwd_combine", "bwd_down_dh", "bwd_down_dw", "bwd_gate_up_dx", "bwd_gate_up_dw",
       "bwd_router_dw", "bwd_router_dx", "bwd_dx_gather", "bias_update", "tile_offsets",
-      "lb_loss", "lb_coef", "route_stats", "accumulate_counts", "quantize"};
+      "lb_loss", "lb_coef", "route_stats", "accumulate_counts", "quantize", "bwd_pack"};
   return (phase >= 0 && phase < ZC_NUM_PHASES) ? names[phase] : "";
 }
 

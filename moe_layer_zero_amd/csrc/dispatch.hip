@@ -151,21 +151,39 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
   }
 }
 
+// Row-tile prefixes from offsets alone: tile_off for bm-row tiles and, if
+// tile_off2 is set, tile_off2 for bm2-row tiles with the expert of each of
+// those tiles (tile_exp2); zeroes the kSchedInts counters of sched if set.
 __global__ __launch_bounds__(1024) void tile_off_kernel(const int32_t* __restrict__ offsets, int N,
-                                                       int bm, int32_t* tile_off) {
+                                                       int bm, int32_t* tile_off, int bm2,
+                                                       int32_t* tile_off2, int32_t* tile_exp2,
+                                                       int32_t* sched) {
   __shared__ int32_t s_til[1024];
+  __shared__ int32_t s_til2[1024];
   const int e = threadIdx.x;
-  const int32_t w = e < N ? (offsets[e + 1] - offsets[e] + bm - 1) / bm : 0;
+  const int32_t rows = e < N ? offsets[e + 1] - offsets[e] : 0;
+  const int32_t w = (rows + bm - 1) / bm;
+  const int32_t w2 = tile_off2 ? (rows + bm2 - 1) / bm2 : 0;
   s_til[e] = w;
+  s_til2[e] = w2;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
     const int32_t c = e >= o ? s_til[e - o] : 0;
+    const int32_t c2 = e >= o ? s_til2[e - o] : 0;
     __syncthreads();
     s_til[e] += c;
+    s_til2[e] += c2;
     __syncthreads();
   }
   if (e < N) tile_off[e] = s_til[e] - w;
   if (e == 0) tile_off[N] = N > 0 ? s_til[N - 1] : 0;
+  if (tile_off2) {
+    if (e < N) tile_off2[e] = s_til2[e] - w2;
+    if (e == 0) tile_off2[N] = N > 0 ? s_til2[N - 1] : 0;
+    if (e < N)
+      for (int32_t t = s_til2[e] - w2; t < s_til2[e]; ++t) tile_exp2[t] = e;
+  }
+  if (sched && e < kSchedInts) sched[e] = 0;
 }
 
 
@@ -261,7 +279,16 @@ hipError_t launch_accumulate_counts(const int32_t* counts, int E, int32_t* acc, 
 
 hipError_t launch_tile_offsets(const int32_t* offsets, int N, int bm, int32_t* tile_off,
                                hipStream_t s) {
-  hipLaunchKernelGGL(tile_off_kernel, dim3(1), dim3(1024), 0, s, offsets, N, bm, tile_off);
+  hipLaunchKernelGGL(tile_off_kernel, dim3(1), dim3(1024), 0, s, offsets, N, bm, tile_off, bm,
+                     nullptr, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_offsets2(const int32_t* offsets, int N, int bm, int32_t* tile_off, int bm2,
+                                int32_t* tile_off2, int32_t* tile_exp2, int32_t* sched,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(tile_off_kernel, dim3(1), dim3(1024), 0, s, offsets, N, bm, tile_off, bm2,
+                     tile_off2, tile_exp2, sched);
   return hipGetLastError();
 }
 

@@ -49,7 +49,11 @@ constexpr int NST = 4;      // LDS ring slots
 constexpr int NTHR = 256;
 constexpr int GMV = 8;      // row tiles per group inside an expert
 
-enum { P_SWIGLU = 0, P_STORE = 1 };
+// P_SWIGLU: gate/up with SwiGLU; P_STORE: down projection (bf16 y);
+// P_DSWIGLU: backward dh = g * (dout W_d) followed by the SwiGLU backward
+// (da, du in fp32 and as exact bf16 hi/lo pairs); P_DX: backward expert dx
+// = [da_hi | da_lo | du_hi | du_lo] [W_g; W_g; W_u; W_u] in fp32.
+enum { P_SWIGLU = 0, P_STORE = 1, P_DSWIGLU = 2, P_DX = 3 };
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -69,6 +73,14 @@ struct PParams {
   const bf16_t* B;          // packed W_g or W_d
   const bf16_t* B2;         // packed W_u (gate/up)
   bf16_t* C;                // h [P][I] or y [P][d]
+  // backward variants
+  const float* gs;          // P_DSWIGLU: out_scale * gate of each row (dispatch order)
+  const float* sa;          // P_DSWIGLU: saved a, u [P][ncols] (fp32)
+  const float* su;
+  float* dadu;              // P_DSWIGLU: da, du [P][2 ncols] (fp32)
+  bf16_t* hilo;             // P_DSWIGLU: da_hi, da_lo, du_hi, du_lo [P][4 ncols]
+  float* Cf;                // P_DX: expert dx [P][ncols] (fp32)
+  int kseg;                 // P_DX: slabs per K segment (I / 64)
 };
 
 // silu(a) = a / (1 + e^-a) with the hardware reciprocal (about 1 ulp) in
@@ -121,6 +133,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
   constexpr int OUTN = EPI == P_SWIGLU ? 128 : 256;  // output columns per tile
+  constexpr bool GATHER = EPI == P_SWIGLU || EPI == P_DSWIGLU;  // A rows are token rows
   const int NT = p.ncols / OUTN;
   const int64_t total = static_cast<int64_t>(p.mt_off[p.N]) * NT;
   const int G = gridDim.x;
@@ -196,17 +209,25 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
       const int chunk = (lane & 7) ^ ((4 * b + (lane >> 4)) & 7);
       if (row < mcount) {
         const int gm = m0 + row;
-        const int src = EPI == P_SWIGLU ? p.perm[gm] / p.kdiv : gm;
+        const int src = GATHER ? p.perm[gm] / p.kdiv : gm;
         aoff[i] = (static_cast<uint32_t>(src) * static_cast<uint32_t>(p.K) + chunk * 8) * 2u;
       } else {
         aoff[i] = p.a_bytes;  // out of range: the load returns zeros, reads nothing
       }
     }
-    // ---- packed B: this wave's two column groups of 32
-    const int64_t mat = static_cast<int64_t>(p.ncols) * p.K;
+    // ---- packed B: this wave's two column groups of 32 (P_DX: of the
+    // segment the slab falls in, see issue)
+    const int64_t mat = static_cast<int64_t>(p.ncols) * (EPI == P_DX ? p.K / 4 : p.K);
     const bf16_t* b0;
     const bf16_t* b1;
-    if constexpr (EPI == P_SWIGLU) {
+    const bf16_t* bu = nullptr;  // P_DX: the W_u segments
+    const int kbs = EPI == P_DX ? kblk / 4 : kblk;  // packed blocks per 32 columns and matrix
+    if constexpr (EPI == P_DX) {
+      const int g = n0 / 32 + 2 * wave;
+      b0 = p.B + e * mat + static_cast<int64_t>(g) * kbs * 512 + lane * 8;
+      b1 = b0 + static_cast<int64_t>(kbs) * 512;
+      bu = p.B2 + e * mat + static_cast<int64_t>(g) * kbs * 512 + lane * 8;
+    } else if constexpr (EPI == P_SWIGLU) {
       const int g = n0 / 32 + wave;
       b0 = p.B + e * mat + static_cast<int64_t>(g) * kblk * 512 + lane * 8;
       b1 = p.B2 + e * mat + static_cast<int64_t>(g) * kblk * 512 + lane * 8;
@@ -231,10 +252,23 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
           lds_void* dst = (lds_void*)(ring + slot * SLOT + (RB * wave + i) * 8 * BK);
           lds_dma16(arsrc, dst, aoff[i], kt * BK * 2);
         }
+        if constexpr (EPI == P_DX) {
+          // K = [da_hi | da_lo | du_hi | du_lo]: segments 0, 1 multiply W_g,
+          // 2, 3 multiply W_u
+          const int seg = kt / p.kseg;
+          const int ks = kt - seg * p.kseg;
+          const bf16_t* c0 = seg < 2 ? b0 : bu;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          bf[0][t] = *reinterpret_cast<const bf16x8_t*>(b0 + (4 * kt + t) * 512);
-          bf[1][t] = *reinterpret_cast<const bf16x8_t*>(b1 + (4 * kt + t) * 512);
+          for (int t = 0; t < 4; ++t) {
+            bf[0][t] = *reinterpret_cast<const bf16x8_t*>(c0 + (4 * ks + t) * 512);
+            bf[1][t] = *reinterpret_cast<const bf16x8_t*>(c0 + (kbs + 4 * ks + t) * 512);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            bf[0][t] = *reinterpret_cast<const bf16x8_t*>(b0 + (4 * kt + t) * 512);
+            bf[1][t] = *reinterpret_cast<const bf16x8_t*>(b1 + (4 * kt + t) * 512);
+          }
         }
       };
 
@@ -343,14 +377,57 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
       __builtin_amdgcn_sched_barrier(0);
 
       // ---- epilogue: lane holds column lane%32 of its column group and rows
-      // 32 rb + 8 (v/4) + 4 (lane/32) + v%4.  The bf16 tile is staged in the
-      // ring (free once every wave has passed the barrier below; TM x OUTN
-      // bf16 fit in its 4 TM x 64), then written out with 16-byte
-      // row-contiguous stores; the last barrier keeps the next tile's loads
-      // from refilling the ring before the staging is read.
+      // 32 rb + 8 (v/4) + 4 (lane/32) + v%4.
+      const int rbase = 4 * khalf;
+      if constexpr (EPI == P_DSWIGLU || EPI == P_DX) {
+        // fp32 results straight from the accumulators: each store covers 32
+        // consecutive columns (128 bytes) of a row
+        const int I = p.ncols;
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int rl = rbase + 32 * rb + 8 * (v >> 2) + (v & 3);
+            if (rl < mcount) {
+              const int64_t gm = m0 + rl;
+#pragma unroll
+              for (int cg = 0; cg < 2; ++cg) {
+                const int n = n0 + 64 * wave + 32 * cg + (lane & 31);
+                if constexpr (EPI == P_DX) {
+                  p.Cf[gm * I + n] = acc[rb][cg][v];
+                } else {
+                  // dh = g dout W_d; a, u saved by the forward;
+                  // da = dh u silu'(a), du = dh silu(a), silu' = s (1 + a (1 - s))
+                  const float dh = acc[rb][cg][v] * p.gs[gm];
+                  const float a = p.sa[gm * I + n];
+                  const float u = p.su[gm * I + n];
+                  const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+                  const float da = dh * u * (sg * (1.0f + a * (1.0f - sg)));
+                  const float du = dh * (a * sg);
+                  p.dadu[gm * 2 * I + n] = da;
+                  p.dadu[gm * 2 * I + I + n] = du;
+                  const bf16_t ah = f2bf(da), uh = f2bf(du);
+                  bf16_t* hl = p.hilo + gm * 4 * I + n;
+                  hl[0] = ah;
+                  hl[I] = f2bf(da - bf2f(ah));
+                  hl[2 * I] = uh;
+                  hl[3 * I] = f2bf(du - bf2f(uh));
+                }
+              }
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (tid == 0) s_claim[0] = next_n;
+        __syncthreads();  // every wave done reading the ring before the next tile's loads
+        return;
+      }
+      // The bf16 tile is staged in the ring (free once every wave has passed
+      // the barrier below; TM x OUTN bf16 fit in its 4 TM x 64), then written
+      // out with 16-byte row-contiguous stores; the last barrier keeps the
+      // next tile's loads from refilling the ring before the staging is read.
       __syncthreads();  // every wave done reading the ring
       bf16_t* st = ring;  // OUTN columns per row
-      const int rbase = 4 * khalf;
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
@@ -412,11 +489,66 @@ __global__ __launch_bounds__(256) void pack_kernel(const bf16_t* __restrict__ sr
   }
 }
 
+// Packed layout of the transposes of nmat row-major [R][C] matrices (each
+// packed as the [C][R] matrix it transposes to): 64 x 64 tiles through LDS,
+// read along rows, written as 16-byte packed chunks (8 consecutive source
+// rows of one source column).
+__global__ __launch_bounds__(256) void pack_t_kernel(const bf16_t* __restrict__ src,
+                                                     bf16_t* __restrict__ dst, int R, int C) {
+  __shared__ bf16_t t[64][64 + 8];
+  const int64_t m = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const bf16_t* sm = src + m * static_cast<int64_t>(R) * C;
+  for (int q = threadIdx.x; q < 64 * 8; q += 256) {
+    const int r = q >> 3, cc = (q & 7) * 8;
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(sm + static_cast<int64_t>(r0 + r) * C + c0 + cc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      t[r][cc + 2 * j] = static_cast<bf16_t>(w[j] & 0xffffu);
+      t[r][cc + 2 * j + 1] = static_cast<bf16_t>(w[j] >> 16);
+    }
+  }
+  __syncthreads();
+  // transposed matrix: R' = C rows, C' = R reduction steps; element (r', c')
+  // at ((r'/32) (C'/16) + c'/16) 512 + (r'%32 + 32 ((c'/8)%2)) 8 + c'%8
+  bf16_t* dm = dst + m * static_cast<int64_t>(R) * C;
+  const int kb = R / 16;
+  for (int q = threadIdx.x; q < 64 * 8; q += 256) {
+    const int rp = q >> 3, cg = (q & 7) * 8;  // r' = c0 + rp, c' = r0 + cg .. + 7
+    const int R1 = c0 + rp, C1 = r0 + cg;
+    u32x4_t w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = static_cast<uint32_t>(t[cg + 2 * j][rp]) |
+             (static_cast<uint32_t>(t[cg + 2 * j + 1][rp]) << 16);
+    const int64_t o = (static_cast<int64_t>(R1 / 32) * kb + C1 / 16) * 512 +
+                      (R1 % 32 + 32 * ((C1 / 8) % 2)) * 8;
+    *reinterpret_cast<u32x4_t*>(dm + o) = w;
+  }
+}
+
 // Kernel of each (epilogue, tile height); tiles of up to 64 rows leave room
 // for two workgroups per CU.
+// The backward variants stop at 128-row tiles (a 256-row tile would spill).
 typedef void (*fwdp_fn)(PParams);
 fwdp_fn pick_kernel(int epi, int tm, int* per_cu) {
   *per_cu = tm <= 64 ? 2 : 1;
+  if (epi == P_DSWIGLU) {
+    switch (tm) {
+      case 32: return fwdp_kernel<P_DSWIGLU, 32, true>;
+      case 64: return fwdp_kernel<P_DSWIGLU, 64, true>;
+      case 128: return fwdp_kernel<P_DSWIGLU, 128, true>;
+    }
+    return nullptr;
+  }
+  if (epi == P_DX) {
+    switch (tm) {
+      case 32: return fwdp_kernel<P_DX, 32, true>;
+      case 64: return fwdp_kernel<P_DX, 64, true>;
+      case 128: return fwdp_kernel<P_DX, 128, true>;
+    }
+    return nullptr;
+  }
   if (epi == P_SWIGLU) {
     switch (tm) {
       case 32: return fwdp_kernel<P_SWIGLU, 32, true>;
@@ -479,6 +611,39 @@ hipError_t launch_fwdp_down(const bf16_t* h, int64_t h_elems, const bf16_t* wd_p
   p.A = h; p.a_bytes = static_cast<uint32_t>(h_elems * 2);
   p.B = wd_p; p.C = y;
   return launch_tm(P_STORE, tm, p, cu, s);
+}
+
+hipError_t launch_pack_weights_t(const bf16_t* src, bf16_t* dst, int64_t nmat, int R, int C,
+                                 hipStream_t s) {
+  if (nmat == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_t_kernel, dim3(C / 64, R / 64, static_cast<unsigned>(nmat)), dim3(256), 0,
+                     s, src, dst, R, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwdp_dh(const bf16_t* dout, int64_t dout_elems, const bf16_t* wdt_p,
+                          const int32_t* offsets, const int32_t* perm, const int32_t* mt_off,
+                          const int32_t* tile_exp, int32_t* sched, int tm, int N, int I, int d,
+                          int K, const float* gs, const float* sa, const float* su, float* dadu,
+                          bf16_t* hilo, int cu, hipStream_t s) {
+  PParams p{};
+  p.N = N; p.ncols = I; p.K = d;
+  p.offsets = offsets; p.mt_off = mt_off; p.tile_exp = tile_exp; p.sched = sched;
+  p.A = dout; p.a_bytes = static_cast<uint32_t>(dout_elems * 2); p.perm = perm; p.kdiv = K;
+  p.B = wdt_p; p.gs = gs; p.sa = sa; p.su = su; p.dadu = dadu; p.hilo = hilo;
+  return launch_tm(P_DSWIGLU, tm, p, cu, s);
+}
+
+hipError_t launch_bwdp_dx(const bf16_t* hilo, int64_t hilo_elems, const bf16_t* wgt_p,
+                          const bf16_t* wut_p, const int32_t* offsets, const int32_t* mt_off,
+                          const int32_t* tile_exp, int32_t* sched, int tm, int N, int I, int d,
+                          float* dxp, int cu, hipStream_t s) {
+  PParams p{};
+  p.N = N; p.ncols = d; p.K = 4 * I; p.kseg = I / 64;
+  p.offsets = offsets; p.mt_off = mt_off; p.tile_exp = tile_exp; p.sched = sched;
+  p.A = hilo; p.a_bytes = static_cast<uint32_t>(hilo_elems * 2);
+  p.B = wgt_p; p.B2 = wut_p; p.Cf = dxp;
+  return launch_tm(P_DX, tm, p, cu, s);
 }
 
 hipError_t launch_pack_weights(const bf16_t* src, bf16_t* dst, int64_t nmat, int R, int C,

@@ -101,6 +101,11 @@ hipError_t launch_accumulate_counts(const int32_t* counts, int E, int32_t* acc, 
 // routing of its forward call).
 hipError_t launch_tile_offsets(const int32_t* offsets, int N, int bm, int32_t* tile_off,
                                hipStream_t s);
+// ... and also the bm2-row prefix with the expert of each of its tiles, and
+// zeroed tile counters (for the packed-weight backward GEMMs).
+hipError_t launch_tile_offsets2(const int32_t* offsets, int N, int bm, int32_t* tile_off, int bm2,
+                                int32_t* tile_off2, int32_t* tile_exp2, int32_t* sched,
+                                hipStream_t s);
 
 // Grouped / dense GEMMs (gemm.hip); the backward's fp32 intermediates enter
 // bf16 GEMMs as exact hi+lo bf16 pairs.
@@ -168,6 +173,22 @@ hipError_t launch_fwdp_down(const bf16_t* h, int64_t h_elems, const bf16_t* wd_p
 // nmat row-major [R][C] bf16 matrices -> packed layout (R % 32 == 0, C % 16 == 0).
 hipError_t launch_pack_weights(const bf16_t* src, bf16_t* dst, int64_t nmat, int R, int C,
                                hipStream_t s);
+// ... the packed layout of their transposes ([C][R] each; R, C multiples of 64).
+hipError_t launch_pack_weights_t(const bf16_t* src, bf16_t* dst, int64_t nmat, int R, int C,
+                                 hipStream_t s);
+// Backward expert GEMMs of bf16 layers on transposed packed weights (tile
+// bookkeeping as for the forward): dh = gs * (dout[tok] W_d) with the SwiGLU
+// backward in the epilogue -> dadu [P][2I] fp32 and hilo [P][4I] = exact
+// bf16 hi/lo pairs of da and du; expert dx = hilo [W_g;W_g;W_u;W_u] [P][d] fp32.
+hipError_t launch_bwdp_dh(const bf16_t* dout, int64_t dout_elems, const bf16_t* wdt_p,
+                          const int32_t* offsets, const int32_t* perm, const int32_t* mt_off,
+                          const int32_t* tile_exp, int32_t* sched, int tm, int N, int I, int d,
+                          int K, const float* gs, const float* sa, const float* su, float* dadu,
+                          bf16_t* hilo, int cu, hipStream_t s);
+hipError_t launch_bwdp_dx(const bf16_t* hilo, int64_t hilo_elems, const bf16_t* wgt_p,
+                          const bf16_t* wut_p, const int32_t* offsets, const int32_t* mt_off,
+                          const int32_t* tile_exp, int32_t* sched, int tm, int N, int I, int d,
+                          float* dxp, int cu, hipStream_t s);
 
 // MXFP8 expert GEMMs (gemm_fwdq.hip): E4M3 codes with one E8M0 scale per
 // 32 reduction steps.  Activation quantizer (rows x K bf16 -> codes and
