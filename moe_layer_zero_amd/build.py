@@ -20,7 +20,7 @@ OUT = os.path.join(HERE, "libzcmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["api.hip", "router.hip", "dispatch.hip", "gemm.hip", "gemm_fwd.hip", "gemm_fwdp.hip",
-           "gemm_fwdq.hip", "combine.hip", "pid.hip"]
+           "gemm_fwdq.hip", "gemm_dw.hip", "combine.hip", "pid.hip"]
 STRICT_FP = {"router.hip", "pid.hip"}
 
 COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

@@ -268,17 +268,21 @@ struct BwdWs {
   int32_t* tile_off;
   float *gs, *dg, *dl, *dadu, *dxp, *dxr, *rdw, *lbc;
   // packed-weight backward (use_bwdp): tile prefix and experts, counters,
-  // transposed packed W_d, W_g, W_u, exact bf16 hi/lo pairs of da and du
+  // transposed packed W_d, W_g, W_u, exact bf16 hi/lo pairs of da, du and
+  // g h, and x and dout rows in dispatch order
   int32_t *mt2, *texp2, *sched;
-  bf16_t *wdt, *wgt, *wut, *hilo;
+  bf16_t *wdt, *wgt, *wut, *hilo, *ghlo, *xd, *doutd;
 };
+constexpr int kBwdSched = 48;  // dh, dx, dW_d, dW_g, dW_u: 8 counters each
 // The backward's dh and expert-dx GEMMs run on transposed packed weights
-// (packed into the workspace by each call) for bf16 layers with d and I
-// multiples of 256 whose dout and hi/lo byte offsets fit 32 bits.
+// (packed into the workspace by each call), and its expert weight gradients
+// on operands gathered into dispatch order, for bf16 layers with d and I
+// multiples of 256 whose byte offsets into dout, x and the hi/lo pairs fit
+// 32 bits (the weight-gradient loads run up to 64 rows past an expert's).
 bool use_bwdp(const zc_moe_desc* d) {
   if (d->dtype != ZC_BF16 || d->N == 0 || d->d % 256 || d->I % 256) return false;
-  const int64_t rows = d->T * d->K;
-  return d->T * d->d * 2 < (int64_t(1) << 32) && rows * 4 * d->I * 2 < (int64_t(1) << 32);
+  const int64_t rows = d->T * d->K + 64, lim = int64_t(1) << 32;
+  return rows * d->d * 2 < lim && rows * 4 * d->I * 2 < lim;
 }
 int bwdp_rows_per_tile(const zc_moe_desc* d) {
   const int tm = zc::fwdp_rows_per_tile(d->T * d->K / d->N);
@@ -287,8 +291,10 @@ int bwdp_rows_per_tile(const zc_moe_desc* d) {
 int64_t bwdp_bytes(const zc_moe_desc* d) {
   if (!use_bwdp(d)) return 0;
   const int64_t wbytes = d->N * d->I * d->d * 2;
-  return a256(4 * (d->N + 1)) + a256(4 * max_tiles2(d)) + a256(4 * zc::kSchedInts) +
-         3 * a256(wbytes) + a256(d->T * d->K * 4 * d->I * 2);
+  const int64_t rows = d->T * d->K;
+  return a256(4 * (d->N + 1)) + a256(4 * max_tiles2(d)) + a256(4 * kBwdSched) +
+         3 * a256(wbytes) + a256(rows * 4 * d->I * 2) + a256(rows * 2 * d->I * 2) +
+         2 * a256(rows * d->d * 2);
 }
 // fp32 partials of the router weight gradient (token chunks), 0 when unsplit
 int64_t rdw_bytes(const zc_moe_desc* d) {
@@ -321,7 +327,7 @@ BwdWs carve_bwd(char* p, const zc_moe_desc* d) {
   w.rdw = rdw_bytes(d) > 0 ? take(rdw_bytes(d)) : nullptr;
   w.lbc = take(4 * E);
   w.mt2 = w.texp2 = w.sched = nullptr;
-  w.wdt = w.wgt = w.wut = w.hilo = nullptr;
+  w.wdt = w.wgt = w.wut = w.hilo = w.ghlo = w.xd = w.doutd = nullptr;
   if (use_bwdp(d)) {
     auto takeb = [&p](int64_t bytes) {
       char* q = p;
@@ -331,11 +337,14 @@ BwdWs carve_bwd(char* p, const zc_moe_desc* d) {
     const int64_t wbytes = d->N * d->I * d->d * 2;
     w.mt2 = reinterpret_cast<int32_t*>(takeb(4 * (d->N + 1)));
     w.texp2 = reinterpret_cast<int32_t*>(takeb(4 * max_tiles2(d)));
-    w.sched = reinterpret_cast<int32_t*>(takeb(4 * zc::kSchedInts));
+    w.sched = reinterpret_cast<int32_t*>(takeb(4 * kBwdSched));
     w.wdt = reinterpret_cast<bf16_t*>(takeb(wbytes));
     w.wgt = reinterpret_cast<bf16_t*>(takeb(wbytes));
     w.wut = reinterpret_cast<bf16_t*>(takeb(wbytes));
     w.hilo = reinterpret_cast<bf16_t*>(takeb(rows * 4 * d->I * 2));
+    w.ghlo = reinterpret_cast<bf16_t*>(takeb(rows * 2 * d->I * 2));
+    w.xd = reinterpret_cast<bf16_t*>(takeb(rows * d->d * 2));
+    w.doutd = reinterpret_cast<bf16_t*>(takeb(rows * d->d * 2));
   }
   return w;
 }
@@ -529,7 +538,7 @@ zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg
     if (bwdp) {
       ZC_LAUNCH(ZC_PH_TILE_OFFSETS,
                 zc::launch_tile_offsets2(r->offsets, N, zc::kGemmBM, w.tile_off, tmb, w.mt2,
-                                         w.texp2, w.sched, s),
+                                         w.texp2, w.sched, kBwdSched, s),
                 "tile offsets");
       ZC_LAUNCH(ZC_PH_BWD_PACK,
                 zc::launch_pack_weights_t(reinterpret_cast<const bf16_t*>(wd), w.wdt, N, dd, I, s),
@@ -550,21 +559,36 @@ zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg
                                       lb ? w.lbc : nullptr, w.gs, w.dg, w.dl, ldl, s),
             "combine backward launch");
   if (N > 0) {
-    if (Tn > 0 && bwdp)
+    if (Tn > 0 && bwdp) {
+      ZC_LAUNCH(ZC_PH_BWD_GATHER,
+                zc::launch_gather_rows(reinterpret_cast<const bf16_t*>(dout), r->perm, r->offsets,
+                                       N, K, dd, rows, w.doutd, s),
+                "row gather launch");
+      ZC_LAUNCH(ZC_PH_BWD_GATHER,
+                zc::launch_gather_rows(reinterpret_cast<const bf16_t*>(x), r->perm, r->offsets, N,
+                                       K, dd, rows, w.xd, s),
+                "row gather launch");
       ZC_LAUNCH(ZC_PH_BWD_DOWN_DH,
                 zc::launch_bwdp_dh(reinterpret_cast<const bf16_t*>(dout), d->T * d->d, w.wdt,
                                    r->offsets, r->perm, w.mt2, w.texp2, w.sched, tmb, N, I, dd, K,
-                                   w.gs, sv.a, sv.u, w.dadu, w.hilo, cu, s),
+                                   w.gs, sv.a, sv.u, sv.h, w.hilo, w.ghlo, cu, s),
                 "down backward (dh) launch");
-    else if (Tn > 0)
+    } else if (Tn > 0) {
       ZC_LAUNCH(ZC_PH_BWD_DOWN_DH,
                 zc::launch_bwd_down_dh<T>(dout, r->perm, K, w.gs, wd, sv.a, sv.u, r->offsets,
                                           w.tile_off, N, I, dd, rows, w.dadu, cu, s),
                 "down backward (dh) launch");
-    ZC_LAUNCH(ZC_PH_BWD_DOWN_DW,
-              zc::launch_bwd_down_dw<T>(dout, r->perm, K, sv.h, w.gs, r->offsets, N, I, dd, dwd, cu,
-                                        s),
-              "down weight-gradient launch");
+    }
+    if (bwdp)
+      ZC_LAUNCH(ZC_PH_BWD_DOWN_DW,
+                zc::launch_dw(false, N, dd, I, r->offsets, w.sched + 16, w.ghlo, w.ghlo + I, 2 * I,
+                              w.doutd, dd, rows, reinterpret_cast<bf16_t*>(dwd), cu, s),
+                "down weight-gradient launch");
+    else
+      ZC_LAUNCH(ZC_PH_BWD_DOWN_DW,
+                zc::launch_bwd_down_dw<T>(dout, r->perm, K, sv.h, w.gs, r->offsets, N, I, dd, dwd,
+                                          cu, s),
+                "down weight-gradient launch");
     if (Tn > 0 && bwdp) {
       ZC_LAUNCH(ZC_PH_BWD_PACK,
                 zc::launch_pack_weights_t(reinterpret_cast<const bf16_t*>(wg), w.wgt, N, I, dd, s),
@@ -582,10 +606,22 @@ zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg
                                             w.dxp, cu, s),
                 "gate/up backward (dx) launch");
     }
-    ZC_LAUNCH(ZC_PH_BWD_GATE_UP_DW,
-              zc::launch_bwd_gateup_dw<T>(w.dadu, x, r->offsets, r->perm, N, I, dd, K, dwg, dwu, cu,
-                                          s),
-              "gate/up weight-gradient launch");
+    if (bwdp) {
+      ZC_LAUNCH(ZC_PH_BWD_GATE_UP_DW,
+                zc::launch_dw(true, N, I, dd, r->offsets, w.sched + 24, w.hilo, w.hilo + I, 4 * I,
+                              w.xd, dd, rows, reinterpret_cast<bf16_t*>(dwg), cu, s),
+                "gate/up weight-gradient launch");
+      ZC_LAUNCH(ZC_PH_BWD_GATE_UP_DW,
+                zc::launch_dw(true, N, I, dd, r->offsets, w.sched + 32, w.hilo + 2 * I,
+                              w.hilo + 3 * I, 4 * I, w.xd, dd, rows, reinterpret_cast<bf16_t*>(dwu),
+                              cu, s),
+                "gate/up weight-gradient launch");
+    } else {
+      ZC_LAUNCH(ZC_PH_BWD_GATE_UP_DW,
+                zc::launch_bwd_gateup_dw<T>(w.dadu, x, r->offsets, r->perm, N, I, dd, K, dwg, dwu,
+                                            cu, s),
+                "gate/up weight-gradient launch");
+    }
   }
   ZC_LAUNCH(ZC_PH_BWD_ROUTER_DW, zc::launch_router_dw<T>(w.dl, ldl, x, Tn, E, dd, dwr, w.rdw, cu, s),
             "router weight-gradient launch");
@@ -869,7 +905,8 @@ const char* zc_moe_phase_name(int phase) {
       "router_gemm", "topk", "dispatch", "gate_up_gemm", "down_gemm", "combine",
       "bwd_combine", "bwd_down_dh", "bwd_down_dw", "bwd_gate_up_dx", "bwd_gate_up_dw",
       "bwd_router_dw", "bwd_router_dx", "bwd_dx_gather", "bias_update", "tile_offsets",
-      "lb_loss", "lb_coef", "route_stats", "accumulate_counts", "quantize", "bwd_pack"};
+      "lb_loss", "lb_coef", "route_stats", "accumulate_counts", "quantize", "bwd_pack",
+      "bwd_gather"};
   return (phase >= 0 && phase < ZC_NUM_PHASES) ? names[phase] : "";
 }
 

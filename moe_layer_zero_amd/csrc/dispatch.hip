@@ -153,11 +153,11 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
 
 // Row-tile prefixes from offsets alone: tile_off for bm-row tiles and, if
 // tile_off2 is set, tile_off2 for bm2-row tiles with the expert of each of
-// those tiles (tile_exp2); zeroes the kSchedInts counters of sched if set.
+// those tiles (tile_exp2); zeroes the nsched (<= 1024) counters of sched if set.
 __global__ __launch_bounds__(1024) void tile_off_kernel(const int32_t* __restrict__ offsets, int N,
                                                        int bm, int32_t* tile_off, int bm2,
                                                        int32_t* tile_off2, int32_t* tile_exp2,
-                                                       int32_t* sched) {
+                                                       int32_t* sched, int nsched) {
   __shared__ int32_t s_til[1024];
   __shared__ int32_t s_til2[1024];
   const int e = threadIdx.x;
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(1024) void tile_off_kernel(const int32_t* __restric
     if (e < N)
       for (int32_t t = s_til2[e] - w2; t < s_til2[e]; ++t) tile_exp2[t] = e;
   }
-  if (sched && e < kSchedInts) sched[e] = 0;
+  if (sched && e < nsched) sched[e] = 0;
 }
 
 
@@ -280,15 +280,15 @@ hipError_t launch_accumulate_counts(const int32_t* counts, int E, int32_t* acc, 
 hipError_t launch_tile_offsets(const int32_t* offsets, int N, int bm, int32_t* tile_off,
                                hipStream_t s) {
   hipLaunchKernelGGL(tile_off_kernel, dim3(1), dim3(1024), 0, s, offsets, N, bm, tile_off, bm,
-                     nullptr, nullptr, nullptr);
+                     nullptr, nullptr, nullptr, 0);
   return hipGetLastError();
 }
 
 hipError_t launch_tile_offsets2(const int32_t* offsets, int N, int bm, int32_t* tile_off, int bm2,
-                                int32_t* tile_off2, int32_t* tile_exp2, int32_t* sched,
+                                int32_t* tile_off2, int32_t* tile_exp2, int32_t* sched, int nsched,
                                 hipStream_t s) {
   hipLaunchKernelGGL(tile_off_kernel, dim3(1), dim3(1024), 0, s, offsets, N, bm, tile_off, bm2,
-                     tile_off2, tile_exp2, sched);
+                     tile_off2, tile_exp2, sched, nsched);
   return hipGetLastError();
 }
 

@@ -1,0 +1,309 @@
+// Weight gradients of the FFN experts on gfx950 matrix cores.
+//
+// "LongCat-Flash Technical Report", section 2.1: each FFN expert sees only
+// the tokens routed to it, so its weight gradient is a sum over its own
+// rows of the dispatch order:
+//   dW_g[e] = sum_p da_p^T x_p,  dW_u[e] = sum_p du_p^T x_p,
+//   dW_d[e] = sum_p dout_p^T (g_p h_p),
+// for p in offsets[e] .. offsets[e+1].  Generally, per expert,
+//   C_e[m][n] = sum_p A[p][m] B[p][n]
+// with both operands stored row by row (the reduction index p is the row).
+// The fp32 operand (da / du, or g h) comes as an exact bf16 pair
+// (hi, lo = bf16(v - hi)) and is contracted twice against its exact bf16
+// partner, so no value is rounded before the contraction.
+//
+// Tile: 256 x 256 outputs per 256-thread workgroup; wave w owns rows
+// 64w .. 64w+63 of the tile and all 256 columns (2 x 8 blocks of 32 x 32
+// fp32 accumulators).  Operand rows stream through LDS in slabs of 32 rows
+// x 256 columns (16 KB per operand), three slabs in flight, filled by
+// buffer_load ... lds.  The matrix cores want 8 consecutive reduction steps
+// per lane; ds_read_b64_tr_b16 gives each lane of a 16-lane group one
+// column of a 4-row x 16-column block (lane s of the group addresses row
+// s/4, columns 4(s%4) .. +3; measured on MI355X), so two such reads turn
+// the row-major slab into an MFMA operand without a transposed copy in
+// memory.  Inside a slab the 16-byte chunk c of row r is stored at chunk
+// c ^ 2(r & 3), which puts the four rows of a transposed read on different
+// banks.  Tiles are dealt to the XCDs like the forward GEMMs' (contiguous
+// chunks per XCD, claimed from per-XCD counters, then the other XCDs').
+#include "zc_common.h"
+
+namespace zc {
+namespace {
+
+constexpr int DK = 32;                 // rows per slab
+constexpr int DT = 256;                // tile edge
+constexpr int SLAB = DK * DT * 2;      // bytes of one operand slab (16 KB)
+constexpr int SLOT = 3 * SLAB;         // split hi, split lo, exact partner
+constexpr int NSL = 3;                 // slots (slabs in flight)
+constexpr int V = 12;                  // loads per wave per slab (3 operands x 4)
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+
+struct DParams {
+  int N;                    // experts
+  int M, Ncol;              // output [M][Ncol] per expert
+  const int32_t* offsets;   // [N+1] rows of each expert in dispatch order
+  int32_t* sched;           // [8] per-XCD tile counters, zero at launch
+  const bf16_t* X;          // split operand, hi part: rows [P][ldx]
+  const bf16_t* XL;         // split operand, lo part (same pitch)
+  int64_t ldx;
+  const bf16_t* Y;          // exact partner: rows [P][ldy]
+  int64_t ldy;
+  int64_t rows;             // rows of X and Y (range of the loads)
+  bf16_t* C;                // output per expert, [M][Ncol] row-major
+};
+
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16_t cvt_bf16(float f) {
+  uint32_t r;
+  asm volatile("v_cvt_pk_bf16_f32 %0, %1, 0" : "=v"(r) : "v"(f));
+  return static_cast<bf16_t>(r);
+}
+
+// One 32x32x16 operand: lane l gets column col0 + l % 32 of rows k0 + 8 (l / 32)
+// .. + 7 of a row-major 32 x 256 slab at `slab`.
+__device__ __forceinline__ bf16x8_t tr_operand(lds_u8* slab, int k0, int col0, int lane) {
+  const int s = lane & 15;
+  const int c = col0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);   // first column of the lane's read
+  const int kb = k0 + 8 * (lane >> 5) + (s >> 2);
+  s16x4_t q[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int k = kb + 4 * r;
+    const int a = k * (DT * 2) + (((c >> 3) ^ ((k & 3) << 1)) << 4) + (c & 7) * 2;
+    q[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(slab + a));
+  }
+  // whole-vector casts: a bit cast of a single vector element reads
+  // element 0 whatever the index with this compiler
+  const bf16x4_t lo = __builtin_bit_cast(bf16x4_t, q[0]);
+  const bf16x4_t hi = __builtin_bit_cast(bf16x4_t, q[1]);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// SA: the split operand is A (the output rows); otherwise it is B (the columns).
+template <bool SA>
+__global__ __launch_bounds__(256, 1) void dw_kernel(DParams p) {
+  __shared__ __align__(16) uint8_t ring[NSL * SLOT + 16];
+  int32_t* const s_claim = reinterpret_cast<int32_t*>(ring + NSL * SLOT);
+  lds_u8* const ring_lds = (lds_u8*)ring;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int MT = p.M / DT, NT = p.Ncol / DT;
+  const int64_t total = static_cast<int64_t>(p.N) * MT * NT;
+  const int G = gridDim.x;
+  const int C = G / 8;
+  int cx = blockIdx.x % 8;
+  int hops = 0;
+  auto tile_of = [&](int x, int n) -> int64_t {
+    return static_cast<int64_t>(n / C) * 8 * C + x * C + n % C;
+  };
+  // the claim of thread 0 on counter cx -> a tile, or -1 when all are taken
+  auto next_tile = [&](int32_t pre) -> int64_t {
+    __syncthreads();
+    if (tid == 0) s_claim[0] = pre;
+    __syncthreads();
+    int n = __builtin_amdgcn_readfirstlane(s_claim[0]);
+    for (;;) {
+      const int64_t L = tile_of(cx, n);
+      if (L < total) return L;
+      if (++hops == 8) return -1;
+      cx = (cx + 1) & 7;
+      __syncthreads();
+      if (tid == 0) s_claim[0] = atomicAdd(p.sched + cx, 1);
+      __syncthreads();
+      n = __builtin_amdgcn_readfirstlane(s_claim[0]);
+    }
+  };
+
+  // operand order in a slot: 0 = split hi, 1 = split lo, 2 = exact partner
+  for (;;) {
+    int32_t pre = 0;
+    if (tid == 0) pre = atomicAdd(p.sched + cx, 1);
+    const int64_t L = next_tile(pre);
+    if (L < 0) break;
+    const int e = static_cast<int>(L / (MT * NT));
+    const int rem = static_cast<int>(L - static_cast<int64_t>(e) * MT * NT);
+    const int m0 = (rem / NT) * DT, n0 = (rem % NT) * DT;
+    const int r0 = p.offsets[e], r1 = p.offsets[e + 1];
+    const int nslab = (r1 - r0 + DK - 1) / DK;
+    const int tail = (r1 - r0) - DK * (nslab - 1);   // rows of the last slab
+    // the expert's rows only: a load past them returns zeros and reads nothing
+    const uint32_t xbytes = static_cast<uint32_t>((r1 - r0) * p.ldx * 2);
+    const uint32_t ybytes = static_cast<uint32_t>((r1 - r0) * p.ldy * 2);
+    const int xcol = SA ? m0 : n0, ycol = SA ? n0 : m0;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t*>(p.X + r0 * p.ldx + xcol), (short)0, xbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rxl = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t*>(p.XL + r0 * p.ldx + xcol), (short)0, xbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t*>(p.Y + r0 * p.ldy + ycol), (short)0, ybytes, 0x00020000);
+    // lane's rows and source chunks: instruction i of wave w copies rows
+    // 8w + 2i + lane/32, chunk lane%32 of the slab from source chunk
+    // (lane%32) ^ 2(row & 3)
+    uint32_t xo[4], yo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 8 * wave + 2 * i + (lane >> 5);
+      const int ch = (lane & 31) ^ ((row & 3) << 1);
+      xo[i] = static_cast<uint32_t>(row * p.ldx * 2 + ch * 16);
+      yo[i] = static_cast<uint32_t>(row * p.ldy * 2 + ch * 16);
+    }
+    const uint32_t xstep = static_cast<uint32_t>(DK * p.ldx * 2);
+    const uint32_t ystep = static_cast<uint32_t>(DK * p.ldy * 2);
+    auto issue = [&](int kt, int slot) {
+      uint8_t* base = ring + slot * SLOT + (8 * wave) * (DT * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lds_dma16(rx, (lds_void*)(base + 0 * SLAB + 2 * i * DT * 2), xo[i] + kt * xstep);
+        lds_dma16(rxl, (lds_void*)(base + 1 * SLAB + 2 * i * DT * 2), xo[i] + kt * xstep);
+        lds_dma16(ry, (lds_void*)(base + 2 * SLAB + 2 * i * DT * 2), yo[i] + kt * ystep);
+      }
+    };
+
+    f32x16_t acc[2][8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    auto compute = [&](int slot) {
+      lds_u8* const sb = ring_lds + slot * SLOT;
+      // A (rows of the output tile, this wave's 64) and B (all 256 columns)
+      lds_u8* const a_hi = sb + (SA ? 0 : 2) * SLAB;
+      lds_u8* const b_hi = sb + (SA ? 2 : 0) * SLAB;
+#pragma unroll
+      for (int ks = 0; ks < DK / 16; ++ks) {
+        bf16x8_t a[2], al[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          a[rb] = tr_operand(a_hi, 16 * ks, 64 * wave + 32 * rb, lane);
+          if constexpr (SA) al[rb] = tr_operand(sb + SLAB, 16 * ks, 64 * wave + 32 * rb, lane);
+        }
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const bf16x8_t b = tr_operand(b_hi, 16 * ks, 32 * nb, lane);
+          if constexpr (SA) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+              acc[rb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb], b, acc[rb][nb], 0, 0, 0);
+              acc[rb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[rb], b, acc[rb][nb], 0, 0, 0);
+            }
+          } else {
+            const bf16x8_t bl = tr_operand(sb + SLAB, 16 * ks, 32 * nb, lane);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+              acc[rb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb], b, acc[rb][nb], 0, 0, 0);
+              acc[rb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb], bl, acc[rb][nb], 0, 0, 0);
+            }
+          }
+        }
+      }
+    };
+
+    // slab kt: wait until only the next slab's loads are outstanding,
+    // barrier (slab kt visible, slot of kt-1 free), issue kt+2, multiply kt.
+    // Slabs past the expert's rows are issued too (they read nothing), so
+    // every slab has exactly V loads per wave.  A lane whose load is out of
+    // range leaves its LDS bytes as they were, so the rows of the last slab
+    // past the expert's end are cleared before that slab is used.
+    __builtin_amdgcn_sched_barrier(0);
+    issue(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int kt = 0; kt < nslab; ++kt) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(V));
+      __builtin_amdgcn_s_barrier();
+      if (kt == nslab - 1 && tail < DK) {
+        lds_u8* const sb = ring_lds + (kt % NSL) * SLOT + tail * (DT * 2);
+        const int per = (DK - tail) * (DT * 2 / 16);   // 16-byte pieces per operand
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        for (int q = tid; q < 3 * per; q += 256) {
+          const int op = q / per;
+          *reinterpret_cast<lds_u32x4*>(sb + op * SLAB + (q - op * per) * 16) = z;
+        }
+        __syncthreads();
+      }
+      issue(kt + 2, (kt + 2) % NSL);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(kt % NSL);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();  // every wave done with the ring before the next tile's loads
+
+    // ---- epilogue: lane holds column lane%32 of block nb, rows
+    // 64 w + 32 rb + 8 (v/4) + 4 (lane/32) + v%4
+    bf16_t* Ce = p.C + static_cast<int64_t>(e) * p.M * p.Ncol;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = m0 + 64 * wave + 32 * rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int n = n0 + 32 * nb + (lane & 31);
+          Ce[static_cast<int64_t>(m) * p.Ncol + n] = cvt_bf16(acc[rb][nb][v]);
+        }
+  }
+}
+
+// dst[p] = src[perm[p] / K] for the P rows of the dispatch order (width w
+// bf16, a multiple of 8).
+__global__ __launch_bounds__(256) void gather_rows_kernel(const bf16_t* __restrict__ src,
+                                                          const int32_t* __restrict__ perm,
+                                                          const int32_t* __restrict__ offsets,
+                                                          int N, int K, int w,
+                                                          bf16_t* __restrict__ dst) {
+  const int P = offsets[N];
+  const int cpr = w / 8;
+  for (int64_t q = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+       q < static_cast<int64_t>(P) * cpr; q += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t row = q / cpr;
+    const int c = static_cast<int>(q - row * cpr) * 8;
+    const int64_t t = perm[row] / K;
+    *reinterpret_cast<u32x4_t*>(dst + row * w + c) =
+        *reinterpret_cast<const u32x4_t*>(src + t * w + c);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gather_rows(const bf16_t* src, const int32_t* perm, const int32_t* offsets,
+                              int N, int K, int w, int64_t max_rows, bf16_t* dst, hipStream_t s) {
+  const int64_t want = (max_rows * (w / 8) + 255) / 256;
+  const int grid = static_cast<int>(want < 1 ? 1 : (want > 16384 ? 16384 : want));
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(grid), dim3(256), 0, s, src, perm, offsets, N, K, w,
+                     dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_dw(bool split_a, int N, int M, int Ncol, const int32_t* offsets, int32_t* sched,
+                     const bf16_t* X, const bf16_t* XL, int64_t ldx, const bf16_t* Y, int64_t ldy,
+                     int64_t rows, bf16_t* C, int cu, hipStream_t s) {
+  DParams p{};
+  p.N = N; p.M = M; p.Ncol = Ncol; p.offsets = offsets; p.sched = sched;
+  p.X = X; p.XL = XL; p.ldx = ldx; p.Y = Y; p.ldy = ldy; p.rows = rows; p.C = C;
+  if (split_a)
+    hipLaunchKernelGGL(dw_kernel<true>, dim3(cu), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(dw_kernel<false>, dim3(cu), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace zc

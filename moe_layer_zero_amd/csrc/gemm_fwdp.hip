@@ -51,7 +51,7 @@ constexpr int GMV = 8;      // row tiles per group inside an expert
 
 // P_SWIGLU: gate/up with SwiGLU; P_STORE: down projection (bf16 y);
 // P_DSWIGLU: backward dh = g * (dout W_d) followed by the SwiGLU backward
-// (da, du in fp32 and as exact bf16 hi/lo pairs); P_DX: backward expert dx
+// (da, du as exact bf16 hi/lo pairs, and g h likewise); P_DX: backward expert dx
 // = [da_hi | da_lo | du_hi | du_lo] [W_g; W_g; W_u; W_u] in fp32.
 enum { P_SWIGLU = 0, P_STORE = 1, P_DSWIGLU = 2, P_DX = 3 };
 
@@ -75,10 +75,11 @@ struct PParams {
   bf16_t* C;                // h [P][I] or y [P][d]
   // backward variants
   const float* gs;          // P_DSWIGLU: out_scale * gate of each row (dispatch order)
-  const float* sa;          // P_DSWIGLU: saved a, u [P][ncols] (fp32)
+  const float* sa;          // P_DSWIGLU: saved a, u, h [P][ncols] (fp32)
   const float* su;
-  float* dadu;              // P_DSWIGLU: da, du [P][2 ncols] (fp32)
+  const float* sh;
   bf16_t* hilo;             // P_DSWIGLU: da_hi, da_lo, du_hi, du_lo [P][4 ncols]
+  bf16_t* ghlo;             // P_DSWIGLU: (g h)_hi, (g h)_lo [P][2 ncols]
   float* Cf;                // P_DX: expert dx [P][ncols] (fp32)
   int kseg;                 // P_DX: slabs per K segment (I / 64)
 };
@@ -396,22 +397,26 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
                 if constexpr (EPI == P_DX) {
                   p.Cf[gm * I + n] = acc[rb][cg][v];
                 } else {
-                  // dh = g dout W_d; a, u saved by the forward;
-                  // da = dh u silu'(a), du = dh silu(a), silu' = s (1 + a (1 - s))
-                  const float dh = acc[rb][cg][v] * p.gs[gm];
+                  // dh = g dout W_d; a, u, h saved by the forward;
+                  // da = dh u silu'(a), du = dh silu(a), silu' = s (1 + a (1 - s));
+                  // also g h, the down projection's weight-gradient operand
+                  const float g = p.gs[gm];
+                  const float dh = acc[rb][cg][v] * g;
                   const float a = p.sa[gm * I + n];
                   const float u = p.su[gm * I + n];
+                  const float gh = g * p.sh[gm * I + n];
                   const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
                   const float da = dh * u * (sg * (1.0f + a * (1.0f - sg)));
                   const float du = dh * (a * sg);
-                  p.dadu[gm * 2 * I + n] = da;
-                  p.dadu[gm * 2 * I + I + n] = du;
-                  const bf16_t ah = f2bf(da), uh = f2bf(du);
+                  const bf16_t ah = f2bf(da), uh = f2bf(du), hh = f2bf(gh);
                   bf16_t* hl = p.hilo + gm * 4 * I + n;
                   hl[0] = ah;
                   hl[I] = f2bf(da - bf2f(ah));
                   hl[2 * I] = uh;
                   hl[3 * I] = f2bf(du - bf2f(uh));
+                  bf16_t* gl = p.ghlo + gm * 2 * I + n;
+                  gl[0] = hh;
+                  gl[I] = f2bf(gh - bf2f(hh));
                 }
               }
             }
@@ -624,13 +629,13 @@ hipError_t launch_pack_weights_t(const bf16_t* src, bf16_t* dst, int64_t nmat, i
 hipError_t launch_bwdp_dh(const bf16_t* dout, int64_t dout_elems, const bf16_t* wdt_p,
                           const int32_t* offsets, const int32_t* perm, const int32_t* mt_off,
                           const int32_t* tile_exp, int32_t* sched, int tm, int N, int I, int d,
-                          int K, const float* gs, const float* sa, const float* su, float* dadu,
-                          bf16_t* hilo, int cu, hipStream_t s) {
+                          int K, const float* gs, const float* sa, const float* su, const float* sh,
+                          bf16_t* hilo, bf16_t* ghlo, int cu, hipStream_t s) {
   PParams p{};
   p.N = N; p.ncols = I; p.K = d;
   p.offsets = offsets; p.mt_off = mt_off; p.tile_exp = tile_exp; p.sched = sched;
   p.A = dout; p.a_bytes = static_cast<uint32_t>(dout_elems * 2); p.perm = perm; p.kdiv = K;
-  p.B = wdt_p; p.gs = gs; p.sa = sa; p.su = su; p.dadu = dadu; p.hilo = hilo;
+  p.B = wdt_p; p.gs = gs; p.sa = sa; p.su = su; p.sh = sh; p.hilo = hilo; p.ghlo = ghlo;
   return launch_tm(P_DSWIGLU, tm, p, cu, s);
 }
 

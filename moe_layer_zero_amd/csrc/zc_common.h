@@ -104,7 +104,7 @@ hipError_t launch_tile_offsets(const int32_t* offsets, int N, int bm, int32_t* t
 // ... and also the bm2-row prefix with the expert of each of its tiles, and
 // zeroed tile counters (for the packed-weight backward GEMMs).
 hipError_t launch_tile_offsets2(const int32_t* offsets, int N, int bm, int32_t* tile_off, int bm2,
-                                int32_t* tile_off2, int32_t* tile_exp2, int32_t* sched,
+                                int32_t* tile_off2, int32_t* tile_exp2, int32_t* sched, int nsched,
                                 hipStream_t s);
 
 // Grouped / dense GEMMs (gemm.hip); the backward's fp32 intermediates enter
@@ -178,13 +178,24 @@ hipError_t launch_pack_weights_t(const bf16_t* src, bf16_t* dst, int64_t nmat, i
                                  hipStream_t s);
 // Backward expert GEMMs of bf16 layers on transposed packed weights (tile
 // bookkeeping as for the forward): dh = gs * (dout[tok] W_d) with the SwiGLU
-// backward in the epilogue -> dadu [P][2I] fp32 and hilo [P][4I] = exact
-// bf16 hi/lo pairs of da and du; expert dx = hilo [W_g;W_g;W_u;W_u] [P][d] fp32.
+// backward in the epilogue -> hilo [P][4I] = exact bf16 hi/lo pairs of da
+// and du, ghlo [P][2I] = those of gs * h; expert dx = hilo [W_g;W_g;W_u;W_u]
+// -> [P][d] fp32.
 hipError_t launch_bwdp_dh(const bf16_t* dout, int64_t dout_elems, const bf16_t* wdt_p,
                           const int32_t* offsets, const int32_t* perm, const int32_t* mt_off,
                           const int32_t* tile_exp, int32_t* sched, int tm, int N, int I, int d,
-                          int K, const float* gs, const float* sa, const float* su, float* dadu,
-                          bf16_t* hilo, int cu, hipStream_t s);
+                          int K, const float* gs, const float* sa, const float* su, const float* sh,
+                          bf16_t* hilo, bf16_t* ghlo, int cu, hipStream_t s);
+// Expert weight gradients (gemm_dw.hip): per expert e, C_e = sum over its
+// rows p of A[p]^T B[p] with the split operand X (exact bf16 hi/lo pair X,
+// XL) as A (split_a) or B and its exact partner Y as the other; output
+// [M][Ncol] bf16 per expert; sched: 8 counters, zero at launch.
+hipError_t launch_dw(bool split_a, int N, int M, int Ncol, const int32_t* offsets, int32_t* sched,
+                     const bf16_t* X, const bf16_t* XL, int64_t ldx, const bf16_t* Y, int64_t ldy,
+                     int64_t rows, bf16_t* C, int cu, hipStream_t s);
+// dst[p] = src[perm[p] / K] (rows of width w) for the FFN picks in dispatch order.
+hipError_t launch_gather_rows(const bf16_t* src, const int32_t* perm, const int32_t* offsets,
+                              int N, int K, int w, int64_t max_rows, bf16_t* dst, hipStream_t s);
 hipError_t launch_bwdp_dx(const bf16_t* hilo, int64_t hilo_elems, const bf16_t* wgt_p,
                           const bf16_t* wut_p, const int32_t* offsets, const int32_t* mt_off,
                           const int32_t* tile_exp, int32_t* sched, int tm, int N, int I, int d,

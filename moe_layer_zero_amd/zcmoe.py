@@ -31,7 +31,7 @@ EXPORTS = ("zc_moe_workspace_size", "zc_moe_saved_size", "zc_moe_route", "zc_moe
            "zc_moe_profile",
            "zc_moe_profile_read",
            "zc_moe_phase_name", "zc_status_string", "zc_last_error")
-ZC_NUM_PHASES = 22
+ZC_NUM_PHASES = 23
 
 
 class ZcError(RuntimeError):

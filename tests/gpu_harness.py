@@ -146,6 +146,28 @@ def routing_agreement(gpu_idx: np.ndarray, orc_keys: np.ndarray, orc_idx: np.nda
     return same, len(bad)
 
 
+def replace_near_ties(L: dict, N: int, K: int, gate_norm: int = 1) -> int:
+    """Overwrite, in the host layer L, the x row of every token whose K-th
+    and (K+1)-th oracle keys lie within the routing tolerance of
+    routing_agreement with the row of the next clear token, so that a test
+    needing identical routing on every token keeps its full token count.
+    Returns the number of rows replaced."""
+    xh, wrh = host(L["x"]), host(L["wr"])
+    lg = oracle.logits(xh, wrh)
+    o = oracle.route(lg, L["bias"].numpy(), N, K, gate_norm=gate_norm)
+    if K >= o.keys.shape[1]:
+        return 0
+    ks = -np.sort(-o.keys, axis=1)
+    gap = ks[:, K - 1] - ks[:, K]
+    lg_max = np.abs(lg).max()
+    tie = np.array([gap[t] < 16.0 * LOGIT_RTOL * lg_max * _pmax(lg[t]) for t in range(len(gap))])
+    clear = np.flatnonzero(~tie)
+    assert clear.size, "every token is a near-tie"
+    for t in np.flatnonzero(tie):
+        L["x"][t] = L["x"][clear[np.searchsorted(clear, t) % clear.size]]
+    return int(tie.sum())
+
+
 def _pmax(lg_row: np.ndarray) -> float:
     e = np.exp(lg_row - lg_row.max())
     return float(e.max() / e.sum())

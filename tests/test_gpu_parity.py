@@ -284,12 +284,16 @@ def test_forward_packed_prefill_full_size():
 
 
 # ------------------------------------------------------------ backward
-def backward_case(sh, gate_norm=1, out_scale=1.0, experts_checked=None):
+def backward_case(sh, gate_norm=1, out_scale=1.0, experts_checked=None, bias=None):
     L = synth.make_layer(sh, "cpu")
+    if bias is not None:
+        L["bias"] = bias
+    nrep = H.replace_near_ties(L, sh.N, sh.K, gate_norm)
     dY = synth.make_dy(sh)
     Lg = H.to_dev(L)
     desc = H.desc_of(sh, gate_norm, out_scale)
-    print(f"[backward] {sh.name} T={sh.T} gate_norm={gate_norm}", flush=True)
+    print(f"[backward] {sh.name} T={sh.T} gate_norm={gate_norm} (near-tie rows replaced: "
+          f"{nrep})", flush=True)
     route, out, saved = H.run_forward(desc, Lg, saved=True)
     g = H.run_backward(desc, Lg, route, saved, dY.cuda())
     xh, wrh = H.host(L["x"]), H.host(L["wr"])
@@ -309,6 +313,7 @@ def backward_case(sh, gate_norm=1, out_scale=1.0, experts_checked=None):
         want = np.stack([ref[name][e] for e in es])
         errs[name] = H.assert_close(got, want, dt, key)
     print("  errors " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()), flush=True)
+    return route, g
 
 
 def test_backward_tiny_fp32():
@@ -329,3 +334,26 @@ def test_backward_train_shape_bf16():
     # the training layer's shapes with fewer tokens, so the fp64 oracle
     # finishes in seconds; all 128 experts' gradients compared
     backward_case(CF["train_bf16"].with_T(256))
+
+
+def test_backward_bf16_several_slabs_per_expert():
+    # about 85 rows per FFN expert: the weight gradients reduce over several
+    # 32-row slabs with a ragged last one; experts of every size checked
+    sh = CF["train_bf16"].with_T(2048)
+    backward_case(sh, experts_checked=[0, 1, 17, 64, 100, 127])
+
+
+def test_backward_bf16_literal_gates_and_scale():
+    backward_case(CF["small_bf16"].with_T(300), gate_norm=0, out_scale=0.5)
+
+
+def test_backward_bf16_expert_without_rows():
+    # expert 3 is never picked: its weight gradients are exactly zero
+    sh = CF["train_bf16"].with_T(256)
+    b = torch.zeros(sh.E)
+    b[3] = -100.0
+    route, g = backward_case(sh, experts_checked=[2, 3, 4], bias=b)
+    cnt = route.offsets[4].item() - route.offsets[3].item()
+    assert cnt == 0
+    for k in ("dwg", "dwu", "dwd"):
+        assert torch.count_nonzero(g[k][3]).item() == 0
