@@ -197,8 +197,13 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
     const int rr = q - grp * GMV * NT;
     const int mt = fm + rr % gsz;
     const int nt = rr / gsz;
-    const int m0 = p.offsets[e] + mt * TM;
-    const int mcount = min(TM, p.offsets[e + 1] - m0);
+    // the expert's 32-row blocks spread evenly over its mte row tiles (at
+    // most TM / 32 each), so the row tiles that share a weight panel do the
+    // same work, stream the panel at the same pace and find it in L2
+    const int nbe = (p.offsets[e + 1] - p.offsets[e] + 31) >> 5;
+    const int blo = nbe * mt / mte, bhi = nbe * (mt + 1) / mte;
+    const int m0 = p.offsets[e] + 32 * blo;
+    const int mcount = min(p.offsets[e] + 32 * bhi, p.offsets[e + 1]) - m0;
     const int n0 = nt * OUTN;
 
     // ---- byte offsets of the RB A row pieces this lane copies per slab
