@@ -121,8 +121,10 @@ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 template <int EPI, int TM, bool LOADS_FIRST>
 __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   constexpr int RB = TM / 32;       // 32-row blocks per tile = A loads per wave per slab
-  constexpr int SLOT = TM * BK;     // bf16 per ring slot
-  constexpr int V = RB + 8;         // loads per wave per slab (A rows + 8 B blocks)
+  // P_DX slabs hold the hi and the lo piece of the same reduction steps
+  constexpr int APC = EPI == P_DX ? 2 : 1;
+  constexpr int SLOT = APC * TM * BK;  // bf16 per ring slot
+  constexpr int V = APC * RB + 8;      // loads per wave per slab (A rows + 8 B blocks)
   static_assert(TM == 32 || TM == 64 || TM == 128 || TM == 256, "tile height");
   static_assert(LOADS_FIRST || TM == 256, "interleaved issue is laid out for 256-row tiles");
   // the ring, then one int: the next tile index claimed by thread 0 (kept in
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   if (tid == 0) s_claim[0] = atomicAdd(p.sched + cx, 1);
   __syncthreads();
   int cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
-  const int nk = p.K / BK;
+  const int nk = p.K / (APC * BK);  // P_DX: K = 4I holds both pieces
   const int kblk = p.K / 16;  // packed 1 KB blocks per 32 output columns
 
   // A buffer resource: raw, range-checked against a_bytes
@@ -253,23 +255,33 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
       constexpr bool LF = LOADS_FIRST || NRB != 8;
       bf16x8_t bq[NST][2][4];  // B fragments of the slabs in flight
       auto issue = [&](int kt, int slot, bf16x8_t (&bf)[2][4]) {
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          lds_void* dst = (lds_void*)(ring + slot * SLOT + (RB * wave + i) * 8 * BK);
-          lds_dma16(arsrc, dst, aoff[i], kt * BK * 2);
-        }
         if constexpr (EPI == P_DX) {
-          // K = [da_hi | da_lo | du_hi | du_lo]: segments 0, 1 multiply W_g,
-          // 2, 3 multiply W_u
+          // A rows = [da_hi | da_lo | du_hi | du_lo]: slabs 0 .. kseg-1 take
+          // the hi and lo pieces of da (times W_g), the next kseg those of du
+          // (times W_u); the hi piece fills the first half of the slot
           const int seg = kt / p.kseg;
           const int ks = kt - seg * p.kseg;
-          const bf16_t* c0 = seg < 2 ? b0 : bu;
+          const int hoff = (2 * seg * p.kseg + ks) * BK * 2;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+              lds_void* dst =
+                  (lds_void*)(ring + slot * SLOT + h * TM * BK + (RB * wave + i) * 8 * BK);
+              lds_dma16(arsrc, dst, aoff[i], hoff + h * p.kseg * BK * 2);
+            }
+          const bf16_t* c0 = seg == 0 ? b0 : bu;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             bf[0][t] = *reinterpret_cast<const bf16x8_t*>(c0 + (4 * ks + t) * 512);
             bf[1][t] = *reinterpret_cast<const bf16x8_t*>(c0 + (kbs + 4 * ks + t) * 512);
           }
         } else {
+#pragma unroll
+          for (int i = 0; i < RB; ++i) {
+            lds_void* dst = (lds_void*)(ring + slot * SLOT + (RB * wave + i) * 8 * BK);
+            lds_dma16(arsrc, dst, aoff[i], kt * BK * 2);
+          }
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             bf[0][t] = *reinterpret_cast<const bf16x8_t*>(b0 + (4 * kt + t) * 512);
@@ -294,8 +306,17 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
 #pragma unroll
           for (int rb = 0; rb < NRB; ++rb) {
             const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(a_s + rb * 32 * BK + co);
-            acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[0][t], acc[rb][0], 0, 0, 0);
-            acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[1][t], acc[rb][1], 0, 0, 0);
+            if constexpr (EPI == P_DX) {
+              const bf16x8_t al =
+                  *reinterpret_cast<const bf16x8_t*>(a_s + TM * BK + rb * 32 * BK + co);
+              acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[0][t], acc[rb][0], 0, 0, 0);
+              acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[1][t], acc[rb][1], 0, 0, 0);
+              acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bf[0][t], acc[rb][0], 0, 0, 0);
+              acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bf[1][t], acc[rb][1], 0, 0, 0);
+            } else {
+              acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[0][t], acc[rb][0], 0, 0, 0);
+              acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[1][t], acc[rb][1], 0, 0, 0);
+            }
           }
         }
       };
@@ -303,7 +324,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
       // Issue order inside a slab (4 NRB fragment reads, 8 NRB MFMAs, V loads):
       // loads first, or spread over the first MFMAs; fragment reads run up to
       // three ahead of the MFMAs that use them.
-      constexpr int NDS = 4 * NRB;
+      constexpr int NDS = 4 * APC * NRB;
       constexpr int DS0 = NDS < 3 ? NDS : 3;
       auto sched = [&](bool with_loads) {
         if (with_loads && LF) __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
