@@ -218,9 +218,9 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DParams p) {
     // slab kt: wait until only the next slab's loads are outstanding,
     // barrier (slab kt visible, slot of kt-1 free), issue kt+2, multiply kt.
     // Slabs past the expert's rows are issued too (they read nothing), so
-    // every slab has exactly V loads per wave.  A lane whose load is out of
-    // range leaves its LDS bytes as they were, so the rows of the last slab
-    // past the expert's end are cleared before that slab is used.
+    // every slab has exactly V loads per wave.  The rows of the last slab
+    // past the expert's end are cleared before that slab is used, so the
+    // sums do not depend on what an out-of-range lane leaves in LDS.
     __builtin_amdgcn_sched_barrier(0);
     issue(0, 0);
     __builtin_amdgcn_sched_barrier(0);
