@@ -571,8 +571,12 @@ zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg
       ZC_LAUNCH(ZC_PH_BWD_DOWN_DH,
                 zc::launch_bwdp_dh(reinterpret_cast<const bf16_t*>(dout), d->T * d->d, w.wdt,
                                    r->offsets, r->perm, w.mt2, w.texp2, w.sched, tmb, N, I, dd, K,
-                                   w.gs, sv.a, sv.u, sv.h, w.hilo, w.ghlo, cu, s),
+                                   w.gs, w.dadu, cu, s),
                 "down backward (dh) launch");
+      ZC_LAUNCH(ZC_PH_BWD_DOWN_DH,
+                zc::launch_swiglu_bwd(w.dadu, w.gs, sv.a, sv.u, sv.h, r->offsets, N, I, rows,
+                                      w.hilo, w.ghlo, s),
+                "SwiGLU backward launch");
     } else if (Tn > 0) {
       ZC_LAUNCH(ZC_PH_BWD_DOWN_DH,
                 zc::launch_bwd_down_dh<T>(dout, r->perm, K, w.gs, wd, sv.a, sv.u, r->offsets,

@@ -50,8 +50,8 @@ constexpr int NTHR = 256;
 constexpr int GMV = 8;      // row tiles per group inside an expert
 
 // P_SWIGLU: gate/up with SwiGLU; P_STORE: down projection (bf16 y);
-// P_DSWIGLU: backward dh = g * (dout W_d) followed by the SwiGLU backward
-// (da, du as exact bf16 hi/lo pairs, and g h likewise); P_DX: backward expert dx
+// P_DSWIGLU: backward dh = g * (dout W_d) in fp32 (swiglu_bwd_kernel then
+// forms da, du and g h as exact bf16 hi/lo pairs); P_DX: backward expert dx
 // = [da_hi | da_lo | du_hi | du_lo] [W_g; W_g; W_u; W_u] in fp32.
 enum { P_SWIGLU = 0, P_STORE = 1, P_DSWIGLU = 2, P_DX = 3 };
 
@@ -75,12 +75,7 @@ struct PParams {
   bf16_t* C;                // h [P][I] or y [P][d]
   // backward variants
   const float* gs;          // P_DSWIGLU: out_scale * gate of each row (dispatch order)
-  const float* sa;          // P_DSWIGLU: saved a, u, h [P][ncols] (fp32)
-  const float* su;
-  const float* sh;
-  bf16_t* hilo;             // P_DSWIGLU: da_hi, da_lo, du_hi, du_lo [P][4 ncols]
-  bf16_t* ghlo;             // P_DSWIGLU: (g h)_hi, (g h)_lo [P][2 ncols]
-  float* Cf;                // P_DX: expert dx [P][ncols] (fp32)
+  float* Cf;                // P_DSWIGLU: dh, P_DX: expert dx, [P][ncols] (fp32)
   int kseg;                 // P_DX: slabs per K segment (I / 64)
 };
 
@@ -423,26 +418,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
                 if constexpr (EPI == P_DX) {
                   p.Cf[gm * I + n] = acc[rb][cg][v];
                 } else {
-                  // dh = g dout W_d; a, u, h saved by the forward;
-                  // da = dh u silu'(a), du = dh silu(a), silu' = s (1 + a (1 - s));
-                  // also g h, the down projection's weight-gradient operand
-                  const float g = p.gs[gm];
-                  const float dh = acc[rb][cg][v] * g;
-                  const float a = p.sa[gm * I + n];
-                  const float u = p.su[gm * I + n];
-                  const float gh = g * p.sh[gm * I + n];
-                  const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
-                  const float da = dh * u * (sg * (1.0f + a * (1.0f - sg)));
-                  const float du = dh * (a * sg);
-                  const bf16_t ah = f2bf(da), uh = f2bf(du), hh = f2bf(gh);
-                  bf16_t* hl = p.hilo + gm * 4 * I + n;
-                  hl[0] = ah;
-                  hl[I] = f2bf(da - bf2f(ah));
-                  hl[2 * I] = uh;
-                  hl[3 * I] = f2bf(du - bf2f(uh));
-                  bf16_t* gl = p.ghlo + gm * 2 * I + n;
-                  gl[0] = hh;
-                  gl[I] = f2bf(gh - bf2f(hh));
+                  p.Cf[gm * I + n] = acc[rb][cg][v] * p.gs[gm];  // dh = g dout W_d
                 }
               }
             }
@@ -494,6 +470,69 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
       default: if constexpr (RB >= 8) run(std::integral_constant<int, 8>{}); break;
     }
     cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
+  }
+}
+
+// SwiGLU backward of the FFN picks in dispatch order, from dh = g (dout W_d)
+// and the a, u, h the forward saved (all fp32, [P][I]):
+//   da = dh u silu'(a), du = dh silu(a), silu'(a) = s (1 + a (1 - s)), s = sigmoid(a),
+// and g h (the down projection's weight-gradient operand), each written as an
+// exact bf16 pair (hi, lo = bf16(v - hi)): hilo [P][4I] = da_hi, da_lo, du_hi,
+// du_lo; ghlo [P][2I] = (g h)_hi, (g h)_lo.  One thread per 8 consecutive
+// columns of a row: 16-byte loads and stores.
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(
+    const float* __restrict__ dh, const float* __restrict__ gs, const float* __restrict__ sa,
+    const float* __restrict__ su, const float* __restrict__ sh, const int32_t* __restrict__ offsets,
+    int N, int I, bf16_t* __restrict__ hilo, bf16_t* __restrict__ ghlo) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  const int64_t P = offsets[N];
+  const int cpr = I / 8;
+  auto pack = [](float x0, float x1) -> uint32_t {
+    return static_cast<uint32_t>(f2bf(x0)) | (static_cast<uint32_t>(f2bf(x1)) << 16);
+  };
+  for (int64_t q = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; q < P * cpr;
+       q += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t row = q / cpr;
+    const int c = static_cast<int>(q - row * cpr) * 8;
+    const int64_t o = row * I + c;
+    const float g = gs[row];
+    float va[8], vu[8], vg[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(dh + o + 4 * h);
+      const f32x4_t a4 = *reinterpret_cast<const f32x4_t*>(sa + o + 4 * h);
+      const f32x4_t u4 = *reinterpret_cast<const f32x4_t*>(su + o + 4 * h);
+      const f32x4_t h4 = *reinterpret_cast<const f32x4_t*>(sh + o + 4 * h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = a4[j];
+        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+        va[4 * h + j] = d4[j] * u4[j] * (sg * (1.0f + a * (1.0f - sg)));
+        vu[4 * h + j] = d4[j] * (a * sg);
+        vg[4 * h + j] = g * h4[j];
+      }
+    }
+    // hi parts, then lo parts = the rounding residue of each
+    u32x4_t w[6];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x[3][2] = {{va[2 * j], va[2 * j + 1]}, {vu[2 * j], vu[2 * j + 1]},
+                             {vg[2 * j], vg[2 * j + 1]}};
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const float h0 = bf2f(f2bf(x[k][0])), h1 = bf2f(f2bf(x[k][1]));
+        w[2 * k][j] = pack(h0, h1);
+        w[2 * k + 1][j] = pack(x[k][0] - h0, x[k][1] - h1);
+      }
+    }
+    bf16_t* hl = hilo + row * 4 * I + c;
+    *reinterpret_cast<u32x4_t*>(hl) = w[0];
+    *reinterpret_cast<u32x4_t*>(hl + I) = w[1];
+    *reinterpret_cast<u32x4_t*>(hl + 2 * I) = w[2];
+    *reinterpret_cast<u32x4_t*>(hl + 3 * I) = w[3];
+    bf16_t* gl = ghlo + row * 2 * I + c;
+    *reinterpret_cast<u32x4_t*>(gl) = w[4];
+    *reinterpret_cast<u32x4_t*>(gl + I) = w[5];
   }
 }
 
@@ -655,14 +694,23 @@ hipError_t launch_pack_weights_t(const bf16_t* src, bf16_t* dst, int64_t nmat, i
 hipError_t launch_bwdp_dh(const bf16_t* dout, int64_t dout_elems, const bf16_t* wdt_p,
                           const int32_t* offsets, const int32_t* perm, const int32_t* mt_off,
                           const int32_t* tile_exp, int32_t* sched, int tm, int N, int I, int d,
-                          int K, const float* gs, const float* sa, const float* su, const float* sh,
-                          bf16_t* hilo, bf16_t* ghlo, int cu, hipStream_t s) {
+                          int K, const float* gs, float* dh, int cu, hipStream_t s) {
   PParams p{};
   p.N = N; p.ncols = I; p.K = d;
   p.offsets = offsets; p.mt_off = mt_off; p.tile_exp = tile_exp; p.sched = sched;
   p.A = dout; p.a_bytes = static_cast<uint32_t>(dout_elems * 2); p.perm = perm; p.kdiv = K;
-  p.B = wdt_p; p.gs = gs; p.sa = sa; p.su = su; p.sh = sh; p.hilo = hilo; p.ghlo = ghlo;
+  p.B = wdt_p; p.gs = gs; p.Cf = dh;
   return launch_tm(P_DSWIGLU, tm, p, cu, s);
+}
+
+hipError_t launch_swiglu_bwd(const float* dh, const float* gs, const float* sa, const float* su,
+                             const float* sh, const int32_t* offsets, int N, int I,
+                             int64_t max_rows, bf16_t* hilo, bf16_t* ghlo, hipStream_t s) {
+  const int64_t want = (max_rows * (I / 8) + 255) / 256;
+  const int grid = static_cast<int>(want < 1 ? 1 : (want > 16384 ? 16384 : want));
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(grid), dim3(256), 0, s, dh, gs, sa, su, sh, offsets,
+                     N, I, hilo, ghlo);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwdp_dx(const bf16_t* hilo, int64_t hilo_elems, const bf16_t* wgt_p,

@@ -177,15 +177,18 @@ hipError_t launch_pack_weights(const bf16_t* src, bf16_t* dst, int64_t nmat, int
 hipError_t launch_pack_weights_t(const bf16_t* src, bf16_t* dst, int64_t nmat, int R, int C,
                                  hipStream_t s);
 // Backward expert GEMMs of bf16 layers on transposed packed weights (tile
-// bookkeeping as for the forward): dh = gs * (dout[tok] W_d) with the SwiGLU
-// backward in the epilogue -> hilo [P][4I] = exact bf16 hi/lo pairs of da
-// and du, ghlo [P][2I] = those of gs * h; expert dx = hilo [W_g;W_g;W_u;W_u]
-// -> [P][d] fp32.
+// bookkeeping as for the forward): dh = gs * (dout[tok] W_d) -> [P][I] fp32;
+// expert dx = hilo [W_g;W_g;W_u;W_u] -> [P][d] fp32.
 hipError_t launch_bwdp_dh(const bf16_t* dout, int64_t dout_elems, const bf16_t* wdt_p,
                           const int32_t* offsets, const int32_t* perm, const int32_t* mt_off,
                           const int32_t* tile_exp, int32_t* sched, int tm, int N, int I, int d,
-                          int K, const float* gs, const float* sa, const float* su, const float* sh,
-                          bf16_t* hilo, bf16_t* ghlo, int cu, hipStream_t s);
+                          int K, const float* gs, float* dh, int cu, hipStream_t s);
+// SwiGLU backward from dh and the saved a, u, h ([P][I] fp32 each): hilo
+// [P][4I] = exact bf16 hi/lo pairs of da and du, ghlo [P][2I] = those of
+// gs * h; I a multiple of 8.
+hipError_t launch_swiglu_bwd(const float* dh, const float* gs, const float* sa, const float* su,
+                             const float* sh, const int32_t* offsets, int N, int I,
+                             int64_t max_rows, bf16_t* hilo, bf16_t* ghlo, hipStream_t s);
 // Expert weight gradients (gemm_dw.hip): per expert e, C_e = sum over its
 // rows p of A[p]^T B[p] with the split operand X (exact bf16 hi/lo pair X,
 // XL) as A (split_a) or B and its exact partner Y as the other; output
