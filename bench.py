@@ -38,8 +38,8 @@ FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, vendor figure
 # size gives), valid for the kernel source they were measured on: reported
 # as roofline.traffic only while that source is unchanged.
 GATE_UP_TRAFFIC = {"source": "moe_layer_zero_amd/csrc/gemm_fwdp.hip",
-                   "sha256": "933c72dbdc993c606660fa3e38d7f905f6c2ecd250e0673da5ab4e1946aa680a",
-                   "fetch_bytes": 31908307883, "write_bytes": 588773376}
+                   "sha256": "b1e3cf9e21a9b21e981f80163015f6a530254ef9b74386594d3bbbf57f84e763",
+                   "fetch_bytes": 31834031872, "write_bytes": 588773376}
 
 
 def measured_traffic():
