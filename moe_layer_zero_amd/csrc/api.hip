@@ -266,6 +266,8 @@ int64_t fwd_ws_bytes(const zc_moe_desc* d) {
 
 struct BwdWs {
   int32_t* tile_off;
+  // dadu: da, du [P][2I] on the generic path; dh [P][I] on the packed-weight
+  // path (its SwiGLU backward then writes the hi/lo pairs below)
   float *gs, *dg, *dl, *dadu, *dxp, *dxr, *rdw, *lbc;
   // packed-weight backward (use_bwdp): tile prefix and experts, counters,
   // transposed packed W_d, W_g, W_u, exact bf16 hi/lo pairs of da, du and
