@@ -284,7 +284,8 @@ def test_forward_packed_prefill_full_size():
 
 
 # ------------------------------------------------------------ backward
-def backward_case(sh, gate_norm=1, out_scale=1.0, experts_checked=None, bias=None):
+def backward_case(sh, gate_norm=1, out_scale=1.0, experts_checked=None, bias=None,
+                  dwr_rows=None):
     L = synth.make_layer(sh, "cpu")
     if bias is not None:
         L["bias"] = bias
@@ -305,8 +306,19 @@ def backward_case(sh, gate_norm=1, out_scale=1.0, experts_checked=None, bias=Non
                           o.topk_idx, o.gates, H.host(dY), sh.N, sh.Z, gate_norm=gate_norm,
                           out_scale=out_scale, want_experts=experts_checked)
     dt = sh.torch_dtype
-    errs = {"dx": H.assert_close(g["dx"], ref["dx"], dt, "dx"),
-            "dwr": H.assert_close(g["dwr"], ref["dwr"], dt, "dW_r")}
+    errs = {"dx": H.assert_close(g["dx"], ref["dx"], dt, "dx")}
+    if dwr_rows is None:
+        errs["dwr"] = H.assert_close(g["dwr"], ref["dwr"], dt, "dW_r")
+    else:
+        # only these router rows receive gradient (renormalised gates give
+        # the other experts' scores none): the bound on them, exact zeros
+        # elsewhere, as for a subset of expert gradients
+        rows = torch.tensor(dwr_rows)
+        errs["dwr"] = H.assert_close(g["dwr"][rows.cuda()], ref["dwr"][dwr_rows], dt, "dW_r")
+        rest = torch.ones(sh.E, dtype=torch.bool)
+        rest[rows] = False
+        assert not np.any(ref["dwr"][rest.numpy()])
+        assert torch.count_nonzero(g["dwr"][rest.cuda()]).item() == 0
     es = list(ref["dwg"].keys())
     for name, key in (("dwg", "dW_g"), ("dwu", "dW_u"), ("dwd", "dW_d")):
         got = g[name][torch.tensor(es).cuda()]
@@ -357,3 +369,25 @@ def test_backward_bf16_expert_without_rows():
     assert cnt == 0
     for k in ("dwg", "dwu", "dwd"):
         assert torch.count_nonzero(g[k][3]).item() == 0
+
+
+def test_backward_bf16_64_row_tiles():
+    # about 64 rows per FFN expert: the backward GEMMs run 64-row tiles
+    sh = CF["train_bf16"].with_T(1024)
+    backward_case(sh, experts_checked=[0, 5, 64, 127])
+
+
+def test_backward_bf16_few_experts_take_every_token():
+    # experts 0..K-1 are picked by every token (their bias exceeds any score
+    # gap): 257 rows each, eight full 32-row slabs and a one-row tail in the
+    # weight gradients; every other FFN expert gets no rows
+    sh = CF["train_bf16"].with_T(257)
+    b = torch.zeros(sh.E)
+    b[: sh.K] = 1.0
+    route, g = backward_case(sh, experts_checked=[0, sh.K - 1, sh.K], bias=b,
+                             dwr_rows=list(range(sh.K)))
+    off = route.offsets.cpu().numpy()
+    assert all(off[e + 1] - off[e] == sh.T for e in range(sh.K))
+    assert off[-1] == sh.T * sh.K
+    for k in ("dwg", "dwu", "dwd"):
+        assert torch.count_nonzero(g[k][sh.K:]).item() == 0
