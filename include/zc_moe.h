@@ -175,8 +175,9 @@ zc_status zc_moe_forward(const zc_moe_desc* desc, const void* x,
  * takes its score gradient (f held fixed, it counts discrete picks):
  *   dl_j += p_j (c_j - sum_k p_k c_k),  c_j = alpha f_{g(j)} / T,
  * with p the fp32 softmax of the token's scores and g(j) the group of j.
- * Every gradient buffer is overwritten (not accumulated).  r and saved must
- * come from the zc_moe_forward call being differentiated. */
+ * Every gradient buffer is overwritten (not accumulated): with T == 0 the
+ * weight gradients are zeros, and x, saved, dout and dx may be NULL.  r and
+ * saved must come from the zc_moe_forward call being differentiated. */
 zc_status zc_moe_backward(const zc_moe_desc* desc, const void* x,
                           const void* w_router, const void* w_gate,
                           const void* w_up, const void* w_down,

@@ -734,7 +734,7 @@ zc_status zc_moe_backward(const zc_moe_desc* desc, const void* x, const void* w_
   ZC_CHECK(check_ptr(x, "x", none));
   ZC_CHECK(check_ptr(w_router, "w_router"));
   ZC_CHECK(check_weights(desc, w_gate, w_up, w_down));
-  ZC_CHECK(check_ptr(saved, "saved"));
+  ZC_CHECK(check_ptr(saved, "saved", none));
   ZC_CHECK(check_ptr(dout, "dout", none));
   ZC_CHECK(check_ptr(dx, "dx", none));
   ZC_CHECK(check_ptr(dw_router, "dw_router"));

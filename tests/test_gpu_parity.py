@@ -391,3 +391,22 @@ def test_backward_bf16_few_experts_take_every_token():
     assert off[-1] == sh.T * sh.K
     for k in ("dwg", "dwu", "dwd"):
         assert torch.count_nonzero(g[k][sh.K:]).item() == 0
+
+
+@pytest.mark.parametrize("shape", ["small_bf16", "tiny_fp32"])
+def test_backward_with_no_tokens_gives_zero_weight_gradients(shape):
+    # an empty batch: every weight gradient is exactly zero (written, not
+    # left as it was), on the packed-weight path (bf16) and the generic one
+    sh = CF[shape]
+    Lg = H.to_dev(synth.make_layer(sh.with_T(0), "cpu"))
+    desc = H.desc_of(sh.with_T(0))
+    route, out, saved = H.run_forward(desc, Lg, saved=True)
+    assert out.numel() == 0 and route.offsets.abs().sum().item() == 0
+    dx = torch.empty_like(Lg["x"])
+    g = {k: torch.full_like(Lg[w], float("nan")) for k, w in
+         (("dwr", "wr"), ("dwg", "wg"), ("dwu", "wu"), ("dwd", "wd"))}
+    zcmoe.zc_moe_backward(desc, Lg["x"], Lg["wr"], Lg["wg"], Lg["wu"], Lg["wd"], route, saved,
+                          torch.empty_like(Lg["x"]), dx, g["dwr"], g["dwg"], g["dwu"], g["dwd"])
+    torch.cuda.synchronize()
+    for k, t in g.items():
+        assert torch.count_nonzero(t).item() == 0, k
