@@ -134,10 +134,14 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DParams p) {
     if (tid == 0) pre = atomicAdd(p.sched + cx, 1);
     const int64_t L = next_tile(pre);
     if (L < 0) break;
-    const int e = static_cast<int>(L / (MT * NT));
-    const int rem = static_cast<int>(L - static_cast<int64_t>(e) * MT * NT);
+    // wave-uniform tile coordinates and row range, in scalar registers (the
+    // buffer resources below are built from them; a value the compiler
+    // cannot prove uniform would wrap every load in a per-lane loop)
+    const int e = __builtin_amdgcn_readfirstlane(static_cast<int>(L / (MT * NT)));
+    const int rem = __builtin_amdgcn_readfirstlane(static_cast<int>(L - static_cast<int64_t>(e) * MT * NT));
     const int m0 = (rem / NT) * DT, n0 = (rem % NT) * DT;
-    const int r0 = p.offsets[e], r1 = p.offsets[e + 1];
+    const int r0 = __builtin_amdgcn_readfirstlane(p.offsets[e]);
+    const int r1 = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
     const int nslab = (r1 - r0 + DK - 1) / DK;
     const int tail = (r1 - r0) - DK * (nslab - 1);   // rows of the last slab
     // the expert's rows only: a load past them returns zeros and reads nothing
