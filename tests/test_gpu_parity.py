@@ -410,3 +410,17 @@ def test_backward_with_no_tokens_gives_zero_weight_gradients(shape):
     torch.cuda.synchronize()
     for k, t in g.items():
         assert torch.count_nonzero(t).item() == 0, k
+
+
+# d and I multiples of 64 but not of 256: the bf16 layer takes the generic
+# grouped-GEMM backward (and the 256 x 256 row-major forward with partial
+# column tiles)
+BF16_ODD = synth.LayerShape("bf16_odd", 12, 300, 384, 16, 8, 192, 4, "bf16", 0.02, "uniform")
+
+
+def test_forward_bf16_dims_not_multiple_of_256():
+    forward_case(BF16_ODD)
+
+
+def test_backward_bf16_dims_not_multiple_of_256():
+    backward_case(BF16_ODD)
