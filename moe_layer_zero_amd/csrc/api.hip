@@ -587,7 +587,7 @@ zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg
     }
     if (bwdp)
       ZC_LAUNCH(ZC_PH_BWD_DOWN_DW,
-                zc::launch_dw(false, N, dd, I, r->offsets, w.sched + 16, w.ghlo, w.ghlo + I, 2 * I,
+                zc::launch_dw(true, N, I, dd, r->offsets, w.sched + 16, w.ghlo, w.ghlo + I, 2 * I,
                               w.doutd, dd, rows, reinterpret_cast<bf16_t*>(dwd), cu, s),
                 "down weight-gradient launch");
     else
@@ -614,11 +614,11 @@ zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg
     }
     if (bwdp) {
       ZC_LAUNCH(ZC_PH_BWD_GATE_UP_DW,
-                zc::launch_dw(true, N, I, dd, r->offsets, w.sched + 24, w.hilo, w.hilo + I, 4 * I,
+                zc::launch_dw(false, N, I, dd, r->offsets, w.sched + 24, w.hilo, w.hilo + I, 4 * I,
                               w.xd, dd, rows, reinterpret_cast<bf16_t*>(dwg), cu, s),
                 "gate/up weight-gradient launch");
       ZC_LAUNCH(ZC_PH_BWD_GATE_UP_DW,
-                zc::launch_dw(true, N, I, dd, r->offsets, w.sched + 32, w.hilo + 2 * I,
+                zc::launch_dw(false, N, I, dd, r->offsets, w.sched + 32, w.hilo + 2 * I,
                               w.hilo + 3 * I, 4 * I, w.xd, dd, rows, reinterpret_cast<bf16_t*>(dwu),
                               cu, s),
                 "gate/up weight-gradient launch");

@@ -6,16 +6,17 @@
 //   dW_g[e] = sum_p da_p^T x_p,  dW_u[e] = sum_p du_p^T x_p,
 //   dW_d[e] = sum_p dout_p^T (g_p h_p),
 // for p in offsets[e] .. offsets[e+1].  Generally, per expert,
-//   C_e[m][n] = sum_p A[p][m] B[p][n]
+//   C_e[m][n] = sum_p X[p][m] Y[p][n]
 // with both operands stored row by row (the reduction index p is the row).
-// The fp32 operand (da / du, or g h) comes as an exact bf16 pair
+// X, the fp32 operand (da / du, or g h), comes as an exact bf16 pair
 // (hi, lo = bf16(v - hi)) and is contracted twice against its exact bf16
-// partner, so no value is rounded before the contraction.
+// partner Y, so no value is rounded before the contraction.  dW_d is the
+// transpose of such a product (X = g h, Y = dout) and is stored transposed.
 //
 // Tile: 256 x 256 outputs per 256-thread workgroup; wave w owns rows
 // 64w .. 64w+63 of the tile and all 256 columns (2 x 8 blocks of 32 x 32
 // fp32 accumulators).  Operand rows stream through LDS in slabs of 32 rows
-// x 256 columns (16 KB per operand), three slabs in flight, filled by
+// x 256 columns (16 KB per operand), double buffered, filled by
 // buffer_load ... lds.  The matrix cores want 8 consecutive reduction steps
 // per lane; ds_read_b64_tr_b16 gives each lane of a 16-lane group one
 // column of a 4-row x 16-column block (lane s of the group addresses row
@@ -34,8 +35,7 @@ constexpr int DK = 32;                 // rows per slab
 constexpr int DT = 256;                // tile edge
 constexpr int SLAB = DK * DT * 2;      // bytes of one operand slab (16 KB)
 constexpr int SLOT = 3 * SLAB;         // split hi, split lo, exact partner
-constexpr int NSL = 3;                 // slots (slabs in flight)
-constexpr int V = 12;                  // loads per wave per slab (3 operands x 4)
+constexpr int NSL = 2;                 // slots (double buffer)
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -47,7 +47,7 @@ typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
 struct DParams {
   int N;                    // experts
-  int M, Ncol;              // output [M][Ncol] per expert
+  int M, Ncol;              // product [M][Ncol] per expert (stored transposed if asked)
   const int32_t* offsets;   // [N+1] rows of each expert in dispatch order
   int32_t* sched;           // [8] per-XCD tile counters, zero at launch
   const bf16_t* X;          // split operand, hi part: rows [P][ldx]
@@ -56,7 +56,7 @@ struct DParams {
   const bf16_t* Y;          // exact partner: rows [P][ldy]
   int64_t ldy;
   int64_t rows;             // rows of X and Y (range of the loads)
-  bf16_t* C;                // output per expert, [M][Ncol] row-major
+  bf16_t* C;                // output per expert: [M][Ncol], or [Ncol][M] when transposed
 };
 
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
@@ -91,8 +91,8 @@ __device__ __forceinline__ bf16x8_t tr_operand(lds_u8* slab, int k0, int col0, i
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// SA: the split operand is A (the output rows); otherwise it is B (the columns).
-template <bool SA>
+// TOUT: store the product transposed ([Ncol][M] per expert).
+template <bool TOUT>
 __global__ __launch_bounds__(256, 1) void dw_kernel(DParams p) {
   __shared__ __align__(16) uint8_t ring[NSL * SLOT + 16];
   int32_t* const s_claim = reinterpret_cast<int32_t*>(ring + NSL * SLOT);
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DParams p) {
     // the expert's rows only: a load past them returns zeros and reads nothing
     const uint32_t xbytes = static_cast<uint32_t>((r1 - r0) * p.ldx * 2);
     const uint32_t ybytes = static_cast<uint32_t>((r1 - r0) * p.ldy * 2);
-    const int xcol = SA ? m0 : n0, ycol = SA ? n0 : m0;
+    const int xcol = m0, ycol = n0;
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<bf16_t*>(p.X + r0 * p.ldx + xcol), (short)0, xbytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rxl = __builtin_amdgcn_make_buffer_rsrc(
@@ -185,56 +185,51 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DParams p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    auto compute = [&](int slot) {
+    // Slab kt: every fragment is read into registers first, then slab kt+1's
+    // loads are issued, then the MFMAs run.  The compiler makes a transposing
+    // LDS read wait for every LDS-DMA load in flight, so loads issued before
+    // the reads would hold the reads (and the MFMAs) until they land; issued
+    // after them, they overlap the MFMAs.  Slot kt & 1 holds slab kt.
+    auto step = [&](int kt, int slot) {
       lds_u8* const sb = ring_lds + slot * SLOT;
-      // A (rows of the output tile, this wave's 64) and B (all 256 columns)
-      lds_u8* const a_hi = sb + (SA ? 0 : 2) * SLAB;
-      lds_u8* const b_hi = sb + (SA ? 2 : 0) * SLAB;
+      bf16x8_t a[DK / 16][2], al[DK / 16][2], b[DK / 16][8];
 #pragma unroll
       for (int ks = 0; ks < DK / 16; ++ks) {
-        bf16x8_t a[2], al[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-          a[rb] = tr_operand(a_hi, 16 * ks, 64 * wave + 32 * rb, lane);
-          if constexpr (SA) al[rb] = tr_operand(sb + SLAB, 16 * ks, 64 * wave + 32 * rb, lane);
+          a[ks][rb] = tr_operand(sb, 16 * ks, 64 * wave + 32 * rb, lane);
+          al[ks][rb] = tr_operand(sb + SLAB, 16 * ks, 64 * wave + 32 * rb, lane);
         }
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          const bf16x8_t b = tr_operand(b_hi, 16 * ks, 32 * nb, lane);
-          if constexpr (SA) {
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-              acc[rb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb], b, acc[rb][nb], 0, 0, 0);
-              acc[rb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[rb], b, acc[rb][nb], 0, 0, 0);
-            }
-          } else {
-            const bf16x8_t bl = tr_operand(sb + SLAB, 16 * ks, 32 * nb, lane);
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-              acc[rb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb], b, acc[rb][nb], 0, 0, 0);
-              acc[rb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb], bl, acc[rb][nb], 0, 0, 0);
-            }
-          }
-        }
+        for (int nb = 0; nb < 8; ++nb) b[ks][nb] = tr_operand(sb + 2 * SLAB, 16 * ks, 32 * nb, lane);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < nslab) issue(kt + 1, slot ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < DK / 16; ++ks)
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            acc[rb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][rb], b[ks][nb], acc[rb][nb], 0, 0, 0);
+            acc[rb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[ks][rb], b[ks][nb], acc[rb][nb], 0, 0, 0);
+          }
+      __builtin_amdgcn_sched_barrier(0);
     };
 
-    // slab kt: wait until only the next slab's loads are outstanding,
-    // barrier (slab kt visible, slot of kt-1 free), issue kt+2, multiply kt.
-    // Slabs past the expert's rows are issued too (they read nothing), so
-    // every slab has exactly V loads per wave.  The rows of the last slab
-    // past the expert's end are cleared before that slab is used, so the
-    // sums do not depend on what an out-of-range lane leaves in LDS.
+    // per slab: all of this wave's loads done, barrier (slab kt visible to
+    // every wave, every read of slab kt-1 done, so its slot may refill).  The
+    // rows of the last slab past the expert's end are cleared before use, so
+    // the sums do not depend on what an out-of-range lane leaves in LDS.
     __builtin_amdgcn_sched_barrier(0);
-    issue(0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(1, 1);
+    if (nslab > 0) issue(0, 0);
     __builtin_amdgcn_sched_barrier(0);
     for (int kt = 0; kt < nslab; ++kt) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(V));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __builtin_amdgcn_s_barrier();
       if (kt == nslab - 1 && tail < DK) {
-        lds_u8* const sb = ring_lds + (kt % NSL) * SLOT + tail * (DT * 2);
+        lds_u8* const sb = ring_lds + (kt & 1) * SLOT + tail * (DT * 2);
         const int per = (DK - tail) * (DT * 2 / 16);   // 16-byte pieces per operand
         const u32x4_t z = {0u, 0u, 0u, 0u};
         for (int q = tid; q < 3 * per; q += 256) {
@@ -243,27 +238,58 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DParams p) {
         }
         __syncthreads();
       }
-      issue(kt + 2, (kt + 2) % NSL);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(kt % NSL);
-      __builtin_amdgcn_sched_barrier(0);
+      step(kt, kt & 1);
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();  // every wave done with the ring before the next tile's loads
 
     // ---- epilogue: lane holds column lane%32 of block nb, rows
     // 64 w + 32 rb + 8 (v/4) + 4 (lane/32) + v%4
     bf16_t* Ce = p.C + static_cast<int64_t>(e) * p.M * p.Ncol;
+    if constexpr (TOUT) {
+      // Transposed: in two passes (rb = 0, 1: product rows 64 w + 32 rb ..
+      // + 31 of every wave), the tile goes through the idle ring as output
+      // rows n x 128 columns mc = 32 w + (row - 64 w - 32 rb), pitch padded
+      // to PT elements against bank conflicts, then out in 16-byte pieces
+      // (every 32 columns are contiguous in the output row).
+      constexpr int PT = 136;
+      bf16_t* st = reinterpret_cast<bf16_t*>(ring);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
+        for (int nb = 0; nb < 8; ++nb) {
+          const int nl = 32 * nb + (lane & 31);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = m0 + 64 * wave + 32 * rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const int n = n0 + 32 * nb + (lane & 31);
-          Ce[static_cast<int64_t>(m) * p.Ncol + n] = cvt_bf16(acc[rb][nb][v]);
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int mc = 32 * wave + 8 * g4 + 4 * (lane >> 5);
+            const uint32_t w0 = cvt_bf16(acc[rb][nb][4 * g4]) |
+                                (static_cast<uint32_t>(cvt_bf16(acc[rb][nb][4 * g4 + 1])) << 16);
+            const uint32_t w1 = cvt_bf16(acc[rb][nb][4 * g4 + 2]) |
+                                (static_cast<uint32_t>(cvt_bf16(acc[rb][nb][4 * g4 + 3])) << 16);
+            *reinterpret_cast<uint2*>(st + nl * PT + mc) = make_uint2(w0, w1);
+          }
         }
+        __syncthreads();
+        for (int c = tid; c < DT * 16; c += 256) {
+          const int nl = c >> 4, cc = c & 15;
+          const int m = m0 + 32 * rb + 64 * (cc >> 2) + 8 * (cc & 3);
+          *reinterpret_cast<u32x4_t*>(Ce + static_cast<int64_t>(n0 + nl) * p.M + m) =
+              *reinterpret_cast<const u32x4_t*>(st + nl * PT + 8 * cc);
+        }
+        __syncthreads();
+      }
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const int n = n0 + 32 * nb + (lane & 31);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int m = m0 + 64 * wave + 32 * rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            Ce[static_cast<int64_t>(m) * p.Ncol + n] = cvt_bf16(acc[rb][nb][v]);
+          }
+        }
+    }
   }
 }
 
@@ -297,13 +323,13 @@ hipError_t launch_gather_rows(const bf16_t* src, const int32_t* perm, const int3
   return hipGetLastError();
 }
 
-hipError_t launch_dw(bool split_a, int N, int M, int Ncol, const int32_t* offsets, int32_t* sched,
-                     const bf16_t* X, const bf16_t* XL, int64_t ldx, const bf16_t* Y, int64_t ldy,
-                     int64_t rows, bf16_t* C, int cu, hipStream_t s) {
+hipError_t launch_dw(bool transposed, int N, int M, int Ncol, const int32_t* offsets,
+                     int32_t* sched, const bf16_t* X, const bf16_t* XL, int64_t ldx, const bf16_t* Y,
+                     int64_t ldy, int64_t rows, bf16_t* C, int cu, hipStream_t s) {
   DParams p{};
   p.N = N; p.M = M; p.Ncol = Ncol; p.offsets = offsets; p.sched = sched;
   p.X = X; p.XL = XL; p.ldx = ldx; p.Y = Y; p.ldy = ldy; p.rows = rows; p.C = C;
-  if (split_a)
+  if (transposed)
     hipLaunchKernelGGL(dw_kernel<true>, dim3(cu), dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(dw_kernel<false>, dim3(cu), dim3(256), 0, s, p);

@@ -189,13 +189,14 @@ hipError_t launch_bwdp_dh(const bf16_t* dout, int64_t dout_elems, const bf16_t* 
 hipError_t launch_swiglu_bwd(const float* dh, const float* gs, const float* sa, const float* su,
                              const float* sh, const int32_t* offsets, int N, int I,
                              int64_t max_rows, bf16_t* hilo, bf16_t* ghlo, hipStream_t s);
-// Expert weight gradients (gemm_dw.hip): per expert e, C_e = sum over its
-// rows p of A[p]^T B[p] with the split operand X (exact bf16 hi/lo pair X,
-// XL) as A (split_a) or B and its exact partner Y as the other; output
-// [M][Ncol] bf16 per expert; sched: 8 counters, zero at launch.
-hipError_t launch_dw(bool split_a, int N, int M, int Ncol, const int32_t* offsets, int32_t* sched,
-                     const bf16_t* X, const bf16_t* XL, int64_t ldx, const bf16_t* Y, int64_t ldy,
-                     int64_t rows, bf16_t* C, int cu, hipStream_t s);
+// Expert weight gradients (gemm_dw.hip): per expert e, the [M][Ncol]
+// product sum over its rows p of X[p]^T Y[p], X given as an exact bf16
+// hi/lo pair (X, XL: columns 0..M of rows of pitch ldx), Y exact bf16;
+// stored [M][Ncol] bf16 per expert, or [Ncol][M] when transposed; sched: 8
+// counters, zero at launch.
+hipError_t launch_dw(bool transposed, int N, int M, int Ncol, const int32_t* offsets,
+                     int32_t* sched, const bf16_t* X, const bf16_t* XL, int64_t ldx, const bf16_t* Y,
+                     int64_t ldy, int64_t rows, bf16_t* C, int cu, hipStream_t s);
 // dst[p] = src[perm[p] / K] (rows of width w) for the FFN picks in dispatch order.
 hipError_t launch_gather_rows(const bf16_t* src, const int32_t* perm, const int32_t* offsets,
                               int N, int K, int w, int64_t max_rows, bf16_t* dst, hipStream_t s);
