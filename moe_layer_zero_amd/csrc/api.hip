@@ -464,16 +464,10 @@ zc_status do_forward(const zc_moe_desc* d, const T* x, const T* wr, const float*
                                        rw.tile_off2, rw.tile_exp, rw.sched, fwd_rows_per_tile(d), N,
                                        I, dd, K, hq, hs, cu, s),
                 "gate/up GEMM launch");
-      // the MXFP8 down GEMM stops at 128-row tiles (its 256-row variant
-      // would not fit the register file): there it runs on the kGemmBM-row
-      // tiling of the first prefix
-      const int tmu = fwd_rows_per_tile(d);
-      const bool split = tmu > zc::kGemmBM;
       ZC_LAUNCH(ZC_PH_DOWN,
                 zc::launch_fwdq_down(hq, hs, rows, reinterpret_cast<const uint8_t*>(wd), r->offsets,
-                                     split ? rw.tile_off : rw.tile_off2,
-                                     split ? rw.tile_exp1 : rw.tile_exp, rw.sched + 8,
-                                     split ? zc::kGemmBM : tmu, N, I, dd,
+                                     rw.tile_off2, rw.tile_exp, rw.sched + 8,
+                                     fwd_rows_per_tile(d), N, I, dd,
                                      reinterpret_cast<bf16_t*>(y), cu, s),
                 "down GEMM launch");
     } else if (d->weight_layout == ZC_WEIGHTS_PACKED) {

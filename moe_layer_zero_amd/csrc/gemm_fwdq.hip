@@ -547,9 +547,8 @@ __global__ __launch_bounds__(256) void mxq_weights_kernel(const bf16_t* __restri
 }
 
 typedef void (*fwdq_fn)(QParams);
-// Tile heights 32 .. 256 for gate/up, 32 .. 128 for down (its 256-row tile
-// does not fit the register file without spills, whose memory traffic in
-// flight would upset the per-slab wait counts).
+// Tile heights 32 .. 256 (the 256-row down tile spills a few registers in
+// its tile setup and epilogue, none inside the k loop).
 fwdq_fn pick_q(int epi, int tm, int* per_cu) {
   *per_cu = tm <= 64 ? 2 : 1;
   if (epi == Q_SWIGLU) {
@@ -564,6 +563,7 @@ fwdq_fn pick_q(int epi, int tm, int* per_cu) {
       case 32: return fwdq_kernel<Q_STORE, 32>;
       case 64: return fwdq_kernel<Q_STORE, 64>;
       case 128: return fwdq_kernel<Q_STORE, 128>;
+      case 256: return fwdq_kernel<Q_STORE, 256>;
     }
   }
   return nullptr;
