@@ -7,6 +7,8 @@ moe_layer_zero_amd/libzcmoe.so.  Flags:
                                          keep packed fp32 ops out of the ISA
   -ffp-contract=off (router, pid)        the routing keys and the bias update
                                          follow a fixed IEEE operation order
+  -mllvm -amdgpu-atomic-optimizer-strategy=None (packed GEMMs)
+                                         tile claims stay single-lane atomics
 """
 import concurrent.futures as cf
 import os
@@ -22,6 +24,10 @@ ARCH = "gfx950"
 SOURCES = ["api.hip", "router.hip", "dispatch.hip", "gemm.hip", "gemm_fwd.hip", "gemm_fwdp.hip",
            "gemm_fwdq.hip", "gemm_dw.hip", "combine.hip", "pid.hip"]
 STRICT_FP = {"router.hip", "pid.hip"}
+# The persistent GEMMs claim tiles with one lane's atomic whose result is used
+# a whole tile later; the atomic optimizer would broadcast it to the wave at
+# once, making every claim wait for all memory operations in flight.
+NO_ATOMIC_OPT = {"gemm_fwdp.hip", "gemm_fwdq.hip"}
 
 COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -33,6 +39,8 @@ def _compile(src: str, verbose: bool) -> str:
     cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
     if src in STRICT_FP:
         cmd.insert(1, "-ffp-contract=off")
+    if src in NO_ATOMIC_OPT:
+        cmd[1:1] = ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   constexpr int OUTN = EPI == P_SWIGLU ? 128 : 256;  // output columns per tile
   constexpr bool GATHER = EPI == P_SWIGLU || EPI == P_DSWIGLU;  // A rows are token rows
   const int NT = p.ncols / OUTN;
-  const int64_t total = static_cast<int64_t>(p.mt_off[p.N]) * NT;
+  const int64_t total = static_cast<int64_t>(ld_scalar(p.mt_off + p.N)) * NT;
   const int G = gridDim.x;
   // Tiles are dealt to the 8 XCDs in chunks of G/8 consecutive tiles, round
   // robin (blocks are dealt to the XCDs round robin, so block b runs on XCD
@@ -185,9 +185,10 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
     if (tid == 0) next_n = atomicAdd(p.sched + cx, 1);
     // ---- which expert, row tile and column tile
     const int lmt = static_cast<int>(L / NT);
-    const int e = p.tile_exp[lmt];
-    const int mte = p.mt_off[e + 1] - p.mt_off[e];
-    const int q = static_cast<int>(L - static_cast<int64_t>(p.mt_off[e]) * NT);
+    const int e = ld_scalar(p.tile_exp + lmt);
+    const int mt_e = ld_scalar(p.mt_off + e);
+    const int mte = ld_scalar(p.mt_off + e + 1) - mt_e;
+    const int q = static_cast<int>(L - static_cast<int64_t>(mt_e) * NT);
     const int grp = q / (GMV * NT);
     const int fm = grp * GMV;
     const int gsz = min(GMV, mte - fm);
@@ -197,10 +198,11 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
     // the expert's 32-row blocks spread evenly over its mte row tiles (at
     // most TM / 32 each), so the row tiles that share a weight panel do the
     // same work, stream the panel at the same pace and find it in L2
-    const int nbe = (p.offsets[e + 1] - p.offsets[e] + 31) >> 5;
+    const int seg0 = ld_scalar(p.offsets + e), seg1 = ld_scalar(p.offsets + e + 1);
+    const int nbe = (seg1 - seg0 + 31) >> 5;
     const int blo = nbe * mt / mte, bhi = nbe * (mt + 1) / mte;
-    const int m0 = p.offsets[e] + 32 * blo;
-    const int mcount = min(p.offsets[e] + 32 * bhi, p.offsets[e + 1]) - m0;
+    const int m0 = seg0 + 32 * blo;
+    const int mcount = min(seg0 + 32 * bhi, seg1) - m0;
     const int n0 = nt * OUTN;
 
     // ---- byte offsets of the RB A row pieces this lane copies per slab
@@ -451,6 +453,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
       }
       __syncthreads();
       constexpr int RC = OUTN / 8;  // 16-byte chunks per row
+#pragma unroll 4
       for (int c = tid; c < mcount * RC; c += NTHR) {
         const int rl = c / RC, cc = (c % RC) * 8;
         *reinterpret_cast<u32x4_t*>(p.C + static_cast<int64_t>(m0 + rl) * p.ncols + n0 + cc) =

@@ -27,6 +27,15 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   return static_cast<bf16_t>(u >> 16);
 }
 
+// A wave-uniform read of a table that no kernel writes while the reading one
+// runs (tile and segment prefixes), as a scalar load: scalar loads are counted
+// apart from the vector memory operations, so the reader does not wait on
+// loads, stores or atomics it has in flight.
+template <typename T>
+__device__ __forceinline__ T ld_scalar(const T* ptr) {
+  return *(const __attribute__((address_space(4))) T*)ptr;
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static __device__ __forceinline__ float ld(const float* p) { return *p; }
