@@ -38,8 +38,8 @@ FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, vendor figure
 # size gives), valid for the kernel source they were measured on: reported
 # as roofline.traffic only while that source is unchanged.
 GATE_UP_TRAFFIC = {"source": "moe_layer_zero_amd/csrc/gemm_fwdp.hip",
-                   "sha256": "b1e3cf9e21a9b21e981f80163015f6a530254ef9b74386594d3bbbf57f84e763",
-                   "fetch_bytes": 31834031872, "write_bytes": 588773376}
+                   "sha256": "042051d4820c15c119f92103cd0b86676dcb24ffa1ae750b0b5464dff5d70122",
+                   "fetch_bytes": 31680321195, "write_bytes": 588773376}
 
 
 def measured_traffic():
