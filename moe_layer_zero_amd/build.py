@@ -27,7 +27,7 @@ STRICT_FP = {"router.hip", "pid.hip"}
 # The persistent GEMMs claim tiles with one lane's atomic whose result is used
 # a whole tile later; the atomic optimizer would broadcast it to the wave at
 # once, making every claim wait for all memory operations in flight.
-NO_ATOMIC_OPT = {"gemm_fwdp.hip", "gemm_fwdq.hip"}
+NO_ATOMIC_OPT = {"gemm_fwdp.hip", "gemm_fwdq.hip", "gemm_dw.hip"}
 
 COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

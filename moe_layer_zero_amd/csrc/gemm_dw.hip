@@ -110,12 +110,8 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DParams p) {
   auto tile_of = [&](int x, int n) -> int64_t {
     return static_cast<int64_t>(n / C) * 8 * C + x * C + n % C;
   };
-  // the claim of thread 0 on counter cx -> a tile, or -1 when all are taken
-  auto next_tile = [&](int32_t pre) -> int64_t {
-    __syncthreads();
-    if (tid == 0) s_claim[0] = pre;
-    __syncthreads();
-    int n = __builtin_amdgcn_readfirstlane(s_claim[0]);
+  // a claimed index n on counter cx -> a tile, or -1 when all are taken
+  auto resolve = [&](int n) -> int64_t {
     for (;;) {
       const int64_t L = tile_of(cx, n);
       if (L < total) return L;
@@ -128,20 +124,24 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DParams p) {
     }
   };
 
+  // Tiles are claimed one ahead: the claim of the next tile is made when a
+  // tile starts and published after its k loop, so its atomic's round trip
+  // is hidden and no claim waits for the previous tile's output stores.
+  if (tid == 0) s_claim[0] = atomicAdd(p.sched + cx, 1);
+  __syncthreads();
+  int64_t L = resolve(__builtin_amdgcn_readfirstlane(s_claim[0]));
   // operand order in a slot: 0 = split hi, 1 = split lo, 2 = exact partner
-  for (;;) {
+  while (L >= 0) {
     int32_t pre = 0;
     if (tid == 0) pre = atomicAdd(p.sched + cx, 1);
-    const int64_t L = next_tile(pre);
-    if (L < 0) break;
     // wave-uniform tile coordinates and row range, in scalar registers (the
     // buffer resources below are built from them; a value the compiler
     // cannot prove uniform would wrap every load in a per-lane loop)
     const int e = __builtin_amdgcn_readfirstlane(static_cast<int>(L / (MT * NT)));
     const int rem = __builtin_amdgcn_readfirstlane(static_cast<int>(L - static_cast<int64_t>(e) * MT * NT));
     const int m0 = (rem / NT) * DT, n0 = (rem % NT) * DT;
-    const int r0 = __builtin_amdgcn_readfirstlane(p.offsets[e]);
-    const int r1 = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
+    const int r0 = ld_scalar(p.offsets + e);
+    const int r1 = ld_scalar(p.offsets + e + 1);
     const int nslab = (r1 - r0 + DK - 1) / DK;
     const int tail = (r1 - r0) - DK * (nslab - 1);   // rows of the last slab
     // the expert's rows only: a load past them returns zeros and reads nothing
@@ -241,6 +241,9 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DParams p) {
       step(kt, kt & 1);
     }
     __syncthreads();  // every wave done with the ring before the next tile's loads
+    if (tid == 0) s_claim[0] = pre;
+    __syncthreads();  // published (every thread read the previous claim a tile ago)
+    const int next_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
 
     // ---- epilogue: lane holds column lane%32 of block nb, rows
     // 64 w + 32 rb + 8 (v/4) + 4 (lane/32) + v%4
@@ -290,6 +293,7 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DParams p) {
           }
         }
     }
+    L = resolve(next_n);
   }
 }
 
