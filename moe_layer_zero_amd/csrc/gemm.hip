@@ -174,7 +174,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(Params p) {
   int mt_tot;
   int64_t total;
   if constexpr (GRP == MGROUP) {
-    mt_tot = p.tile_off[p.ngroups];
+    mt_tot = ld_scalar(p.tile_off + p.ngroups);
     total = static_cast<int64_t>(mt_tot) * ntile_n;
   } else if constexpr (GRP == DENSE) {
     mt_tot = (p.M + BM - 1) / BM;
@@ -206,19 +206,19 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(Params p) {
       int lo = 0, hi = p.ngroups - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (p.tile_off[mid] <= mt) lo = mid;
+        if (ld_scalar(p.tile_off + mid) <= mt) lo = mid;
         else hi = mid - 1;
       }
       g = lo;
-      m0 = p.goff[g] + (mt - p.tile_off[g]) * BM;
-      mcount = min(BM, p.goff[g + 1] - m0);
+      m0 = ld_scalar(p.goff + g) + (mt - ld_scalar(p.tile_off + g)) * BM;
+      mcount = min(BM, ld_scalar(p.goff + g + 1) - m0);
     } else {
       m0 = mt * BM;
       mcount = min(BM, p.M - m0);
       if constexpr (GRP == KGROUP) {
         if (p.goff) {
-          kbeg = p.goff[g];
-          kend = p.goff[g + 1];
+          kbeg = ld_scalar(p.goff + g);
+          kend = ld_scalar(p.goff + g + 1);
         } else {
           kbeg = g * p.kchunk;
           kend = min(p.K, kbeg + p.kchunk);
