@@ -21,14 +21,18 @@ constexpr int kMaxK = 32;
 template <typename T> struct V16;
 template <> struct V16<bf16_t> {
   static constexpr int n = 8;
-  static __device__ __forceinline__ void load(const bf16_t* p, float* f) {
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+  typedef u32x4_t raw_t;  // the 16 bytes as loaded
+  static __device__ __forceinline__ raw_t ld_raw(const bf16_t* p) {
+    return *reinterpret_cast<const u32x4_t*>(p);
+  }
+  static __device__ __forceinline__ void unpack(const raw_t& v, float* f) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       f[2 * e] = __uint_as_float(v[e] << 16);
       f[2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
     }
   }
+  static __device__ __forceinline__ void load(const bf16_t* p, float* f) { unpack(ld_raw(p), f); }
   static __device__ __forceinline__ void store(bf16_t* p, const float* f) {
     u32x4_t v;
 #pragma unroll
@@ -39,11 +43,15 @@ template <> struct V16<bf16_t> {
 };
 template <> struct V16<float> {
   static constexpr int n = 4;
-  static __device__ __forceinline__ void load(const float* p, float* f) {
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p);
+  typedef f32x4_t raw_t;
+  static __device__ __forceinline__ raw_t ld_raw(const float* p) {
+    return *reinterpret_cast<const f32x4_t*>(p);
+  }
+  static __device__ __forceinline__ void unpack(const raw_t& v, float* f) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) f[e] = v[e];
   }
+  static __device__ __forceinline__ void load(const float* p, float* f) { unpack(ld_raw(p), f); }
   static __device__ __forceinline__ void store(float* p, const float* f) {
     *reinterpret_cast<f32x4_t*>(p) = f32x4_t{f[0], f[1], f[2], f[3]};
   }
@@ -97,13 +105,25 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     V16<T>::load(x + t * d + j, v);
 #pragma unroll
     for (int e = 0; e < V; ++e) acc[e] = c * v[e];
-    for (int r = 0; r < K; ++r) {
-      const int q = s_inv[r];
-      if (q < 0) continue;
-      V16<T>::load(y + static_cast<int64_t>(q) * d + j, v);
-      const float g = s_g[r];
+    // picks in groups of four: the group's row loads are issued together,
+    // then added in slot order
+    for (int r0 = 0; r0 < K; r0 += 4) {
+      // (a slot past K or of a zero-computation pick loads the token's own
+      // x piece, just read, and is skipped below)
+      typename V16<T>::raw_t w[4];
 #pragma unroll
-      for (int e = 0; e < V; ++e) acc[e] += g * v[e];
+      for (int u = 0; u < 4; ++u) {
+        const int q = r0 + u < K ? s_inv[r0 + u] : -1;
+        w[u] = V16<T>::ld_raw(q >= 0 ? y + static_cast<int64_t>(q) * d + j : x + t * d + j);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (r0 + u >= K || s_inv[r0 + u] < 0) continue;
+        const float g = s_g[r0 + u];
+        V16<T>::unpack(w[u], v);
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[e] += g * v[e];
+      }
     }
 #pragma unroll
     for (int e = 0; e < V; ++e) acc[e] *= out_scale;
@@ -227,12 +247,21 @@ __global__ __launch_bounds__(kThreads) void dx_gather_kernel(
     V16<T>::load(dout + t * d + j, v);
 #pragma unroll
     for (int e = 0; e < V; ++e) acc[e] = c * v[e];
-    for (int r = 0; r < K; ++r) {
-      const int q = s_inv[r];
-      if (q < 0) continue;
-      load_f32(dxp + static_cast<int64_t>(q) * d + j, v);
+    for (int r0 = 0; r0 < K; r0 += 4) {  // as in the combine: loads of four picks together
+      // (a slot past K or of a zero-computation pick loads the token's own
+      // router-dx piece, read below anyway, and is skipped)
+      float w[4][V];
 #pragma unroll
-      for (int e = 0; e < V; ++e) acc[e] += v[e];
+      for (int u = 0; u < 4; ++u) {
+        const int q = r0 + u < K ? s_inv[r0 + u] : -1;
+        load_f32(q >= 0 ? dxp + static_cast<int64_t>(q) * d + j : dxr + t * d + j, w[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (r0 + u >= K || s_inv[r0 + u] < 0) continue;
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[e] += w[u][e];
+      }
     }
     load_f32(dxr + t * d + j, v);
 #pragma unroll
