@@ -169,19 +169,36 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
   load_picks(topk_idx, gate, inv, t, N, K, s_g, s_inv, &s_c);
   if (threadIdx.x < K && s_inv[threadIdx.x] >= 0) gs[s_inv[threadIdx.x]] = out_scale * s_g[threadIdx.x];
   constexpr int V = V16<T>::n;
-  for (int r = 0; r < K; ++r) {
-    const int q = s_inv[r];
-    const T* src = q >= 0 ? y + static_cast<int64_t>(q) * d : x + t * d;
-    float part = 0.f;
+  // picks in groups of four: one pass over dout for the group, the four
+  // rows' loads issued together; each pick's partial sum runs over j in the
+  // same order as a pass of its own would
+  for (int r0 = 0; r0 < K; r0 += 4) {
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    const T* src[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = r0 + u < K ? s_inv[r0 + u] : -1;
+      src[u] = q >= 0 ? y + static_cast<int64_t>(q) * d : x + t * d;
+    }
     for (int j = threadIdx.x * V; j < d; j += kThreads * V) {
       float dv[V], v[V];
+      typename V16<T>::raw_t w[4];
       V16<T>::load(dout + t * d + j, dv);
-      V16<T>::load(src + j, v);
 #pragma unroll
-      for (int e = 0; e < V; ++e) part += (out_scale * dv[e]) * v[e];
+      for (int u = 0; u < 4; ++u) w[u] = V16<T>::ld_raw(src[u] + j);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        V16<T>::unpack(w[u], v);
+#pragma unroll
+        for (int e = 0; e < V; ++e) part[u] += (out_scale * dv[e]) * v[e];
+      }
     }
-    const float tot = block_sum(part, s_red);
-    if (threadIdx.x == 0) s_dg[r] = tot;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (r0 + u >= K) break;
+      const float tot = block_sum(part[u], s_red);
+      if (threadIdx.x == 0) s_dg[r0 + u] = tot;
+    }
   }
   __syncthreads();
   if (threadIdx.x < K) dg_out[t * K + threadIdx.x] = s_dg[threadIdx.x];
