@@ -48,13 +48,15 @@ def lib():
         L.orc_mx_quantize.argtypes = [_i64, _i64, _i32, _p, _p, _p]
         L.orc_mx_dequantize.argtypes = [_i64, _i64, _p, _p, _p]
         L.orc_forward_mx.argtypes = [_i64, _i64, _i64, _i64, _i64, _i32, _f64, _p, _p, _p, _p,
-                                     _p, _p, _p, _p, _p, _i64, _p, _p, _p, _f64, _p]
+                                     _p, _p, _p, _p, _p, _i64, _p, _p, _p]
+        L.orc_mx_flip_bound.argtypes = [_i64, _i64, _i64, _i64, _i64, _i32, _f64, _p, _p, _p,
+                                        _p, _p, _p, _p, _p, _p, _i64, _p, _f64, _p]
         L.orc_num_threads.restype = C.c_int
         L.orc_num_threads.argtypes = []
         L.orc_pid_update.argtypes = [_i64, _i64, _i64, _p, _i64, _f64, _f64, _p]
         for f in ("orc_logits", "orc_route", "orc_forward", "orc_backward", "orc_pid_update",
                   "orc_lb_loss", "orc_route_stats", "orc_mx_quantize", "orc_mx_dequantize",
-                  "orc_forward_mx"):
+                  "orc_forward_mx", "orc_mx_flip_bound"):
             getattr(L, f).restype = C.c_int
         _LIB = L
     return _LIB
@@ -175,10 +177,13 @@ def forward(x, wg, wu, wd, topk_idx, gates, N, out_scale=1.0, toks=None, want_y=
 
 
 def backward(x, wr, wg, wu, wd, lg, topk_idx, gates, dY, N, Z, gate_norm=1, out_scale=1.0,
-             toks=None, want_experts=None, want_dwr=True, dl_extra=None):
-    """O9.  Returns dict with dx [n,d], dwr [E,d] (or None), dwg/dwu/dwd as
-    {e: array} for experts in want_experts (all N when None).  dl_extra
-    ([T,E], e.g. lb_loss's dlogits) is added to the router-score gradient."""
+             toks=None, want_experts=None, want_dwr=True, dl_extra=None, want_dx=True):
+    """O9.  Returns dict with dx [n,d] (None when not want_dx), dwr [E,d] (or
+    None), dwg/dwu/dwd as {e: array} for experts in want_experts (all N when
+    None).  dl_extra ([T,E], e.g. lb_loss's dlogits) is added to the
+    router-score gradient.  want_dx = want_dwr = False differentiates only
+    the picks of the wanted experts (their weight gradients need nothing
+    else); wg/wu/wd then need blocks for those experts only."""
     x, wr, dY = _c(x), _c(wr), _c(dY)
     T, d = x.shape
     E = N + Z
@@ -196,7 +201,8 @@ def backward(x, wr, wg, wu, wd, lg, topk_idx, gates, dY, N, Z, gate_norm=1, out_
     if ex is not None:
         assert ex.shape == (T, E)
     n = T if tk is None else len(tk)
-    dx = np.empty((n, d), np.float64)
+    assert want_dx or not want_dwr, "the router gradient comes with dx"
+    dx = np.empty((n, d), np.float64) if want_dx else None
     dwr = np.zeros((E, d), np.float64) if want_dwr else None
     wanted = range(N) if want_experts is None else want_experts
     dwg = {e: np.zeros((I, d), np.float64) for e in wanted}
@@ -291,18 +297,7 @@ def mx_weights(w: np.ndarray):
     return mx_quantize(w)
 
 
-def forward_mx(x, wgq, wuq, wdq, topk_idx, gates, N, out_scale=1.0, toks=None, want_y=False,
-               flip_eps=None):
-    """O13: the layer forward with MXFP8 expert operands.  wgq / wuq / wdq:
-    {expert: (codes, scales)} (mx_weights) for every FFN expert the listed
-    tokens pick.  With flip_eps (the accuracy of fp32 dot products relative
-    to their sum of absolute products), also returns the per-element bound
-    of the output change from h codes that sit that close to a code or scale
-    boundary (see orc.c)."""
-    x = _c(x)
-    T, d = x.shape
-    K = topk_idx.shape[1]
-    I = next(iter(wgq.values()))[0].shape[0] if wgq else 32  # no FFN pick: any I
+def _mx_tables(wgq, wuq, wdq, N):
     tabs, keep = [], []
     for src in (wgq, wuq, wdq):
         for part in (0, 1):
@@ -310,17 +305,49 @@ def forward_mx(x, wgq, wuq, wdq, topk_idx, gates, N, out_scale=1.0, toks=None, w
             t, k = _table(arrs, N)
             tabs.append(t)
             keep.append((arrs, k))
+    return tabs, keep
+
+
+def forward_mx(x, wgq, wuq, wdq, topk_idx, gates, N, out_scale=1.0, toks=None, want_y=False):
+    """O13: the layer forward with MXFP8 expert operands (h quantized from its
+    binary64 value).  wgq / wuq / wdq: {expert: (codes, scales)}
+    (mx_weights) for every FFN expert the listed tokens pick."""
+    x = _c(x)
+    T, d = x.shape
+    K = topk_idx.shape[1]
+    I = next(iter(wgq.values()))[0].shape[0] if wgq else 32  # no FFN pick: any I
+    tabs, keep = _mx_tables(wgq, wuq, wdq, N)
     ti = _c(topk_idx, np.int32)
     gg = _c(gates, np.float64)
     tk = None if toks is None else _c(np.asarray(toks), np.int64)
     n = T if tk is None else len(tk)
     out = np.empty((n, d), np.float64)
     y = np.empty((n * K, d), np.float64) if want_y else None
-    fl = np.empty((n, d), np.float64) if flip_eps is not None else None
     rc = lib().orc_forward_mx(T, d, N, I, K, _dt(x), float(out_scale), _ptr(x), *tabs,
-                              _ptr(ti), _ptr(gg), n, _ptr(tk), _ptr(out), _ptr(y),
-                              float(flip_eps or 0.0), _ptr(fl))
+                              _ptr(ti), _ptr(gg), n, _ptr(tk), _ptr(out), _ptr(y))
     assert rc == 0, f"oracle forward_mx failed rc={rc}"
     del keep
-    res = (out,) + ((y,) if want_y else ()) + ((fl,) if flip_eps is not None else ())
-    return res if len(res) > 1 else out
+    return (out, y) if want_y else out
+
+
+def mx_flip_bound(x, wgq, wuq, wdq, topk_idx, gates, N, eps, out_scale=1.0, toks=None):
+    """Tolerance helper for comparisons against forward_mx (not part of the
+    layer): per output element, the largest change that h codes lying within
+    the fp32 uncertainty of h (eps relative to the dot products' sums of
+    absolute products) of a code or scale boundary can cause.  Same
+    arguments as forward_mx; returns [n, d]."""
+    x = _c(x)
+    T, d = x.shape
+    K = topk_idx.shape[1]
+    I = next(iter(wgq.values()))[0].shape[0] if wgq else 32
+    tabs, keep = _mx_tables(wgq, wuq, wdq, N)
+    ti = _c(topk_idx, np.int32)
+    gg = _c(gates, np.float64)
+    tk = None if toks is None else _c(np.asarray(toks), np.int64)
+    n = T if tk is None else len(tk)
+    fl = np.empty((n, d), np.float64)
+    rc = lib().orc_mx_flip_bound(T, d, N, I, K, _dt(x), float(out_scale), _ptr(x), *tabs,
+                                 _ptr(ti), _ptr(gg), n, _ptr(tk), float(eps), _ptr(fl))
+    assert rc == 0, f"oracle mx_flip_bound failed rc={rc}"
+    del keep
+    return fl

@@ -64,6 +64,7 @@ static const double ORC_LN2_TAIL = -0x1.718432a1b0e26p-35;
 static const double ORC_INV_LN2 = 0x1.71547652b82fep+0;
 
 double orc_exp(double z) {
+  if (isnan(z)) return z;
   if (z < -700.0) return 0.0;
   double k = rint(z * ORC_INV_LN2);
   double r = (z - k * ORC_LN2_HEAD) - k * ORC_LN2_TAIL;
@@ -120,7 +121,10 @@ int orc_logits(int64_t T, int64_t d, int64_t E, int dt, const void* x,
  * counts T_i of Eq.(2) and the canonical dispatch order.
  *
  *  keys:   m = max_j l_j; e_j = orc_exp(l_j - m); S = orc_sum64(e);
- *          p_j = e_j / S; key_j = p_j + (double)b_j.
+ *          p_j = e_j / S; key_j = p_j + (double)b_j; a NaN key counts
+ *          as -infinity (a NaN or infinite score makes all of a token's
+ *          keys NaN; the selection below then stays total: picks 0..K-1,
+ *          NaN gates).
  *  top-K:  K rounds; round r takes the unselected j with the largest key,
  *          equal keys going to the smaller j.  Slot r is the r-th pick.
  *  gates:  gate_norm = 1: g_r = e_{s_r} / (sum_{q<K} e_{s_q}, q ascending)
@@ -155,6 +159,7 @@ int orc_route(int64_t T, int64_t E, int64_t N, int64_t K, int gate_norm,
       double S = orc_sum64(e, E);
       for (int64_t j = 0; j < E; ++j) {
         key[j] = e[j] / S + (double)bias[j];
+        if (isnan(key[j])) key[j] = -INFINITY;
         taken[j] = 0;
       }
       if (keys_out)
@@ -314,7 +319,11 @@ int orc_forward(int64_t T, int64_t d, int64_t N, int64_t I, int64_t K, int dt,
  * gates must be the gates of the same gate_norm mode.
  * dl_extra (nullable, [T][E]) is a further gradient of the objective with
  * respect to the router scores (the load-balance loss's, from
- * orc_lb_loss); it is added to dl above before dWr and the dx term. */
+ * orc_lb_loss); it is added to dl above before dWr and the dx term.
+ * dx = NULL asks for the listed experts' weight gradients alone: then dwr
+ * must be NULL, and only the FFN picks of experts with a gradient table
+ * entry are differentiated (the other picks and the router contribute
+ * nothing to those gradients). */
 int orc_backward(int64_t T, int64_t d, int64_t N, int64_t Z, int64_t I,
                  int64_t K, int dt, int gate_norm, double out_scale,
                  const void* x, const void* wr, const void* const* wg,
@@ -325,15 +334,19 @@ int orc_backward(int64_t T, int64_t d, int64_t N, int64_t Z, int64_t I,
                  double* dwr, double* const* dwg, double* const* dwu,
                  double* const* dwd) {
   const int64_t E = N + Z;
-  if (!x || !wr || !wg || !wu || !wd || !logits || !topk_idx || !gates || !dY || !dx)
+  if (!x || !wr || !wg || !wu || !wd || !logits || !topk_idx || !gates || !dY ||
+      (!dx && dwr))
     return 1;
+  const int experts_only = dx == NULL;
   if (!toks) n_tok = T;
   for (int64_t q = 0; q < n_tok; ++q) {
     int64_t t = toks ? toks[q] : q;
     if (t < 0 || t >= T) return 1;
     for (int64_t r = 0; r < K; ++r) {
       int64_t e = topk_idx[t * K + r];
-      if (e < N && (!wg[e] || !wu[e] || !wd[e])) return 1;
+      if (e < N && (!wg[e] || !wu[e] || !wd[e]) &&
+          (!experts_only || dwg[e] || dwu[e] || dwd[e]))
+        return 1;
     }
   }
   /* per-slot saved quantities, needed again for the weight gradients */
@@ -359,15 +372,16 @@ int orc_backward(int64_t T, int64_t d, int64_t N, int64_t Z, int64_t I,
 #pragma omp for schedule(dynamic, 1)
     for (int64_t q = 0; q < n_tok; ++q) {
       int64_t t = toks ? toks[q] : q;
-      double* dxo = dx + q * d;
+      double* dxo = experts_only ? NULL : dx + q * d;
       for (int64_t n = 0; n < d; ++n) {
         dys[n] = out_scale * ld(dY, dt, t * d + n);
-        dxo[n] = 0.0;
+        if (dxo) dxo[n] = 0.0;
       }
       for (int64_t r = 0; r < K; ++r) {
         int64_t e = topk_idx[t * K + r];
         double g = gates[t * K + r];
         int64_t sl = q * K + r;
+        if (experts_only && (e >= N || (!dwg[e] && !dwu[e] && !dwd[e]))) continue;
         if (e >= N) {
           double s = 0.0;
           for (int64_t n = 0; n < d; ++n) s += dys[n] * ld(x, dt, t * d + n);
@@ -393,6 +407,7 @@ int orc_backward(int64_t T, int64_t d, int64_t N, int64_t Z, int64_t I,
           da[i] = dh[i] * u[i] * (sg * (1.0 + a[i] * (1.0 - sg)));
           du[i] = dh[i] * (a[i] * sg);
         }
+        if (experts_only) continue;
         for (int64_t k = 0; k < d; ++k) {
           double acc = 0.0;
           for (int64_t i = 0; i < I; ++i)
@@ -400,6 +415,7 @@ int orc_backward(int64_t T, int64_t d, int64_t N, int64_t Z, int64_t I,
           dxo[k] += acc;
         }
       }
+      if (experts_only) continue;
       /* router: softmax Jacobian restricted as the gate mode dictates */
       double* dl = DL + q * E;
       if (gate_norm) {
@@ -703,51 +719,59 @@ int orc_mx_dequantize(int64_t rows, int64_t cols, const uint8_t* codes, const ui
  *   x'  = MX(x_t) along d (per token);  W' = MX(W) along each weight's
  *         reduction dimension (given as codes + scales per expert, the
  *         output of orc_mx_quantize on [I][d] or [d][I]);
- *   a = W'_g x',  u = W'_u x',  h = silu(a) * u, rounded to fp32 (the
- *         precision in which the GPU takes the quantization decision);
+ *   a = W'_g x',  u = W'_u x',  h = silu(a) * u  (binary64);
  *   h' = MX(h) along I;  y = W'_d h';
  *   out_t = out_scale * ( c_t x_t + sum over FFN picks of g_r y_r ), with
  *         the zero-computation term on the unquantized x_t.
  * Weight tables: per expert e, codes (wgc/wuc [I][d], wdc [d][I]) and
  * scales (wgs/wus [I][d/32], wds [d][I/32]); NULL for experts no listed
  * token picks.  y_out (nullable) receives y per listed (token, slot)
- * [n_tok*K][d] (0 for identity picks).
- *
- * h' is a quantization decision taken on an fp32 value that any other
- * implementation computes in another summation order.  With a and u summed
- * in fp32 to within eps times the sum of their absolute products (Sa, Su),
- * h_i is known to within
- *   tol_i = eps (|silu'(a) u| Sa + |silu(a)| Su) + 2^-21 |h_i|
- * (the last term for the fp32 evaluation of silu and the product), so an
- * h_i within tol_i of a rounding boundary of its code (or a block whose
- * amax is that close to a power of two, which moves its scale) may
- * legitimately come out one code apart.  flip (nullable, [n_tok][d])
- * receives, per output element, the largest change such flips can cause:
- * out_scale * sum over FFN picks of g * sum over those i of
- * |W'_d[n][i]| * (largest distance between the dequantized candidates). */
-static void mx_candidates(const double* h, const double* tol, int64_t I, const uint8_t* qs,
-                          const double* hq, double* delta);
+ * [n_tok*K][d] (0 for identity picks). */
+static int mx_tables_ok(int64_t T, int64_t N, int64_t K, const uint8_t* const* wgc,
+                        const uint8_t* const* wgs, const uint8_t* const* wuc,
+                        const uint8_t* const* wus, const uint8_t* const* wdc,
+                        const uint8_t* const* wds, const int32_t* topk_idx, int64_t n_tok,
+                        const int64_t* toks) {
+  for (int64_t q = 0; q < n_tok; ++q) {
+    const int64_t t = toks ? toks[q] : q;
+    if (t < 0 || t >= T) return 0;
+    for (int64_t r = 0; r < K; ++r) {
+      const int64_t e = topk_idx[t * K + r];
+      if (e < N && (!wgc[e] || !wgs[e] || !wuc[e] || !wus[e] || !wdc[e] || !wds[e])) return 0;
+    }
+  }
+  return 1;
+}
+
+/* Row n of an MXFP8 matrix [R][C] (codes + scales), dequantized:
+ * decode(code) * 2^(S-127).  pow2[S] = 2^(S-127) (exact), so each product is
+ * exact too: E4M3 values times 2^-127 .. 2^127 stay normal binary64. */
+static double mx_pow2[256];
+static void mx_row(const double* val, const uint8_t* codes, const uint8_t* scales, int64_t n,
+                   int64_t C, double* row) {
+  for (int64_t k = 0; k < C; ++k)
+    row[k] = val[codes[n * C + k]] * mx_pow2[scales[(n * C + k) / 32]];
+}
+static void mx_tables(double* val) {
+  for (int c = 0; c < 256; ++c) {
+    val[c] = orc_e4m3_value(c);
+    mx_pow2[c] = ldexp(1.0, c - 127);
+  }
+}
+
 int orc_forward_mx(int64_t T, int64_t d, int64_t N, int64_t I, int64_t K, int dt,
                    double out_scale, const void* x, const uint8_t* const* wgc,
                    const uint8_t* const* wgs, const uint8_t* const* wuc,
                    const uint8_t* const* wus, const uint8_t* const* wdc,
                    const uint8_t* const* wds, const int32_t* topk_idx, const double* gates,
-                   int64_t n_tok, const int64_t* toks, double* out, double* y_out, double eps,
-                   double* flip) {
+                   int64_t n_tok, const int64_t* toks, double* out, double* y_out) {
   if (T < 0 || d <= 0 || d % 32 || I <= 0 || I % 32 || K < 1 || !x || !wgc || !wgs || !wuc ||
       !wus || !wdc || !wds || !topk_idx || !gates || !out)
     return 1;
   if (!toks) n_tok = T;
+  if (!mx_tables_ok(T, N, K, wgc, wgs, wuc, wus, wdc, wds, topk_idx, n_tok, toks)) return 1;
   double val[256];
-  for (int c = 0; c < 256; ++c) val[c] = orc_e4m3_value(c);
-  for (int64_t q = 0; q < n_tok; ++q) {
-    const int64_t t = toks ? toks[q] : q;
-    if (t < 0 || t >= T) return 1;
-    for (int64_t r = 0; r < K; ++r) {
-      const int64_t e = topk_idx[t * K + r];
-      if (e < N && (!wgc[e] || !wgs[e] || !wuc[e] || !wus[e] || !wdc[e] || !wds[e])) return 1;
-    }
-  }
+  mx_tables(val);
   const int64_t wmax = d > I ? d : I;
 #pragma omp parallel
   {
@@ -759,23 +783,16 @@ int orc_forward_mx(int64_t T, int64_t d, int64_t N, int64_t I, int64_t K, int dt
     double* y = (double*)malloc(sizeof(double) * (size_t)d);
     double* wrow = (double*)malloc(sizeof(double) * (size_t)wmax);
     double* urow = (double*)malloc(sizeof(double) * (size_t)d);
-    double* dlt = (double*)malloc(sizeof(double) * (size_t)I);
-    double* tl = (double*)malloc(sizeof(double) * (size_t)I);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t q = 0; q < n_tok; ++q) {
       const int64_t t = toks ? toks[q] : q;
-      if (dt == ORC_BF16) {
-        orc_mx_quantize(1, d, ORC_BF16, (const uint16_t*)x + t * d, qc, qs);
-      } else {
-        orc_mx_quantize(1, d, ORC_F32, (const float*)x + t * d, qc, qs);
-      }
+      orc_mx_quantize(1, d, dt, dt == ORC_BF16 ? (const void*)((const uint16_t*)x + t * d)
+                                              : (const void*)((const float*)x + t * d),
+                      qc, qs);
       orc_mx_dequantize(1, d, qc, qs, xq);
       double* o = out + q * d;
-      double* fo = flip ? flip + q * d : NULL;
       double c = 0.0;
       for (int64_t n = 0; n < d; ++n) o[n] = 0.0;
-      if (fo)
-        for (int64_t n = 0; n < d; ++n) fo[n] = 0.0;
       for (int64_t r = 0; r < K; ++r) {
         const int64_t e = topk_idx[t * K + r];
         const double g = gates[t * K + r];
@@ -787,11 +804,90 @@ int orc_forward_mx(int64_t T, int64_t d, int64_t N, int64_t I, int64_t K, int dt
           continue;
         }
         for (int64_t i = 0; i < I; ++i) {
-          /* rows i of W'_g and W'_u, dequantized */
+          mx_row(val, wgc[e], wgs[e], i, d, wrow);
+          mx_row(val, wuc[e], wus[e], i, d, urow);
+          double a = 0.0, u = 0.0;
           for (int64_t k = 0; k < d; ++k) {
-            wrow[k] = ldexp(val[wgc[e][i * d + k]], (int)wgs[e][(i * d + k) / 32] - 127);
-            urow[k] = ldexp(val[wuc[e][i * d + k]], (int)wus[e][(i * d + k) / 32] - 127);
+            a += wrow[k] * xq[k];
+            u += urow[k] * xq[k];
           }
+          h[i] = silu(a) * u;
+        }
+        orc_mx_quantize(1, I, 2, h, qc, qs);
+        orc_mx_dequantize(1, I, qc, qs, hq);
+        for (int64_t n = 0; n < d; ++n) {
+          mx_row(val, wdc[e], wds[e], n, I, wrow);
+          double acc = 0.0;
+          for (int64_t i = 0; i < I; ++i) acc += wrow[i] * hq[i];
+          y[n] = acc;
+          if (yo) yo[n] = acc;
+        }
+        for (int64_t n = 0; n < d; ++n) o[n] += g * y[n];
+      }
+      for (int64_t n = 0; n < d; ++n) o[n] = out_scale * (c * ld(x, dt, t * d + n) + o[n]);
+    }
+    free(xq); free(qc); free(qs); free(h); free(hq); free(y); free(wrow); free(urow);
+  }
+  return 0;
+}
+
+/* TOLERANCE HELPER for comparisons against O13 -- not part of the layer.
+ * h' is a quantization decision taken on a computed value (h), and any
+ * implementation that sums the dot products a, u in fp32 (and evaluates silu
+ * and the product in fp32) holds an h that differs from the binary64 h of
+ * O13 in its last bits.  With a and u known to within eps times the sum of
+ * their absolute products (Sa, Su), h_i is known to within
+ *   tol_i = eps (|silu'(a) u| Sa + |silu(a)| Su) + 2^-21 |h_i|,
+ * so an h_i within tol_i of a rounding boundary of its code (or a block
+ * whose amax is that close to a power of two, which moves its scale) may
+ * legitimately come out one code apart.  flip [n_tok][d] receives, per
+ * output element, the largest change such code changes can cause:
+ *   out_scale * sum over FFN picks of |g| * sum over the affected i of
+ *   |W'_d[n][i]| * (largest distance between the dequantized candidates).
+ * Same arguments as orc_forward_mx. */
+static void mx_candidates(const double* h, const double* tol, int64_t I, const uint8_t* qs,
+                          const double* hq, double* delta);
+int orc_mx_flip_bound(int64_t T, int64_t d, int64_t N, int64_t I, int64_t K, int dt,
+                      double out_scale, const void* x, const uint8_t* const* wgc,
+                      const uint8_t* const* wgs, const uint8_t* const* wuc,
+                      const uint8_t* const* wus, const uint8_t* const* wdc,
+                      const uint8_t* const* wds, const int32_t* topk_idx, const double* gates,
+                      int64_t n_tok, const int64_t* toks, double eps, double* flip) {
+  if (T < 0 || d <= 0 || d % 32 || I <= 0 || I % 32 || K < 1 || !x || !wgc || !wgs || !wuc ||
+      !wus || !wdc || !wds || !topk_idx || !gates || !flip || !(eps >= 0.0))
+    return 1;
+  if (!toks) n_tok = T;
+  if (!mx_tables_ok(T, N, K, wgc, wgs, wuc, wus, wdc, wds, topk_idx, n_tok, toks)) return 1;
+  double val[256];
+  mx_tables(val);
+  const int64_t wmax = d > I ? d : I;
+#pragma omp parallel
+  {
+    double* xq = (double*)malloc(sizeof(double) * (size_t)d);
+    uint8_t* qc = (uint8_t*)malloc((size_t)wmax);
+    uint8_t* qs = (uint8_t*)malloc((size_t)wmax / 32);
+    double* h = (double*)malloc(sizeof(double) * (size_t)I);
+    double* hq = (double*)malloc(sizeof(double) * (size_t)I);
+    double* wrow = (double*)malloc(sizeof(double) * (size_t)wmax);
+    double* urow = (double*)malloc(sizeof(double) * (size_t)d);
+    double* dlt = (double*)malloc(sizeof(double) * (size_t)I);
+    double* tl = (double*)malloc(sizeof(double) * (size_t)I);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t q = 0; q < n_tok; ++q) {
+      const int64_t t = toks ? toks[q] : q;
+      orc_mx_quantize(1, d, dt, dt == ORC_BF16 ? (const void*)((const uint16_t*)x + t * d)
+                                              : (const void*)((const float*)x + t * d),
+                      qc, qs);
+      orc_mx_dequantize(1, d, qc, qs, xq);
+      double* fo = flip + q * d;
+      for (int64_t n = 0; n < d; ++n) fo[n] = 0.0;
+      for (int64_t r = 0; r < K; ++r) {
+        const int64_t e = topk_idx[t * K + r];
+        const double g = gates[t * K + r];
+        if (e >= N) continue;
+        for (int64_t i = 0; i < I; ++i) {
+          mx_row(val, wgc[e], wgs[e], i, d, wrow);
+          mx_row(val, wuc[e], wus[e], i, d, urow);
           double a = 0.0, u = 0.0, sa = 0.0, su = 0.0;
           for (int64_t k = 0; k < d; ++k) {
             a += wrow[k] * xq[k];
@@ -799,34 +895,24 @@ int orc_forward_mx(int64_t T, int64_t d, int64_t N, int64_t I, int64_t K, int dt
             sa += fabs(wrow[k] * xq[k]);
             su += fabs(urow[k] * xq[k]);
           }
-          h[i] = (double)(float)(silu(a) * u);
+          h[i] = silu(a) * u;
           const double sg = 1.0 / (1.0 + exp(-a));
           tl[i] = eps * (fabs(sg * (1.0 + a * (1.0 - sg)) * u) * sa + fabs(a * sg) * su) +
                   ldexp(fabs(h[i]), -21);
         }
         orc_mx_quantize(1, I, 2, h, qc, qs);
         orc_mx_dequantize(1, I, qc, qs, hq);
-        if (fo) mx_candidates(h, tl, I, qs, hq, dlt);
+        mx_candidates(h, tl, I, qs, hq, dlt);
         for (int64_t n = 0; n < d; ++n) {
+          mx_row(val, wdc[e], wds[e], n, I, wrow);
+          double fl = 0.0;
           for (int64_t i = 0; i < I; ++i)
-            wrow[i] = ldexp(val[wdc[e][n * I + i]], (int)wds[e][(n * I + i) / 32] - 127);
-          double acc = 0.0;
-          for (int64_t i = 0; i < I; ++i) acc += wrow[i] * hq[i];
-          y[n] = acc;
-          if (yo) yo[n] = acc;
-          if (fo) {
-            double fl = 0.0;
-            for (int64_t i = 0; i < I; ++i)
-              if (dlt[i] > 0.0) fl += fabs(wrow[i]) * dlt[i];
-            fo[n] += fabs(out_scale * g) * fl;
-          }
+            if (dlt[i] > 0.0) fl += fabs(wrow[i]) * dlt[i];
+          fo[n] += fabs(out_scale * g) * fl;
         }
-        for (int64_t n = 0; n < d; ++n) o[n] += g * y[n];
       }
-      for (int64_t n = 0; n < d; ++n) o[n] = out_scale * (c * ld(x, dt, t * d + n) + o[n]);
     }
-    free(xq); free(qc); free(qs); free(h); free(hq); free(y); free(wrow); free(urow); free(dlt);
-    free(tl);
+    free(xq); free(qc); free(qs); free(h); free(hq); free(wrow); free(urow); free(dlt); free(tl);
   }
   return 0;
 }

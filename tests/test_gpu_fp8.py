@@ -113,35 +113,23 @@ def check_case(sh, Lg, route, out, toks, n_out=None, bias=None):
     pick = [i for i in range(len(toks)) if same[i]][:n_out]
     experts = sorted({int(e) for i in pick for e in o.topk_idx[i] if e < sh.N})
     wq = {k: {e: oracle.mx_weights(H.host(Lg[k][e])) for e in experts} for k in ("wg", "wu", "wd")}
-    ref, flip = oracle.forward_mx(xh, wq["wg"], wq["wu"], wq["wd"], o.topk_idx, o.gates, sh.N,
-                                  toks=pick, flip_eps=flip_eps(sh.d))
+    ref = oracle.forward_mx(xh, wq["wg"], wq["wu"], wq["wd"], o.topk_idx, o.gates, sh.N,
+                            toks=pick)
+    # the tolerance helper: output change that h codes decided within the
+    # fp32 uncertainty of h may cause (the oracle decides on binary64 h)
+    flip = oracle.mx_flip_bound(xh, wq["wg"], wq["wu"], wq["wd"], o.topk_idx, o.gates, sh.N,
+                                flip_eps(sh.d), toks=pick)
     got = out[torch.from_numpy(toks[pick]).cuda()]
     g64 = H.f64(got)
     # the output: the bf16 bound of gpu_harness plus the near-tie allowance
     rms_out = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
-    dev_out = np.abs(g64 - ref)
-    base_out = H.BF16_RMS_TOL * rms_out + 0.5 * H.bf16_ulp(ref)
-    excess = float((dev_out - base_out - flip).max()) if ref.size else 0.0
-    assert excess <= 0, f"FP8 layer output: exceeds the bound by {excess:.3e} (rms {rms_out:.3e})"
-    err = float(dev_out.max()) / max(rms_out, 1e-30) if ref.size else 0.0
+    err = H._bounded(np.abs(g64 - ref), rms_out, 0.5 * H.bf16_ulp(ref), "FP8 layer output",
+                     flip) if ref.size else 0.0
     # the FFN part alone: the identity term (same x, same gates) removed
-    ident = np.array([sum(o.gates[i, r] for r in range(sh.K) if o.topk_idx[i, r] >= sh.N)
-                      for i in pick])
-    xf = synth.as_f64(xh[pick])
-    ffn_ref = ref - ident[:, None] * xf
-    ffn_got = g64 - ident[:, None] * xf
-    rms = float(np.sqrt(np.mean(ffn_ref ** 2))) if ffn_ref.size else 0.0
-    if rms > 0:
-        base = H.BF16_RMS_TOL * rms + 0.5 * H.bf16_ulp(ref) + 1e-7 * np.abs(xf)
-        dev = np.abs(ffn_got - ffn_ref)
-        excess = float((dev - base - flip).max())
-        assert excess <= 0, f"FFN part: exceeds the bound by {excess:.3e} (rms {rms:.3e})"
-        ffn_err = float(dev.max()) / rms
-        print(f"  elements beyond 2e-2 RMS + ulp/2 (covered by h-code near-ties): "
-              f"{int((dev > base).sum())} of {dev.size}; flip allowance max "
-              f"{float(flip.max()) / rms:.3e} of RMS", flush=True)
-    else:
-        ffn_err = 0.0
+    ffn_err = H.assert_ffn_part(got, ref, o.topk_idx[pick], o.gates[pick], sh.N, xh[pick],
+                                "FP8 layer output", flip=flip) if ref.size else 0.0
+    if ref.size:
+        print(f"  flip allowance max {float(flip.max()):.3e} (absolute)", flush=True)
     print(f"  ambiguous {namb}/{len(toks)}, checked {len(pick)} tokens over {len(experts)} "
           f"experts: err {err:.3e}, FFN-part err {ffn_err:.3e} of its RMS", flush=True)
     return o, pick, experts, ref
@@ -191,7 +179,7 @@ def test_fp8_forward_is_deterministic():
     assert torch.equal(a, b)
 
 
-def big_case(sh, n_logit_tok=128, n_out_tok=6):
+def big_case(sh, n_logit_tok=128, n_out_tok=16):
     print(f"[fp8 forward-big] {sh.name} T={sh.T}", flush=True)
     Lg = synth.make_layer(sh, "cuda")
     desc = H.desc_of(sh)
@@ -210,9 +198,11 @@ def big_case(sh, n_logit_tok=128, n_out_tok=6):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.timeout(600)
 def test_fp8_forward_decode_full_size():
     big_case(CF["decode_bf16"])
 
 
+@pytest.mark.timeout(600)
 def test_fp8_forward_prefill_full_size():
     big_case(CF["prefill_bf16"])

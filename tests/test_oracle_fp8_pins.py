@@ -146,7 +146,7 @@ def _mxq(orc, w):
 
 def test_forward_mx_is_a_composition_of_quantized_matmuls(orc):
     """Dense top-K = N + Z layer: the FP8 forward equals quantize(x) ->
-    numpy matmuls -> fp32 rounding of h -> quantize(h) -> matmul -> gated
+    numpy matmuls -> SwiGLU in binary64 -> quantize(h) -> matmul -> gated
     sum, built from the pinned quantizer and library routines."""
     T, d, N, Z, I, K = 12, 64, 3, 2, 64, 5
     x, wg, wu, wd, lg = _layer(T, d, N, Z, I, K, seed=4)
@@ -166,7 +166,7 @@ def test_forward_mx_is_a_composition_of_quantized_matmuls(orc):
                 continue
             a = G[e] @ xq[t]
             u = U[e] @ xq[t]
-            h = (a / (1 + np.exp(-a)) * u).astype(np.float32).astype(np.float64)
+            h = a / (1 + np.exp(-a)) * u
             hq = orc.mx_dequantize(*orc.mx_quantize(h[None, :]))[0]
             want[t] += g * (D[e] @ hq)
     np.testing.assert_allclose(out, 0.5 * want, rtol=1e-12, atol=1e-12)
@@ -197,24 +197,26 @@ def test_forward_mx_is_close_to_the_unquantized_forward(orc):
 
 def test_forward_mx_flip_bound_covers_perturbed_h(orc):
     """The flip bound (largest output change from h codes within relative
-    eps of a boundary) is 0 for eps = 0 and covers the actual change when
-    every h_i is moved by a random factor within 1 +- eps (numpy composition
-    of the pinned quantizer), and is not vacuous."""
+    eps of a boundary, plus the fp32 rounding of h) is 0 for eps = 0 apart
+    from that rounding, and covers the actual change when every h_i is
+    moved by a random factor within 1 +- eps or is rounded to fp32 (numpy
+    composition of the pinned quantizer), and is not vacuous."""
     T, d, N, Z, I, K = 10, 64, 3, 2, 64, 4
     x, wg, wu, wd, lg = _layer(T, d, N, Z, I, K, seed=7)
     ro = orc.route(lg, np.zeros(N + Z, np.float32), N, K)
     Gq, Uq, Dq = _mxq(orc, wg), _mxq(orc, wu), _mxq(orc, wd)
     eps = 2.0 ** -7
-    out, fl = orc.forward_mx(x, Gq, Uq, Dq, ro.topk_idx, ro.gates, N, flip_eps=eps)
-    _, fl0 = orc.forward_mx(x, Gq, Uq, Dq, ro.topk_idx, ro.gates, N, flip_eps=0.0)
-    assert not fl0.any() and fl.max() > 0
+    out = orc.forward_mx(x, Gq, Uq, Dq, ro.topk_idx, ro.gates, N)
+    fl = orc.mx_flip_bound(x, Gq, Uq, Dq, ro.topk_idx, ro.gates, N, eps)
+    fl0 = orc.mx_flip_bound(x, Gq, Uq, Dq, ro.topk_idx, ro.gates, N, 0.0)
+    assert fl.max() > 0 and (fl0 <= fl).all()
     G = {e: orc.mx_dequantize(*v) for e, v in Gq.items()}
     U = {e: orc.mx_dequantize(*v) for e, v in Uq.items()}
     D = {e: orc.mx_dequantize(*v) for e, v in Dq.items()}
     xq = orc.mx_dequantize(*orc.mx_quantize(x))
     r = rng(8)
     moved = 0.0
-    for trial in range(6):
+    for trial in range(7):
         want = np.zeros((T, d))
         for t in range(T):
             for k in range(K):
@@ -223,11 +225,14 @@ def test_forward_mx_flip_bound_covers_perturbed_h(orc):
                     want[t] += g * x[t].astype(np.float64)
                     continue
                 a, u = G[e] @ xq[t], U[e] @ xq[t]
-                h = (a / (1 + np.exp(-a)) * u).astype(np.float32).astype(np.float64)
-                h = h * (1 + r.uniform(-eps, eps, I))
+                h = a / (1 + np.exp(-a)) * u
+                if trial == 0:  # the h an fp32 evaluation holds
+                    h = h.astype(np.float32).astype(np.float64)
+                else:
+                    h = h * (1 + r.uniform(-eps, eps, I))
                 hq = orc.mx_dequantize(*orc.mx_quantize(h[None, :]))[0]
                 want[t] += g * (D[e] @ hq)
         diff = np.abs(want - out)
         moved = max(moved, diff.max())
-        assert (diff <= fl * (1 + 1e-9) + 1e-13).all()
+        assert (diff <= (fl0 if trial == 0 else fl) * (1 + 1e-9) + 1e-13).all()
     assert moved > 0  # the perturbations did flip codes

@@ -117,6 +117,46 @@ def test_topk_brute_force(orc, seed):
         assert list(out.topk_idx[t]) == _brute_topk(out.keys[t], K)
 
 
+def test_topk_stays_total_on_non_finite_scores(orc):
+    """A NaN score, an infinite one (inf - inf inside the softmax) or a row of
+    -inf scores makes every key of the token NaN; NaN keys order as -inf,
+    so the selection still returns K distinct valid indices -- 0..K-1 for
+    such a token, by the lower-index tie rule.  Eq.(1) gates (p = e/S) are
+    then NaN; renormalised gates are the softmax of the picked scores,
+    NaN as soon as a picked exponential is.  A NaN bias sends only its own
+    expert behind every finite key."""
+    E, N, K = 10, 6, 3
+    r = rng(30)
+    lg = r.standard_normal((5, E)) * 0.5
+    lg[0, 4] = np.nan
+    lg[1, 7] = np.inf
+    lg[2, :] = -np.inf
+    bias = r.uniform(-0.05, 0.05, E).astype(np.float32)
+    out = orc.route(lg, bias, N, K)
+    lit = orc.route(lg, bias, N, K, gate_norm=0)
+    for t in (0, 1, 2):
+        assert list(out.topk_idx[t]) == list(range(K)), t
+        assert list(lit.topk_idx[t]) == list(range(K)), t
+        assert np.isnan(lit.gates[t]).all()
+    # token 0: its NaN score is not among the picks
+    want = torch.softmax(torch.from_numpy(lg[0, :K]), dim=0).numpy()
+    np.testing.assert_allclose(out.gates[0], want, rtol=1e-14)
+    # token 1: e = 0 for every finite score next to the infinite one
+    assert np.isnan(out.gates[1]).all() and np.isnan(out.gates[2]).all()
+    assert ((out.topk_idx >= 0) & (out.topk_idx < E)).all()
+    assert out.counts.sum() == 5 * K
+    # finite scores, NaN bias on the expert each token would pick first
+    p = torch.softmax(torch.from_numpy(lg[3:]), dim=1).numpy()
+    for t in range(2):
+        b = bias.copy()
+        b[int(np.argmax(p[t] + bias))] = np.nan
+        o = orc.route(lg[3 + t:4 + t], b, N, K)
+        keys = p[t] + b.astype(np.float64)
+        keys[np.isnan(keys)] = -np.inf
+        assert list(o.topk_idx[0]) == _brute_topk(keys, K)
+        assert np.isfinite(o.gates).all()
+
+
 def test_keys_are_softmax_plus_bias(orc):
     r = rng(20)
     lg = (r.standard_normal((50, 96)) * 2.0).astype(np.float32)
@@ -331,6 +371,33 @@ def test_backward_against_autograd(orc, gate_norm):
     np.testing.assert_allclose(g["dx"], ts["x"].grad.numpy(), rtol=1e-11, atol=1e-13)
     np.testing.assert_allclose(g["dwr"], ts["wr"].grad.numpy(), rtol=1e-11, atol=1e-13)
     for e in range(N):
+        np.testing.assert_allclose(g["dwg"][e], ts["wg"].grad[e].numpy(), rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(g["dwu"][e], ts["wu"].grad[e].numpy(), rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(g["dwd"][e], ts["wd"].grad[e].numpy(), rtol=1e-11, atol=1e-13)
+
+
+def test_backward_expert_gradients_alone_against_autograd(orc):
+    """Asked for the weight gradients of some experts only (no dx, no router
+    gradient), the backward needs and reads those experts' weights alone and
+    still matches autograd on them."""
+    T, d, N, Z, I, K = 24, 16, 5, 3, 8, 3
+    L = _layer(T, d, N, Z, I, K, seed=43, w_std=0.3)
+    dY = rng(44).standard_normal((T, d)).astype(np.float32)
+    lg, ro, _ = _run(orc, L, N, K)
+    want = [1, 3]
+    only = {k: {e: L[k][e] for e in want} for k in ("wg", "wu", "wd")}
+    g = orc.backward(L["x"], L["wr"], only["wg"], only["wu"], only["wd"], lg, ro.topk_idx,
+                     ro.gates, dY, N, Z, out_scale=0.75, want_experts=want, want_dwr=False,
+                     want_dx=False)
+    assert g["dx"] is None and g["dwr"] is None
+    ts = {k: torch.from_numpy(L[k]).double().requires_grad_(True)
+          for k in ("x", "wr", "wg", "wu", "wd")}
+    loss = _torch_fixed_route_loss(ts["x"], ts["wr"], ts["wg"], ts["wu"], ts["wd"],
+                                   torch.from_numpy(ro.topk_idx).long(), N, 1,
+                                   torch.from_numpy(dY).double(), out_scale=0.75)
+    loss.backward()
+    assert any((ro.topk_idx == e).any() for e in want)
+    for e in want:
         np.testing.assert_allclose(g["dwg"][e], ts["wg"].grad[e].numpy(), rtol=1e-11, atol=1e-13)
         np.testing.assert_allclose(g["dwu"][e], ts["wu"].grad[e].numpy(), rtol=1e-11, atol=1e-13)
         np.testing.assert_allclose(g["dwd"][e], ts["wd"].grad[e].numpy(), rtol=1e-11, atol=1e-13)
