@@ -34,8 +34,11 @@
  *    Expert indices 0..N-1 are FFN experts, N..E-1 zero-computation experts.
  *  - Data pointers must be 16-byte aligned.  bf16 layers need d and I to be
  *    multiples of 64, fp32 layers multiples of 32 (else ZC_ERR_UNSUPPORTED).
- *  - Preconditions not checked by the kernels: finite inputs (NaN or Inf
- *    router scores give an unspecified routing), T*K < 2^31.
+ *  - Non-finite inputs: a NaN or infinite router score makes every routing
+ *    key of its token NaN (through the softmax), and NaN keys rank below
+ *    every number, so the selection stays total: such a token picks experts
+ *    0..K-1 (valid indices) and NaN flows on through its gates or its x
+ *    row; no index leaves its range.  T*K < 2^31 is required (checked).
  */
 #ifndef ZC_MOE_H
 #define ZC_MOE_H
@@ -73,6 +76,13 @@ typedef struct {
                      /*    to 1);  0: gate = R_i exactly as Eq.(1) prints it  */
   float out_scale;   /* scalar on the layer output (1.0 = none)               */
   int32_t weight_layout; /* zc_weight_layout of w_gate, w_up and w_down       */
+  int32_t cu_limit;  /* 0: the GEMMs' persistent grids fill every compute    */
+                     /* unit; n > 0, a multiple of 8 (the grids deal tiles to */
+                     /* the 8 XCDs): they are sized as for min(n, CUs) units. */
+                     /* Results do not depend on it (every sum has a fixed    */
+                     /* order, whichever workgroup computes it); it leaves    */
+                     /* compute units to concurrent work and lets a test      */
+                     /* check that claim.  Other values: ZC_ERR_INVALID.      */
 } zc_moe_desc;
 
 /* Layouts of the FFN expert weights.
@@ -137,7 +147,8 @@ size_t zc_moe_saved_size(const zc_moe_desc* desc);
  *            binary64 (max subtraction, Cody-Waite + degree-13 Taylor
  *            exponential, 64 partial sums combined pairwise at xor distance
  *            32..1, one division per key);
- *   picks  = the K largest keys, ties to the lower expert index;
+ *   picks  = the K largest keys, ties to the lower expert index (a NaN
+ *            key ranks below every number);
  *   gates  = e_j / (sum of the picked e) (gate_norm 1) or p_j (gate_norm 0),
  *            with e_j the exponentials above, rounded to fp32.
  * If x and w_router are both NULL the scores already in r->logits are used

@@ -106,8 +106,16 @@ int cu_count() {
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     n = 256;
+  // the persistent grids deal their tiles to the 8 XCDs in equal shares
+  n = n < 8 ? 8 : n / 8 * 8;
   if (dev < 64) g_cu[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+// Compute units the persistent grids of a call are sized for.
+int cus(const zc_moe_desc* d) {
+  const int n = cu_count();
+  return d->cu_limit > 0 && d->cu_limit < n ? d->cu_limit : n;
 }
 
 int64_t a256(int64_t b) { return (b + 255) & ~int64_t(255); }
@@ -163,6 +171,9 @@ zc_status check_desc(const zc_moe_desc* d) {
       d->weight_layout != ZC_WEIGHTS_MXFP8)
     return fail(ZC_ERR_INVALID, "weight_layout %d is not ROWMAJOR, PACKED or MXFP8",
                 d->weight_layout);
+  if (d->cu_limit < 0 || d->cu_limit % 8)
+    return fail(ZC_ERR_INVALID, "cu_limit %d is neither 0 nor a positive multiple of 8",
+                d->cu_limit);
   if (d->T * d->K >= (int64_t(1) << 31) || d->d >= (int64_t(1) << 24) || d->I >= (int64_t(1) << 24))
     return fail(ZC_ERR_UNSUPPORTED, "T*K, d or I too large for 32-bit indexing");
   const int64_t mult = d->dtype == ZC_BF16 ? 64 : 32;
@@ -411,7 +422,7 @@ zc_status do_route(const zc_moe_desc* d, const T* x, const T* wr, const float* b
   const int Tn = static_cast<int>(d->T), E = static_cast<int>(d->N + d->Z);
   const int N = static_cast<int>(d->N), K = static_cast<int>(d->K);
   if (x && Tn > 0)
-    ZC_LAUNCH(ZC_PH_ROUTER_GEMM, zc::launch_router_gemm<T>(x, wr, r->logits, Tn, E, static_cast<int>(d->d), w.rpart, cu_count(),
+    ZC_LAUNCH(ZC_PH_ROUTER_GEMM, zc::launch_router_gemm<T>(x, wr, r->logits, Tn, E, static_cast<int>(d->d), w.rpart, cus(d),
                                      s),
            "router GEMM launch");
   ZC_LAUNCH(ZC_PH_TOPK, zc::launch_topk(r->logits, bias, Tn, E, K, d->gate_norm, r->topk_idx, r->topk_gate, s),
@@ -446,7 +457,7 @@ zc_status do_forward(const zc_moe_desc* d, const T* x, const T* wr, const float*
     y = static_cast<T*>(sv.y);
   }
   if (N > 0 && Tn > 0) {
-    const int cu = cu_count();
+    const int cu = cus(d);
     if (d->weight_layout == ZC_WEIGHTS_MXFP8) {
       // MXFP8 inference: x quantized once, h quantized in the gate/up
       // epilogue (validated: bf16, no saved buffer)
@@ -524,7 +535,7 @@ zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg
   const int E = static_cast<int>(d->N + d->Z), dd = static_cast<int>(d->d);
   const int I = static_cast<int>(d->I), ldl = static_cast<int>(ldl_of(E));
   const int64_t rows = d->T * d->K;
-  const int cu = cu_count();
+  const int cu = cus(d);
   BwdWs w = carve_bwd(ws, d);
   Saved sv = carve_saved(const_cast<char*>(static_cast<const char*>(saved)), d);
   const T* y = static_cast<const T*>(sv.y);

@@ -11,8 +11,12 @@
 //   S    = sum of e_j: lane L of the wave sums e_j for j = L, L+64, ...
 //          ascending from 0.0, then six rounds v = v + v[lane ^ o] for
 //          o = 32, 16, 8, 4, 2, 1
-//   key_j = e_j / S + (double)b_j
+//   key_j = e_j / S + (double)b_j, a NaN key taken as -infinity
 //   K rounds of "largest key, ties to the lower index"; slot r = round r.
+// A NaN score (or an infinite one, through inf - inf) makes every key of its
+// token NaN; ordering NaN as -infinity keeps the selection total, so such a
+// token picks experts 0..K-1 (valid indices) and gets NaN gates, which carry
+// the NaN into its outputs and gradients.
 //   gate_r = (float)(e_{s_r} / sum_{q<K} e_{s_q})  (renormalised, q ascending)
 //          or (float)(e_{s_r} / S)                 (Eq.(1) as printed)
 // This file is compiled with -ffp-contract=off and the pragma below, so no
@@ -35,6 +39,7 @@ constexpr double kInvLn2 = 0x1.71547652b82fep+0;
 // e^z for z <= 0: 0 below -700; otherwise z = k ln2 + r, e^r by its Taylor
 // series to degree 13 (Horner, fused multiply-adds), times 2^k.
 __device__ __forceinline__ double key_exp(double z) {
+  if (z != z) return z;  // NaN in, NaN out (no conversion of NaN to int below)
   if (z < -700.0) return 0.0;
   const double k = __builtin_rint(z * kInvLn2);
   const double r = (z - k * kLn2Head) - k * kLn2Tail;
@@ -107,6 +112,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(
   for (int i = 0; i < NPER; ++i) {
     const int j = lane + 64 * i;
     kv[i] = j < E ? ev[i] / S + static_cast<double>(bias[j]) : -INFINITY;
+    if (kv[i] != kv[i]) kv[i] = -INFINITY;
   }
 
   uint32_t taken = 0;

@@ -44,7 +44,7 @@ class zc_moe_desc(C.Structure):
     _fields_ = [("T", C.c_int64), ("d", C.c_int64), ("N", C.c_int64), ("Z", C.c_int64),
                 ("I", C.c_int64), ("K", C.c_int64), ("dtype", C.c_int32),
                 ("gate_norm", C.c_int32), ("out_scale", C.c_float),
-                ("weight_layout", C.c_int32)]
+                ("weight_layout", C.c_int32), ("cu_limit", C.c_int32)]
 
 
 class zc_lb_cfg(C.Structure):
@@ -139,6 +139,7 @@ class LayerDesc:
     gate_norm: int = 1
     out_scale: float = 1.0
     weight_layout: int = ZC_WEIGHTS_ROWMAJOR
+    cu_limit: int = 0
 
     @property
     def E(self) -> int:
@@ -149,7 +150,8 @@ class LayerDesc:
             raise ValueError("layer dtype must be float32 or bfloat16")
         return zc_moe_desc(self.T, self.d, self.N, self.Z, self.I, self.K,
                            ZC_F32 if self.dtype == torch.float32 else ZC_BF16,
-                           self.gate_norm, self.out_scale, self.weight_layout)
+                           self.gate_norm, self.out_scale, self.weight_layout,
+                           self.cu_limit)
 
 
 class RouteBuffers:

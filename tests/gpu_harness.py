@@ -32,6 +32,20 @@ LOGIT_RTOL = 1e-5
 F32_RTOL = 1e-4
 BF16_RMS_TOL = 2e-2
 
+# Per-tensor error records of the running session (written out by conftest
+# when ZC_PARITY_MARGINS names a file): test, tensor, elements, raw
+# max|gpu - oracle| / RMS(oracle) (or / max|oracle| for fp32), elements
+# beyond the literal 2e-2 * RMS bound, and the largest share of the
+# half-ulp allowance any element used.
+MARGINS: list = []
+CURRENT_TEST = [""]
+
+
+def _record(what, n, raw, beyond=0, ulp_share=0.0, kind="bf16"):
+    MARGINS.append({"test": CURRENT_TEST[0], "tensor": what, "kind": kind, "elements": int(n),
+                    "max_err_over_scale": float(raw), "beyond_literal_bound": int(beyond),
+                    "max_half_ulp_share_used": float(ulp_share)})
+
 
 def desc_of(sh: synth.LayerShape, gate_norm=1, out_scale=1.0) -> zcmoe.LayerDesc:
     return zcmoe.LayerDesc(sh.T, sh.d, sh.N, sh.Z, sh.I, sh.K, sh.torch_dtype, gate_norm,
@@ -102,14 +116,114 @@ def assert_close(gpu, orc: np.ndarray, dtype, what: str):
     err = float(np.abs(g - orc).max()) if g.size else 0.0
     if dtype == torch.float32:
         ref = float(np.abs(orc).max()) if orc.size else 0.0
+        _record(what, g.size, err / max(ref, 1e-30), kind="f32")
         assert err <= F32_RTOL * max(ref, 1e-30), f"{what}: max err {err:.3e}, max|ref| {ref:.3e}"
         return err / max(ref, 1e-30)
     rms = float(np.sqrt(np.mean(orc * orc))) if orc.size else 0.0
-    allowed = BF16_RMS_TOL * rms + 0.5 * bf16_ulp(orc)
-    excess = (np.abs(g - orc) - allowed).max() if g.size else 0.0
-    assert excess <= 0.0, (f"{what}: max err {err:.3e} (rms {rms:.3e}); exceeds "
-                           f"2e-2*rms + ulp/2 by {excess:.3e}")
-    return err / max(rms, 1e-30)
+    return _bounded(np.abs(g - orc), rms, 0.5 * bf16_ulp(orc), what)
+
+
+def _bounded(dev: np.ndarray, rms: float, extra: np.ndarray, what: str, flip=None) -> float:
+    """|dev| <= 2e-2 * rms + extra (+ flip) element by element; records the
+    margins.  Returns max|dev| / rms."""
+    lit = BF16_RMS_TOL * rms
+    over = dev - lit
+    beyond = int((over > 0).sum()) if dev.size else 0
+    share = float(np.max(np.where(over > 0, over / np.maximum(extra, 1e-300), 0.0))) \
+        if beyond else 0.0
+    raw = float(dev.max()) / max(rms, 1e-30) if dev.size else 0.0
+    _record(what, dev.size, raw, beyond, share)
+    allowed = lit + extra + (0.0 if flip is None else flip)
+    excess = float((dev - allowed).max()) if dev.size else 0.0
+    assert excess <= 0.0, (f"{what}: max err {raw:.3e} x rms {rms:.3e}; exceeds the bound by "
+                           f"{excess:.3e} ({beyond} elements beyond 2e-2*rms)")
+    return raw
+
+
+def ffn_part(out: np.ndarray, topk_idx: np.ndarray, gates: np.ndarray, N: int, x: np.ndarray,
+             out_scale: float = 1.0) -> np.ndarray:
+    """out - out_scale * c_t x_t, c_t = sum of the token's gates on
+    zero-computation experts: the FFN experts' share of the layer output
+    ("LongCat-Flash Technical Report", section 2.1: E_i(x) = x for
+    N < i <= N+Z), with the oracle's binary64 gates."""
+    c = np.where(topk_idx >= N, gates, 0.0).sum(1)
+    return out - out_scale * c[:, None] * x
+
+
+def assert_ffn_part(gpu_out, ref_out: np.ndarray, topk_idx, gates, N: int, xh: np.ndarray,
+                    what: str, out_scale: float = 1.0, flip=None,
+                    dtype=torch.bfloat16) -> float:
+    """The FFN part of the output alone against the oracle's: the identity
+    term c_t x_t (about a third of the picks at the LongCat shapes) would
+    otherwise dominate the output and hide FFN errors.  Bound per element:
+    2e-2 * RMS(oracle FFN part) for bf16 layers, 1e-4 * max|oracle FFN part|
+    for fp32 ones, + half an ulp of the stored output (its rounding, which
+    the subtraction keeps) + the fp32 rounding of c_t (K+1 roundings of at
+    most 2^-24 relative each) times |x|, + flip (FP8 h-code near-ties) when
+    given.  Returns max|error| over RMS (bf16) or max (fp32) of the part."""
+    g = f64(gpu_out)
+    x = synth.as_f64(xh)
+    K = topk_idx.shape[1]
+    ref_f = ffn_part(ref_out, topk_idx, gates, N, x, out_scale)
+    got_f = ffn_part(g, topk_idx, gates, N, x, out_scale)
+    if not ref_f.size or not np.any(ref_f):
+        return 0.0
+    c_err = (K + 1) * 2.0 ** -24 * abs(out_scale) * np.abs(x)
+    dev = np.abs(got_f - ref_f)
+    if dtype == torch.float32:
+        scale = float(np.abs(ref_f).max())
+        allowed = F32_RTOL * scale + 0.5 * f32_ulp(ref_out) + c_err
+        raw = float(dev.max()) / scale
+        _record(what + " (FFN part)", dev.size, raw, kind="f32")
+        excess = float((dev - allowed).max())
+        assert excess <= 0.0, f"{what} (FFN part): max err {raw:.3e} of max|part|, over by {excess:.3e}"
+        return raw
+    rms = float(np.sqrt(np.mean(ref_f * ref_f)))
+    return _bounded(dev, rms, 0.5 * bf16_ulp(ref_out) + c_err, what + " (FFN part)", flip)
+
+
+def f32_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of fp32 numbers at |v| (24 significant bits; normal range)."""
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.exp2(e - 23), 0.0)
+
+
+def covering_tokens(topk_idx: np.ndarray, N: int, window: int = 128, seed: int = 0):
+    """A token sample that puts at least one checked row into every
+    `window`-row stretch of every FFN expert's segment of the dispatch order
+    (an expert's rows are its tokens in ascending order).  The grouped GEMMs
+    cut each segment into row tiles of at most 256 rows, none shorter than
+    128 rows unless the whole segment is, so window = 128 puts a checked row
+    into every row tile of every touched expert.  Greedy: stretches in
+    expert order; an uncovered one takes a seeded random token of its own,
+    which also covers the stretches its other picks fall in.  Returns
+    sorted token ids."""
+    T, K = topk_idx.shape
+    rng = np.random.default_rng(seed)
+    flat = topk_idx.reshape(-1).astype(np.int64)
+    tok = np.repeat(np.arange(T), K)
+    real = flat < N
+    e, t = flat[real], tok[real]
+    order = np.lexsort((t, e))                      # dispatch order: (expert, token)
+    e, t = e[order], t[order]
+    starts = np.searchsorted(e, np.arange(N + 1))
+    row = np.arange(len(e)) - starts[e]             # row inside the expert's segment
+    key = e * (T // window + 1) + row // window     # one id per (expert, stretch)
+    by_tok = {}
+    for k, tt in zip(key.tolist(), t.tolist()):
+        by_tok.setdefault(tt, []).append(k)
+    uniq, first = np.unique(key, return_index=True)  # key is sorted: stretches in order
+    bounds = list(first) + [len(key)]
+    covered, chosen = set(), []
+    for i, k in enumerate(uniq.tolist()):
+        if k in covered:
+            continue
+        cand = t[bounds[i]:bounds[i + 1]]
+        tt = int(cand[rng.integers(len(cand))])
+        chosen.append(tt)
+        covered.update(by_tok[tt])
+    return np.array(sorted(set(chosen)), dtype=np.int64)
 
 
 def bf16_ulp(v: np.ndarray) -> np.ndarray:

@@ -85,6 +85,8 @@ def call_route(L, d, ws_bytes=1 << 30, **over):
     (dict(dtype=torch.bfloat16, I=32), zcmoe.ZC_ERR_UNSUPPORTED),
     (dict(gate_norm=2), zcmoe.ZC_ERR_INVALID),
     (dict(out_scale=float("nan")), zcmoe.ZC_ERR_INVALID),
+    (dict(cu_limit=-8), zcmoe.ZC_ERR_INVALID),
+    (dict(cu_limit=12), zcmoe.ZC_ERR_INVALID),     # not a multiple of 8
 ])
 def test_bad_descriptions(L, bad, code):
     assert call_route(L, desc(**bad)) == code
