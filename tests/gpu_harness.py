@@ -151,16 +151,21 @@ def ffn_part(out: np.ndarray, topk_idx: np.ndarray, gates: np.ndarray, N: int, x
 
 
 def assert_ffn_part(gpu_out, ref_out: np.ndarray, topk_idx, gates, N: int, xh: np.ndarray,
-                    what: str, out_scale: float = 1.0, flip=None,
+                    what: str, y_slots: np.ndarray, out_scale: float = 1.0, flip=None,
                     dtype=torch.bfloat16) -> float:
     """The FFN part of the output alone against the oracle's: the identity
     term c_t x_t (about a third of the picks at the LongCat shapes) would
     otherwise dominate the output and hide FFN errors.  Bound per element:
     2e-2 * RMS(oracle FFN part) for bf16 layers, 1e-4 * max|oracle FFN part|
-    for fp32 ones, + half an ulp of the stored output (its rounding, which
-    the subtraction keeps) + the fp32 rounding of c_t (K+1 roundings of at
-    most 2^-24 relative each) times |x|, + flip (FP8 h-code near-ties) when
-    given.  Returns max|error| over RMS (bf16) or max (fp32) of the part."""
+    for fp32 ones, plus the roundings the layer's stored values carry:
+      half an ulp of the output (kept by the subtraction),
+      |out_scale| sum_r |g_r| half an ulp of y_r (each FFN expert's output
+        is stored in the layer dtype before the combine reads it; y_slots,
+        [n][K][d], are the oracle's exact y, zero on identity picks),
+      the fp32 rounding of c_t (K+1 roundings of at most 2^-24 relative
+        each) times |x|,
+    and flip (FP8 h-code near-ties) when given.  Returns max|error| over
+    RMS (bf16) or max (fp32) of the part."""
     g = f64(gpu_out)
     x = synth.as_f64(xh)
     K = topk_idx.shape[1]
@@ -168,18 +173,19 @@ def assert_ffn_part(gpu_out, ref_out: np.ndarray, topk_idx, gates, N: int, xh: n
     got_f = ffn_part(g, topk_idx, gates, N, x, out_scale)
     if not ref_f.size or not np.any(ref_f):
         return 0.0
-    c_err = (K + 1) * 2.0 ** -24 * abs(out_scale) * np.abs(x)
+    ulp = f32_ulp if dtype == torch.float32 else bf16_ulp
+    y_err = abs(out_scale) * np.einsum("nk,nkd->nd", np.abs(gates), 0.5 * ulp(y_slots))
+    extra = 0.5 * ulp(ref_out) + y_err + (K + 1) * 2.0 ** -24 * abs(out_scale) * np.abs(x)
     dev = np.abs(got_f - ref_f)
     if dtype == torch.float32:
         scale = float(np.abs(ref_f).max())
-        allowed = F32_RTOL * scale + 0.5 * f32_ulp(ref_out) + c_err
         raw = float(dev.max()) / scale
         _record(what + " (FFN part)", dev.size, raw, kind="f32")
-        excess = float((dev - allowed).max())
+        excess = float((dev - F32_RTOL * scale - extra).max())
         assert excess <= 0.0, f"{what} (FFN part): max err {raw:.3e} of max|part|, over by {excess:.3e}"
         return raw
     rms = float(np.sqrt(np.mean(ref_f * ref_f)))
-    return _bounded(dev, rms, 0.5 * bf16_ulp(ref_out) + c_err, what + " (FFN part)", flip)
+    return _bounded(dev, rms, extra, what + " (FFN part)", flip)
 
 
 def f32_ulp(v: np.ndarray) -> np.ndarray:

@@ -113,8 +113,8 @@ def check_case(sh, Lg, route, out, toks, n_out=None, bias=None):
     pick = [i for i in range(len(toks)) if same[i]][:n_out]
     experts = sorted({int(e) for i in pick for e in o.topk_idx[i] if e < sh.N})
     wq = {k: {e: oracle.mx_weights(H.host(Lg[k][e])) for e in experts} for k in ("wg", "wu", "wd")}
-    ref = oracle.forward_mx(xh, wq["wg"], wq["wu"], wq["wd"], o.topk_idx, o.gates, sh.N,
-                            toks=pick)
+    ref, ys = oracle.forward_mx(xh, wq["wg"], wq["wu"], wq["wd"], o.topk_idx, o.gates, sh.N,
+                                toks=pick, want_y=True)
     # the tolerance helper: output change that h codes decided within the
     # fp32 uncertainty of h may cause (the oracle decides on binary64 h)
     flip = oracle.mx_flip_bound(xh, wq["wg"], wq["wu"], wq["wd"], o.topk_idx, o.gates, sh.N,
@@ -127,7 +127,8 @@ def check_case(sh, Lg, route, out, toks, n_out=None, bias=None):
                      flip) if ref.size else 0.0
     # the FFN part alone: the identity term (same x, same gates) removed
     ffn_err = H.assert_ffn_part(got, ref, o.topk_idx[pick], o.gates[pick], sh.N, xh[pick],
-                                "FP8 layer output", flip=flip) if ref.size else 0.0
+                                "FP8 layer output", ys.reshape(len(pick), sh.K, sh.d),
+                                flip=flip) if ref.size else 0.0
     if ref.size:
         print(f"  flip allowance max {float(flip.max()):.3e} (absolute)", flush=True)
     print(f"  ambiguous {namb}/{len(toks)}, checked {len(pick)} tokens over {len(experts)} "

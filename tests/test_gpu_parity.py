@@ -135,12 +135,12 @@ def forward_case(sh, gate_norm=1, out_scale=1.0, bias=None, toks=None, packed=Fa
     o = oracle.route(lg, L["bias"].numpy(), sh.N, sh.K, gate_norm=gate_norm)
     same, namb = H.routing_agreement(route.topk_idx.cpu().numpy(), o.keys, o.topk_idx, lg, sh.K)
     sel = np.flatnonzero(same) if toks is None else np.array([t for t in toks if same[t]])
-    ref = oracle.forward(xh, H.host(L["wg"]), H.host(L["wu"]), H.host(L["wd"]), o.topk_idx,
-                         o.gates, sh.N, out_scale=out_scale, toks=sel)
+    ref, ys = oracle.forward(xh, H.host(L["wg"]), H.host(L["wu"]), H.host(L["wd"]), o.topk_idx,
+                             o.gates, sh.N, out_scale=out_scale, toks=sel, want_y=True)
     got = out[torch.from_numpy(sel).cuda()]
     err = H.assert_close(got, ref, sh.torch_dtype, "layer output")
     ferr = H.assert_ffn_part(got, ref, o.topk_idx[sel], o.gates[sel], sh.N, xh[sel],
-                             "layer output", out_scale, dtype=sh.torch_dtype)
+                             "layer output", ys, out_scale, dtype=sh.torch_dtype)
     print(f"  ambiguous tokens {namb}, checked {len(sel)}, err {err:.3e}, FFN part {ferr:.3e}",
           flush=True)
     return L, Lg, desc, route, out, o
@@ -226,13 +226,13 @@ def big_case(sh, layouts=("rowmajor", "packed"), seed=123):
     wg = {e: H.host(Lg["wg"][e]) for e in experts}
     wu = {e: H.host(Lg["wu"][e]) for e in experts}
     wd = {e: H.host(Lg["wd"][e]) for e in experts}
-    ref = oracle.forward(xh, wg, wu, wd, o.topk_idx, o.gates, sh.N, toks=pick)
+    ref, ys = oracle.forward(xh, wg, wu, wd, o.topk_idx, o.gates, sh.N, toks=pick, want_y=True)
     rows = tk[torch.from_numpy(pick).cuda()]
     for lay, (r, out) in runs.items():
         got = out[rows]
         err = H.assert_close(got, ref, sh.torch_dtype, f"layer output [{lay}]")
         ferr = H.assert_ffn_part(got, ref, o.topk_idx[pick], o.gates[pick], sh.N, xh[pick],
-                                 f"layer output [{lay}]")
+                                 f"layer output [{lay}]", ys)
         print(f"  {lay}: err {err:.3e} of RMS(out), FFN part {ferr:.3e} of its RMS", flush=True)
     touched = int((route0.counts[: sh.N] > 0).sum().item())
     print(f"  ambiguous {namb}/{len(toks)}, P_real {route0.offsets[-1].item()}, checked "

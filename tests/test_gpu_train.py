@@ -128,11 +128,12 @@ def step_parity(sh, L, w_host, dY, xh, wr, lg_gpu, og, route, out, grads):
     toks = H.covering_tokens(gidx, N, 128, seed=77)
     tk = torch.from_numpy(toks).cuda()
     wg, wu, wd = w_host["wg"], w_host["wu"], w_host["wd"]
-    ref_out = oracle.forward(xh, wg, wu, wd, og.topk_idx, og.gates, N, toks=toks)
+    ref_out, ys = oracle.forward(xh, wg, wu, wd, og.topk_idx, og.gates, N, toks=toks,
+                                 want_y=True)
     got = out[tk]
     H.assert_close(got, ref_out, torch.bfloat16, "layer output")
     H.assert_ffn_part(got, ref_out, og.topk_idx[toks], og.gates[toks], N, xh[toks],
-                      "layer output")
+                      "layer output", ys)
     rb = oracle.backward(xh, wr, wg, wu, wd, lg_gpu, og.topk_idx, og.gates, dYh, N, Z, toks=toks,
                          want_experts=[], want_dwr=False)
     H.assert_close(grads["dx"][tk], rb["dx"], torch.bfloat16, "dx")
