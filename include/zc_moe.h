@@ -173,6 +173,28 @@ zc_status zc_moe_forward(const zc_moe_desc* desc, const void* x,
                          const void* w_down, void* out, zc_route_buf* r,
                          void* saved, void* ws, size_t ws_bytes, void* stream);
 
+/* The inference forward of zc_moe_forward (saved = NULL) without a
+ * workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  It allocates nothing: its scratch is a device array inside
+ * the library, ZC_NOALLOC_SCRATCH_BYTES per GPU, held by every GPU the
+ * library runs on until the process ends (looked up once per device, on
+ * the first call with that device current).  Layers whose
+ * zc_moe_workspace_size(desc, ZC_OP_FORWARD) exceeds it are rejected with
+ * ZC_ERR_WORKSPACE before anything is queued; the LongCat-Flash layer at a
+ * 256-token decode batch (57 MB) fits.  The caller still owns x, the
+ * weights, out and r, with the same contract as zc_moe_forward.  Every call
+ * on a GPU shares that GPU's scratch: calls that overlap on one GPU (other
+ * streams, other threads) race and give undefined results; calls queued on
+ * one stream are ordered and safe.  Each call rewrites what it reads of the
+ * scratch before reading it.  Kernel timing events are not recorded. */
+#define ZC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+zc_status zc_moe_forward_noalloc(const zc_moe_desc* desc, const void* x,
+                                 const void* w_router, const float* bias,
+                                 const void* w_gate, const void* w_up,
+                                 const void* w_down, void* out, zc_route_buf* r,
+                                 void* stream);
+
 /* Backward of zc_moe_forward with the routing held fixed (the picked set is
  * piecewise constant in the inputs; the bias gets no gradient, it is
  * decoupled from the training objective).  Given dout [T][d]:

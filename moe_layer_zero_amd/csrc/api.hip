@@ -49,12 +49,17 @@ std::mutex g_prof_mu;
 std::atomic<bool> g_prof_on{false};
 std::vector<PhaseRec> g_prof_recs;
 
+// Set while the calling thread runs the allocation-free forward: its
+// launches record no timing events (creating an event may allocate).
+thread_local bool t_no_events = false;
+
 // Records a start event on construction and an end event in done(), on the
 // stream of the launch, when profiling is on.
 class PhaseScope {
  public:
   PhaseScope(int phase, hipStream_t s) : phase_(phase), s_(s) {
-    if (g_prof_on.load(std::memory_order_relaxed) && hipEventCreate(&a_) == hipSuccess)
+    if (!t_no_events && g_prof_on.load(std::memory_order_relaxed) &&
+        hipEventCreate(&a_) == hipSuccess)
       (void)hipEventRecord(a_, s_);
     else
       a_ = nullptr;
@@ -647,6 +652,37 @@ zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg
   return ZC_OK;
 }
 
+// ---- scratch of the allocation-free forward (zc_moe_forward_noalloc)
+// A file-scope device array: every GPU the library runs on holds its own
+// copy, at its own address, until the process ends.  Host code never uses
+// the array's name as a device address: scratch_ptr() looks each device's
+// copy up once (hipGetSymbolAddress, with that device current) and keeps it.
+constexpr size_t kNoAllocScratch = size_t(64) << 20;  // ZC_NOALLOC_SCRATCH_BYTES
+static __device__ __align__(256) char scratch[kNoAllocScratch];
+static_assert(kNoAllocScratch == ZC_NOALLOC_SCRATCH_BYTES, "header and library disagree");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+zc_status scratch_ptr(void** out) {
+  int dev = -1;
+  ZC_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ZC_ERR_UNSUPPORTED, "device %d: the allocation-free forward tracks devices 0..%d",
+                dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    ZC_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u))
+      return fail(ZC_ERR_HIP, "scratch of device %d at %p is not 256-byte aligned", dev, p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ZC_OK;
+}
+
 zc_status check_weights(const zc_moe_desc* d, const void* wg, const void* wu, const void* wd) {
   const bool opt = d->N == 0;
   ZC_CHECK(check_ptr(wg, "w_gate", opt));
@@ -724,6 +760,25 @@ zc_status zc_moe_forward(const zc_moe_desc* desc, const void* x, const void* w_r
                            bias, static_cast<const float*>(w_gate),
                            static_cast<const float*>(w_up), static_cast<const float*>(w_down),
                            static_cast<float*>(out), r, saved, w, s);
+}
+
+zc_status zc_moe_forward_noalloc(const zc_moe_desc* desc, const void* x, const void* w_router,
+                                 const float* bias, const void* w_gate, const void* w_up,
+                                 const void* w_down, void* out, zc_route_buf* r, void* stream) {
+  ZC_CHECK(check_desc(desc));
+  const int64_t need = fwd_ws_bytes(desc);
+  if (need > static_cast<int64_t>(kNoAllocScratch))
+    return fail(ZC_ERR_WORKSPACE,
+                "the allocation-free forward holds %zu bytes of scratch per device; this layer "
+                "needs %lld (zc_moe_workspace_size(desc, ZC_OP_FORWARD))",
+                kNoAllocScratch, (long long)need);
+  void* ws = nullptr;
+  ZC_CHECK(scratch_ptr(&ws));
+  t_no_events = true;
+  const zc_status st = zc_moe_forward(desc, x, w_router, bias, w_gate, w_up, w_down, out, r,
+                                      nullptr, ws, kNoAllocScratch, stream);
+  t_no_events = false;
+  return st;
 }
 
 zc_status zc_moe_backward(const zc_moe_desc* desc, const void* x, const void* w_router,

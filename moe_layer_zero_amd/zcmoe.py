@@ -25,7 +25,7 @@ ZC_PACK_GATE_UP, ZC_PACK_DOWN = 0, 1
 
 # Every symbol include/zc_moe.h declares.
 EXPORTS = ("zc_moe_workspace_size", "zc_moe_saved_size", "zc_moe_route", "zc_moe_forward",
-           "zc_moe_backward", "zc_moe_lb_loss", "zc_moe_route_stats", "zc_moe_accumulate_counts",
+           "zc_moe_forward_noalloc", "zc_moe_backward", "zc_moe_lb_loss", "zc_moe_route_stats", "zc_moe_accumulate_counts",
            "zc_moe_pid_update", "zc_moe_pack_weights", "zc_moe_quantized_weight_bytes",
            "zc_moe_quantize_weights",
            "zc_moe_profile",
@@ -76,6 +76,7 @@ def lib() -> C.CDLL:
         L.zc_moe_saved_size.restype = sz
         L.zc_moe_route.argtypes = [P, v, v, v, D, v, sz, v]
         L.zc_moe_forward.argtypes = [P, v, v, v, v, v, v, v, D, v, v, sz, v]
+        L.zc_moe_forward_noalloc.argtypes = [P, v, v, v, v, v, v, v, D, v]
         LB = C.POINTER(zc_lb_cfg)
         L.zc_moe_backward.argtypes = [P, v, v, v, v, v, D, v, v, v, v, v, v, v, LB, v, sz, v]
         L.zc_moe_lb_loss.argtypes = [P, LB, D, v, v, sz, v]
@@ -86,7 +87,8 @@ def lib() -> C.CDLL:
         L.zc_moe_quantized_weight_bytes.argtypes = [P]
         L.zc_moe_quantized_weight_bytes.restype = sz
         L.zc_moe_quantize_weights.argtypes = [P, C.c_int, v, v, v]
-        for f in ("zc_moe_route", "zc_moe_forward", "zc_moe_backward", "zc_moe_lb_loss",
+        for f in ("zc_moe_route", "zc_moe_forward", "zc_moe_forward_noalloc",
+                  "zc_moe_backward", "zc_moe_lb_loss",
                   "zc_moe_route_stats", "zc_moe_accumulate_counts", "zc_moe_pid_update",
                   "zc_moe_pack_weights", "zc_moe_quantize_weights"):
             getattr(L, f).restype = C.c_int
@@ -239,6 +241,24 @@ def zc_moe_forward(desc: LayerDesc, x, w_router, bias, w_gate, w_up, w_down, out
     _check(lib().zc_moe_forward(C.byref(d), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate),
                                 _ptr(w_up), _ptr(w_down), _ptr(out), C.byref(r), _ptr(saved),
                                 _ptr(ws), ws.numel(), _stream(stream)), "zc_moe_forward")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # ZC_NOALLOC_SCRATCH_BYTES
+
+
+def zc_moe_forward_noalloc(desc: LayerDesc, x, w_router, bias, w_gate, w_up, w_down, out,
+                           route: RouteBuffers, stream=None):
+    """The inference forward on the library's own per-device scratch (no
+    workspace argument, nothing allocated); rejects layers whose forward
+    workspace exceeds NOALLOC_SCRATCH_BYTES."""
+    _check_layer_tensor(x, (desc.T, desc.d), desc.dtype, "x")
+    _check_layer_tensor(out, (desc.T, desc.d), desc.dtype, "out")
+    _check_layer_tensor(bias, (desc.E,), torch.float32, "bias")
+    _check_weights(desc, w_router, w_gate, w_up, w_down)
+    d, r = desc.c(), route.c()
+    _check(lib().zc_moe_forward_noalloc(C.byref(d), _ptr(x), _ptr(w_router), _ptr(bias),
+                                        _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out),
+                                        C.byref(r), _stream(stream)), "zc_moe_forward_noalloc")
 
 
 @dataclass

@@ -258,3 +258,20 @@ def test_quantized_weight_argument_checks(L):
     bf = desc(dtype=torch.bfloat16, d=512, I=512).c()
     assert L.zc_moe_workspace_size(C.byref(mx), zcmoe.ZC_OP_FORWARD) > \
         L.zc_moe_workspace_size(C.byref(bf), zcmoe.ZC_OP_FORWARD)
+
+
+def test_noalloc_forward_rejects_oversized_layers_before_any_work(L):
+    # a layer whose forward workspace exceeds the library's scratch: refused
+    # on the host (fake, never dereferenced pointers)
+    d = desc(dtype=torch.bfloat16, T=4096, d=1024, N=64, Z=32, I=512, K=6)
+    assert zcmoe.zc_moe_workspace_size(d, zcmoe.ZC_OP_FORWARD) > zcmoe.NOALLOC_SCRATCH_BYTES
+    dd, r = d.c(), route_buf()
+    st = L.zc_moe_forward_noalloc(C.byref(dd), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  C.byref(r), None)
+    assert st == zcmoe.ZC_ERR_WORKSPACE
+    assert "scratch" in L.zc_last_error().decode()
+    # and the LongCat-Flash decode batch fits
+    dec = desc(dtype=torch.bfloat16, T=256, d=6144, N=512, Z=256, I=2048, K=12)
+    for lay in (zcmoe.ZC_WEIGHTS_ROWMAJOR, zcmoe.ZC_WEIGHTS_PACKED, zcmoe.ZC_WEIGHTS_MXFP8):
+        dec.weight_layout = lay
+        assert zcmoe.zc_moe_workspace_size(dec, zcmoe.ZC_OP_FORWARD) <= zcmoe.NOALLOC_SCRATCH_BYTES
