@@ -33,23 +33,25 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
 FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, vendor figure
 
-# HBM bytes of one prefill gate/up launch read from rocprofv3 counters
-# (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a plain copy of known
-# size gives), valid for the kernel source they were measured on: reported
-# as roofline.traffic only while that source is unchanged.
-GATE_UP_TRAFFIC = {"source": "moe_layer_zero_amd/csrc/gemm_fwdp.hip",
-                   "sha256": "042051d4820c15c119f92103cd0b86676dcb24ffa1ae750b0b5464dff5d70122",
-                   "fetch_bytes": 31659601877, "write_bytes": 588773376}
+# HBM bytes of one prefill launch of each expert GEMM, read from rocprofv3
+# counters (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0, the factors a plain copy
+# of known size gives; profiles/fwdp_gemm_prefill_decode.md), valid for the
+# kernel source they were measured on: reported as traffic only while that
+# source is unchanged.
+TRAFFIC_SOURCE = {"source": "moe_layer_zero_amd/csrc/gemm_fwdp.hip",
+                  "sha256": "042051d4820c15c119f92103cd0b86676dcb24ffa1ae750b0b5464dff5d70122"}
+TRAFFIC = {"gate_up_gemm": {"fetch_bytes": 31659601877, "write_bytes": 588773376},
+           "down_gemm": {"fetch_bytes": 16674661035, "write_bytes": 1857983488}}
 
 
-def measured_traffic():
-    path = os.path.join(ROOT, GATE_UP_TRAFFIC["source"])
-    if GATE_UP_TRAFFIC["sha256"] is None or not os.path.exists(path):
+def measured_traffic(kernel: str = "gate_up_gemm"):
+    path = os.path.join(ROOT, TRAFFIC_SOURCE["source"])
+    if TRAFFIC_SOURCE["sha256"] is None or not os.path.exists(path):
         return None
     sha = hashlib.sha256(open(path, "rb").read()).hexdigest()
-    if sha != GATE_UP_TRAFFIC["sha256"]:
+    if sha != TRAFFIC_SOURCE["sha256"] or kernel not in TRAFFIC:
         return None
-    return GATE_UP_TRAFFIC["fetch_bytes"] + GATE_UP_TRAFFIC["write_bytes"]
+    return TRAFFIC[kernel]["fetch_bytes"] + TRAFFIC[kernel]["write_bytes"]
 
 
 def log(*a):
@@ -117,15 +119,12 @@ def layer_forward_bench(sh, steps, warmup, packed=True, fp8=False):
     return Lg, ms, phases, p_real, touched, counts
 
 
-def gate_up_roofline(sh, p_real, touched, gu_ms):
-    """Roofline of the gate/up GEMM for one launch: algorithmic flop
-    (4 d I per FFN pick) and bytes (gate and up weights of every touched
-    expert once, the gathered x row and the h row of every pick), against
-    the vendor peaks; the binding roofline is the one with the higher floor."""
-    d, I = sh.d, sh.I
-    flops = 4.0 * d * I * p_real
-    nbytes = 2.0 * 2 * d * I * touched + 2.0 * d * p_real + 2.0 * I * p_real
-    t = gu_ms * 1e-3
+def gemm_roofline(kernel, flops, nbytes, ms):
+    """Roofline of one expert-GEMM launch from its algorithmic flop and bytes
+    and its measured duration, against the vendor peaks; the binding
+    roofline is the one with the higher floor, and the other fraction rides
+    along (mfma_frac / hbm_frac) so the matrix-core share is always shown."""
+    t = ms * 1e-3
     tflops, gbs = flops / t / 1e12, nbytes / t / 1e9
     hbm_floor = nbytes / (HBM_PEAK_GBS * 1e9)
     mfma_floor = flops / (BF16_PEAK_TFLOPS * 1e12)
@@ -134,10 +133,28 @@ def gate_up_roofline(sh, p_real, touched, gu_ms):
     hbm = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(gbs / HBM_PEAK_GBS, 4)}
     roof = dict(hbm if hbm_floor > mfma_floor else mfma)
-    roof.update(kernel="gate_up_gemm", traffic=measured_traffic(),
+    roof.update(kernel=kernel, traffic=measured_traffic(kernel),
+                mfma_frac=mfma["frac"], hbm_frac=hbm["frac"],
                 algorithmic={"flop": flops, "bytes": nbytes, "hbm_floor_ms": hbm_floor * 1e3,
                              "mfma_floor_ms": mfma_floor * 1e3})
     return roof, mfma, hbm
+
+
+def gate_up_roofline(sh, p_real, touched, gu_ms):
+    """Gate/up GEMM: 4 d I flop per FFN pick; bytes: gate and up weights of
+    every touched expert once, the gathered x row and the h row of every
+    pick."""
+    d, I = sh.d, sh.I
+    return gemm_roofline("gate_up_gemm", 4.0 * d * I * p_real,
+                         2.0 * 2 * d * I * touched + 2.0 * d * p_real + 2.0 * I * p_real, gu_ms)
+
+
+def down_roofline(sh, p_real, touched, dn_ms):
+    """Down GEMM: 2 d I flop per FFN pick; bytes: down weights of every
+    touched expert once, the h row read and the y row written per pick."""
+    d, I = sh.d, sh.I
+    return gemm_roofline("down_gemm", 2.0 * d * I * p_real,
+                         2.0 * d * I * touched + 2.0 * I * p_real + 2.0 * d * p_real, dn_ms)
 
 
 def prefill(steps, warmup, packed=True):
@@ -149,6 +166,7 @@ def prefill(steps, warmup, packed=True):
     gu_ms = ph["gate_up_gemm"][0]
     dn_ms = ph["down_gemm"][0]
     roof, mfma, hbm = gate_up_roofline(sh, p_real, touched, gu_ms)
+    droof, dmfma, dhbm = down_roofline(sh, p_real, touched, dn_ms)
     res = {
         "ms_per_step": ms,
         "tokens_per_s": sh.T / (ms / 1e3),
@@ -161,6 +179,9 @@ def prefill(steps, warmup, packed=True):
         "gate_up_hbm_frac": hbm["frac"],
         "gate_up_tflops": flops_gu / (gu_ms * 1e-3) / 1e12,
         "down_tflops": flops_dn / (dn_ms * 1e-3) / 1e12,
+        "down_mfma_frac": dmfma["frac"],
+        "down_hbm_frac": dhbm["frac"],
+        "down_roofline": droof,
         "expert_gemms_tflops": (flops_gu + flops_dn) / ((gu_ms + dn_ms) * 1e-3) / 1e12,
         "expert_gemms_mfma_frac": (flops_gu + flops_dn) / ((gu_ms + dn_ms) * 1e-3) / 1e12
         / BF16_PEAK_TFLOPS,

@@ -28,10 +28,23 @@ def _bench_module():
 
 def test_traffic_only_for_the_measured_source(tmp_path):
     b = _bench_module()
-    src = os.path.join(ROOT, b.GATE_UP_TRAFFIC["source"])
+    src = os.path.join(ROOT, b.TRAFFIC_SOURCE["source"])
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    want = b.GATE_UP_TRAFFIC["fetch_bytes"] + b.GATE_UP_TRAFFIC["write_bytes"]
-    assert b.measured_traffic() == (want if sha == b.GATE_UP_TRAFFIC["sha256"] else None)
+    for k in ("gate_up_gemm", "down_gemm"):
+        want = b.TRAFFIC[k]["fetch_bytes"] + b.TRAFFIC[k]["write_bytes"]
+        assert b.measured_traffic(k) == (want if sha == b.TRAFFIC_SOURCE["sha256"] else None)
+    assert b.measured_traffic("combine") is None
     # any other source text: no traffic figure
-    b.GATE_UP_TRAFFIC = dict(b.GATE_UP_TRAFFIC, sha256="0" * 64)
+    b.TRAFFIC_SOURCE = dict(b.TRAFFIC_SOURCE, sha256="0" * 64)
     assert b.measured_traffic() is None
+
+
+def test_roofline_picks_the_higher_floor_and_keeps_both_fractions():
+    b = _bench_module()
+    # 1e12 flop and 1e10 bytes in 1 ms: MFMA floor 0.4 ms > HBM floor 1.25 ms? no:
+    # HBM floor 1e10 / 8e12 = 1.25 ms, MFMA floor 1e12 / 2.5e15 = 0.4 ms -> hbm
+    roof, mfma, hbm = b.gemm_roofline("gate_up_gemm", 1e12, 1e10, 2.0)
+    assert roof["bound"] == "hbm" and roof["frac"] == hbm["frac"]
+    assert roof["mfma_frac"] == mfma["frac"] == round(1e12 / 2e-3 / 1e12 / 2500.0, 4)
+    roof, mfma, hbm = b.gemm_roofline("down_gemm", 1e13, 1e9, 10.0)
+    assert roof["bound"] == "mfma" and roof["hbm_frac"] == hbm["frac"]
