@@ -259,6 +259,51 @@ def train(steps, warmup):
     return res
 
 
+def train_telemetry(path, steps=None, T=None):
+    """Budget-control telemetry of the training workload ("LongCat-Flash
+    Technical Report", section 2.1.1 tracks how many FFN experts each token
+    activates, Fig.3b/3c): the router + Eq.(2) loop from zero bias on the
+    step inputs of the training run (weights are fixed, so the bias
+    trajectory depends on the routing alone), one JSON line per step to
+    `path`: mean and population std of the FFN experts per token and their
+    histogram (zc_moe_route_stats), the zero-computation share of the picks,
+    the coefficient of variation and max/mean of the per-FFN-expert token
+    counts, the device-level load-balance loss, and the FFN bias range after
+    the step's update.  Outside any timed region."""
+    sh = synth.CONFIGS["train_bf16"]
+    if T is not None:
+        sh = sh.with_T(T)
+    steps = synth.TRAIN_STEPS if steps is None else steps
+    L = synth.make_layer(sh, "cuda", want_experts=False)
+    desc = desc_of(sh)
+    route = zcmoe.RouteBuffers(desc)
+    bias = torch.zeros(sh.E, device="cuda")
+    lb = zcmoe.LoadBalance(synth.TRAIN_LB_D, synth.TRAIN_K_E, synth.TRAIN_LB_ALPHA)
+    lines = []
+    with open(path, "w") as f:
+        for s in range(steps):
+            zcmoe.zc_moe_route(desc, synth.step_x(sh, s, "cuda"), L["wr"], bias, route)
+            hist, mom = zcmoe.zc_moe_route_stats(desc, route)
+            lbo = zcmoe.zc_moe_lb_loss(desc, lb, route)
+            zcmoe.zc_moe_pid_update(sh.N, sh.Z, sh.K, route.counts, sh.T, synth.TRAIN_MU,
+                                    synth.TRAIN_K_E, bias)
+            c = route.counts.cpu().numpy()[: sh.N].astype(np.float64)
+            m = mom.cpu().numpy()
+            b = bias.cpu().numpy()[: sh.N]
+            rec = {"step": s, "tokens": sh.T, "mean_ffn_experts": float(m[0]),
+                   "std_ffn_experts": float(m[1]), "hist": hist.cpu().numpy().tolist(),
+                   "zero_pick_fraction": 1.0 - float(c.sum()) / (sh.T * sh.K),
+                   "ffn_count_cv": float(c.std() / c.mean()) if c.mean() > 0 else 0.0,
+                   "ffn_count_max_over_mean": float(c.max() / c.mean()) if c.mean() > 0 else 0.0,
+                   "lb_loss": float(lbo[0].item()), "bias_ffn_min": float(b.min()),
+                   "bias_ffn_max": float(b.max()), "mu": synth.TRAIN_MU, "K_e": synth.TRAIN_K_E}
+            f.write(json.dumps(rec) + "\n")
+            lines.append(rec)
+    del L
+    torch.cuda.empty_cache()
+    return lines
+
+
 def fp8_forward(name, steps, warmup):
     """The MXFP8 inference forward (E4M3 codes, one E8M0 scale per 32
     reduction steps) of the prefill or decode layer.  Algorithmic bytes of
@@ -355,6 +400,9 @@ def main():
                     help="inference on row-major expert weights instead of the packed layout")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--telemetry", default=None, metavar="PATH",
+                    help="also write the training loop's per-step routing telemetry "
+                         "(JSON lines) to PATH, outside the timed region")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer's benchmark has no multi-GPU path "
@@ -381,6 +429,10 @@ def main():
         if args.only in (None, key):
             extra[key.replace("-", "_")] = fp8_forward(name, args.steps, args.warmup)
             log(f"[bench] {key} {extra[key.replace('-', '_')]['ms_per_step']:.3f} ms/step")
+    if args.telemetry:
+        tl = train_telemetry(args.telemetry)
+        log(f"[bench] telemetry: {len(tl)} steps to {args.telemetry}, last mean FFN experts "
+            f"{tl[-1]['mean_ffn_experts']:.4f}")
     cpu = None if args.no_cpu_baseline or args.only not in (None, "prefill") else cpu_baseline()
     if res is None:  # a secondary workload alone: report it as the line
         k = args.only

@@ -977,7 +977,12 @@ const char* zc_moe_phase_name(int phase) {
 }
 
 const char* zc_status_string(zc_status s) {
-  switch (s) {
+  // callers from C or Python may pass any int: read it as one, never as an
+  // out-of-range value of the enum type
+  int v = 0;
+  static_assert(sizeof v == sizeof s, "zc_status is an int");
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case ZC_OK: return "ok";
     case ZC_ERR_INVALID: return "invalid argument";
     case ZC_ERR_UNSUPPORTED: return "unsupported shape";

@@ -105,3 +105,75 @@ def test_micro_batch_accumulation_with_decaying_mu_is_bit_exact():
                   flush=True)
     late = float(np.mean(means[-30:]))
     assert abs(late - Ke) < 0.01 * Ke, late
+
+
+def test_training_bias_resumes_bit_exactly_from_a_checkpoint(tmp_path):
+    """The training workload's router and Eq.(2) loop on the GPU (T = 8192,
+    128 + 64 experts, top-8, mu = 1, K_e = 6): stopped after 10 steps, the
+    fp32 bias saved to disk, every buffer dropped, the bias read back into
+    fresh buffers -- the next 10 steps give the same counts and biases bit
+    for bit as the run that never stopped (the bias is the only state)."""
+    sh = synth.CONFIGS["train_bf16"]
+    L = synth.make_layer(sh, "cuda", want_experts=False)
+    desc = zcmoe.LayerDesc(sh.T, sh.d, sh.N, sh.Z, sh.I, sh.K, torch.bfloat16)
+
+    def steps(bias, s0, s1):
+        route = zcmoe.RouteBuffers(desc)
+        out = []
+        for s in range(s0, s1):
+            zcmoe.zc_moe_route(desc, synth.step_x(sh, s, "cuda"), L["wr"], bias, route)
+            zcmoe.zc_moe_pid_update(sh.N, sh.Z, sh.K, route.counts, sh.T, synth.TRAIN_MU,
+                                    synth.TRAIN_K_E, bias)
+            torch.cuda.synchronize()
+            out.append((route.counts.cpu().numpy().copy(), bias.cpu().numpy().copy()))
+        return out
+
+    whole = steps(torch.zeros(sh.E, device="cuda"), 0, 20)
+    b = torch.zeros(sh.E, device="cuda")
+    first = steps(b, 0, 10)
+    np.save(tmp_path / "bias.npy", b.cpu().numpy())
+    del b
+    torch.cuda.synchronize()
+    resumed = torch.from_numpy(np.load(tmp_path / "bias.npy")).cuda()
+    second = steps(resumed, 10, 20)
+    for (c1, b1), (c2, b2) in zip(whole, first + second):
+        np.testing.assert_array_equal(c1, c2)
+        np.testing.assert_array_equal(b1, b2)
+    # and the loop converges toward K_e = 6 FFN experts per token
+    late = np.mean([c[: sh.N].sum() / sh.T for c, _ in whole[15:]])
+    assert abs(late - synth.TRAIN_K_E) < 0.05 * synth.TRAIN_K_E, late
+
+
+def test_per_step_telemetry_lines(tmp_path):
+    """bench.py --telemetry: one JSON line per training step with the
+    budget-control statistics; checked against the oracle's statistics of
+    the same routing for the first step and for consistency on all."""
+    import importlib.util
+    import json
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_telemetry", os.path.join(root, "bench.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    path = str(tmp_path / "telemetry.jsonl")
+    lines = b.train_telemetry(path, steps=6, T=1024)
+    recs = [json.loads(l) for l in open(path)]
+    assert recs == json.loads(json.dumps(lines)) and len(recs) == 6
+    sh = synth.CONFIGS["train_bf16"]
+    for r in recs:
+        h = np.array(r["hist"])
+        assert h.sum() == 1024 and len(h) == sh.K + 1
+        assert abs((h * np.arange(sh.K + 1)).sum() / 1024 - r["mean_ffn_experts"]) < 1e-12
+        assert abs(r["zero_pick_fraction"] - (1 - r["mean_ffn_experts"] / sh.K)) < 1e-12
+        assert r["lb_loss"] > 0 and r["ffn_count_cv"] >= 0
+    # first step (zero bias): the oracle's statistics of the oracle's routing
+    # the same (GPU-drawn) inputs bench.py routed
+    L = synth.make_layer(sh.with_T(1024), "cuda", want_experts=False)
+    x = synth.to_np(synth.step_x(sh.with_T(1024), 0, "cuda"))
+    o = oracle.route(oracle.logits(x, synth.to_np(L["wr"])), np.zeros(sh.E, np.float32), sh.N,
+                     sh.K, want_keys=False)
+    hist, m, s = oracle.route_stats(o.topk_idx, sh.N)
+    # scores differ in their last bits (fp32 vs fp64): near-ties may flip
+    # a pick or two
+    assert abs(m - recs[0]["mean_ffn_experts"]) < 4.0 / 1024
+    assert abs(s - recs[0]["std_ffn_experts"]) < 0.01

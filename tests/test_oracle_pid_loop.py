@@ -29,3 +29,34 @@ def test_router_only_loop_converges(orc):
     assert abs(late - synth.TRAIN_K_E) < 0.01 * synth.TRAIN_K_E, means
     # zero-computation biases never move
     assert not b[sh.N:].any()
+
+
+def test_router_only_loop_resumes_from_a_saved_bias(orc, tmp_path):
+    """The expert bias is the controller's only state (Eq.(2) reads the
+    current counts and bias, nothing else): a loop stopped at step 10, its
+    bias written to disk and read back, continues bit for bit as if it had
+    never stopped."""
+    sh = synth.CONFIGS["train_bf16"].with_T(512)
+    L = synth.make_layer(sh, "cpu", want_experts=False)
+    wr = synth.to_np(L["wr"])
+
+    def steps(b, s0, s1):
+        traj = []
+        for s in range(s0, s1):
+            x = synth.to_np(synth.step_x(sh, s))
+            r = orc.route(orc.logits(x, wr), b, sh.N, sh.K, want_keys=False)
+            b = orc.pid_update(r.counts, sh.T, b, sh.N, sh.Z, sh.K, synth.TRAIN_MU,
+                               synth.TRAIN_K_E)
+            traj.append((r.counts.copy(), b.copy()))
+        return b, traj
+
+    b0 = np.zeros(sh.E, np.float32)
+    _, whole = steps(b0, 0, 20)
+    b10, first = steps(b0, 0, 10)
+    np.save(tmp_path / "bias.npy", b10)
+    resumed = np.load(tmp_path / "bias.npy")
+    assert resumed.dtype == np.float32
+    _, second = steps(resumed, 10, 20)
+    for (c1, b1), (c2, b2) in zip(whole, first + second):
+        np.testing.assert_array_equal(c1, c2)
+        np.testing.assert_array_equal(b1, b2)
