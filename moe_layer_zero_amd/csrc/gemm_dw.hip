@@ -65,6 +65,9 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_void* ds
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
 }
 
+// Only for values the compiler has moved out of AGPR accumulators (its
+// own, hazard-checked moves): an MFMA result still in a VGPR, read by inline
+// asm, is outside the compiler's hazard tracking.
 __device__ __forceinline__ bf16_t cvt_bf16(float f) {
   uint32_t r;
   asm volatile("v_cvt_pk_bf16_f32 %0, %1, 0" : "=v"(r) : "v"(f));

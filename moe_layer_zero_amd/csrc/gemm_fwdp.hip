@@ -24,7 +24,8 @@
 // global memory into registers with 1 KB contiguous loads: no LDS, no barrier.
 //
 // Tile: 256 rows x 256 MFMA columns per 256-thread workgroup (gate/up: 128
-// gate + 128 up columns = 128 columns of h).  Wave w owns all 256 rows and 64
+// gate + 128 up columns = 128 columns of h; the 256-row down projection
+// runs the eight-wave variant below, down8_kernel).  Wave w owns all 256 rows and 64
 // columns (gate/up: 32 gate + the matching 32 up columns, so SwiGLU is done
 // in registers): 8 x 2 blocks of 32 x 32 fp32 accumulators (256 registers).
 // Activation rows are staged through a 4-slot LDS ring, 64 reduction steps
@@ -48,6 +49,7 @@ constexpr int BK = 64;      // reduction steps per slab
 constexpr int NST = 4;      // LDS ring slots
 constexpr int NTHR = 256;
 constexpr int GMV = 8;      // row tiles per group inside an expert
+constexpr int DSDEPTH = 4;  // fragment reads ahead of their MFMAs (eight-wave kernel)
 
 // P_SWIGLU: gate/up with SwiGLU; P_STORE: down projection (bf16 y);
 // P_DSWIGLU: backward dh = g * (dout W_d) in fp32 (swiglu_bwd_kernel then
@@ -93,6 +95,9 @@ __device__ __forceinline__ float silu_f(float a) {
 // conversions, and the 256-row kernel then spills inside its k loop.  (The
 // gate/up epilogue keeps f2bf: with any branch-free rounding there the
 // register allocator spills inside the k loop as well.)
+// Only for values the compiler has moved out of AGPR accumulators (its
+// own, hazard-checked moves): an MFMA result still in a VGPR, read by inline
+// asm, is outside the compiler's hazard tracking.
 __device__ __forceinline__ bf16_t cvt_bf16(float f) {
   uint32_t r;
   asm volatile("v_cvt_pk_bf16_f32 %0, %1, 0" : "=v"(r) : "v"(f));
@@ -110,10 +115,10 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_void* ds
 // s_waitcnt immediate for "vmcnt <= n" (expcnt and lgkmcnt not waited)
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
-// TM: rows per tile (32, 64, 128 or 256).  LOADS_FIRST: a slab's loads are
-// issued right after its barrier; otherwise they are spread over the first
-// half of its MFMAs (256-row tiles only).
-template <int EPI, int TM, bool LOADS_FIRST>
+// TM: rows per tile (32, 64, 128 or 256).  A slab's loads are issued right
+// after its barrier, ahead of its fragment reads and MFMAs (spreading them
+// over the MFMAs measured slower for the 256-row gate/up tiles).
+template <int EPI, int TM>
 __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   constexpr int RB = TM / 32;       // 32-row blocks per tile = A loads per wave per slab
   // P_DX slabs hold the hi and the lo piece of the same reduction steps
@@ -121,7 +126,6 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   constexpr int SLOT = APC * TM * BK;  // bf16 per ring slot
   constexpr int V = APC * RB + 8;      // loads per wave per slab (A rows + 8 B blocks)
   static_assert(TM == 32 || TM == 64 || TM == 128 || TM == 256, "tile height");
-  static_assert(LOADS_FIRST || TM == 256, "interleaved issue is laid out for 256-row tiles");
   // the ring, then one int: the next tile index claimed by thread 0 (kept in
   // the same LDS object, see the note on the tables of the decode)
   __shared__ __align__(16) bf16_t ring[NST * SLOT + 16];
@@ -248,8 +252,6 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
     const int nrb = (mcount + 31) >> 5;
     auto run = [&](auto nrb_c) {
       constexpr int NRB = decltype(nrb_c)::value;
-      // interleaved issue is laid out for a full 256-row tile
-      constexpr bool LF = LOADS_FIRST || NRB != 8;
       bf16x8_t bq[NST][2][4];  // B fragments of the slabs in flight
       auto issue = [&](int kt, int slot, bf16x8_t (&bf)[2][4]) {
         if constexpr (EPI == P_DX) {
@@ -319,29 +321,12 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
       };
 
       // Issue order inside a slab (4 NRB fragment reads, 8 NRB MFMAs, V loads):
-      // loads first, or spread over the first MFMAs; fragment reads run up to
-      // three ahead of the MFMAs that use them.
+      // loads first; fragment reads run up to three ahead of the MFMAs that
+      // use them.
       constexpr int NDS = 4 * APC * NRB;
       constexpr int DS0 = NDS < 3 ? NDS : 3;
       auto sched = [&](bool with_loads) {
-        if (with_loads && LF) __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
-        if (with_loads && !LF) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-          for (int g = 0; g < 16; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-#pragma unroll
-          for (int g = 0; g < 14; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-          return;
-        }
+        if (with_loads) __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, DS0, 0);
 #pragma unroll
         for (int g = 0; g < NDS - DS0; ++g) {
@@ -476,6 +461,230 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   }
 }
 
+// The down projection on 256-row tiles (the prefill shape) with eight
+// waves: two per SIMD, each owning all 256 rows of the tile and one group of
+// 32 output columns, so 8 accumulator blocks (128 registers) instead of 16
+// and the pair of waves on a SIMD fits one register file; one wave's matrix
+// work runs while the other waits on its loads or fragment reads.  The
+// activation ring is shared by the eight waves as before (each reads the
+// whole A slab: LDS reads with eight waves per CU measure above 170 bytes
+// per clock on this part, twice what one wave per SIMD draws).  Every
+// output element sums the same MFMA steps in the same order as the
+// four-wave kernel, so the two give identical bits.  Measured at the
+// prefill workload: 4.00 ms against 4.29 ms for the four-wave kernel; the
+// same split of the gate/up GEMM (gate and up columns on different waves,
+// joined through LDS in the epilogue) gave no gain (8.09 vs 7.95 ms) and is
+// not used.
+constexpr int NTHR8 = 512;
+__global__ __launch_bounds__(NTHR8, 1) void down8_kernel(PParams p) {
+  constexpr int TM = 256;
+  constexpr int SLOT = TM * BK;        // bf16 per ring slot (32 KB)
+  constexpr int AW = 4;                // A copies per wave per slab (32 1-KB blocks / 8 waves)
+  constexpr int V = AW + 4;            // loads per wave per slab
+  __shared__ __align__(16) bf16_t ring[NST * SLOT + 16];
+  int32_t* const s_claim = reinterpret_cast<int32_t*>(ring + NST * SLOT);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int OUTN = 256;
+  const int NT = p.ncols / OUTN;
+  const int64_t total = static_cast<int64_t>(ld_scalar(p.mt_off + p.N)) * NT;
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % 8;
+  const int C = G / 8;
+  int cx = xcd;
+  int hops = 0;
+  auto tile_of = [&](int x, int n) -> int64_t {
+    return static_cast<int64_t>(n / C) * 8 * C + x * C + n % C;
+  };
+  if (tid == 0) s_claim[0] = atomicAdd(p.sched + cx, 1);
+  __syncthreads();
+  int cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
+  const int nk = p.K / BK;
+  const int kblk = p.K / 16;
+  const __amdgpu_buffer_rsrc_t arsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(p.A), (short)0, p.a_bytes, 0x00020000);
+  const int s7 = (lane >> 1) & 7;
+  const int khalf = lane >> 5;
+  const int frag_lane = (lane & 31) * BK;
+
+  for (;;) {
+    const int64_t L = tile_of(cx, cur_n);
+    if (L >= total) {
+      if (++hops == 8) break;
+      cx = (cx + 1) & 7;
+      __syncthreads();
+      if (tid == 0) s_claim[0] = atomicAdd(p.sched + cx, 1);
+      __syncthreads();
+      cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
+      continue;
+    }
+    int32_t next_n = 0;
+    if (tid == 0) next_n = atomicAdd(p.sched + cx, 1);
+    const int lmt = static_cast<int>(L / NT);
+    const int e = ld_scalar(p.tile_exp + lmt);
+    const int mt_e = ld_scalar(p.mt_off + e);
+    const int mte = ld_scalar(p.mt_off + e + 1) - mt_e;
+    const int q = static_cast<int>(L - static_cast<int64_t>(mt_e) * NT);
+    const int grp = q / (GMV * NT);
+    const int fm = grp * GMV;
+    const int gsz = min(GMV, mte - fm);
+    const int rr = q - grp * GMV * NT;
+    const int mt = fm + rr % gsz;
+    const int nt = rr / gsz;
+    const int seg0 = ld_scalar(p.offsets + e), seg1 = ld_scalar(p.offsets + e + 1);
+    const int nbe = (seg1 - seg0 + 31) >> 5;
+    const int blo = nbe * mt / mte, bhi = nbe * (mt + 1) / mte;
+    const int m0 = seg0 + 32 * blo;
+    const int mcount = min(seg0 + 32 * bhi, seg1) - m0;
+    const int n0 = nt * OUTN;
+
+    uint32_t aoff[AW];
+#pragma unroll
+    for (int i = 0; i < AW; ++i) {
+      const int b = AW * wave + i;
+      const int row = 8 * b + (lane >> 3);
+      const int chunk = (lane & 7) ^ ((4 * b + (lane >> 4)) & 7);
+      if (row < mcount) {
+        const int gm = m0 + row;
+        aoff[i] = (static_cast<uint32_t>(gm) * static_cast<uint32_t>(p.K) + chunk * 8) * 2u;
+      } else {
+        aoff[i] = p.a_bytes;
+      }
+    }
+    const int64_t mat = static_cast<int64_t>(p.ncols) * p.K;
+    // wave w's 32 output columns: packed column group n0/32 + w
+    const bf16_t* bsrc =
+        p.B + e * mat + static_cast<int64_t>(n0 / 32 + wave) * kblk * 512 + lane * 8;
+
+    const int nrb = (mcount + 31) >> 5;
+    auto run = [&](auto nrb_c) {
+      constexpr int NRB = decltype(nrb_c)::value;
+      bf16x8_t bq[NST][4];
+      auto issue = [&](int kt, int slot, bf16x8_t (&bf)[4]) {
+#pragma unroll
+        for (int i = 0; i < AW; ++i) {
+          lds_void* dst = (lds_void*)(ring + slot * SLOT + (AW * wave + i) * 8 * BK);
+          lds_dma16(arsrc, dst, aoff[i], kt * BK * 2);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bf[t] = *reinterpret_cast<const bf16x8_t*>(bsrc + (4 * kt + t) * 512);
+      };
+      f32x16_t acc[NRB];
+#pragma unroll
+      for (int i = 0; i < NRB; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+      auto compute = [&](int slot, const bf16x8_t (&bf)[4]) {
+        const bf16_t* a_s = ring + slot * SLOT + frag_lane;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int co = ((2 * t + khalf) ^ s7) << 3;
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(a_s + rb * 32 * BK + co);
+            acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[t], acc[rb], 0, 0, 0);
+          }
+        }
+      };
+      constexpr int NDS = 4 * NRB;
+      constexpr int DS0 = NDS < DSDEPTH ? NDS : DSDEPTH;
+      auto sched = [&](bool with_loads) {
+        if (with_loads) __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, DS0, 0);
+#pragma unroll
+        for (int g = 0; g < NDS - DS0; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, DS0, 0);
+      };
+      __builtin_amdgcn_sched_barrier(0);
+      issue(0, 0, bq[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(1, 1, bq[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(2, 2, bq[2]);
+      __builtin_amdgcn_sched_barrier(0);
+      int kt = 0;
+      for (; kt < nk - 4; kt += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
+          __builtin_amdgcn_s_barrier();
+          issue(kt + u + 3, (u + 3) & 3, bq[(u + 3) & 3]);
+          compute(u, bq[u]);
+          sched(true);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
+      __builtin_amdgcn_s_barrier();
+      issue(kt + 3, 3, bq[3]);
+      compute(0, bq[0]);
+      sched(true);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
+      __builtin_amdgcn_s_barrier();
+      compute(1, bq[1]);
+      sched(false);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(V));
+      __builtin_amdgcn_s_barrier();
+      compute(2, bq[2]);
+      sched(false);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __builtin_amdgcn_s_barrier();
+      compute(3, bq[3]);
+      sched(false);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- epilogue: lane holds column lane%32 of its group and rows
+      // 32 rb + 8 (v/4) + 4 (lane/32) + v%4
+      const int rbase = 4 * khalf;
+      __syncthreads();  // every wave done reading the ring: it becomes the staging
+      {
+        bf16_t* st = ring;  // [256][256] bf16 = the whole ring
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int rl = rbase + 32 * rb + 8 * (v >> 2) + (v & 3);
+            // a conversion the compiler sees: the accumulators are plain
+            // VGPRs here, and an MFMA result read by inline asm is not
+            // covered by the compiler's hazard tracking
+            st[rl * OUTN + 32 * wave + (lane & 31)] =
+                __builtin_bit_cast(bf16_t, static_cast<__bf16>(acc[rb][v]));
+          }
+      }
+      __syncthreads();
+      constexpr int RC = OUTN / 8;
+      const bf16_t* st = ring;
+#pragma unroll 4
+      for (int c = tid; c < mcount * RC; c += NTHR8) {
+        const int rl = c / RC, cc = (c % RC) * 8;
+        *reinterpret_cast<u32x4_t*>(p.C + static_cast<int64_t>(m0 + rl) * p.ncols + n0 + cc) =
+            *reinterpret_cast<const u32x4_t*>(st + rl * OUTN + cc);
+      }
+      if (tid == 0) s_claim[0] = next_n;
+      __syncthreads();
+    };
+    switch (nrb) {
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      case 3: run(std::integral_constant<int, 3>{}); break;
+      case 4: run(std::integral_constant<int, 4>{}); break;
+      case 5: run(std::integral_constant<int, 5>{}); break;
+      case 6: run(std::integral_constant<int, 6>{}); break;
+      case 7: run(std::integral_constant<int, 7>{}); break;
+      default: run(std::integral_constant<int, 8>{}); break;
+    }
+    cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
+  }
+}
+
 // SwiGLU backward of the FFN picks in dispatch order, from dh = g (dout W_d)
 // and the a, u, h the forward saved (all fp32, [P][I]):
 //   da = dh u silu'(a), du = dh silu(a), silu'(a) = s (1 + a (1 - s)), s = sigmoid(a),
@@ -601,46 +810,51 @@ __global__ __launch_bounds__(256) void pack_t_kernel(const bf16_t* __restrict__ 
 }
 
 // Kernel of each (epilogue, tile height); tiles of up to 64 rows leave room
-// for two workgroups per CU.
-// The backward variants stop at 128-row tiles (a 256-row tile would spill).
+// for two workgroups per CU.  The 256-row down projection runs the
+// eight-wave down8_kernel (launch_tm).  The backward variants stop at
+// 128-row tiles (a 256-row tile would spill).
 typedef void (*fwdp_fn)(PParams);
 fwdp_fn pick_kernel(int epi, int tm, int* per_cu) {
   *per_cu = tm <= 64 ? 2 : 1;
   if (epi == P_DSWIGLU) {
     switch (tm) {
-      case 32: return fwdp_kernel<P_DSWIGLU, 32, true>;
-      case 64: return fwdp_kernel<P_DSWIGLU, 64, true>;
-      case 128: return fwdp_kernel<P_DSWIGLU, 128, true>;
+      case 32: return fwdp_kernel<P_DSWIGLU, 32>;
+      case 64: return fwdp_kernel<P_DSWIGLU, 64>;
+      case 128: return fwdp_kernel<P_DSWIGLU, 128>;
     }
     return nullptr;
   }
   if (epi == P_DX) {
     switch (tm) {
-      case 32: return fwdp_kernel<P_DX, 32, true>;
-      case 64: return fwdp_kernel<P_DX, 64, true>;
-      case 128: return fwdp_kernel<P_DX, 128, true>;
+      case 32: return fwdp_kernel<P_DX, 32>;
+      case 64: return fwdp_kernel<P_DX, 64>;
+      case 128: return fwdp_kernel<P_DX, 128>;
     }
     return nullptr;
   }
   if (epi == P_SWIGLU) {
     switch (tm) {
-      case 32: return fwdp_kernel<P_SWIGLU, 32, true>;
-      case 64: return fwdp_kernel<P_SWIGLU, 64, true>;
-      case 128: return fwdp_kernel<P_SWIGLU, 128, true>;
-      case 256: return fwdp_kernel<P_SWIGLU, 256, true>;
+      case 32: return fwdp_kernel<P_SWIGLU, 32>;
+      case 64: return fwdp_kernel<P_SWIGLU, 64>;
+      case 128: return fwdp_kernel<P_SWIGLU, 128>;
+      case 256: return fwdp_kernel<P_SWIGLU, 256>;
     }
   } else {
     switch (tm) {
-      case 32: return fwdp_kernel<P_STORE, 32, true>;
-      case 64: return fwdp_kernel<P_STORE, 64, true>;
-      case 128: return fwdp_kernel<P_STORE, 128, true>;
-      case 256: return fwdp_kernel<P_STORE, 256, false>;
+      case 32: return fwdp_kernel<P_STORE, 32>;
+      case 64: return fwdp_kernel<P_STORE, 64>;
+      case 128: return fwdp_kernel<P_STORE, 128>;
+
     }
   }
   return nullptr;
 }
 
 hipError_t launch_tm(int epi, int tm, const PParams& p, int cu, hipStream_t s) {
+  if (tm == 256 && epi == P_STORE) {
+    hipLaunchKernelGGL(down8_kernel, dim3(cu), dim3(NTHR8), 0, s, p);
+    return hipGetLastError();
+  }
   int per_cu = 1;
   fwdp_fn k = pick_kernel(epi, tm, &per_cu);
   if (!k) return hipErrorInvalidValue;

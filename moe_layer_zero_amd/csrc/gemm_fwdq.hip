@@ -88,6 +88,9 @@ __device__ __forceinline__ float silu_f(float a) {
   return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
 }
 
+// Only for values the compiler has moved out of AGPR accumulators (its
+// own, hazard-checked moves): an MFMA result still in a VGPR, read by inline
+// asm, is outside the compiler's hazard tracking.
 __device__ __forceinline__ bf16_t cvt_bf16(float f) {
   uint32_t r;
   asm volatile("v_cvt_pk_bf16_f32 %0, %1, 0" : "=v"(r) : "v"(f));
