@@ -327,7 +327,7 @@ enum {
   ZC_PH_BWD_COMBINE, ZC_PH_BWD_DOWN_DH, ZC_PH_BWD_DOWN_DW, ZC_PH_BWD_GATE_UP_DX,
   ZC_PH_BWD_GATE_UP_DW, ZC_PH_BWD_ROUTER_DW, ZC_PH_BWD_ROUTER_DX, ZC_PH_BWD_DX_GATHER,
   ZC_PH_BIAS_UPDATE, ZC_PH_TILE_OFFSETS, ZC_PH_LB_LOSS, ZC_PH_LB_COEF, ZC_PH_ROUTE_STATS,
-  ZC_PH_ACCUMULATE, ZC_PH_QUANTIZE, ZC_PH_BWD_PACK, ZC_PH_BWD_GATHER, ZC_NUM_PHASES
+  ZC_PH_ACCUMULATE, ZC_PH_QUANTIZE, ZC_PH_BWD_GATHER, ZC_NUM_PHASES
 };
 zc_status zc_moe_profile(int on);
 zc_status zc_moe_profile_read(double* total_ms, int32_t* count);

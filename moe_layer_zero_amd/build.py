@@ -22,12 +22,12 @@ OUT = os.path.join(HERE, "libzcmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["api.hip", "router.hip", "dispatch.hip", "gemm.hip", "gemm_fwd.hip", "gemm_fwdp.hip",
-           "gemm_fwdq.hip", "gemm_dw.hip", "combine.hip", "pid.hip"]
+           "gemm_fwdq.hip", "gemm_dw.hip", "gemm_rmw.hip", "combine.hip", "pid.hip"]
 STRICT_FP = {"router.hip", "pid.hip"}
 # The persistent GEMMs claim tiles with one lane's atomic whose result is used
 # a whole tile later; the atomic optimizer would broadcast it to the wave at
 # once, making every claim wait for all memory operations in flight.
-NO_ATOMIC_OPT = {"gemm_fwdp.hip", "gemm_fwdq.hip", "gemm_dw.hip"}
+NO_ATOMIC_OPT = {"gemm_fwdp.hip", "gemm_fwdq.hip", "gemm_dw.hip", "gemm_rmw.hip"}
 
 COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -285,34 +285,32 @@ struct BwdWs {
   // dadu: da, du [P][2I] on the generic path; dh [P][I] on the packed-weight
   // path (its SwiGLU backward then writes the hi/lo pairs below)
   float *gs, *dg, *dl, *dadu, *dxp, *dxr, *rdw, *lbc;
-  // packed-weight backward (use_bwdp): tile prefix and experts, counters,
-  // transposed packed W_d, W_g, W_u, exact bf16 hi/lo pairs of da, du and
-  // g h, and x and dout rows in dispatch order
+  // matrix-core backward (use_bwdp): tile prefix and experts, counters,
+  // exact bf16 hi/lo pairs of da, du and g h, and x and dout rows in
+  // dispatch order
   int32_t *mt2, *texp2, *sched;
-  bf16_t *wdt, *wgt, *wut, *hilo, *ghlo, *xd, *doutd;
+  bf16_t *hilo, *ghlo, *xd, *doutd;
 };
 constexpr int kBwdSched = 48;  // dh, dx, dW_d, dW_g, dW_u: 8 counters each
-// The backward's dh and expert-dx GEMMs run on transposed packed weights
-// (packed into the workspace by each call), and its expert weight gradients
-// on operands gathered into dispatch order, for bf16 layers with d and I
-// multiples of 256 whose byte offsets into dout, x and the hi/lo pairs fit
-// 32 bits (the weight-gradient loads run up to 64 rows past an expert's).
+// The backward's dh and expert-dx GEMMs read the row-major weights directly
+// (gemm_rmw.hip), and its expert weight gradients run on operands gathered
+// into dispatch order, for bf16 layers with d and I multiples of 256 whose
+// byte offsets into dout, x, the hi/lo pairs and the weights fit 31 bits
+// (the weight-gradient loads run up to 64 rows past an expert's).
 bool use_bwdp(const zc_moe_desc* d) {
   if (d->dtype != ZC_BF16 || d->N == 0 || d->d % 256 || d->I % 256) return false;
-  const int64_t rows = d->T * d->K + 64, lim = int64_t(1) << 32;
-  return rows * d->d * 2 < lim && rows * 4 * d->I * 2 < lim;
+  return zc::rmw_supported(d->T * d->K, d->T, d->d, d->I);
 }
+// Row-tile height of the dh and dx GEMMs: the average rows per FFN expert
+// rounded up to 64 or 128.
 int bwdp_rows_per_tile(const zc_moe_desc* d) {
-  const int tm = zc::fwdp_rows_per_tile(d->T * d->K / d->N);
-  return tm > zc::kGemmBM ? zc::kGemmBM : tm;
+  return d->T * d->K / d->N <= 64 ? 64 : zc::kGemmBM;
 }
 int64_t bwdp_bytes(const zc_moe_desc* d) {
   if (!use_bwdp(d)) return 0;
-  const int64_t wbytes = d->N * d->I * d->d * 2;
   const int64_t rows = d->T * d->K;
   return a256(4 * (d->N + 1)) + a256(4 * max_tiles2(d)) + a256(4 * kBwdSched) +
-         3 * a256(wbytes) + a256(rows * 4 * d->I * 2) + a256(rows * 2 * d->I * 2) +
-         2 * a256(rows * d->d * 2);
+         a256(rows * 4 * d->I * 2) + a256(rows * 2 * d->I * 2) + 2 * a256(rows * d->d * 2);
 }
 // fp32 partials of the router weight gradient (token chunks), 0 when unsplit
 int64_t rdw_bytes(const zc_moe_desc* d) {
@@ -345,20 +343,16 @@ BwdWs carve_bwd(char* p, const zc_moe_desc* d) {
   w.rdw = rdw_bytes(d) > 0 ? take(rdw_bytes(d)) : nullptr;
   w.lbc = take(4 * E);
   w.mt2 = w.texp2 = w.sched = nullptr;
-  w.wdt = w.wgt = w.wut = w.hilo = w.ghlo = w.xd = w.doutd = nullptr;
+  w.hilo = w.ghlo = w.xd = w.doutd = nullptr;
   if (use_bwdp(d)) {
     auto takeb = [&p](int64_t bytes) {
       char* q = p;
       p += a256(bytes);
       return q;
     };
-    const int64_t wbytes = d->N * d->I * d->d * 2;
     w.mt2 = reinterpret_cast<int32_t*>(takeb(4 * (d->N + 1)));
     w.texp2 = reinterpret_cast<int32_t*>(takeb(4 * max_tiles2(d)));
     w.sched = reinterpret_cast<int32_t*>(takeb(4 * kBwdSched));
-    w.wdt = reinterpret_cast<bf16_t*>(takeb(wbytes));
-    w.wgt = reinterpret_cast<bf16_t*>(takeb(wbytes));
-    w.wut = reinterpret_cast<bf16_t*>(takeb(wbytes));
     w.hilo = reinterpret_cast<bf16_t*>(takeb(rows * 4 * d->I * 2));
     w.ghlo = reinterpret_cast<bf16_t*>(takeb(rows * 2 * d->I * 2));
     w.xd = reinterpret_cast<bf16_t*>(takeb(rows * d->d * 2));
@@ -399,17 +393,27 @@ int64_t lb_ws_bytes(const zc_moe_desc* d) {
   return a256(static_cast<int64_t>(zc::lb_scratch_bytes(d->T, d->N + d->Z)));
 }
 
-// The 256 x 256 forward kernels: bf16 layers, no activations saved for a
-// backward pass, 32-bit element offsets (rows * columns < 2^31), and on
+// The 256 x 256 forward kernels: bf16 layers with row-major weights (with a
+// saved buffer the gate/up epilogue also writes a, u, h in fp32 for the
+// backward), 32-bit element offsets (rows * columns < 2^31), and on
 // average at least 64 rows per FFN expert (T*K/N, known on the host without
 // reading the counts back); decode-sized batches keep the 128 x 128 kernel,
 // whose larger grid streams a few rows' worth of weights per expert better.
 template <typename T>
-bool use_fwd_kernels(const zc_moe_desc* d, const void* saved) {
-  if (!std::is_same<T, bf16_t>::value || saved) return false;
+bool use_fwd_kernels(const zc_moe_desc* d) {
+  if (!std::is_same<T, bf16_t>::value) return false;
   if (d->N == 0 || d->T * d->K < 64 * d->N) return false;
   const int64_t rows = d->T * d->K, cols = d->I > d->d ? d->I : d->d;
   return rows * cols < (int64_t(1) << 31) && d->T * d->d < (int64_t(1) << 31);
+}
+
+// The training kernels on row-major weights (forward with saved
+// activations): bf16 layers with d and I multiples of 256 whose byte offsets
+// fit 31 bits.
+template <typename T>
+bool use_rmw(const zc_moe_desc* d) {
+  return std::is_same<T, bf16_t>::value && d->N > 0 && d->weight_layout == ZC_WEIGHTS_ROWMAJOR &&
+         zc::rmw_supported(d->T * d->K, d->T, d->d, d->I);
 }
 
 // Router + dispatch on an already validated call.
@@ -502,14 +506,31 @@ zc_status do_forward(const zc_moe_desc* d, const T* x, const T* wr, const float*
                                      fwd_rows_per_tile(d), N, I, dd, reinterpret_cast<bf16_t*>(y),
                                      cu, s),
                 "down GEMM launch");
-    } else if (use_fwd_kernels<T>(d, saved)) {
-      // bf16 inference: 256 x 256 tiles, weights streamed once per expert
+    } else if (saved && use_rmw<T>(d)) {
+      // bf16 training forward on row-major weights: a, u, h kept in fp32
+      ZC_LAUNCH(ZC_PH_GATE_UP,
+                zc::launch_rmw_gateup(reinterpret_cast<const bf16_t*>(x), d->T,
+                                      reinterpret_cast<const bf16_t*>(wg),
+                                      reinterpret_cast<const bf16_t*>(wu), r->offsets, r->perm,
+                                      rw.tile_off2, rw.tile_exp, rw.sched, fwd_rows_per_tile(d), N,
+                                      I, dd, K, reinterpret_cast<bf16_t*>(h), sa, su, sh, cu, s),
+                "gate/up GEMM launch");
+      ZC_LAUNCH(ZC_PH_DOWN,
+                zc::launch_rmw_down(reinterpret_cast<const bf16_t*>(h), rows,
+                                    reinterpret_cast<const bf16_t*>(wd), r->offsets, rw.tile_off2,
+                                    rw.tile_exp, rw.sched + 8, fwd_rows_per_tile(d), N, I, dd,
+                                    reinterpret_cast<bf16_t*>(y), cu, s),
+                "down GEMM launch");
+    } else if (use_fwd_kernels<T>(d)) {
+      // bf16 inference on row-major weights: 256 x 256 tiles, weights
+      // streamed once per expert; with a saved buffer (a layer the training
+      // kernels do not take) the gate/up epilogue also keeps a, u, h
       ZC_LAUNCH(ZC_PH_GATE_UP,
                 zc::launch_fwd_gateup(reinterpret_cast<const bf16_t*>(x),
                                       reinterpret_cast<const bf16_t*>(wg),
                                       reinterpret_cast<const bf16_t*>(wu), r->offsets, r->perm,
                                       rw.tile_off2, N, I, dd, K, reinterpret_cast<bf16_t*>(h),
-                                      nullptr, nullptr, nullptr, cu, s),
+                                      sa, su, sh, cu, s),
                 "gate/up GEMM launch");
       ZC_LAUNCH(ZC_PH_DOWN,
                 zc::launch_fwd_down(reinterpret_cast<const bf16_t*>(h),
@@ -552,9 +573,6 @@ zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg
                 zc::launch_tile_offsets2(r->offsets, N, zc::kGemmBM, w.tile_off, tmb, w.mt2,
                                          w.texp2, w.sched, kBwdSched, s),
                 "tile offsets");
-      ZC_LAUNCH(ZC_PH_BWD_PACK,
-                zc::launch_pack_weights_t(reinterpret_cast<const bf16_t*>(wd), w.wdt, N, dd, I, s),
-                "transposed weight packing launch");
     } else {
       ZC_LAUNCH(ZC_PH_TILE_OFFSETS,
                 zc::launch_tile_offsets(r->offsets, N, zc::kGemmBM, w.tile_off, s), "tile offsets");
@@ -581,9 +599,8 @@ zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg
                                        K, dd, rows, w.xd, s),
                 "row gather launch");
       ZC_LAUNCH(ZC_PH_BWD_DOWN_DH,
-                zc::launch_bwdp_dh(reinterpret_cast<const bf16_t*>(dout), d->T * d->d, w.wdt,
-                                   r->offsets, r->perm, w.mt2, w.texp2, w.sched, tmb, N, I, dd, K,
-                                   w.gs, w.dadu, cu, s),
+                zc::launch_rmw_dh(w.doutd, rows, reinterpret_cast<const bf16_t*>(wd), r->offsets,
+                                  w.mt2, w.texp2, w.sched, tmb, N, I, dd, w.gs, w.dadu, cu, s),
                 "down backward (dh) launch");
       ZC_LAUNCH(ZC_PH_BWD_DOWN_DH,
                 zc::launch_swiglu_bwd(w.dadu, w.gs, sv.a, sv.u, sv.h, r->offsets, N, I, rows,
@@ -606,15 +623,10 @@ zc_status do_backward(const zc_moe_desc* d, const T* x, const T* wr, const T* wg
                                           cu, s),
                 "down weight-gradient launch");
     if (Tn > 0 && bwdp) {
-      ZC_LAUNCH(ZC_PH_BWD_PACK,
-                zc::launch_pack_weights_t(reinterpret_cast<const bf16_t*>(wg), w.wgt, N, I, dd, s),
-                "transposed weight packing launch");
-      ZC_LAUNCH(ZC_PH_BWD_PACK,
-                zc::launch_pack_weights_t(reinterpret_cast<const bf16_t*>(wu), w.wut, N, I, dd, s),
-                "transposed weight packing launch");
       ZC_LAUNCH(ZC_PH_BWD_GATE_UP_DX,
-                zc::launch_bwdp_dx(w.hilo, rows * 4 * d->I, w.wgt, w.wut, r->offsets, w.mt2,
-                                   w.texp2, w.sched + 8, tmb, N, I, dd, w.dxp, cu, s),
+                zc::launch_rmw_dx(w.hilo, rows, reinterpret_cast<const bf16_t*>(wg),
+                                  reinterpret_cast<const bf16_t*>(wu), r->offsets, w.mt2, w.texp2,
+                                  w.sched + 8, tmb, N, I, dd, w.dxp, cu, s),
                 "gate/up backward (dx) launch");
     } else if (Tn > 0) {
       ZC_LAUNCH(ZC_PH_BWD_GATE_UP_DX,
@@ -971,8 +983,7 @@ const char* zc_moe_phase_name(int phase) {
       "router_gemm", "topk", "dispatch", "gate_up_gemm", "down_gemm", "combine",
       "bwd_combine", "bwd_down_dh", "bwd_down_dw", "bwd_gate_up_dx", "bwd_gate_up_dw",
       "bwd_router_dw", "bwd_router_dx", "bwd_dx_gather", "bias_update", "tile_offsets",
-      "lb_loss", "lb_coef", "route_stats", "accumulate_counts", "quantize", "bwd_pack",
-      "bwd_gather"};
+      "lb_loss", "lb_coef", "route_stats", "accumulate_counts", "quantize", "bwd_gather"};
   return (phase >= 0 && phase < ZC_NUM_PHASES) ? names[phase] : "";
 }
 

@@ -21,7 +21,10 @@
 // is stored at slot c ^ (r & 7), so the 32 rows a fragment read touches at one
 // k land in distinct bank groups.  One workgroup per CU (128 KB of LDS).
 // Rows past the end of an expert's segment (and columns past the output)
-// load a valid row instead and are never stored.
+// load a valid row instead and are never stored.  The training forward's
+// variant also writes the gate and up sums a, u and h = silu(a) u in fp32
+// (the backward's operands), straight from the accumulators: each half wave
+// stores 32 consecutive columns of one row.
 // Tile order: expert-major; inside an expert, groups of up to 8 row tiles,
 // row tile fastest.  Workgroup b takes logical tiles (b mod 8) * G/8 + b/8 +
 // i * G, so each XCD (blocks are dealt to the 8 XCDs round-robin) works on 32
@@ -40,7 +43,9 @@ constexpr int NSTAGE = 4;        // slabs in flight (LDS ring)
 constexpr int NTHR = 256;
 constexpr int GMV = 8;           // row tiles per group inside an expert
 
-enum { FWD_SWIGLU = 0, FWD_STORE = 1 };
+// FWD_SWIGLU_SAVE: gate/up that also writes a, u and h in fp32 (the training
+// forward keeps them for the backward)
+enum { FWD_SWIGLU = 0, FWD_STORE = 1, FWD_SWIGLU_SAVE = 2 };
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -56,7 +61,7 @@ struct FwdParams {
   const bf16_t* B;          // W_g [N][I][d] or W_d [N][d][I]
   const bf16_t* B2;         // W_u (gate/up)
   bf16_t* C;                // h [P][I] or y [P][d]
-  float* wa;                // gate/up: a, u, h saved in fp32 (nullable)
+  float* wa;                // FWD_SWIGLU_SAVE: a, u, h in fp32, [P][I]
   float* wu;
   float* wh;
 };
@@ -76,7 +81,8 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdParams p) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  constexpr int OUTN = EPI == FWD_SWIGLU ? TN / 2 : TN;  // output columns per tile
+  constexpr bool GU = EPI != FWD_STORE;  // gate/up: SwiGLU of gate and up columns
+  constexpr int OUTN = GU ? TN / 2 : TN;  // output columns per tile
   const int NT = (p.ncols + OUTN - 1) / OUTN;
   const int64_t total = static_cast<int64_t>(p.mt_off[p.N]) * NT;
   const int G = gridDim.x;
@@ -114,21 +120,21 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdParams p) {
     // ---- source element offsets of the 8 A rows and 8 B rows this lane copies
     int aoff[4], boff[4];
     const bf16_t* bb0 = p.B + static_cast<int64_t>(e) * p.ncols * p.K;
-    const bf16_t* bb1 = EPI == FWD_SWIGLU ? p.B2 + static_cast<int64_t>(e) * p.ncols * p.K : bb0;
+    const bf16_t* bb1 = GU ? p.B2 + static_cast<int64_t>(e) * p.ncols * p.K : bb0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = min(lrow + 16 * i, mcount - 1);  // past the segment: any valid row
       const int gm = m0 + row;
-      const int src = EPI == FWD_SWIGLU ? p.perm[gm] / p.kdiv : gm;
+      const int src = GU ? p.perm[gm] / p.kdiv : gm;
       aoff[i] = src * p.K + lchunk;
       int col;
-      if constexpr (EPI == FWD_SWIGLU)
+      if constexpr (GU)
         col = n0 + ((lrow + 16 * i) & 127);  // rows 0..127 gate, 128..255 up, same columns
       else
         col = n0 + lrow + 16 * i;
       boff[i] = min(col, p.ncols - 1) * p.K + lchunk;
     }
-    const bool b_up = EPI == FWD_SWIGLU && wave >= 2;  // this wave's B rows are 128..255
+    const bool b_up = GU && wave >= 2;  // this wave's B rows are 128..255
 
     // 8 loads per wave per slab (4 of A, 4 of B)
     auto fetch = [&](int k0, int buf) {
@@ -155,8 +161,8 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdParams p) {
     // k step, the per-block row offsets are compile-time constants.
     const int s7 = (lane >> 1) & 3;
     const int a_lane = (wm * 128 + (lane & 31)) * BK;
-    const int b_lane = ((EPI == FWD_SWIGLU ? wn * 64 : wn * 128) + (lane & 31)) * BK;
-    constexpr int jrow[4] = {0, 32, EPI == FWD_SWIGLU ? 128 : 64, EPI == FWD_SWIGLU ? 160 : 96};
+    const int b_lane = ((GU ? wn * 64 : wn * 128) + (lane & 31)) * BK;
+    constexpr int jrow[4] = {0, 32, GU ? 128 : 64, GU ? 160 : 96};
     const int khalf = lane >> 5;  // which 8-element half of a 16-k step
 
     // k loop over a ring of NSTAGE slabs, NSTAGE-1 in flight.  Each slab
@@ -219,18 +225,38 @@ __global__ __launch_bounds__(NTHR, 1) void fwd_kernel(FwdParams p) {
     // keeps rows * columns below 2^31.)
     const int rb0 = wm * 128 + 4 * (lane >> 5);
     bf16_t* st = smem;  // OUTN columns per row
+    // saved a, u, h: buffers spanning exactly this tile's rows, so stores to
+    // rows past the segment are out of range and dropped by the hardware
+    // (unused, and dropped by the compiler, in the other variants)
+    // (tile row range made visibly uniform: descriptors live in scalar registers)
+    const int64_t so0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(m0)) * p.ncols;
+    const int snb = __builtin_amdgcn_readfirstlane(mcount) * p.ncols * 4;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(p.wa + so0, (short)0, snb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(p.wu + so0, (short)0, snb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(p.wh + so0, (short)0, snb, 0x00020000);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < (EPI == FWD_SWIGLU ? 2 : 4); ++j) {
-        const int cl = (EPI == FWD_SWIGLU ? wn * 64 : wn * 128) + j * 32 + (lane & 31);
+      for (int j = 0; j < (GU ? 2 : 4); ++j) {
+        const int cl = (GU ? wn * 64 : wn * 128) + j * 32 + (lane & 31);
+        // byte offset of (row rb0 + 32 i, column n0 + cl) from the tile's
+        // first row; a column past the output gets an offset past the end
+        const int svo = n0 + cl < p.ncols ? ((rb0 + 32 * i) * p.ncols + n0 + cl) * 4 : 0x7fffffff;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int rl = rb0 + 32 * i + 8 * (v >> 2) + (v & 3);
           float val = acc[i][j][v];
-          if constexpr (EPI == FWD_SWIGLU) {
+          if constexpr (GU) {
             const float u = acc[i][j + 2][v];
             const float hv = silu_f(val) * u;
+            if constexpr (EPI == FWD_SWIGLU_SAVE) {
+              // one row of 32 consecutive columns per half wave (128-byte
+              // pieces); the row step is uniform and goes in the scalar offset
+              const int so = (8 * (v >> 2) + (v & 3)) * p.ncols * 4;
+              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), ra, svo, so, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, u), ru, svo, so, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, hv), rh, svo, so, 0);
+            }
             val = hv;
           }
           st[rl * OUTN + cl] = f2bf(val);
@@ -262,7 +288,12 @@ hipError_t launch_fwd_gateup(const bf16_t* x, const bf16_t* wg, const bf16_t* wu
   p.A = x; p.perm = perm; p.kdiv = K;
   p.B = wg; p.B2 = wu; p.C = h;
   p.wa = save_a; p.wu = save_u; p.wh = save_h;
-  hipLaunchKernelGGL(fwd_kernel<FWD_SWIGLU>, dim3(cu), dim3(NTHR), 0, s, p);
+  if (save_a || save_u || save_h) {
+    if (!save_a || !save_u || !save_h) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fwd_kernel<FWD_SWIGLU_SAVE>, dim3(cu), dim3(NTHR), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(fwd_kernel<FWD_SWIGLU>, dim3(cu), dim3(NTHR), 0, s, p);
+  }
   return hipGetLastError();
 }
 

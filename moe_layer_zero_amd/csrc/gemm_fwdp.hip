@@ -51,11 +51,8 @@ constexpr int NTHR = 256;
 constexpr int GMV = 8;      // row tiles per group inside an expert
 constexpr int DSDEPTH = 4;  // fragment reads ahead of their MFMAs (eight-wave kernel)
 
-// P_SWIGLU: gate/up with SwiGLU; P_STORE: down projection (bf16 y);
-// P_DSWIGLU: backward dh = g * (dout W_d) in fp32 (swiglu_bwd_kernel then
-// forms da, du and g h as exact bf16 hi/lo pairs); P_DX: backward expert dx
-// = [da_hi | da_lo | du_hi | du_lo] [W_g; W_g; W_u; W_u] in fp32.
-enum { P_SWIGLU = 0, P_STORE = 1, P_DSWIGLU = 2, P_DX = 3 };
+// P_SWIGLU: gate/up with SwiGLU; P_STORE: down projection (bf16 y).
+enum { P_SWIGLU = 0, P_STORE = 1 };
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -75,10 +72,6 @@ struct PParams {
   const bf16_t* B;          // packed W_g or W_d
   const bf16_t* B2;         // packed W_u (gate/up)
   bf16_t* C;                // h [P][I] or y [P][d]
-  // backward variants
-  const float* gs;          // P_DSWIGLU: out_scale * gate of each row (dispatch order)
-  float* Cf;                // P_DSWIGLU: dh, P_DX: expert dx, [P][ncols] (fp32)
-  int kseg;                 // P_DX: slabs per K segment (I / 64)
 };
 
 // silu(a) = a / (1 + e^-a) with the hardware reciprocal (about 1 ulp) in
@@ -121,10 +114,8 @@ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 template <int EPI, int TM>
 __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   constexpr int RB = TM / 32;       // 32-row blocks per tile = A loads per wave per slab
-  // P_DX slabs hold the hi and the lo piece of the same reduction steps
-  constexpr int APC = EPI == P_DX ? 2 : 1;
-  constexpr int SLOT = APC * TM * BK;  // bf16 per ring slot
-  constexpr int V = APC * RB + 8;      // loads per wave per slab (A rows + 8 B blocks)
+  constexpr int SLOT = TM * BK;  // bf16 per ring slot
+  constexpr int V = RB + 8;      // loads per wave per slab (A rows + 8 B blocks)
   static_assert(TM == 32 || TM == 64 || TM == 128 || TM == 256, "tile height");
   // the ring, then one int: the next tile index claimed by thread 0 (kept in
   // the same LDS object, see the note on the tables of the decode)
@@ -135,7 +126,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
   constexpr int OUTN = EPI == P_SWIGLU ? 128 : 256;  // output columns per tile
-  constexpr bool GATHER = EPI == P_SWIGLU || EPI == P_DSWIGLU;  // A rows are token rows
+  constexpr bool GATHER = EPI == P_SWIGLU;  // A rows are token rows
   const int NT = p.ncols / OUTN;
   const int64_t total = static_cast<int64_t>(ld_scalar(p.mt_off + p.N)) * NT;
   const int G = gridDim.x;
@@ -158,7 +149,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   if (tid == 0) s_claim[0] = atomicAdd(p.sched + cx, 1);
   __syncthreads();
   int cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
-  const int nk = p.K / (APC * BK);  // P_DX: K = 4I holds both pieces
+  const int nk = p.K / BK;
   const int kblk = p.K / 16;  // packed 1 KB blocks per 32 output columns
 
   // A buffer resource: raw, range-checked against a_bytes
@@ -224,19 +215,11 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
         aoff[i] = p.a_bytes;  // out of range: the load returns zeros, reads nothing
       }
     }
-    // ---- packed B: this wave's two column groups of 32 (P_DX: of the
-    // segment the slab falls in, see issue)
-    const int64_t mat = static_cast<int64_t>(p.ncols) * (EPI == P_DX ? p.K / 4 : p.K);
+    // ---- packed B: this wave's two column groups of 32
+    const int64_t mat = static_cast<int64_t>(p.ncols) * p.K;
     const bf16_t* b0;
     const bf16_t* b1;
-    const bf16_t* bu = nullptr;  // P_DX: the W_u segments
-    const int kbs = EPI == P_DX ? kblk / 4 : kblk;  // packed blocks per 32 columns and matrix
-    if constexpr (EPI == P_DX) {
-      const int g = n0 / 32 + 2 * wave;
-      b0 = p.B + e * mat + static_cast<int64_t>(g) * kbs * 512 + lane * 8;
-      b1 = b0 + static_cast<int64_t>(kbs) * 512;
-      bu = p.B2 + e * mat + static_cast<int64_t>(g) * kbs * 512 + lane * 8;
-    } else if constexpr (EPI == P_SWIGLU) {
+    if constexpr (EPI == P_SWIGLU) {
       const int g = n0 / 32 + wave;
       b0 = p.B + e * mat + static_cast<int64_t>(g) * kblk * 512 + lane * 8;
       b1 = p.B2 + e * mat + static_cast<int64_t>(g) * kblk * 512 + lane * 8;
@@ -254,38 +237,15 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
       constexpr int NRB = decltype(nrb_c)::value;
       bf16x8_t bq[NST][2][4];  // B fragments of the slabs in flight
       auto issue = [&](int kt, int slot, bf16x8_t (&bf)[2][4]) {
-        if constexpr (EPI == P_DX) {
-          // A rows = [da_hi | da_lo | du_hi | du_lo]: slabs 0 .. kseg-1 take
-          // the hi and lo pieces of da (times W_g), the next kseg those of du
-          // (times W_u); the hi piece fills the first half of the slot
-          const int seg = kt / p.kseg;
-          const int ks = kt - seg * p.kseg;
-          const int hoff = (2 * seg * p.kseg + ks) * BK * 2;
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+        for (int i = 0; i < RB; ++i) {
+          lds_void* dst = (lds_void*)(ring + slot * SLOT + (RB * wave + i) * 8 * BK);
+          lds_dma16(arsrc, dst, aoff[i], kt * BK * 2);
+        }
 #pragma unroll
-            for (int i = 0; i < RB; ++i) {
-              lds_void* dst =
-                  (lds_void*)(ring + slot * SLOT + h * TM * BK + (RB * wave + i) * 8 * BK);
-              lds_dma16(arsrc, dst, aoff[i], hoff + h * p.kseg * BK * 2);
-            }
-          const bf16_t* c0 = seg == 0 ? b0 : bu;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            bf[0][t] = *reinterpret_cast<const bf16x8_t*>(c0 + (4 * ks + t) * 512);
-            bf[1][t] = *reinterpret_cast<const bf16x8_t*>(c0 + (kbs + 4 * ks + t) * 512);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < RB; ++i) {
-            lds_void* dst = (lds_void*)(ring + slot * SLOT + (RB * wave + i) * 8 * BK);
-            lds_dma16(arsrc, dst, aoff[i], kt * BK * 2);
-          }
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            bf[0][t] = *reinterpret_cast<const bf16x8_t*>(b0 + (4 * kt + t) * 512);
-            bf[1][t] = *reinterpret_cast<const bf16x8_t*>(b1 + (4 * kt + t) * 512);
-          }
+        for (int t = 0; t < 4; ++t) {
+          bf[0][t] = *reinterpret_cast<const bf16x8_t*>(b0 + (4 * kt + t) * 512);
+          bf[1][t] = *reinterpret_cast<const bf16x8_t*>(b1 + (4 * kt + t) * 512);
         }
       };
 
@@ -305,17 +265,8 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
 #pragma unroll
           for (int rb = 0; rb < NRB; ++rb) {
             const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(a_s + rb * 32 * BK + co);
-            if constexpr (EPI == P_DX) {
-              const bf16x8_t al =
-                  *reinterpret_cast<const bf16x8_t*>(a_s + TM * BK + rb * 32 * BK + co);
-              acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[0][t], acc[rb][0], 0, 0, 0);
-              acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[1][t], acc[rb][1], 0, 0, 0);
-              acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bf[0][t], acc[rb][0], 0, 0, 0);
-              acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bf[1][t], acc[rb][1], 0, 0, 0);
-            } else {
-              acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[0][t], acc[rb][0], 0, 0, 0);
-              acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[1][t], acc[rb][1], 0, 0, 0);
-            }
+            acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[0][t], acc[rb][0], 0, 0, 0);
+            acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[1][t], acc[rb][1], 0, 0, 0);
           }
         }
       };
@@ -323,7 +274,7 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
       // Issue order inside a slab (4 NRB fragment reads, 8 NRB MFMAs, V loads):
       // loads first; fragment reads run up to three ahead of the MFMAs that
       // use them.
-      constexpr int NDS = 4 * APC * NRB;
+      constexpr int NDS = 4 * NRB;
       constexpr int DS0 = NDS < 3 ? NDS : 3;
       auto sched = [&](bool with_loads) {
         if (with_loads) __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
@@ -388,34 +339,6 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
       // ---- epilogue: lane holds column lane%32 of its column group and rows
       // 32 rb + 8 (v/4) + 4 (lane/32) + v%4.
       const int rbase = 4 * khalf;
-      if constexpr (EPI == P_DSWIGLU || EPI == P_DX) {
-        // fp32 results straight from the accumulators: each store covers 32
-        // consecutive columns (128 bytes) of a row
-        const int I = p.ncols;
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int rl = rbase + 32 * rb + 8 * (v >> 2) + (v & 3);
-            if (rl < mcount) {
-              const int64_t gm = m0 + rl;
-#pragma unroll
-              for (int cg = 0; cg < 2; ++cg) {
-                const int n = n0 + 64 * wave + 32 * cg + (lane & 31);
-                if constexpr (EPI == P_DX) {
-                  p.Cf[gm * I + n] = acc[rb][cg][v];
-                } else {
-                  p.Cf[gm * I + n] = acc[rb][cg][v] * p.gs[gm];  // dh = g dout W_d
-                }
-              }
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (tid == 0) s_claim[0] = next_n;
-        __syncthreads();  // every wave done reading the ring before the next tile's loads
-        return;
-      }
       // The bf16 tile is staged in the ring (free once every wave has passed
       // the barrier below; TM x OUTN bf16 fit in its 4 TM x 64), then written
       // out with 16-byte row-contiguous stores; the last barrier keeps the
@@ -771,67 +694,12 @@ __global__ __launch_bounds__(256) void pack_kernel(const bf16_t* __restrict__ sr
   }
 }
 
-// Packed layout of the transposes of nmat row-major [R][C] matrices (each
-// packed as the [C][R] matrix it transposes to): 64 x 64 tiles through LDS,
-// read along rows, written as 16-byte packed chunks (8 consecutive source
-// rows of one source column).
-__global__ __launch_bounds__(256) void pack_t_kernel(const bf16_t* __restrict__ src,
-                                                     bf16_t* __restrict__ dst, int R, int C) {
-  __shared__ bf16_t t[64][64 + 8];
-  const int64_t m = blockIdx.z;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const bf16_t* sm = src + m * static_cast<int64_t>(R) * C;
-  for (int q = threadIdx.x; q < 64 * 8; q += 256) {
-    const int r = q >> 3, cc = (q & 7) * 8;
-    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(sm + static_cast<int64_t>(r0 + r) * C + c0 + cc);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      t[r][cc + 2 * j] = static_cast<bf16_t>(w[j] & 0xffffu);
-      t[r][cc + 2 * j + 1] = static_cast<bf16_t>(w[j] >> 16);
-    }
-  }
-  __syncthreads();
-  // transposed matrix: R' = C rows, C' = R reduction steps; element (r', c')
-  // at ((r'/32) (C'/16) + c'/16) 512 + (r'%32 + 32 ((c'/8)%2)) 8 + c'%8
-  bf16_t* dm = dst + m * static_cast<int64_t>(R) * C;
-  const int kb = R / 16;
-  for (int q = threadIdx.x; q < 64 * 8; q += 256) {
-    const int rp = q >> 3, cg = (q & 7) * 8;  // r' = c0 + rp, c' = r0 + cg .. + 7
-    const int R1 = c0 + rp, C1 = r0 + cg;
-    u32x4_t w;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      w[j] = static_cast<uint32_t>(t[cg + 2 * j][rp]) |
-             (static_cast<uint32_t>(t[cg + 2 * j + 1][rp]) << 16);
-    const int64_t o = (static_cast<int64_t>(R1 / 32) * kb + C1 / 16) * 512 +
-                      (R1 % 32 + 32 * ((C1 / 8) % 2)) * 8;
-    *reinterpret_cast<u32x4_t*>(dm + o) = w;
-  }
-}
-
 // Kernel of each (epilogue, tile height); tiles of up to 64 rows leave room
 // for two workgroups per CU.  The 256-row down projection runs the
-// eight-wave down8_kernel (launch_tm).  The backward variants stop at
-// 128-row tiles (a 256-row tile would spill).
+// eight-wave down8_kernel (launch_tm).
 typedef void (*fwdp_fn)(PParams);
 fwdp_fn pick_kernel(int epi, int tm, int* per_cu) {
   *per_cu = tm <= 64 ? 2 : 1;
-  if (epi == P_DSWIGLU) {
-    switch (tm) {
-      case 32: return fwdp_kernel<P_DSWIGLU, 32>;
-      case 64: return fwdp_kernel<P_DSWIGLU, 64>;
-      case 128: return fwdp_kernel<P_DSWIGLU, 128>;
-    }
-    return nullptr;
-  }
-  if (epi == P_DX) {
-    switch (tm) {
-      case 32: return fwdp_kernel<P_DX, 32>;
-      case 64: return fwdp_kernel<P_DX, 64>;
-      case 128: return fwdp_kernel<P_DX, 128>;
-    }
-    return nullptr;
-  }
   if (epi == P_SWIGLU) {
     switch (tm) {
       case 32: return fwdp_kernel<P_SWIGLU, 32>;
@@ -900,26 +768,6 @@ hipError_t launch_fwdp_down(const bf16_t* h, int64_t h_elems, const bf16_t* wd_p
   return launch_tm(P_STORE, tm, p, cu, s);
 }
 
-hipError_t launch_pack_weights_t(const bf16_t* src, bf16_t* dst, int64_t nmat, int R, int C,
-                                 hipStream_t s) {
-  if (nmat == 0) return hipSuccess;
-  hipLaunchKernelGGL(pack_t_kernel, dim3(C / 64, R / 64, static_cast<unsigned>(nmat)), dim3(256), 0,
-                     s, src, dst, R, C);
-  return hipGetLastError();
-}
-
-hipError_t launch_bwdp_dh(const bf16_t* dout, int64_t dout_elems, const bf16_t* wdt_p,
-                          const int32_t* offsets, const int32_t* perm, const int32_t* mt_off,
-                          const int32_t* tile_exp, int32_t* sched, int tm, int N, int I, int d,
-                          int K, const float* gs, float* dh, int cu, hipStream_t s) {
-  PParams p{};
-  p.N = N; p.ncols = I; p.K = d;
-  p.offsets = offsets; p.mt_off = mt_off; p.tile_exp = tile_exp; p.sched = sched;
-  p.A = dout; p.a_bytes = static_cast<uint32_t>(dout_elems * 2); p.perm = perm; p.kdiv = K;
-  p.B = wdt_p; p.gs = gs; p.Cf = dh;
-  return launch_tm(P_DSWIGLU, tm, p, cu, s);
-}
-
 hipError_t launch_swiglu_bwd(const float* dh, const float* gs, const float* sa, const float* su,
                              const float* sh, const int32_t* offsets, int N, int I,
                              int64_t max_rows, bf16_t* hilo, bf16_t* ghlo, hipStream_t s) {
@@ -928,18 +776,6 @@ hipError_t launch_swiglu_bwd(const float* dh, const float* gs, const float* sa, 
   hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(grid), dim3(256), 0, s, dh, gs, sa, su, sh, offsets,
                      N, I, hilo, ghlo);
   return hipGetLastError();
-}
-
-hipError_t launch_bwdp_dx(const bf16_t* hilo, int64_t hilo_elems, const bf16_t* wgt_p,
-                          const bf16_t* wut_p, const int32_t* offsets, const int32_t* mt_off,
-                          const int32_t* tile_exp, int32_t* sched, int tm, int N, int I, int d,
-                          float* dxp, int cu, hipStream_t s) {
-  PParams p{};
-  p.N = N; p.ncols = d; p.K = 4 * I; p.kseg = I / 64;
-  p.offsets = offsets; p.mt_off = mt_off; p.tile_exp = tile_exp; p.sched = sched;
-  p.A = hilo; p.a_bytes = static_cast<uint32_t>(hilo_elems * 2);
-  p.B = wgt_p; p.B2 = wut_p; p.Cf = dxp;
-  return launch_tm(P_DX, tm, p, cu, s);
 }
 
 hipError_t launch_pack_weights(const bf16_t* src, bf16_t* dst, int64_t nmat, int R, int C,

@@ -182,16 +182,6 @@ hipError_t launch_fwdp_down(const bf16_t* h, int64_t h_elems, const bf16_t* wd_p
 // nmat row-major [R][C] bf16 matrices -> packed layout (R % 32 == 0, C % 16 == 0).
 hipError_t launch_pack_weights(const bf16_t* src, bf16_t* dst, int64_t nmat, int R, int C,
                                hipStream_t s);
-// ... the packed layout of their transposes ([C][R] each; R, C multiples of 64).
-hipError_t launch_pack_weights_t(const bf16_t* src, bf16_t* dst, int64_t nmat, int R, int C,
-                                 hipStream_t s);
-// Backward expert GEMMs of bf16 layers on transposed packed weights (tile
-// bookkeeping as for the forward): dh = gs * (dout[tok] W_d) -> [P][I] fp32;
-// expert dx = hilo [W_g;W_g;W_u;W_u] -> [P][d] fp32.
-hipError_t launch_bwdp_dh(const bf16_t* dout, int64_t dout_elems, const bf16_t* wdt_p,
-                          const int32_t* offsets, const int32_t* perm, const int32_t* mt_off,
-                          const int32_t* tile_exp, int32_t* sched, int tm, int N, int I, int d,
-                          int K, const float* gs, float* dh, int cu, hipStream_t s);
 // SwiGLU backward from dh and the saved a, u, h ([P][I] fp32 each): hilo
 // [P][4I] = exact bf16 hi/lo pairs of da and du, ghlo [P][2I] = those of
 // gs * h; I a multiple of 8.
@@ -209,10 +199,33 @@ hipError_t launch_dw(bool transposed, int N, int M, int Ncol, const int32_t* off
 // dst[p] = src[perm[p] / K] (rows of width w) for the FFN picks in dispatch order.
 hipError_t launch_gather_rows(const bf16_t* src, const int32_t* perm, const int32_t* offsets,
                               int N, int K, int w, int64_t max_rows, bf16_t* dst, hipStream_t s);
-hipError_t launch_bwdp_dx(const bf16_t* hilo, int64_t hilo_elems, const bf16_t* wgt_p,
-                          const bf16_t* wut_p, const int32_t* offsets, const int32_t* mt_off,
-                          const int32_t* tile_exp, int32_t* sched, int tm, int N, int I, int d,
-                          float* dxp, int cu, hipStream_t s);
+
+// Grouped GEMMs of the training step on row-major weights (gemm_rmw.hip):
+// the forward keeping a, u, h in fp32, and the backward's dh = gs * (dout
+// W_d) and expert dx = [da_hi | da_lo | du_hi | du_lo] [W_g; W_g; W_u; W_u]
+// (fp32, [P][I] and [P][d]) reading the row-major weights directly.  Tile
+// tables as for the packed-weight kernels: the tm-row prefix mt_off, the
+// expert of each tile, 8 per-XCD counters zeroed before the launch (tm = 64,
+// 128 or 256; dh and dx take 64 or 128).  rmw_supported: d and I multiples
+// of 256 and every byte offset within 31 bits.
+bool rmw_supported(int64_t rows, int64_t Tn, int64_t d, int64_t I);
+hipError_t launch_rmw_gateup(const bf16_t* x, int64_t Tn, const bf16_t* wg, const bf16_t* wu,
+                             const int32_t* offsets, const int32_t* perm, const int32_t* mt_off,
+                             const int32_t* tile_exp, int32_t* sched, int tm, int N, int I, int d,
+                             int K, bf16_t* h, float* sa, float* su, float* sh, int cu,
+                             hipStream_t s);
+hipError_t launch_rmw_down(const bf16_t* h, int64_t rows, const bf16_t* wd,
+                           const int32_t* offsets, const int32_t* mt_off, const int32_t* tile_exp,
+                           int32_t* sched, int tm, int N, int I, int d, bf16_t* y, int cu,
+                           hipStream_t s);
+hipError_t launch_rmw_dh(const bf16_t* doutd, int64_t rows, const bf16_t* wd,
+                         const int32_t* offsets, const int32_t* mt_off, const int32_t* tile_exp,
+                         int32_t* sched, int tm, int N, int I, int d, const float* gs, float* dh,
+                         int cu, hipStream_t s);
+hipError_t launch_rmw_dx(const bf16_t* hilo, int64_t rows, const bf16_t* wg, const bf16_t* wu,
+                         const int32_t* offsets, const int32_t* mt_off, const int32_t* tile_exp,
+                         int32_t* sched, int tm, int N, int I, int d, float* dxp, int cu,
+                         hipStream_t s);
 
 // MXFP8 expert GEMMs (gemm_fwdq.hip): E4M3 codes with one E8M0 scale per
 // 32 reduction steps.  Activation quantizer (rows x K bf16 -> codes and
