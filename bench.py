@@ -388,6 +388,36 @@ def copy_probe(nbytes: int):
     print(json.dumps({"copy_probe_bytes": nbytes, "launches": 3}), flush=True)
 
 
+def bmm_reference(steps: int):
+    """The vendor library on the prefill gate/up GEMM's volume, for scale:
+    hipBLASLt (torch.bmm, bf16) on 512 experts of 288 rows each (the prefill
+    workload's 143644 FFN picks spread evenly, rounded up to 32) times
+    [6144 x 4096] weights -- the same weight bytes and about the same flop
+    as the grouped kernel, without its ragged segments, row gather or
+    SwiGLU.  Prints one JSON line."""
+    sh = synth.CONFIGS["prefill_bf16"]
+    E, M, K, N = sh.N, 288, sh.d, 2 * sh.I
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(E, M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = (torch.randn(E, K, N, device="cuda", dtype=torch.bfloat16, generator=g) * 0.01).contiguous()
+    out = torch.empty(E, M, N, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.bmm(a, b, out=out)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        torch.bmm(a, b, out=out)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    flop = 2.0 * E * M * K * N
+    print(json.dumps({"reference": "hipBLASLt bmm (torch.bmm, bf16)", "shape": [E, M, K, N],
+                      "ms": round(ms, 4), "tflops": round(flop / ms / 1e9, 1),
+                      "weight_GBps": round(E * K * N * 2 / ms / 1e6, 1), "steps": steps}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -400,6 +430,8 @@ def main():
                     help="inference on row-major expert weights instead of the packed layout")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--bmm-reference", action="store_true",
+                    help="only time hipBLASLt's batched GEMM on the prefill gate/up volume")
     ap.add_argument("--telemetry", default=None, metavar="PATH",
                     help="also write the training loop's per-step routing telemetry "
                          "(JSON lines) to PATH, outside the timed region")
@@ -411,6 +443,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.bmm_reference:
+        bmm_reference(max(args.steps, 20))
         return
     zcmoe.lib()
     extra = {}

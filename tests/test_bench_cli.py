@@ -48,3 +48,12 @@ def test_roofline_picks_the_higher_floor_and_keeps_both_fractions():
     assert roof["mfma_frac"] == mfma["frac"] == round(1e12 / 2e-3 / 1e12 / 2500.0, 4)
     roof, mfma, hbm = b.gemm_roofline("down_gemm", 1e13, 1e9, 10.0)
     assert roof["bound"] == "mfma" and roof["hbm_frac"] == hbm["frac"]
+
+
+def test_side_modes_are_listed_in_the_help():
+    """--copy-probe and --bmm-reference are separate modes (their own JSON
+    line, no benchmark line); both must stay reachable from the command line."""
+    out = subprocess.run([sys.executable, "bench.py", "--help"], capture_output=True, text=True,
+                         cwd=ROOT, timeout=120)
+    assert out.returncode == 0
+    assert "--copy-probe" in out.stdout and "--bmm-reference" in out.stdout
