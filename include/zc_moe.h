@@ -137,7 +137,11 @@ size_t zc_moe_workspace_size(const zc_moe_desc* desc, int op);
 
 /* Bytes of the activation buffer `saved` that zc_moe_forward fills for
  * zc_moe_backward (pre-activations, hidden and expert outputs of every FFN
- * pick, sized for the worst case T*K picks). */
+ * pick, sized for the worst case T*K picks).  Layout, each piece starting
+ * at a multiple of 256 bytes: a = x W_g^T, u = x W_u^T and h = silu(a) * u
+ * in fp32, [T*K][I] each, row p = the p-th FFN pick in dispatch order (the
+ * route's perm; rows from offsets[N] on are unused), then the expert
+ * outputs y, [T*K][d] in the layer dtype. */
 size_t zc_moe_saved_size(const zc_moe_desc* desc);
 
 /* Router and dispatch: Eq.(1)'s scores, biased top-K and gates, then the

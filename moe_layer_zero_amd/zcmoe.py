@@ -193,6 +193,21 @@ def saved_buffer(desc: LayerDesc, device="cuda") -> torch.Tensor:
     return torch.empty(max(zc_moe_saved_size(desc), 256), dtype=torch.uint8, device=device)
 
 
+def saved_views(desc: LayerDesc, saved: torch.Tensor) -> dict:
+    """Views of a filled saved buffer (its layout is the one zc_moe_saved_size
+    documents): a, u, h fp32 [T*K][I] and y [T*K][d] in the layer dtype,
+    rows in dispatch order."""
+    rows, I, d = desc.T * desc.K, desc.I, desc.d
+    a256 = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    piece = a256(rows * I * 4)
+    out = {}
+    for i, k in enumerate(("a", "u", "h")):
+        out[k] = saved[i * piece:i * piece + rows * I * 4].view(torch.float32).view(rows, I)
+    es = 4 if desc.dtype == torch.float32 else 2
+    out["y"] = saved[3 * piece:3 * piece + rows * d * es].view(desc.dtype).view(rows, d)
+    return out
+
+
 def _check_layer_tensor(t, shape, dtype, name):
     if t is None:
         return

@@ -36,6 +36,8 @@ def lib():
         L.orc_route.argtypes = [_i64, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p]
         L.orc_forward.argtypes = [_i64, _i64, _i64, _i64, _i64, _i32, _f64, _p, _p, _p, _p,
                                   _p, _p, _i64, _p, _p, _p]
+        L.orc_ffn_act.argtypes = [_i64, _i64, _i64, _i64, _i32, _p, _p, _p, _i64, _p, _p, _p,
+                                  _p, _p]
         L.orc_backward.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i32, _i32, _f64, _p, _p,
                                    _p, _p, _p, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _p,
                                    _p]
@@ -54,7 +56,8 @@ def lib():
         L.orc_num_threads.restype = C.c_int
         L.orc_num_threads.argtypes = []
         L.orc_pid_update.argtypes = [_i64, _i64, _i64, _p, _i64, _f64, _f64, _p]
-        for f in ("orc_logits", "orc_route", "orc_forward", "orc_backward", "orc_pid_update",
+        for f in ("orc_logits", "orc_route", "orc_forward", "orc_ffn_act", "orc_backward",
+                  "orc_pid_update",
                   "orc_lb_loss", "orc_route_stats", "orc_mx_quantize", "orc_mx_dequantize",
                   "orc_forward_mx", "orc_mx_flip_bound"):
             getattr(L, f).restype = C.c_int
@@ -174,6 +177,28 @@ def forward(x, wg, wu, wd, topk_idx, gates, N, out_scale=1.0, toks=None, want_y=
     assert rc == 0, "oracle forward failed (missing expert weights or bad token)"
     del kg, ku, kd
     return (out, y) if want_y else out
+
+
+def ffn_activations(x, wg, wu, N, tok, ex):
+    """O6's pre-activations and hidden row of the picks (tok[q], ex[q]):
+    a = W_g[e] x_t, u = W_u[e] x_t, h = silu(a) u, each [n][I] in binary64.
+    wg/wu: [N,...] arrays or per-expert dicts {e: block} sharing x's
+    storage dtype."""
+    x = _c(x)
+    T, d = x.shape
+    e0 = next(iter(wg.values())) if isinstance(wg, dict) else wg[0]
+    I = e0.shape[0]
+    tg, kg = _table(wg, N)
+    tu, ku = _table(wu, N)
+    tk = _c(np.asarray(tok), np.int64)
+    te = _c(np.asarray(ex), np.int32)
+    n = len(tk)
+    a, u, h = (np.empty((n, I), np.float64) for _ in range(3))
+    rc = lib().orc_ffn_act(T, d, N, I, _dt(x), _ptr(x), tg, tu, n, _ptr(tk), _ptr(te), _ptr(a),
+                           _ptr(u), _ptr(h))
+    assert rc == 0, "oracle activations failed (missing expert weights or bad pick)"
+    del kg, ku
+    return a, u, h
 
 
 def backward(x, wr, wg, wu, wd, lg, topk_idx, gates, dY, N, Z, gate_norm=1, out_scale=1.0,

@@ -223,9 +223,8 @@ int orc_route(int64_t T, int64_t E, int64_t N, int64_t K, int gate_norm,
  * Wg, Wu are [I][d] and Wd is [d][I], row-major ("out x in"). */
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
-static void ffn_row(int64_t d, int64_t I, int dt, const void* x, int64_t xoff,
-                    const void* wg, const void* wu, const void* wd, double* a,
-                    double* u, double* h, double* y) {
+static void ffn_act(int64_t d, int64_t I, int dt, const void* x, int64_t xoff,
+                    const void* wg, const void* wu, double* a, double* u, double* h) {
   for (int64_t i = 0; i < I; ++i) {
     double sa = 0.0, su = 0.0;
     for (int64_t k = 0; k < d; ++k) {
@@ -237,11 +236,40 @@ static void ffn_row(int64_t d, int64_t I, int dt, const void* x, int64_t xoff,
     u[i] = su;
     h[i] = silu(sa) * su;
   }
+}
+
+static void ffn_row(int64_t d, int64_t I, int dt, const void* x, int64_t xoff,
+                    const void* wg, const void* wu, const void* wd, double* a,
+                    double* u, double* h, double* y) {
+  ffn_act(d, I, dt, x, xoff, wg, wu, a, u, h);
   for (int64_t n = 0; n < d; ++n) {
     double s = 0.0;
     for (int64_t i = 0; i < I; ++i) s += ld(wd, dt, n * I + i) * h[i];
     y[n] = s;
   }
+}
+
+/* O6, first half, for a list of picks: the expert's pre-activations and
+ * hidden row a = Wg x_t, u = Wu x_t, h = silu(a) * u of pick q = (token
+ * tok[q], FFN expert ex[q]), written to a, u, h [n][I].  wg/wu are
+ * per-expert pointer tables of length N (an entry may be NULL when no pick
+ * names that expert). */
+int orc_ffn_act(int64_t T, int64_t d, int64_t N, int64_t I, int dt, const void* x,
+                const void* const* wg, const void* const* wu, int64_t n,
+                const int64_t* tok, const int32_t* ex, double* a, double* u, double* h) {
+  if (!x || !wg || !wu || !tok || !ex || !a || !u || !h) return 1;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t q = 0; q < n; ++q) {
+    const int64_t t = tok[q];
+    const int32_t e = ex[q];
+    if (t < 0 || t >= T || e < 0 || e >= N || !wg[e] || !wu[e]) {
+      bad = 1;
+      continue;
+    }
+    ffn_act(d, I, dt, x, t * d, wg[e], wu[e], a + q * I, u + q * I, h + q * I);
+  }
+  return bad ? 1 : 0;
 }
 
 /* O6 + O7 -- layer output for the tokens toks[0..n_tok) (all tokens when

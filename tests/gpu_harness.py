@@ -56,6 +56,13 @@ def to_dev(L: dict, dev="cuda") -> dict:
     return {k: v.to(dev) for k, v in L.items()}
 
 
+def bf16_to_f64(a: np.ndarray) -> np.ndarray:
+    """float64 values of bf16 bit patterns (uint16 arrays); other arrays as is."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     return synth.to_np(t)
 

@@ -275,3 +275,26 @@ def test_noalloc_forward_rejects_oversized_layers_before_any_work(L):
     for lay in (zcmoe.ZC_WEIGHTS_ROWMAJOR, zcmoe.ZC_WEIGHTS_PACKED, zcmoe.ZC_WEIGHTS_MXFP8):
         dec.weight_layout = lay
         assert zcmoe.zc_moe_workspace_size(dec, zcmoe.ZC_OP_FORWARD) <= zcmoe.NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("dims", [(64, 128, 8, 4, 64, 2, "fp32"), (300, 1024, 64, 32, 512, 6, "bf16"),
+                                  (8192, 2048, 128, 64, 1024, 8, "bf16")])
+def test_saved_buffer_layout_matches_the_library_size(dims):
+    """The saved buffer is a, u, h in fp32 ([T*K][I] each) then y ([T*K][d] in
+    the layer dtype), each piece 256-byte aligned: the library's size and the
+    binding's views agree with that layout."""
+    T, d, N, Z, I, K, dt = dims
+    desc = zcmoe.LayerDesc(T=T, d=d, N=N, Z=Z, I=I, K=K,
+                           dtype=torch.float32 if dt == "fp32" else torch.bfloat16)
+    rows, es = T * K, 4 if dt == "fp32" else 2
+    a256 = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    size = zcmoe.zc_moe_saved_size(desc)
+    assert size == 3 * a256(rows * I * 4) + a256(rows * d * es)
+    buf = torch.zeros(size, dtype=torch.uint8)
+    v = zcmoe.saved_views(desc, buf)
+    base = buf.data_ptr()
+    for i, k in enumerate(("a", "u", "h")):
+        assert v[k].shape == (rows, I) and v[k].dtype == torch.float32
+        assert v[k].data_ptr() - base == i * a256(rows * I * 4)
+    assert v["y"].shape == (rows, d) and v["y"].dtype == desc.dtype
+    assert v["y"].data_ptr() - base == 3 * a256(rows * I * 4)

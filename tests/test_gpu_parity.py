@@ -358,6 +358,79 @@ def test_backward_fp32_long_batch_splits_router_gradient():
     backward_case(CF["tiny_fp32"].with_T(1024))
 
 
+# ------------------------------------------------------------ training forward
+def training_forward_case(sh, stride=7):
+    """The forward that keeps its activations for the backward (bf16 layers
+    with row-major weights run the training kernels): the layer output and
+    its FFN part against the oracle on a token sample with a row in every
+    128-row stretch of every expert's dispatch segment, and the saved fp32
+    a = x W_g^T, u = x W_u^T, h = silu(a) u of every `stride`-th FFN pick in
+    dispatch order (so every 32-row block of every row tile) and of the last
+    row of every expert segment, against the oracle's binary64 values.
+    Bounds: an fp32 sum of d exact bf16 products in any order is within
+    gamma_d * sum |w x| (gamma_d = d u / (1 - d u), u = 2^-24); h carries
+    that through silu (slope at most 1.1) plus 2^-20 |h| for its
+    exponential, reciprocal and products."""
+    L = synth.make_layer(sh, "cpu")
+    Lg = H.to_dev(L)
+    desc = H.desc_of(sh)
+    print(f"[training-forward] {sh.name} T={sh.T}", flush=True)
+    route, out, saved = H.run_forward(desc, Lg, saved=True)
+    xh, wrh = H.host(L["x"]), H.host(L["wr"])
+    wg, wu, wd = H.host(L["wg"]), H.host(L["wu"]), H.host(L["wd"])
+    lg = oracle.logits(xh, wrh)
+    H.assert_logits(route.logits, lg)
+    o = oracle.route(lg, L["bias"].numpy(), sh.N, sh.K)
+    gidx = route.topk_idx.cpu().numpy()
+    same, namb = H.routing_agreement(gidx, o.keys, o.topk_idx, lg, sh.K)
+    toks = np.array([t for t in H.covering_tokens(gidx, sh.N, 128, seed=5) if same[t]])
+    ref, ys = oracle.forward(xh, wg, wu, wd, o.topk_idx, o.gates, sh.N, toks=toks, want_y=True)
+    got = out[torch.from_numpy(toks).cuda()]
+    H.assert_close(got, ref, torch.bfloat16, "layer output (training forward)")
+    H.assert_ffn_part(got, ref, o.topk_idx[toks], o.gates[toks], sh.N, xh[toks],
+                      "layer output (training forward)", ys)
+    # saved activations of sampled picks: they depend only on x_t and W_e,
+    # so the GPU's own routing names the picks
+    offs = route.offsets.cpu().numpy()
+    perm = route.perm.cpu().numpy()
+    P = int(offs[sh.N])
+    ends = offs[1:][offs[1:] > offs[:-1]] - 1
+    rows = np.union1d(np.arange(0, P, stride), ends)
+    tok = perm[rows] // sh.K
+    ex = gidx[tok, perm[rows] % sh.K]
+    assert (ex < sh.N).all()
+    a, u, h = oracle.ffn_activations(xh, wg, wu, sh.N, tok, ex)
+    sv = zcmoe.saved_views(desc, saved)
+    ridx = torch.from_numpy(rows).cuda()
+    ga, gu, gh = (sv[k][ridx].double().cpu().numpy() for k in ("a", "u", "h"))
+    x64 = H.bf16_to_f64(xh)
+    gamma = sh.d * 2.0 ** -24 / (1 - sh.d * 2.0 ** -24)
+    worst = {"a": 0.0, "u": 0.0, "h": 0.0}
+    for e in np.unique(ex):
+        qs = np.flatnonzero(ex == e)
+        xa = np.abs(x64[tok[qs]])                                   # [n][d]
+        tol_a = gamma * (xa @ np.abs(H.bf16_to_f64(wg[e])).T) + 1e-30  # [n][I]
+        tol_u = gamma * (xa @ np.abs(H.bf16_to_f64(wu[e])).T) + 1e-30
+        tol_h = (1.1 * tol_a * (np.abs(u[qs]) + tol_u) + (np.abs(a[qs]) + tol_a) * tol_u
+                 + 2.0 ** -20 * np.abs(h[qs]) + 1e-30)
+        for k, g_, r_, t_ in (("a", ga, a, tol_a), ("u", gu, u, tol_u), ("h", gh, h, tol_h)):
+            ratio = np.abs(g_[qs] - r_[qs]) / t_
+            worst[k] = max(worst[k], float(ratio.max()))
+            bad = np.argwhere(ratio > 1.0)
+            assert len(bad) == 0, (f"saved {k} of dispatch row {rows[qs[bad[0][0]]]} (expert "
+                                   f"{e}, column {bad[0][1]}): {float(ratio.max()):.3f} of its "
+                                   f"bound")
+    print(f"  {len(toks)} tokens, {len(rows)} saved rows; worst error / bound: "
+          + ", ".join(f"{k} {v:.3f}" for k, v in worst.items()), flush=True)
+
+
+@pytest.mark.parametrize("shape", ["small_bf16", "small_bf16_T300", "train_bf16_T1024"])
+def test_training_forward_output_and_saved_activations(shape):
+    sh = {"small_bf16": CF["small_bf16"], "small_bf16_T300": CF["small_bf16"].with_T(300),
+          "train_bf16_T1024": CF["train_bf16"].with_T(1024)}[shape]
+    training_forward_case(sh)
+
+
 def test_backward_train_shape_bf16():
     # the training layer's shapes with fewer tokens, so the fp64 oracle
     # finishes in seconds; all 128 experts' gradients compared

@@ -321,6 +321,62 @@ def test_forward_single_expert_is_swiglu_mlp(orc):
     np.testing.assert_array_equal(ro.gates, 1.0)
 
 
+def test_ffn_activations_on_permutation_weights(orc):
+    """a = W_g[e] x_t, u = W_u[e] x_t, h = silu(a) u of a pick, in closed
+    form: with W_g[e] = alpha_e P_e and W_u[e] = beta_e Q_e for permutation
+    matrices (row i holds one entry, in column pi_e(i) or sigma_e(i)),
+    a_i = alpha_e x[t, pi_e(i)] and u_i = beta_e x[t, sigma_e(i)].  Distinct
+    non-involutive permutations per expert make a transposed weight, a swapped
+    gate/up pair, a wrong expert or token row fail; silu comes from torch."""
+    r = rng(91)
+    T, d, N, I = 7, 12, 3, 9
+    x = r.standard_normal((T, d)).astype(np.float32)
+    wg = np.zeros((N, I, d), np.float32)
+    wu = np.zeros((N, I, d), np.float32)
+    alpha = np.array([0.5, -1.25, 2.0])
+    beta = np.array([1.5, 0.75, -0.5])
+    pis, sigmas = [], []
+    for e in range(N):
+        pi = r.permutation(d)[:I]
+        sg = r.permutation(d)[:I]
+        pis.append(pi)
+        sigmas.append(sg)
+        wg[e, np.arange(I), pi] = alpha[e]
+        wu[e, np.arange(I), sg] = beta[e]
+    tok = np.array([0, 3, 6, 3, 1])
+    ex = np.array([2, 0, 1, 1, 2])
+    a, u, h = orc.ffn_activations(x, wg, wu, N, tok, ex)
+    for q, (t, e) in enumerate(zip(tok, ex)):
+        a_ref = alpha[e] * x[t, pis[e]].astype(np.float64)
+        u_ref = beta[e] * x[t, sigmas[e]].astype(np.float64)
+        np.testing.assert_array_equal(a[q], a_ref)
+        np.testing.assert_array_equal(u[q], u_ref)
+        h_ref = F.silu(torch.from_numpy(a_ref)).numpy() * u_ref
+        np.testing.assert_allclose(h[q], h_ref, rtol=1e-14, atol=0)
+
+
+def test_ffn_activations_match_torch_swiglu_hidden_row(orc):
+    """On random bf16 weights the hidden row of each pick equals torch's
+    silu(x W_g^T) * (x W_u^T) in float64 (a special case reducing to
+    library linear layers), for the picks' experts and tokens."""
+    r = rng(92)
+    T, d, N, I = 6, 32, 4, 16
+    L = _layer(T, d, N, 0, I, 1, seed=93)
+    bits = {k: synth.to_np(torch.from_numpy(L[k]).to(torch.bfloat16)) for k in ("x", "wg", "wu")}
+    tok = r.integers(0, T, 10)
+    ex = r.integers(0, N, 10)
+    a, u, h = orc.ffn_activations(bits["x"], bits["wg"], bits["wu"], N, tok, ex)
+    xv = torch.from_numpy(bits["x"].astype(np.int32) << 16).view(torch.float32).double()
+    for q, (t, e) in enumerate(zip(tok, ex)):
+        wgv = torch.from_numpy(bits["wg"][e].astype(np.int32) << 16).view(torch.float32).double()
+        wuv = torch.from_numpy(bits["wu"][e].astype(np.int32) << 16).view(torch.float32).double()
+        a_ref = F.linear(xv[t], wgv)
+        u_ref = F.linear(xv[t], wuv)
+        np.testing.assert_allclose(a[q], a_ref.numpy(), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(u[q], u_ref.numpy(), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(h[q], (F.silu(a_ref) * u_ref).numpy(), rtol=1e-12, atol=1e-14)
+
+
 def test_forward_token_subset_and_out_scale(orc):
     T, d, N, Z, I, K = 30, 16, 4, 2, 8, 2
     L = _layer(T, d, N, Z, I, K, seed=35)
