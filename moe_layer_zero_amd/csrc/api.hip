@@ -416,6 +416,16 @@ bool use_rmw(const zc_moe_desc* d) {
          zc::rmw_supported(d->T * d->K, d->T, d->d, d->I);
 }
 
+// Router scores on the 256 x 256-tile kernel: bf16 layers with E a multiple
+// of 256 and at least 128 such tiles (T * E >= 2^23); smaller batches keep
+// the generic kernel, which splits the hidden dimension to fill the GPU.
+template <typename T>
+bool use_dense_router(const zc_moe_desc* d) {
+  const int64_t E = d->N + d->Z;
+  return std::is_same<T, bf16_t>::value && d->T * E >= (int64_t(1) << 23) &&
+         zc::rmw_dense_supported(d->T, E, d->d);
+}
+
 // Router + dispatch on an already validated call.
 // Row-tile height of the second tile prefix (tile_off2): the packed-weight
 // forward picks it from the average rows per FFN expert; the row-major bf16
@@ -430,10 +440,19 @@ zc_status do_route(const zc_moe_desc* d, const T* x, const T* wr, const float* b
                    zc_route_buf* r, const RouteWs& w, hipStream_t s) {
   const int Tn = static_cast<int>(d->T), E = static_cast<int>(d->N + d->Z);
   const int N = static_cast<int>(d->N), K = static_cast<int>(d->K);
-  if (x && Tn > 0)
-    ZC_LAUNCH(ZC_PH_ROUTER_GEMM, zc::launch_router_gemm<T>(x, wr, r->logits, Tn, E, static_cast<int>(d->d), w.rpart, cus(d),
-                                     s),
-           "router GEMM launch");
+  if (x && Tn > 0) {
+    if (use_dense_router<T>(d))
+      ZC_LAUNCH(ZC_PH_ROUTER_GEMM,
+                zc::launch_rmw_dense(reinterpret_cast<const bf16_t*>(x), Tn,
+                                     reinterpret_cast<const bf16_t*>(wr), E,
+                                     static_cast<int>(d->d), r->logits, cus(d), s),
+                "router GEMM launch");
+    else
+      ZC_LAUNCH(ZC_PH_ROUTER_GEMM,
+                zc::launch_router_gemm<T>(x, wr, r->logits, Tn, E, static_cast<int>(d->d),
+                                          w.rpart, cus(d), s),
+                "router GEMM launch");
+  }
   ZC_LAUNCH(ZC_PH_TOPK, zc::launch_topk(r->logits, bias, Tn, E, K, d->gate_norm, r->topk_idx, r->topk_gate, s),
          "top-K launch");
   ZC_LAUNCH(ZC_PH_DISPATCH, zc::launch_dispatch(r->topk_idx, Tn, E, N, K, zc::kGemmBM,

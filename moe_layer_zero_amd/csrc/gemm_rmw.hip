@@ -1,5 +1,6 @@
 // Grouped expert GEMMs of the training step on row-major bf16 weights: the
-// forward that keeps its activations, and the backward's dh and expert dx.
+// forward that keeps its activations, and the backward's dh and expert dx;
+// and, on the same pipeline, the dense router product of large batches.
 //
 // "LongCat-Flash Technical Report", section 2.1: each FFN expert runs on the
 // rows routed to it (its segment of the dispatch order); zero-computation
@@ -8,6 +9,7 @@
 //   down:    y = h W_d[e]^T
 //   dh:      dh = g (dout W_d[e])        (fp32; g = out_scale * gate of the row)
 //   dx:      dx_e = da W_g[e] + du W_u[e] (fp32; da, du as exact bf16 hi + lo pairs)
+//   router:  logits = x W_r^T over all T rows (fp32; section 2.1's router scores)
 // with W_g, W_u [N][I][d] and W_d [N][d][I].  The forward contracts weight
 // rows with activation rows (the reduction runs along a weight row); dh and
 // dx contract over the weight's rows.  The matrix cores want 8 consecutive
@@ -42,7 +44,9 @@ constexpr int NTHR = 256;
 constexpr int GMV = 8;             // row tiles per group inside an expert
 constexpr int WSLAB = 256 * BK;    // bf16 of a weight slab (256 x 32, or 32 x 256)
 
-enum { R_SWIGLU = 0, R_STORE = 1, R_DSWIGLU = 2, R_DX = 3 };
+// R_DENSE: one dense product C = A B^T in fp32 over M rows (the router
+// scores logits = x W_r^T), tiles assigned statically instead of claimed.
+enum { R_SWIGLU = 0, R_STORE = 1, R_DSWIGLU = 2, R_DX = 3, R_DENSE = 4 };
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -52,6 +56,7 @@ typedef __attribute__((address_space(3))) bf16_t lds_bf16;
 
 struct RParams {
   int N;                    // experts
+  int M;                    // R_DENSE: rows of the product
   int ncols;                // output columns (gate/up: I, columns of h)
   int K;                    // reduction steps per weight matrix (dx: I, run twice)
   const int32_t* offsets;   // [N+1] rows of each expert in dispatch order
@@ -145,6 +150,8 @@ __global__ __launch_bounds__(NTHR, 1) void rmw_kernel(RParams p) {
   constexpr int ASLAB = TM * BK;                    // bf16 of one A piece
   constexpr int SLOT = APC * ASLAB + WSLAB;         // bf16 per ring slot
   constexpr bool TR = EPI == R_DSWIGLU || EPI == R_DX;  // weight rows are reduction steps
+  constexpr bool DENSE = EPI == R_DENSE;
+  constexpr bool F32OUT = TR || DENSE;              // fp32 results stored from the accumulators
   constexpr bool GATHER = EPI == R_SWIGLU;          // A rows are token rows
   constexpr int OUTN = EPI == R_SWIGLU ? 128 : 256;  // output columns per tile
   static_assert(TM == 64 || TM == 128 || TM == 256, "tile height");
@@ -157,7 +164,10 @@ __global__ __launch_bounds__(NTHR, 1) void rmw_kernel(RParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int NT = p.ncols / OUTN;
-  const int64_t total = static_cast<int64_t>(ld_scalar(p.mt_off + p.N)) * NT;
+  // dense: one segment of M rows, ceil(M / TM) row tiles
+  const int mtd = (p.M + TM - 1) / TM;
+  const int64_t total =
+      static_cast<int64_t>(DENSE ? mtd : ld_scalar(p.mt_off + p.N)) * NT;
   const int G = gridDim.x;
   const int C = G / 8;
   int cx = blockIdx.x % 8;
@@ -165,9 +175,15 @@ __global__ __launch_bounds__(NTHR, 1) void rmw_kernel(RParams p) {
   auto tile_of = [&](int x, int n) -> int64_t {
     return static_cast<int64_t>(n / C) * 8 * C + x * C + n % C;
   };
-  if (tid == 0) s_claim[0] = atomicAdd(p.sched + cx, 1);
-  __syncthreads();
-  int cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
+  int cur_n = 0;
+  // dense: workgroup b takes tiles (b mod 8) C + b / 8 + i G (a contiguous
+  // range per XCD: a row tile's column tiles share their A rows in one L2)
+  int64_t Ld = static_cast<int64_t>(blockIdx.x % 8) * C + blockIdx.x / 8;
+  if constexpr (!DENSE) {
+    if (tid == 0) s_claim[0] = atomicAdd(p.sched + cx, 1);
+    __syncthreads();
+    cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
+  }
   const int kseg = p.K / BK;                  // slabs per weight matrix
   const int nk = (EPI == R_DX ? 2 : 1) * kseg;
   const __amdgpu_buffer_rsrc_t arsrc =
@@ -195,23 +211,30 @@ __global__ __launch_bounds__(NTHR, 1) void rmw_kernel(RParams p) {
   }
 
   for (;;) {
-    const int64_t L = tile_of(cx, cur_n);
-    if (L >= total) {
-      if (++hops == 8) break;
-      cx = (cx + 1) & 7;
-      __syncthreads();  // every thread has read the last claim
-      if (tid == 0) s_claim[0] = atomicAdd(p.sched + cx, 1);
-      __syncthreads();
-      cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
-      continue;
-    }
+    int64_t L;
     int32_t next_n = 0;
-    if (tid == 0) next_n = atomicAdd(p.sched + cx, 1);
+    if constexpr (DENSE) {
+      L = Ld;
+      if (L >= total) break;
+      Ld += G;
+    } else {
+      L = tile_of(cx, cur_n);
+      if (L >= total) {
+        if (++hops == 8) break;
+        cx = (cx + 1) & 7;
+        __syncthreads();  // every thread has read the last claim
+        if (tid == 0) s_claim[0] = atomicAdd(p.sched + cx, 1);
+        __syncthreads();
+        cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
+        continue;
+      }
+      if (tid == 0) next_n = atomicAdd(p.sched + cx, 1);
+    }
     // ---- expert, row tile, column tile (wave-uniform)
     const int lmt = static_cast<int>(L / NT);
-    const int e = ld_scalar(p.tile_exp + lmt);
-    const int mt_e = ld_scalar(p.mt_off + e);
-    const int mte = ld_scalar(p.mt_off + e + 1) - mt_e;
+    const int e = DENSE ? 0 : ld_scalar(p.tile_exp + lmt);
+    const int mt_e = DENSE ? 0 : ld_scalar(p.mt_off + e);
+    const int mte = DENSE ? mtd : ld_scalar(p.mt_off + e + 1) - mt_e;
     const int q = static_cast<int>(L - static_cast<int64_t>(mt_e) * NT);
     const int grp = q / (GMV * NT);
     const int fm = grp * GMV;
@@ -219,7 +242,8 @@ __global__ __launch_bounds__(NTHR, 1) void rmw_kernel(RParams p) {
     const int rr = q - grp * GMV * NT;
     const int mt = fm + rr % gsz;
     const int nt = rr / gsz;
-    const int seg0 = ld_scalar(p.offsets + e), seg1 = ld_scalar(p.offsets + e + 1);
+    const int seg0 = DENSE ? 0 : ld_scalar(p.offsets + e);
+    const int seg1 = DENSE ? p.M : ld_scalar(p.offsets + e + 1);
     const int nbe = (seg1 - seg0 + 31) >> 5;
     const int blo = nbe * mt / mte, bhi = nbe * (mt + 1) / mte;
     const int m0 = seg0 + 32 * blo;
@@ -389,7 +413,7 @@ __global__ __launch_bounds__(NTHR, 1) void rmw_kernel(RParams p) {
       // ---- epilogue: lane holds column lane%32 of its column block and rows
       // 32 rb + 8 (v/4) + 4 (lane/32) + v%4
       const int rbase = 4 * khalf;
-      if constexpr (TR) {
+      if constexpr (F32OUT) {
         // fp32 results straight from the accumulators: each store covers 32
         // consecutive columns (128 bytes) of a row
 #pragma unroll
@@ -409,7 +433,9 @@ __global__ __launch_bounds__(NTHR, 1) void rmw_kernel(RParams p) {
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (tid == 0) s_claim[0] = next_n;
+        if constexpr (!DENSE) {
+          if (tid == 0) s_claim[0] = next_n;
+        }
         __syncthreads();  // every wave done reading the ring before the next tile's loads
         return;
       }
@@ -480,7 +506,7 @@ __global__ __launch_bounds__(NTHR, 1) void rmw_kernel(RParams p) {
       case 7: if constexpr (RB >= 8) run(std::integral_constant<int, 7>{}); break;
       default: if constexpr (RB >= 8) run(std::integral_constant<int, 8>{}); break;
     }
-    cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
+    if constexpr (!DENSE) cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
   }
 }
 
@@ -509,6 +535,8 @@ rmw_fn pick(int epi, int tm) {
         case 128: return rmw_kernel<R_DX, 128>;
       }
       return nullptr;
+    case R_DENSE:
+      return tm == 256 ? rmw_kernel<R_DENSE, 256> : nullptr;
   }
 #undef ZC_RMW_TM
   return nullptr;
@@ -568,6 +596,22 @@ hipError_t launch_rmw_dh(const bf16_t* doutd, int64_t rows, const bf16_t* wd,
   p.B = wd; p.ldb = I; p.mat = static_cast<int64_t>(d) * I;
   p.gs = gs; p.Cf = dh;
   return launch(R_DSWIGLU, tm, p, cu, s);
+}
+
+bool rmw_dense_supported(int64_t M, int64_t n, int64_t K) {
+  const int64_t lim = int64_t(1) << 31;
+  return n % 256 == 0 && K % BK == 0 && M * K * 2 < lim && n * K * 2 < lim && M * n * 4 < lim;
+}
+
+hipError_t launch_rmw_dense(const bf16_t* a, int64_t M, const bf16_t* b, int n, int K, float* c,
+                            int cu, hipStream_t s) {
+  if (!rmw_dense_supported(M, n, K)) return hipErrorInvalidValue;
+  RParams p{};
+  p.N = 1; p.M = static_cast<int>(M); p.ncols = n; p.K = K;
+  p.A = a; p.a_bytes = static_cast<uint32_t>(M * K * 2); p.lda = K;
+  p.B = b; p.ldb = K; p.mat = static_cast<int64_t>(n) * K;
+  p.Cf = c;
+  return launch(R_DENSE, 256, p, cu, s);
 }
 
 hipError_t launch_rmw_dx(const bf16_t* hilo, int64_t rows, const bf16_t* wg, const bf16_t* wu,

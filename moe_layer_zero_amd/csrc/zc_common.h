@@ -222,6 +222,12 @@ hipError_t launch_rmw_dh(const bf16_t* doutd, int64_t rows, const bf16_t* wd,
                          const int32_t* offsets, const int32_t* mt_off, const int32_t* tile_exp,
                          int32_t* sched, int tm, int N, int I, int d, const float* gs, float* dh,
                          int cu, hipStream_t s);
+// Dense c[M][n] = a[M][K] b[n][K]^T in fp32 on the same kernel (the router
+// scores of large batches): n a multiple of 256, K of 32, byte offsets
+// within 31 bits (rmw_dense_supported).
+bool rmw_dense_supported(int64_t M, int64_t n, int64_t K);
+hipError_t launch_rmw_dense(const bf16_t* a, int64_t M, const bf16_t* b, int n, int K, float* c,
+                            int cu, hipStream_t s);
 hipError_t launch_rmw_dx(const bf16_t* hilo, int64_t rows, const bf16_t* wg, const bf16_t* wu,
                          const int32_t* offsets, const int32_t* mt_off, const int32_t* tile_exp,
                          int32_t* sched, int tm, int N, int I, int d, float* dxp, int cu,

@@ -358,6 +358,30 @@ def test_backward_fp32_long_batch_splits_router_gradient():
     backward_case(CF["tiny_fp32"].with_T(1024))
 
 
+# ------------------------------------------------------------ router scores, large batches
+@pytest.mark.parametrize("T", [8192, 8292])
+def test_router_scores_of_a_large_batch(T):
+    """Large bf16 batches with E a multiple of 256 compute the router scores
+    (section 2.1's logits = x W_r^T, fp32 accumulation) on the 256 x 256-tile
+    kernel: against the oracle's binary64 scores within the logits bound, on
+    an exact number of row tiles and on a ragged last one; and the routing
+    of those scores is the oracle's bit for bit."""
+    sh = synth.LayerShape("router_big", 41, T, 320, 768, 256, 64, 8, "bf16", 0.05, "uniform")
+    assert sh.T * sh.E >= 1 << 23  # the size the tiled router takes
+    L = synth.make_layer(sh, "cuda", want_experts=False)
+    desc = H.desc_of(sh)
+    route = zcmoe.RouteBuffers(desc)
+    print(f"[router-big] T={T} E={sh.E} d={sh.d}", flush=True)
+    zcmoe.zc_moe_route(desc, L["x"], L["wr"], L["bias"], route)
+    torch.cuda.synchronize()
+    lg = oracle.logits(H.host(L["x"]), H.host(L["wr"]))
+    H.assert_logits(route.logits, lg)
+    lg_gpu = route.logits.cpu().numpy()
+    o = oracle.route(lg_gpu, L["bias"].cpu().numpy(), sh.N, sh.K, want_keys=False)
+    np.testing.assert_array_equal(route.topk_idx.cpu().numpy(), o.topk_idx)
+    np.testing.assert_array_equal(route.counts.cpu().numpy(), o.counts)
+
+
 # ------------------------------------------------------------ training forward
 def training_forward_case(sh, stride=7):
     """The forward that keeps its activations for the backward (bf16 layers
