@@ -110,7 +110,12 @@ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // TM: rows per tile (32, 64, 128 or 256).  A slab's loads are issued right
 // after its barrier, ahead of its fragment reads and MFMAs (spreading them
-// over the MFMAs measured slower for the 256-row gate/up tiles).
+// over the MFMAs measured slower for the 256-row gate/up tiles).  The
+// weight fragments are loaded with the non-temporal hint: each weight byte
+// is used by the tiles of one expert only, and so marked the stream ran
+// 4% faster at prefill (gate/up) and 6% faster at decode, though the
+// L2-miss bytes did not drop.  (The eight-wave down kernel keeps plain
+// loads: there the hint slowed it and the combine that reads its output.)
 template <int EPI, int TM>
 __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   constexpr int RB = TM / 32;       // 32-row blocks per tile = A loads per wave per slab
@@ -244,8 +249,8 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          bf[0][t] = *reinterpret_cast<const bf16x8_t*>(b0 + (4 * kt + t) * 512);
-          bf[1][t] = *reinterpret_cast<const bf16x8_t*>(b1 + (4 * kt + t) * 512);
+          bf[0][t] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(b0 + (4 * kt + t) * 512));
+          bf[1][t] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(b1 + (4 * kt + t) * 512));
         }
       };
 

@@ -250,6 +250,11 @@ __global__ __launch_bounds__(NTHR, 1) void fwdq_kernel(QParams p) {
     const int nrb = (mcount + 31) >> 5;
     auto run = [&](auto nrb_c) {
       constexpr int NRB = decltype(nrb_c)::value;
+      // weight operands: each byte is used by one expert's tiles only, so
+      // the loads carry the non-temporal hint (as in the bf16 kernels)
+      auto ldw = [](const uint8_t* q) {
+        return __builtin_nontemporal_load(reinterpret_cast<const i32x4_t*>(q));
+      };
       i32x8_t bq[NST][2][2];   // B operands in flight: [slot][column group][step]
       auto issue = [&](int kt, int slot) {
 #pragma unroll
@@ -263,10 +268,10 @@ __global__ __launch_bounds__(NTHR, 1) void fwdq_kernel(QParams p) {
         lds_dma4(bsr1, (lds_void*)(bsd + 256), bso1, kt * 128);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          bq[slot][0][st].lo = *reinterpret_cast<const i32x4_t*>(b0 + (4 * kt + 2 * st) * 1024);
-          bq[slot][0][st].hi = *reinterpret_cast<const i32x4_t*>(b0 + (4 * kt + 2 * st + 1) * 1024);
-          bq[slot][1][st].lo = *reinterpret_cast<const i32x4_t*>(b1 + (4 * kt + 2 * st) * 1024);
-          bq[slot][1][st].hi = *reinterpret_cast<const i32x4_t*>(b1 + (4 * kt + 2 * st + 1) * 1024);
+          bq[slot][0][st].lo = ldw(b0 + (4 * kt + 2 * st) * 1024);
+          bq[slot][0][st].hi = ldw(b0 + (4 * kt + 2 * st + 1) * 1024);
+          bq[slot][1][st].lo = ldw(b1 + (4 * kt + 2 * st) * 1024);
+          bq[slot][1][st].hi = ldw(b1 + (4 * kt + 2 * st + 1) * 1024);
         }
       };
 
