@@ -407,13 +407,16 @@ bool use_fwd_kernels(const zc_moe_desc* d) {
   return rows * cols < (int64_t(1) << 31) && d->T * d->d < (int64_t(1) << 31);
 }
 
-// The training kernels on row-major weights (forward with saved
-// activations): bf16 layers with d and I multiples of 256 whose byte offsets
-// fit 31 bits.
+// The row-major weight kernels of gemm_rmw.hip (forward, with or without
+// saved activations): bf16 layers with d and I multiples of 256 whose byte
+// offsets fit 31 bits.
+bool rmw_layer(const zc_moe_desc* d) {
+  return d->dtype == ZC_BF16 && d->N > 0 && d->weight_layout == ZC_WEIGHTS_ROWMAJOR &&
+         zc::rmw_fwd_supported(d->T * d->K, d->T, d->d, d->I);
+}
 template <typename T>
 bool use_rmw(const zc_moe_desc* d) {
-  return std::is_same<T, bf16_t>::value && d->N > 0 && d->weight_layout == ZC_WEIGHTS_ROWMAJOR &&
-         zc::rmw_supported(d->T * d->K, d->T, d->d, d->I);
+  return std::is_same<T, bf16_t>::value && rmw_layer(d);
 }
 
 // Router scores on the 256 x 256-tile kernel: bf16 layers with E a multiple
@@ -428,11 +431,14 @@ bool use_dense_router(const zc_moe_desc* d) {
 
 // Router + dispatch on an already validated call.
 // Row-tile height of the second tile prefix (tile_off2): the packed-weight
-// forward picks it from the average rows per FFN expert; the row-major bf16
-// forward kernels use 256.
+// forward picks it from the average rows per FFN expert, the row-major
+// kernels of gemm_rmw.hip likewise but at least 64 rows, the other row-major
+// bf16 forward kernels use 256.
 int fwd_rows_per_tile(const zc_moe_desc* d) {
-  if (d->weight_layout == ZC_WEIGHTS_ROWMAJOR || d->N == 0) return zc::kFwdBM;
-  return zc::fwdp_rows_per_tile(d->T * d->K / d->N);
+  if (d->N == 0) return zc::kFwdBM;
+  const int tm = zc::fwdp_rows_per_tile(d->T * d->K / d->N);
+  if (d->weight_layout != ZC_WEIGHTS_ROWMAJOR) return tm;
+  return rmw_layer(d) ? (tm < 64 ? 64 : tm) : zc::kFwdBM;
 }
 
 template <typename T>
@@ -525,8 +531,9 @@ zc_status do_forward(const zc_moe_desc* d, const T* x, const T* wr, const float*
                                      fwd_rows_per_tile(d), N, I, dd, reinterpret_cast<bf16_t*>(y),
                                      cu, s),
                 "down GEMM launch");
-    } else if (saved && use_rmw<T>(d)) {
-      // bf16 training forward on row-major weights: a, u, h kept in fp32
+    } else if (use_rmw<T>(d)) {
+      // bf16 on row-major weights; with a saved buffer (training) a, u, h
+      // are also kept in fp32
       ZC_LAUNCH(ZC_PH_GATE_UP,
                 zc::launch_rmw_gateup(reinterpret_cast<const bf16_t*>(x), d->T,
                                       reinterpret_cast<const bf16_t*>(wg),
@@ -541,9 +548,9 @@ zc_status do_forward(const zc_moe_desc* d, const T* x, const T* wr, const float*
                                     reinterpret_cast<bf16_t*>(y), cu, s),
                 "down GEMM launch");
     } else if (use_fwd_kernels<T>(d)) {
-      // bf16 inference on row-major weights: 256 x 256 tiles, weights
-      // streamed once per expert; with a saved buffer (a layer the training
-      // kernels do not take) the gate/up epilogue also keeps a, u, h
+      // bf16 on row-major weights whose d or I is not a multiple of 256:
+      // 256 x 256 tiles, weights streamed once per expert; with a saved
+      // buffer the gate/up epilogue also keeps a, u, h
       ZC_LAUNCH(ZC_PH_GATE_UP,
                 zc::launch_fwd_gateup(reinterpret_cast<const bf16_t*>(x),
                                       reinterpret_cast<const bf16_t*>(wg),

@@ -1,4 +1,6 @@
-// Forward expert GEMMs of bf16 layers: gate/up (+ SwiGLU) and down.
+// Forward expert GEMMs of bf16 layers: gate/up (+ SwiGLU) and down, for
+// row-major weights the kernels of gemm_rmw.hip do not take (d or I not a
+// multiple of 256).
 //
 // "LongCat-Flash Technical Report", section 2.1: each FFN expert runs only on
 // the tokens routed to it; zero-computation experts never reach this file.

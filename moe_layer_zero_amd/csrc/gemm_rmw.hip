@@ -1,11 +1,12 @@
-// Grouped expert GEMMs of the training step on row-major bf16 weights: the
-// forward that keeps its activations, and the backward's dh and expert dx;
-// and, on the same pipeline, the dense router product of large batches.
+// Grouped expert GEMMs on row-major bf16 weights: the forward (for
+// inference, and for training with its activations kept), the backward's dh
+// and expert dx, and, on the same pipeline, the dense router product of large
+// batches.
 //
 // "LongCat-Flash Technical Report", section 2.1: each FFN expert runs on the
 // rows routed to it (its segment of the dispatch order); zero-computation
 // experts never reach these GEMMs.  For the rows p of expert e's segment:
-//   gate/up: a = x W_g[e]^T, u = x W_u[e]^T, h = silu(a) u   (a, u, h also kept in fp32)
+//   gate/up: a = x W_g[e]^T, u = x W_u[e]^T, h = silu(a) u   (training: a, u, h also kept in fp32)
 //   down:    y = h W_d[e]^T
 //   dh:      dh = g (dout W_d[e])        (fp32; g = out_scale * gate of the row)
 //   dx:      dx_e = da W_g[e] + du W_u[e] (fp32; da, du as exact bf16 hi + lo pairs)
@@ -44,9 +45,11 @@ constexpr int NTHR = 256;
 constexpr int GMV = 8;             // row tiles per group inside an expert
 constexpr int WSLAB = 256 * BK;    // bf16 of a weight slab (256 x 32, or 32 x 256)
 
-// R_DENSE: one dense product C = A B^T in fp32 over M rows (the router
-// scores logits = x W_r^T), tiles assigned statically instead of claimed.
-enum { R_SWIGLU = 0, R_STORE = 1, R_DSWIGLU = 2, R_DX = 3, R_DENSE = 4 };
+// R_SWIGLU: gate/up with a, u, h also stored in fp32 (training); R_GLU: the
+// same product storing h only (inference).  R_DENSE: one dense product
+// C = A B^T in fp32 over M rows (the router scores logits = x W_r^T), tiles
+// assigned statically instead of claimed.
+enum { R_SWIGLU = 0, R_STORE = 1, R_DSWIGLU = 2, R_DX = 3, R_DENSE = 4, R_GLU = 5 };
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -152,8 +155,9 @@ __global__ __launch_bounds__(NTHR, 1) void rmw_kernel(RParams p) {
   constexpr bool TR = EPI == R_DSWIGLU || EPI == R_DX;  // weight rows are reduction steps
   constexpr bool DENSE = EPI == R_DENSE;
   constexpr bool F32OUT = TR || DENSE;              // fp32 results stored from the accumulators
-  constexpr bool GATHER = EPI == R_SWIGLU;          // A rows are token rows
-  constexpr int OUTN = EPI == R_SWIGLU ? 128 : 256;  // output columns per tile
+  constexpr bool SWI = EPI == R_SWIGLU || EPI == R_GLU;  // gate/up product
+  constexpr bool GATHER = SWI;                      // A rows are token rows
+  constexpr int OUTN = SWI ? 128 : 256;             // output columns per tile
   static_assert(TM == 64 || TM == 128 || TM == 256, "tile height");
   static_assert(NST * SLOT * 2 + 64 <= 160 * 1024, "LDS");
   __shared__ __align__(16) bf16_t ring[NST * SLOT + 16];
@@ -268,7 +272,7 @@ __global__ __launch_bounds__(NTHR, 1) void rmw_kernel(RParams p) {
     const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<bf16_t*>(p.B + e * p.mat), (short)0, mbytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t brsrc2 = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16_t*>((EPI == R_SWIGLU || EPI == R_DX ? p.B2 : p.B) + e * p.mat), (short)0,
+        const_cast<bf16_t*>((SWI || EPI == R_DX ? p.B2 : p.B) + e * p.mat), (short)0,
         mbytes, 0x00020000);
     uint32_t boff[4];
 #pragma unroll
@@ -279,12 +283,12 @@ __global__ __launch_bounds__(NTHR, 1) void rmw_kernel(RParams p) {
         boff[i] = static_cast<uint32_t>((r * p.ldb + n0 + sc * 8) * 2);
       } else {
         const int r = 16 * (4 * wave + i) + (lane >> 2);  // slab row
-        const int n = EPI == R_SWIGLU ? n0 + (r & 127) : n0 + r;
+        const int n = SWI ? n0 + (r & 127) : n0 + r;
         boff[i] = static_cast<uint32_t>((n * p.ldb + lchunk) * 2);
       }
     }
     // gate/up: waves 0, 1 copy gate rows, waves 2, 3 up rows
-    const bool b_second = EPI == R_SWIGLU && wave >= 2;
+    const bool b_second = SWI && wave >= 2;
 
     const int nrb = (mcount + 31) >> 5;
     auto run = [&](auto nrb_c) {
@@ -348,7 +352,7 @@ __global__ __launch_bounds__(NTHR, 1) void rmw_kernel(RParams p) {
             const int co = ((2 * ks + khalf) ^ s3) << 3;
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
-              const int r0 = EPI == R_SWIGLU ? 128 * cb + 32 * wave : 64 * wave + 32 * cb;
+              const int r0 = SWI ? 128 * cb + 32 * wave : 64 * wave + 32 * cb;
               b[ks][cb] = *reinterpret_cast<const bf16x8_t*>(w_s + r0 * BK + co);
             }
           }
@@ -472,6 +476,17 @@ __global__ __launch_bounds__(NTHR, 1) void rmw_kernel(RParams p) {
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+      } else if constexpr (EPI == R_GLU) {
+        const int cl = 32 * wave + (lane & 31);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int rl = rbase + 32 * rb + 8 * (v >> 2) + (v & 3);
+            st[rl * OUTN + cl] = f2bf(silu_f(acc[rb][0][v]) * acc[rb][1][v]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       } else {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
@@ -521,6 +536,7 @@ rmw_fn pick(int epi, int tm) {
   return nullptr;
   switch (epi) {
     case R_SWIGLU: ZC_RMW_TM(R_SWIGLU)
+    case R_GLU: ZC_RMW_TM(R_GLU)
     case R_STORE: ZC_RMW_TM(R_STORE)
     case R_DSWIGLU:  // backward: up to 128 rows (dx's two A pieces fill the ring;
                      // a 256-row dh tile would spill)
@@ -544,12 +560,21 @@ rmw_fn pick(int epi, int tm) {
 
 hipError_t launch(int epi, int tm, const RParams& p, int cu, hipStream_t s) {
   rmw_fn k = pick(epi, tm);
-  if (!k || cu % 8 || p.ncols % (epi == R_SWIGLU ? 128 : 256) || p.K % BK) return hipErrorInvalidValue;
+  const int outn = epi == R_SWIGLU || epi == R_GLU ? 128 : 256;
+  if (!k || cu % 8 || p.ncols % outn || p.K % BK) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k, dim3(cu), dim3(NTHR), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
+
+bool rmw_fwd_supported(int64_t rows, int64_t Tn, int64_t d, int64_t I) {
+  // buffer offsets into x (gate/up), h (down) and one weight matrix; h, y and
+  // the fp32 saves are addressed with 64-bit row offsets
+  const int64_t lim = int64_t(1) << 31;
+  return d % 256 == 0 && I % 256 == 0 && d * I * 2 < lim && Tn * d * 2 < lim &&
+         (rows + 64) * I * 2 < lim;
+}
 
 bool rmw_supported(int64_t rows, int64_t Tn, int64_t d, int64_t I) {
   const int64_t lim = int64_t(1) << 31;
@@ -562,14 +587,15 @@ hipError_t launch_rmw_gateup(const bf16_t* x, int64_t Tn, const bf16_t* wg, cons
                              const int32_t* tile_exp, int32_t* sched, int tm, int N, int I, int d,
                              int K, bf16_t* h, float* sa, float* su, float* sh, int cu,
                              hipStream_t s) {
-  if (!sa || !su || !sh) return hipErrorInvalidValue;
+  const bool save = sa != nullptr;  // training: a, u, h in fp32 as well
+  if (save != (su != nullptr) || save != (sh != nullptr)) return hipErrorInvalidValue;
   RParams p{};
   p.N = N; p.ncols = I; p.K = d;
   p.offsets = offsets; p.mt_off = mt_off; p.tile_exp = tile_exp; p.sched = sched;
   p.A = x; p.a_bytes = static_cast<uint32_t>(Tn * d * 2); p.lda = d; p.perm = perm; p.kdiv = K;
   p.B = wg; p.B2 = wu; p.ldb = d; p.mat = static_cast<int64_t>(I) * d;
   p.C = h; p.sa = sa; p.su = su; p.sh = sh;
-  return launch(R_SWIGLU, tm, p, cu, s);
+  return launch(save ? R_SWIGLU : R_GLU, tm, p, cu, s);
 }
 
 hipError_t launch_rmw_down(const bf16_t* h, int64_t rows, const bf16_t* wd,

@@ -200,14 +200,17 @@ hipError_t launch_dw(bool transposed, int N, int M, int Ncol, const int32_t* off
 hipError_t launch_gather_rows(const bf16_t* src, const int32_t* perm, const int32_t* offsets,
                               int N, int K, int w, int64_t max_rows, bf16_t* dst, hipStream_t s);
 
-// Grouped GEMMs of the training step on row-major weights (gemm_rmw.hip):
-// the forward keeping a, u, h in fp32, and the backward's dh = gs * (dout
+// Grouped GEMMs on row-major weights (gemm_rmw.hip): the forward (with
+// sa, su, sh given it also keeps a, u, h in fp32; all three null: h only),
+// and the backward's dh = gs * (dout
 // W_d) and expert dx = [da_hi | da_lo | du_hi | du_lo] [W_g; W_g; W_u; W_u]
 // (fp32, [P][I] and [P][d]) reading the row-major weights directly.  Tile
 // tables as for the packed-weight kernels: the tm-row prefix mt_off, the
 // expert of each tile, 8 per-XCD counters zeroed before the launch (tm = 64,
-// 128 or 256; dh and dx take 64 or 128).  rmw_supported: d and I multiples
-// of 256 and every byte offset within 31 bits.
+// 128 or 256; dh and dx take 64 or 128).  rmw_fwd_supported (forward) and
+// rmw_supported (forward and backward): d and I multiples of 256 and every
+// byte offset the kernels take within 31 bits.
+bool rmw_fwd_supported(int64_t rows, int64_t Tn, int64_t d, int64_t I);
 bool rmw_supported(int64_t rows, int64_t Tn, int64_t d, int64_t I);
 hipError_t launch_rmw_gateup(const bf16_t* x, int64_t Tn, const bf16_t* wg, const bf16_t* wu,
                              const int32_t* offsets, const int32_t* perm, const int32_t* mt_off,
