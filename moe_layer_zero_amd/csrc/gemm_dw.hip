@@ -15,9 +15,10 @@
 //
 // Tile: 256 x 256 outputs per 256-thread workgroup; wave w owns rows
 // 64w .. 64w+63 of the tile and all 256 columns (2 x 8 blocks of 32 x 32
-// fp32 accumulators).  Operand rows stream through LDS in slabs of 32 rows
-// x 256 columns (16 KB per operand), double buffered, filled by
-// buffer_load ... lds.  The matrix cores want 8 consecutive reduction steps
+// fp32 accumulators).  Operand rows stream through a 3-slot LDS ring in
+// slabs of 32 rows x 256 columns (16 KB per operand), two slabs in flight
+// while one is multiplied, filled by buffer_load ... lds.  The matrix cores
+// want 8 consecutive reduction steps
 // per lane; ds_read_b64_tr_b16 gives each lane of a 16-lane group one
 // column of a 4-row x 16-column block (lane s of the group addresses row
 // s/4, columns 4(s%4) .. +3; measured on MI355X), so two such reads turn
@@ -26,6 +27,8 @@
 // c ^ 2(r & 3), which puts the four rows of a transposed read on different
 // banks.  Tiles are dealt to the XCDs like the forward GEMMs' (contiguous
 // chunks per XCD, claimed from per-XCD counters, then the other XCDs').
+#include <utility>
+
 #include "zc_common.h"
 
 namespace zc {
@@ -35,7 +38,7 @@ constexpr int DK = 32;                 // rows per slab
 constexpr int DT = 256;                // tile edge
 constexpr int SLAB = DK * DT * 2;      // bytes of one operand slab (16 KB)
 constexpr int SLOT = 3 * SLAB;         // split hi, split lo, exact partner
-constexpr int NSL = 2;                 // slots (double buffer)
+constexpr int NSL = 3;                 // ring slots
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -61,8 +64,48 @@ struct DParams {
 
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+// One 16-byte-per-lane copy from a buffer straight into LDS at the
+// wave-uniform byte address lds (64 lanes -> 1 KB).  Written as inline asm:
+// the compiler would make every transposing LDS read wait for all such
+// copies in flight, which would drain the ring each slab.  The copy has no
+// register result; the explicit vmcnt waits and barriers of the k loop order
+// it with the reads, and nothing else in this kernel uses m0.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+
+// Fragment f of a slab in read order (see the k loop): kind 0 / 1 = split
+// hi / lo column block rb, kind 2 = partner column block nb; ks = 16-row half.
+struct Frag { int kind, ks, blk; };
+constexpr Frag kFrag[24] = {
+    {0, 0, 0}, {0, 0, 1}, {1, 0, 0}, {1, 0, 1}, {2, 0, 0}, {2, 0, 1}, {2, 0, 2}, {2, 0, 3},
+    {0, 1, 0}, {2, 0, 4}, {0, 1, 1}, {2, 0, 5}, {1, 1, 0}, {2, 0, 6}, {1, 1, 1}, {2, 0, 7},
+    {2, 1, 0}, {2, 1, 1}, {2, 1, 2}, {2, 1, 3}, {2, 1, 4}, {2, 1, 5}, {2, 1, 6}, {2, 1, 7}};
+constexpr int frag_index(int kind, int ks, int blk) {
+  for (int f = 0; f < 24; ++f)
+    if (kFrag[f].kind == kind && kFrag[f].ks == ks && kFrag[f].blk == blk) return f;
+  return -1;
+}
+// MFMA group g = (ks, nb) = (g / 8, g % 8) needs fragments 0 .. need(g) - 1
+constexpr int need(int g) {
+  int n = frag_index(2, g / 8, g % 8);
+  for (int k = 0; k < 2; ++k)
+    for (int r = 0; r < 2; ++r) {
+      const int f = frag_index(k, g / 8, r);
+      n = f > n ? f : n;
+    }
+  return n + 1;
+}
+constexpr int kAhead = 2;  // groups between a fragment's read and its first use
+// fragments read before group g's MFMAs are issued
+constexpr int reads_before(int g) { return need(g + kAhead < 16 ? g + kAhead : 15); }
+
+template <int... G, class F>
+__device__ __forceinline__ void each_group(std::integer_sequence<int, G...>, F&& f) {
+  (f(std::integral_constant<int, G>{}), ...);
 }
 
 // Only for values the compiler has moved out of AGPR accumulators (its
@@ -170,13 +213,15 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DParams p) {
     }
     const uint32_t xstep = static_cast<uint32_t>(DK * p.ldx * 2);
     const uint32_t ystep = static_cast<uint32_t>(DK * p.ldy * 2);
+    const uint32_t ring_addr = static_cast<uint32_t>((uintptr_t)ring_lds);  // LDS byte address
     auto issue = [&](int kt, int slot) {
-      uint8_t* base = ring + slot * SLOT + (8 * wave) * (DT * 2);
+      const uint32_t base = __builtin_amdgcn_readfirstlane(
+          ring_addr + slot * SLOT + (8 * wave) * (DT * 2));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        lds_dma16(rx, (lds_void*)(base + 0 * SLAB + 2 * i * DT * 2), xo[i] + kt * xstep);
-        lds_dma16(rxl, (lds_void*)(base + 1 * SLAB + 2 * i * DT * 2), xo[i] + kt * xstep);
-        lds_dma16(ry, (lds_void*)(base + 2 * SLAB + 2 * i * DT * 2), yo[i] + kt * ystep);
+        lds_dma16(rx, base + 0 * SLAB + 2 * i * DT * 2, xo[i] + kt * xstep);
+        lds_dma16(rxl, base + 1 * SLAB + 2 * i * DT * 2, xo[i] + kt * xstep);
+        lds_dma16(ry, base + 2 * SLAB + 2 * i * DT * 2, yo[i] + kt * ystep);
       }
     };
 
@@ -188,51 +233,64 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DParams p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    // Slab kt: every fragment is read into registers first, then slab kt+1's
-    // loads are issued, then the MFMAs run.  The compiler makes a transposing
-    // LDS read wait for every LDS-DMA load in flight, so loads issued before
-    // the reads would hold the reads (and the MFMAs) until they land; issued
-    // after them, they overlap the MFMAs.  Slot kt & 1 holds slab kt.
+    // Slab kt (slot kt % 3): the fragments are read in kFrag order, each
+    // kAhead MFMA groups before its first use (written out in that order and
+    // held there by scheduling groups); slab kt+2's copies go out after the
+    // first reads.  Group g = (ks, nb) adds, for rb = 0, 1, the hi and then
+    // the lo product of rows 16 ks .. +15 into acc[rb][nb].
     auto step = [&](int kt, int slot) {
       lds_u8* const sb = ring_lds + slot * SLOT;
-      bf16x8_t a[DK / 16][2], al[DK / 16][2], b[DK / 16][8];
+      bf16x8_t fr[24];
+      auto read = [&](int f) {
+        const Frag q = kFrag[f];
+        fr[f] = q.kind < 2 ? tr_operand(sb + q.kind * SLAB, 16 * q.ks, 64 * wave + 32 * q.blk, lane)
+                           : tr_operand(sb + 2 * SLAB, 16 * q.ks, 32 * q.blk, lane);
+      };
 #pragma unroll
-      for (int ks = 0; ks < DK / 16; ++ks) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          a[ks][rb] = tr_operand(sb, 16 * ks, 64 * wave + 32 * rb, lane);
-          al[ks][rb] = tr_operand(sb + SLAB, 16 * ks, 64 * wave + 32 * rb, lane);
-        }
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) b[ks][nb] = tr_operand(sb + 2 * SLAB, 16 * ks, 32 * nb, lane);
-      }
+      for (int f = 0; f < reads_before(0); ++f) read(f);
       __builtin_amdgcn_sched_barrier(0);
-      if (kt + 1 < nslab) issue(kt + 1, slot ^ 1);
+      if (kt + 2 < nslab) issue(kt + 2, (slot + 2) % 3);
       __builtin_amdgcn_sched_barrier(0);
+      each_group(std::make_integer_sequence<int, 16>{}, [&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        constexpr int ks = g / 8, nb = g % 8;
+        constexpr int f0 = reads_before(g), f1 = g < 15 ? reads_before(g + 1) : 24;
 #pragma unroll
-      for (int ks = 0; ks < DK / 16; ++ks)
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            acc[rb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][rb], b[ks][nb], acc[rb][nb], 0, 0, 0);
-            acc[rb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[ks][rb], b[ks][nb], acc[rb][nb], 0, 0, 0);
-          }
+        for (int f = f0; f < f1; ++f) read(f);
+        const bf16x8_t y = fr[frag_index(2, ks, nb)];
+        acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[frag_index(0, ks, 0)], y, acc[0][nb], 0, 0, 0);
+        acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[frag_index(0, ks, 1)], y, acc[1][nb], 0, 0, 0);
+        acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[frag_index(1, ks, 0)], y, acc[0][nb], 0, 0, 0);
+        acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[frag_index(1, ks, 1)], y, acc[1][nb], 0, 0, 0);
+      });
+      each_group(std::make_integer_sequence<int, 16>{}, [&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        constexpr int nr = (g < 15 ? reads_before(g + 1) : 24) - reads_before(g);
+        if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, 2 * nr, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      });
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // per slab: all of this wave's loads done, barrier (slab kt visible to
-    // every wave, every read of slab kt-1 done, so its slot may refill).  The
-    // rows of the last slab past the expert's end are cleared before use, so
-    // the sums do not depend on what an out-of-range lane leaves in LDS.
+    // per slab: this wave's copies of slab kt done (slab kt+1's may still be
+    // in flight), barrier (slab kt visible to every wave, every read of slab
+    // kt-1 done, so its slot may refill with slab kt+2).  The rows of the
+    // last slab past the expert's end are cleared before use, so the sums do
+    // not depend on what an out-of-range lane leaves in LDS.
     __builtin_amdgcn_sched_barrier(0);
     if (nslab > 0) issue(0, 0);
+    if (nslab > 1) issue(1, 1);
     __builtin_amdgcn_sched_barrier(0);
     for (int kt = 0; kt < nslab; ++kt) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      if (kt + 1 < nslab)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(12));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      const int slot = kt % 3;
       if (kt == nslab - 1 && tail < DK) {
-        lds_u8* const sb = ring_lds + (kt & 1) * SLOT + tail * (DT * 2);
+        lds_u8* const sb = ring_lds + slot * SLOT + tail * (DT * 2);
         const int per = (DK - tail) * (DT * 2 / 16);   // 16-byte pieces per operand
         const u32x4_t z = {0u, 0u, 0u, 0u};
         for (int q = tid; q < 3 * per; q += 256) {
@@ -241,7 +299,7 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DParams p) {
         }
         __syncthreads();
       }
-      step(kt, kt & 1);
+      step(kt, slot);
     }
     __syncthreads();  // every wave done with the ring before the next tile's loads
     if (tid == 0) s_claim[0] = pre;
