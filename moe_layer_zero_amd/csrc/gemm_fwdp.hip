@@ -105,6 +105,15 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_void* ds
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
 }
 
+// Workgroup barrier ordering LDS accesses only: unlike __syncthreads it
+// does not wait for global loads in flight (the next tile's slabs).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS accesses done
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // s_waitcnt immediate for "vmcnt <= n" (expcnt and lgkmcnt not waited)
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
@@ -389,72 +398,97 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
   }
 }
 
-// The down projection on 256-row tiles (the prefill shape) with eight
-// waves: two per SIMD, each owning all 256 rows of the tile and one group of
-// 32 output columns, so 8 accumulator blocks (128 registers) instead of 16
-// and the pair of waves on a SIMD fits one register file; one wave's matrix
-// work runs while the other waits on its loads or fragment reads.  The
-// activation ring is shared by the eight waves as before (each reads the
-// whole A slab: LDS reads with eight waves per CU measure above 170 bytes
-// per clock on this part, twice what one wave per SIMD draws).  Every
-// output element sums the same MFMA steps in the same order as the
-// four-wave kernel, so the two give identical bits.  Measured at the
-// prefill workload: 4.00 ms against 4.29 ms for the four-wave kernel; the
-// same split of the gate/up GEMM (gate and up columns on different waves,
-// joined through LDS in the epilogue) gave no gain (8.09 vs 7.95 ms) and is
-// not used.
 constexpr int NTHR8 = 512;
+
+// The down projection on 256-row tiles (the prefill shape), eight waves:
+// two per SIMD, each owning all 256 rows of the tile and one group of 32
+// output columns (8 accumulator blocks, 128 registers), so the pair of waves
+// on a SIMD fits one register file and one wave's matrix work covers the
+// other's waits.  Every wave reads the whole A slab from the shared LDS ring
+// (LDS reads with eight waves per CU measure above 170 bytes per clock on
+// this part).  Each A fragment feeds a single MFMA here, so the fragment
+// reads must run ahead of their MFMAs (four in flight): a kernel whose
+// register allocation left one fragment register, each read waited for
+// before its MFMA, kept the matrix cores about half busy.  What makes room
+// for the four fragments: one code path for every tile (all eight row
+// blocks multiplied; rows past the tile's end are zeros, at this workload
+// 13% of the MFMAs), weight fragments loaded through a buffer resource
+// (scalar base, one lane-offset register) and every per-tile value in
+// scalar registers.
+//
+// The next tile's first three slabs are loaded under this tile's last three
+// slabs and its epilogue, so the weight stream does not stop between tiles.
+// The next tile is known four slabs before the end: its claim went out
+// during the previous tile's drain (a vector atomic whose result thread 0
+// first reads after more than two slabs of younger loads, so the slab waits
+// already cover it).  The epilogue stages the tile in two halves of 128
+// rows through ring slot 3 and 32 KB past the ring (slots 0 to 2 are
+// receiving the next tile meanwhile) and writes 16-byte row pieces through a
+// buffer resource that ends at the tile's last row.  Every slab wait is
+// "vmcnt <= 2V": loads return in issue order, so with two younger slabs of V
+// loads each in flight the awaited slab has landed, whatever stores or
+// atomics are interleaved (they only make a wait stricter).
+// Measured at the prefill workload: 3.71 ms against 4.02 ms for the same
+// eight-wave split with per-row-block code paths and a drained pipeline
+// between tiles.
 __global__ __launch_bounds__(NTHR8, 1) void down8_kernel(PParams p) {
   constexpr int TM = 256;
-  constexpr int SLOT = TM * BK;        // bf16 per ring slot (32 KB)
-  constexpr int AW = 4;                // A copies per wave per slab (32 1-KB blocks / 8 waves)
-  constexpr int V = AW + 4;            // loads per wave per slab
-  __shared__ __align__(16) bf16_t ring[NST * SLOT + 16];
-  int32_t* const s_claim = reinterpret_cast<int32_t*>(ring + NST * SLOT);
+  constexpr int SLOT = TM * BK;  // bf16 per ring slot (32 KB)
+  constexpr int AW = 4;          // A copies per wave per slab
+  constexpr int V = AW + 4;      // loads per wave per slab
+  constexpr int OUTN = 256;
+  constexpr int HR = 128;        // rows per staging half
+  // ring slots 0..3, then 32 KB: staging = slot 3 + that (HR x OUTN bf16,
+  // 160 KB in all); s_next (the next tile, written by thread 0 four slabs
+  // before a tile's end and read by every wave after that slab's barrier)
+  // sits inside the staging, which is only written in the epilogue
+  __shared__ __align__(16) bf16_t lds[5 * SLOT];
+  bf16_t* const ring = lds;
+  bf16_t* const stage = lds + 3 * SLOT;
+  int32_t* const s_next = reinterpret_cast<int32_t*>(lds + 4 * SLOT);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr int OUTN = 256;
   const int NT = p.ncols / OUTN;
   const int64_t total = static_cast<int64_t>(ld_scalar(p.mt_off + p.N)) * NT;
   const int G = gridDim.x;
-  const int xcd = blockIdx.x % 8;
   const int C = G / 8;
-  int cx = xcd;
-  int hops = 0;
-  auto tile_of = [&](int x, int n) -> int64_t {
-    return static_cast<int64_t>(n / C) * 8 * C + x * C + n % C;
-  };
-  if (tid == 0) s_claim[0] = atomicAdd(p.sched + cx, 1);
-  __syncthreads();
-  int cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
   const int nk = p.K / BK;
   const int kblk = p.K / 16;
+  const int64_t mat = static_cast<int64_t>(p.ncols) * p.K;
   const __amdgpu_buffer_rsrc_t arsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(p.A), (short)0, p.a_bytes, 0x00020000);
   const int s7 = (lane >> 1) & 7;
   const int khalf = lane >> 5;
   const int frag_lane = (lane & 31) * BK;
 
-  for (;;) {
-    const int64_t L = tile_of(cx, cur_n);
-    if (L >= total) {
-      if (++hops == 8) break;
+  // ---- tile claims (thread 0 only): per-XCD counters, then the other XCDs'
+  int cx = blockIdx.x % 8;
+  int hops = 0;
+  auto resolve = [&](int32_t n) -> int32_t {
+    int64_t L = static_cast<int64_t>(n / C) * 8 * C + cx * C + n % C;
+    while (L >= total) {
+      if (++hops >= 8) return -1;
       cx = (cx + 1) & 7;
-      __syncthreads();
-      if (tid == 0) s_claim[0] = atomicAdd(p.sched + cx, 1);
-      __syncthreads();
-      cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
-      continue;
+      const int32_t m = atomicAdd(p.sched + cx, 1);
+      L = static_cast<int64_t>(m / C) * 8 * C + cx * C + m % C;
     }
-    int32_t next_n = 0;
-    if (tid == 0) next_n = atomicAdd(p.sched + cx, 1);
-    const int lmt = static_cast<int>(L / NT);
+    return static_cast<int32_t>(L);
+  };
+
+  // ---- a tile: its rows and columns (wave-uniform, scalar registers)
+  struct Tile {
+    int m0, mcount, n0;
+    uint32_t abase;                // byte offset of row m0 in A
+    __amdgpu_buffer_rsrc_t brsrc;  // this wave's packed weight column group
+  };
+  auto locate = [&](int32_t L, Tile& t) {
+    const int lmt = L / NT;
     const int e = ld_scalar(p.tile_exp + lmt);
     const int mt_e = ld_scalar(p.mt_off + e);
     const int mte = ld_scalar(p.mt_off + e + 1) - mt_e;
-    const int q = static_cast<int>(L - static_cast<int64_t>(mt_e) * NT);
+    const int q = L - mt_e * NT;
     const int grp = q / (GMV * NT);
     const int fm = grp * GMV;
     const int gsz = min(GMV, mte - fm);
@@ -464,41 +498,67 @@ __global__ __launch_bounds__(NTHR8, 1) void down8_kernel(PParams p) {
     const int seg0 = ld_scalar(p.offsets + e), seg1 = ld_scalar(p.offsets + e + 1);
     const int nbe = (seg1 - seg0 + 31) >> 5;
     const int blo = nbe * mt / mte, bhi = nbe * (mt + 1) / mte;
-    const int m0 = seg0 + 32 * blo;
-    const int mcount = min(seg0 + 32 * bhi, seg1) - m0;
-    const int n0 = nt * OUTN;
+    t.m0 = seg0 + 32 * blo;
+    t.mcount = min(seg0 + 32 * bhi, seg1) - t.m0;
+    t.n0 = nt * OUTN;
+    t.abase = static_cast<uint32_t>(t.m0) * static_cast<uint32_t>(p.K) * 2u;
+    const bf16_t* bw = p.B + e * mat + static_cast<int64_t>(t.n0 / 32 + wave) * kblk * 512;
+    t.brsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(bw), (short)0,
+                                                static_cast<uint32_t>(kblk) * 1024u, 0x00020000);
+  };
+  // this lane's A copies: copy i of wave w covers rows 8 (4 w + i) + lane/8
+  // of the tile, 16 bytes at chunk (lane%8) ^ ((4 (4 w + i) + lane/16) % 8);
+  // that chunk depends on i only through i % 2.  A copy past the tile's rows
+  // loads from outside the buffer (no data).
+  const int lrow = lane >> 3;
+  uint32_t achunk[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    achunk[j] = (static_cast<uint32_t>(lrow) * static_cast<uint32_t>(p.K) +
+                 (((lane & 7) ^ ((4 * j + (lane >> 4)) & 7)) * 8)) * 2u;
+  const uint32_t blane = lane * 16;  // byte offset of this lane's piece of a 1 KB block
 
-    uint32_t aoff[AW];
+  bf16x8_t bq[NST][4];  // B fragments of the slabs in flight
+  auto issue = [&](const Tile& t, int kt, int slot, bf16x8_t (&bf)[4]) {
 #pragma unroll
     for (int i = 0; i < AW; ++i) {
       const int b = AW * wave + i;
-      const int row = 8 * b + (lane >> 3);
-      const int chunk = (lane & 7) ^ ((4 * b + (lane >> 4)) & 7);
-      if (row < mcount) {
-        const int gm = m0 + row;
-        aoff[i] = (static_cast<uint32_t>(gm) * static_cast<uint32_t>(p.K) + chunk * 8) * 2u;
-      } else {
-        aoff[i] = p.a_bytes;
-      }
+      lds_void* dst = (lds_void*)(ring + slot * SLOT + b * 8 * BK);
+      const uint32_t off = lrow < t.mcount - 8 * b
+                               ? t.abase + static_cast<uint32_t>(8 * b) * static_cast<uint32_t>(p.K) * 2u + achunk[i & 1]
+                               : p.a_bytes;
+      lds_dma16(arsrc, dst, off, kt * BK * 2);
     }
-    const int64_t mat = static_cast<int64_t>(p.ncols) * p.K;
-    // wave w's 32 output columns: packed column group n0/32 + w
-    const bf16_t* bsrc =
-        p.B + e * mat + static_cast<int64_t>(n0 / 32 + wave) * kblk * 512 + lane * 8;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      bf[u] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(t.brsrc, blane, (4 * kt + u) * 1024, 0));
+  };
 
-    const int nrb = (mcount + 31) >> 5;
-    auto run = [&](auto nrb_c) {
-      constexpr int NRB = decltype(nrb_c)::value;
-      bf16x8_t bq[NST][4];
-      auto issue = [&](int kt, int slot, bf16x8_t (&bf)[4]) {
-#pragma unroll
-        for (int i = 0; i < AW; ++i) {
-          lds_void* dst = (lds_void*)(ring + slot * SLOT + (AW * wave + i) * 8 * BK);
-          lds_dma16(arsrc, dst, aoff[i], kt * BK * 2);
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) bf[t] = *reinterpret_cast<const bf16x8_t*>(bsrc + (4 * kt + t) * 512);
-      };
+  // ---- first tile, and the claim of the second
+  int32_t pend = 0;
+  if (tid == 0) {
+    const int32_t L0 = resolve(atomicAdd(p.sched + cx, 1));
+    if (L0 >= 0) pend = atomicAdd(p.sched + cx, 1);
+    s_next[0] = L0;
+  }
+  __syncthreads();
+  int32_t Lc = __builtin_amdgcn_readfirstlane(s_next[0]);
+  if (Lc < 0) return;
+  Tile tc;
+  locate(Lc, tc);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(tc, 0, 0, bq[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(tc, 1, 1, bq[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(tc, 2, 2, bq[2]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  for (;;) {
+    int32_t Ln = -1;
+    Tile tn;
+    {
+      constexpr int NRB = 8;  // every row block: rows past the tile's end are zeros
       f32x16_t acc[NRB];
 #pragma unroll
       for (int i = 0; i < NRB; ++i)
@@ -518,8 +578,8 @@ __global__ __launch_bounds__(NTHR8, 1) void down8_kernel(PParams p) {
       };
       constexpr int NDS = 4 * NRB;
       constexpr int DS0 = NDS < DSDEPTH ? NDS : DSDEPTH;
-      auto sched = [&](bool with_loads) {
-        if (with_loads) __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
+      auto sched = [&]() {
+        __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, DS0, 0);
 #pragma unroll
         for (int g = 0; g < NDS - DS0; ++g) {
@@ -528,89 +588,103 @@ __global__ __launch_bounds__(NTHR8, 1) void down8_kernel(PParams p) {
         }
         __builtin_amdgcn_sched_group_barrier(0x008, DS0, 0);
       };
-      __builtin_amdgcn_sched_barrier(0);
-      issue(0, 0, bq[0]);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(1, 1, bq[1]);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(2, 2, bq[2]);
-      __builtin_amdgcn_sched_barrier(0);
       int kt = 0;
       for (; kt < nk - 4; kt += 4) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
           __builtin_amdgcn_s_barrier();
-          issue(kt + u + 3, (u + 3) & 3, bq[(u + 3) & 3]);
+          issue(tc, kt + u + 3, (u + 3) & 3, bq[(u + 3) & 3]);
           compute(u, bq[u]);
-          sched(true);
+          sched();
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      // slab nk-4: the next tile is named (its claim was issued a whole tile
+      // ago) and located
+      if (tid == 0) s_next[0] = pend < 0 ? -1 : resolve(pend);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
       __builtin_amdgcn_s_barrier();
-      issue(kt + 3, 3, bq[3]);
+      issue(tc, kt + 3, 3, bq[3]);
+      __builtin_amdgcn_sched_barrier(0);
+      Ln = __builtin_amdgcn_readfirstlane(s_next[0]);
+      if (Ln >= 0) {
+        locate(Ln, tn);
+      } else {
+        tn = tc;  // no next tile: the drain re-reads this tile's first slabs, unused
+      }
+      __builtin_amdgcn_sched_barrier(0);
       compute(0, bq[0]);
-      sched(true);
+      __builtin_amdgcn_sched_barrier(0);
+      // slabs nk-3 .. nk-1, each with one of the next tile's first three
+      // slabs in flight; the claim of the tile after it goes out first
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
+      __builtin_amdgcn_s_barrier();
+      if (tid == 0) pend = Ln >= 0 ? atomicAdd(p.sched + cx, 1) : -1;
+      issue(tn, 0, 0, bq[0]);
+      compute(1, bq[1]);
+      sched();
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
       __builtin_amdgcn_s_barrier();
-      compute(1, bq[1]);
-      sched(false);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(V));
-      __builtin_amdgcn_s_barrier();
+      issue(tn, 1, 1, bq[1]);
       compute(2, bq[2]);
-      sched(false);
+      sched();
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V));
       __builtin_amdgcn_s_barrier();
+      issue(tn, 2, 2, bq[2]);
       compute(3, bq[3]);
-      sched(false);
+      sched();
       __builtin_amdgcn_sched_barrier(0);
 
       // ---- epilogue: lane holds column lane%32 of its group and rows
-      // 32 rb + 8 (v/4) + 4 (lane/32) + v%4
+      // 32 rb + 8 (v/4) + 4 (lane/32) + v%4; two halves of 128 rows, each
+      // staged (bf16) and written with 16-byte row-contiguous stores.  The
+      // stores go through a buffer resource ending at the tile's last row,
+      // so rows past it are dropped by the range check, without branches.
       const int rbase = 4 * khalf;
-      __syncthreads();  // every wave done reading the ring: it becomes the staging
-      {
-        bf16_t* st = ring;  // [256][256] bf16 = the whole ring
+      constexpr int RC = OUTN / 8;  // 16-byte chunks per row
+      const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
+          p.C + static_cast<int64_t>(tc.m0) * p.ncols, (short)0,
+          static_cast<uint32_t>(tc.mcount) * static_cast<uint32_t>(p.ncols) * 2u, 0x00020000);
+      const int srow = tid / RC, scol = (tid % RC) * 8;
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
+      for (int h = 0; h < 2; ++h) {
+        if (h * HR >= tc.mcount) break;
+        lds_barrier();  // slot 3 read by every wave / the first half stored
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int rl = rbase + 32 * rb + 8 * (v >> 2) + (v & 3);
-            // a conversion the compiler sees: the accumulators are plain
-            // VGPRs here, and an MFMA result read by inline asm is not
-            // covered by the compiler's hazard tracking
-            st[rl * OUTN + 32 * wave + (lane & 31)] =
-                __builtin_bit_cast(bf16_t, static_cast<__bf16>(acc[rb][v]));
+        for (int rb = 4 * h; rb < 4 * h + 4; ++rb) {
+          if (rb < NRB) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int rl = rbase + 32 * (rb - 4 * h) + 8 * (v >> 2) + (v & 3);
+              stage[rl * OUTN + 32 * wave + (lane & 31)] =
+                  __builtin_bit_cast(bf16_t, static_cast<__bf16>(acc[rb][v]));
+            }
           }
+        }
+        lds_barrier();
+        const uint32_t obase =
+            (static_cast<uint32_t>(h * HR + srow) * static_cast<uint32_t>(p.ncols) +
+             static_cast<uint32_t>(tc.n0 + scol)) * 2u;
+        const uint32_t ostep = static_cast<uint32_t>(NTHR8 / RC) * static_cast<uint32_t>(p.ncols) * 2u;
+#pragma unroll
+        for (int i = 0; i < HR * RC / NTHR8; ++i) {
+          const u32x4_t vv =
+              *reinterpret_cast<const u32x4_t*>(stage + (srow + i * (NTHR8 / RC)) * OUTN + scol);
+          __builtin_amdgcn_raw_buffer_store_b128(vv, crsrc, obase + i * ostep, 0, 0);
+        }
       }
-      __syncthreads();
-      constexpr int RC = OUTN / 8;
-      const bf16_t* st = ring;
-#pragma unroll 4
-      for (int c = tid; c < mcount * RC; c += NTHR8) {
-        const int rl = c / RC, cc = (c % RC) * 8;
-        *reinterpret_cast<u32x4_t*>(p.C + static_cast<int64_t>(m0 + rl) * p.ncols + n0 + cc) =
-            *reinterpret_cast<const u32x4_t*>(st + rl * OUTN + cc);
-      }
-      if (tid == 0) s_claim[0] = next_n;
-      __syncthreads();
-    };
-    switch (nrb) {
-      case 1: run(std::integral_constant<int, 1>{}); break;
-      case 2: run(std::integral_constant<int, 2>{}); break;
-      case 3: run(std::integral_constant<int, 3>{}); break;
-      case 4: run(std::integral_constant<int, 4>{}); break;
-      case 5: run(std::integral_constant<int, 5>{}); break;
-      case 6: run(std::integral_constant<int, 6>{}); break;
-      case 7: run(std::integral_constant<int, 7>{}); break;
-      default: run(std::integral_constant<int, 8>{}); break;
+      // with fewer than eight slabs the next tile writes s_next (in the
+      // staging) before its first barrier: every wave has read the staging
+      if (nk < 8) lds_barrier();
     }
-    cur_n = __builtin_amdgcn_readfirstlane(s_claim[0]);
+    if (Ln < 0) break;
+    tc = tn;
   }
+  // the unused slabs of the drain land in LDS before the workgroup ends
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 // SwiGLU backward of the FFN picks in dispatch order, from dh = g (dout W_d)
