@@ -290,6 +290,21 @@ def test_forward_packed_all_zero_computation_picks():
     assert route.offsets[-1].item() == 0
 
 
+def test_forward_packed_four_slab_down_tiles_on_any_grid():
+    # I = 256: the 256-row down projection has four 64-step slabs per tile,
+    # so the next tile's first three slabs load under the last three and the
+    # epilogue; grids of 8 and 64 workgroups make each workgroup run many
+    # such tiles back to back.  Every token against the oracle, then the
+    # same bits on the smaller grids.
+    import dataclasses
+    sh = synth.LayerShape("down_k256", 10, 4096, 2048, 8, 4, 256, 4, "bf16", 0.02, "zero")
+    L, Lg, desc, route, out, o = forward_case(sh, packed=True)
+    for lim in (64, 8):
+        print(f"[forward] {sh.name} packed, cu_limit={lim}", flush=True)
+        _, b, _ = H.run_forward(dataclasses.replace(desc, cu_limit=lim), Lg, packed=True)
+        assert torch.equal(out, b)
+
+
 def test_forward_packed_is_deterministic():
     sh = CF["small_bf16"]
     Lg = H.to_dev(synth.make_layer(sh, "cpu"))
