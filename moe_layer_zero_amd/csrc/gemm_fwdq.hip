@@ -289,26 +289,33 @@ __global__ __launch_bounds__(NTHR, 1) void fwdq_kernel(QParams p) {
         const uint8_t* bsl = ring + slot * SLOT + TM * BKQ + SC_A + 512 * wave + 2 * lane;
         const uint32_t sb0 = *reinterpret_cast<const uint16_t*>(bsl);
         const uint32_t sb1 = *reinterpret_cast<const uint16_t*>(bsl + 256);
+        // fragment f = s NRB + rb (64-step half s, row block rb): two code
+        // reads and one scale read, issued two fragments ahead of the
+        // fragment's MFMAs in program order as well as in the groups below
+        constexpr int NF = 2 * NRB;
+        auto frag = [&](int f, i32x8_t& a, uint32_t& asw) {
+          const int s = f / NRB, rb = f % NRB;
+          a.lo = *reinterpret_cast<const i32x4_t*>(a_s + rb * 32 * BKQ + (((4 * s + khalf) ^ s7) << 4));
+          a.hi = *reinterpret_cast<const i32x4_t*>(a_s + rb * 32 * BKQ + (((4 * s + 2 + khalf) ^ s7) << 4));
+          asw = *reinterpret_cast<const uint16_t*>(a_sc + rb * 32 * 4);
+        };
+        i32x8_t af[3];
+        uint32_t aw[3];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int c0 = ((4 * s + khalf) ^ s7) << 4;
-          const int c1 = ((4 * s + 2 + khalf) ^ s7) << 4;
+        for (int f = 0; f < 2 && f < NF; ++f) frag(f, af[f], aw[f]);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          if (f + 2 < NF) frag(f + 2, af[(f + 2) % 3], aw[(f + 2) % 3]);
+          const int s = f / NRB, rb = f % NRB;
           const uint32_t b0s = s == 0 ? (sb0 & 0xffu) : (sb0 >> 8);
           const uint32_t b1s = s == 0 ? (sb1 & 0xffu) : (sb1 >> 8);
-#pragma unroll
-          for (int rb = 0; rb < NRB; ++rb) {
-            i32x8_t a;
-            a.lo = *reinterpret_cast<const i32x4_t*>(a_s + rb * 32 * BKQ + c0);
-            a.hi = *reinterpret_cast<const i32x4_t*>(a_s + rb * 32 * BKQ + c1);
-            const uint32_t asw = *reinterpret_cast<const uint16_t*>(a_sc + rb * 32 * 4);
-            const uint32_t as = s == 0 ? (asw & 0xffu) : (asw >> 8);
-            acc[rb][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                a, bq[slot][0][s], acc[rb][0], 0, 0, 0, static_cast<int>(as), 0,
-                static_cast<int>(b0s));
-            acc[rb][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                a, bq[slot][1][s], acc[rb][1], 0, 0, 0, static_cast<int>(as), 0,
-                static_cast<int>(b1s));
-          }
+          const uint32_t as = s == 0 ? (aw[f % 3] & 0xffu) : (aw[f % 3] >> 8);
+          acc[rb][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              af[f % 3], bq[slot][0][s], acc[rb][0], 0, 0, 0, static_cast<int>(as), 0,
+              static_cast<int>(b0s));
+          acc[rb][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              af[f % 3], bq[slot][1][s], acc[rb][1], 0, 0, 0, static_cast<int>(as), 0,
+              static_cast<int>(b1s));
         }
       };
 

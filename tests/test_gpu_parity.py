@@ -282,8 +282,10 @@ def test_forward_packed_single_expert_mlp():
     forward_case(sh, packed=True)
 
 
-def test_forward_packed_all_zero_computation_picks():
-    sh = CF["small_bf16"].with_T(300)
+@pytest.mark.parametrize("T", [300, 4096])
+def test_forward_packed_all_zero_computation_picks(T):
+    # 4096 tokens: the 256-row kernels, launched on an empty tile list
+    sh = CF["small_bf16"].with_T(T)
     b = torch.zeros(sh.E)
     b[sh.N:] = 1.0
     L, Lg, desc, route, out, o = forward_case(sh, bias=b, packed=True)
