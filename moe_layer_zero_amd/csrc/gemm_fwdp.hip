@@ -271,16 +271,38 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+      // fragment f = t NRB + rb (reduction step t, row block rb).  For 4 to
+      // 6 occupied row blocks the scheduler, left to itself, waits for each
+      // fragment read right before its MFMAs in two slabs of every four;
+      // there the reads are written three fragments ahead in program order.
       auto compute = [&](int slot, const bf16x8_t (&bf)[2][4]) {
         const bf16_t* a_s = ring + slot * SLOT + frag_lane;
+        if constexpr (NRB >= 4 && NRB <= 6) {
+          constexpr int NF = 4 * NRB;
+          auto frag = [&](int f) {
+            const int t = f / NRB, rb = f % NRB;
+            return *reinterpret_cast<const bf16x8_t*>(a_s + rb * 32 * BK + (((2 * t + khalf) ^ s7) << 3));
+          };
+          bf16x8_t a[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int co = ((2 * t + khalf) ^ s7) << 3;
+          for (int f = 0; f < 3; ++f) a[f] = frag(f);
 #pragma unroll
-          for (int rb = 0; rb < NRB; ++rb) {
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(a_s + rb * 32 * BK + co);
-            acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[0][t], acc[rb][0], 0, 0, 0);
-            acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[1][t], acc[rb][1], 0, 0, 0);
+          for (int f = 0; f < NF; ++f) {
+            if (f + 3 < NF) a[(f + 3) & 3] = frag(f + 3);
+            const int t = f / NRB, rb = f % NRB;
+            acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[f & 3], bf[0][t], acc[rb][0], 0, 0, 0);
+            acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[f & 3], bf[1][t], acc[rb][1], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int co = ((2 * t + khalf) ^ s7) << 3;
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+              const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(a_s + rb * 32 * BK + co);
+              acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[0][t], acc[rb][0], 0, 0, 0);
+              acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[1][t], acc[rb][1], 0, 0, 0);
+            }
           }
         }
       };
