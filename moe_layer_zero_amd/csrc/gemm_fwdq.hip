@@ -467,6 +467,386 @@ __global__ __launch_bounds__(NTHR, 1) void fwdq_kernel(QParams p) {
   }
 }
 
+// LDS-only barrier: this wave's LDS accesses are complete, then the
+// workgroup meets.  (A workgroup fence would also wait for every vector
+// memory access in flight, i.e. drain the slab pipeline.)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The FP8 down projection of 256-row tiles (the prefill shape) with no
+// bubble between tiles: the next tile's first three slabs are loaded under
+// this tile's last three slabs and its epilogue, so the weight stream does
+// not stop at tile boundaries.  With reductions of 2048 steps a tile is
+// only 16 slabs long, and a pipeline drained and refilled at every tile
+// boundary idles the memory path for about a quarter of each tile.
+//
+// Same operands, fragments and MFMA order as fwdq_kernel<Q_STORE, 256>
+// (bit-identical results); what differs:
+//  - one code path for every tile: all eight row blocks are multiplied
+//    (rows past the tile's end are loaded as zeros), so the registers that
+//    carry the next tile's slabs are the same whatever the tile's height;
+//  - the next tile is known four slabs before the end (its claim went out
+//    during the previous tile's drain) and located then; every per-tile
+//    value is a scalar except one lane offset;
+//  - weight codes and scales are read through per-tile buffer resources;
+//  - the epilogue stages 64 rows at a time in ring slot 3 (slots 0..2 are
+//    receiving the next tile), all four quarters whatever the tile's
+//    height, so every thread issues 32 row-piece stores per tile, those
+//    past the tile's rows dropped by the buffer range check.
+//    With that fixed count the first three slabs of a tile wait for
+//    "vmcnt <= 62": issued after each of them are two slabs of V loads and
+//    the 32 stores, 2V + 32 >= 62 operations, so the bound covers it (the
+//    counter has six bits, and at 62 the compiler also sees the slab's
+//    weight registers as loaded); from the fourth slab on, "vmcnt <= 2V"
+//    as in the steady state.  (Loads return in issue order; stores and atomics in
+//    between only make a wait stricter.)  The prologue issues 32 stores
+//    that write nothing, so the first tile starts from the same count.
+template <bool NT_W>
+__global__ __launch_bounds__(NTHR, 1) void downq_kernel(QParams p) {
+  constexpr int TM = 256;
+  constexpr int RB = TM / 32;                // A copies per wave per slab
+  constexpr int SLOT = TM * BKQ + SC_BYTES;  // bytes per ring slot
+  constexpr int V = RB + 11;                 // loads per wave per slab
+  constexpr int NRB = 8;
+  constexpr int OUTN = 256;
+  constexpr int QR = 64;                     // rows per staging quarter
+  constexpr int RC = OUTN / 8;               // 16-byte pieces per row
+  constexpr int NSTORE = (TM / QR) * (QR * RC / NTHR);
+  static_assert(QR * OUTN * 2 <= SLOT, "a quarter fits one ring slot");
+  static_assert(2 * V + NSTORE >= 62 && 2 * V <= 62, "wait bounds");
+  __shared__ __align__(16) uint8_t ring[NST * SLOT + 16];
+  int32_t* const s_next = reinterpret_cast<int32_t*>(ring + NST * SLOT);
+  bf16_t* const stage = reinterpret_cast<bf16_t*>(ring + 3 * SLOT);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int NT = p.ncols / OUTN;
+  const int64_t total = static_cast<int64_t>(ld_scalar(p.mt_off + p.N)) * NT;
+  const int G = gridDim.x;
+  const int C = G / 8;
+  const int nk = p.K / BKQ;
+  const int kb32 = p.K / 32;
+  const int64_t mat = static_cast<int64_t>(p.ncols) * p.K;
+  const int64_t nexp = static_cast<int64_t>(p.N) * mat;  // weight scales follow all codes
+  const __amdgpu_buffer_rsrc_t arsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.A), (short)0, p.a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.As), (short)0, p.as_bytes, 0x00020000);
+  const int s7 = (lane >> 1) & 7;
+  const int khalf = lane >> 5;
+  const int frag_lane = (lane & 31) * BKQ;
+
+  // ---- tile claims (thread 0 only): per-XCD counters, then the other XCDs'
+  int cx = blockIdx.x % 8;
+  int hops = 0;
+  auto resolve = [&](int32_t n) __attribute__((always_inline)) -> int32_t {
+    int64_t L = static_cast<int64_t>(n / C) * 8 * C + cx * C + n % C;
+    while (L >= total) {
+      if (++hops >= 8) return -1;
+      cx = (cx + 1) & 7;
+      const int32_t m = atomicAdd(p.sched + cx, 1);
+      L = static_cast<int64_t>(m / C) * 8 * C + cx * C + m % C;
+    }
+    return static_cast<int32_t>(L);
+  };
+
+  struct Tile {
+    int m0, mcount, n0;
+    uint32_t abase;                 // byte offset of row m0's codes in A
+    uint32_t sa;                    // this lane's activation-scale row (past the end: none)
+    __amdgpu_buffer_rsrc_t brsrc;   // codes of this wave's two column groups
+    __amdgpu_buffer_rsrc_t bsrsrc;  // and their scales
+  };
+  // field by field: a whole-struct copy goes through private memory
+  auto copy = [](Tile& d, const Tile& t) __attribute__((always_inline)) {
+    d.m0 = t.m0;
+    d.mcount = t.mcount;
+    d.n0 = t.n0;
+    d.abase = t.abase;
+    d.sa = t.sa;
+    d.brsrc = t.brsrc;
+    d.bsrsrc = t.bsrsrc;
+  };
+  auto locate = [&](int32_t L, Tile& t) __attribute__((always_inline)) {
+    const int lmt = L / NT;
+    const int e = ld_scalar(p.tile_exp + lmt);
+    const int mt_e = ld_scalar(p.mt_off + e);
+    const int mte = ld_scalar(p.mt_off + e + 1) - mt_e;
+    const int q = L - mt_e * NT;
+    const int grp = q / (GMV * NT);
+    const int fm = grp * GMV;
+    const int gsz = min(GMV, mte - fm);
+    const int rr = q - grp * GMV * NT;
+    const int mt = fm + rr % gsz;
+    const int nt = rr / gsz;
+    // the expert's 32-row blocks spread evenly over its row tiles
+    const int seg0 = ld_scalar(p.offsets + e), seg1 = ld_scalar(p.offsets + e + 1);
+    const int nbe = (seg1 - seg0 + 31) >> 5;
+    const int blo = nbe * mt / mte, bhi = nbe * (mt + 1) / mte;
+    t.m0 = seg0 + 32 * blo;
+    t.mcount = min(seg0 + 32 * bhi, seg1) - t.m0;
+    t.n0 = nt * OUTN;
+    t.abase = static_cast<uint32_t>(t.m0) * static_cast<uint32_t>(p.K);
+    const int row = 64 * wave + lane;
+    t.sa = row < t.mcount ? static_cast<uint32_t>(t.m0 + row) * static_cast<uint32_t>(kb32)
+                          : p.as_bytes;
+    const int g = t.n0 / 32 + 2 * wave;  // the first of the wave's two column groups
+    t.brsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(p.B + e * mat + static_cast<int64_t>(g) * nk * 4096), (short)0,
+        static_cast<uint32_t>(nk) * 8192u, 0x00020000);
+    t.bsrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(p.B + nexp + e * (mat / 32) + static_cast<int64_t>(g) * nk * 128),
+        (short)0, static_cast<uint32_t>(nk) * 256u, 0x00020000);
+  };
+
+  // A copy i of wave w: rows 8 b + lane/8 (b = 8 w + i), 16 bytes at chunk
+  // (lane%8) ^ ((4 b + lane/16) % 8), which depends on i only through i % 2
+  const int lrow = lane >> 3;
+  uint32_t achunk[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    achunk[j] = static_cast<uint32_t>(lrow) * static_cast<uint32_t>(p.K) +
+                static_cast<uint32_t>(((lane & 7) ^ ((4 * j + (lane >> 4)) & 7)) * 16);
+  const uint32_t blane0 = lane * 16;
+  const uint32_t blane1 = static_cast<uint32_t>(nk) * 4096u + lane * 16;
+  // weight scales: lanes 0..31 carry a group's 128 bytes of a slab, lanes
+  // 32..63 point past the resource (no data)
+  const uint32_t bsl0 = lane < 32 ? 4u * lane : static_cast<uint32_t>(nk) * 256u;
+  const uint32_t bsl1 = lane < 32 ? static_cast<uint32_t>(nk) * 128u + 4u * lane
+                                  : static_cast<uint32_t>(nk) * 256u;
+  auto ldw = [](__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) __attribute__((always_inline)) {
+    return __builtin_bit_cast(i32x4_t,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, NT_W ? 2 : 0));
+  };
+
+  i32x8_t bq[NST][2][2];  // B operands in flight: [slot][column group][step]
+  // LDS destinations of a slab's copies: one scalar base per slab, made
+  // opaque so that the compiler does not keep every (slot, copy) address of
+  // the loop in a scalar register of its own
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  auto issue = [&](const Tile& t, int kt, int slot) __attribute__((always_inline)) {
+    lds_u8* base = (lds_u8*)(ring + slot * SLOT);
+    asm volatile("" : "+s"(base));
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int b = RB * wave + i;
+      const uint32_t off = lrow < t.mcount - 8 * b
+                               ? t.abase + static_cast<uint32_t>(8 * b) * static_cast<uint32_t>(p.K) + achunk[i & 1]
+                               : p.a_bytes;
+      lds_dma16(arsrc, (lds_void*)(base + b * 8 * BKQ), off, kt * BKQ);
+    }
+    lds_dma4(srsrc, (lds_void*)(base + TM * BKQ + 256 * wave), t.sa, kt * 4);
+    lds_u8* const bsd = base + TM * BKQ + SC_A + 512 * wave;
+    lds_dma4(t.bsrsrc, (lds_void*)bsd, bsl0, kt * 128);
+    lds_dma4(t.bsrsrc, (lds_void*)(bsd + 256), bsl1, kt * 128);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      bq[slot][0][st].lo = ldw(t.brsrc, blane0, (4 * kt + 2 * st) * 1024);
+      bq[slot][0][st].hi = ldw(t.brsrc, blane0, (4 * kt + 2 * st + 1) * 1024);
+      bq[slot][1][st].lo = ldw(t.brsrc, blane1, (4 * kt + 2 * st) * 1024);
+      bq[slot][1][st].hi = ldw(t.brsrc, blane1, (4 * kt + 2 * st + 1) * 1024);
+    }
+  };
+
+  f32x16_t acc[NRB][2];
+  auto compute = [&](int slot) __attribute__((always_inline)) {
+    const uint8_t* a_s = ring + slot * SLOT + frag_lane;
+    const uint8_t* a_sc = ring + slot * SLOT + TM * BKQ + (lane & 31) * 4 + 2 * khalf;
+    const uint8_t* bsl = ring + slot * SLOT + TM * BKQ + SC_A + 512 * wave + 2 * lane;
+    const uint32_t sb0 = *reinterpret_cast<const uint16_t*>(bsl);
+    const uint32_t sb1 = *reinterpret_cast<const uint16_t*>(bsl + 256);
+    constexpr int NF = 2 * NRB;
+    auto frag = [&](int f, i32x8_t& a, uint32_t& asw) __attribute__((always_inline)) {
+      const int s = f / NRB, rb = f % NRB;
+      a.lo = *reinterpret_cast<const i32x4_t*>(a_s + rb * 32 * BKQ + (((4 * s + khalf) ^ s7) << 4));
+      a.hi = *reinterpret_cast<const i32x4_t*>(a_s + rb * 32 * BKQ + (((4 * s + 2 + khalf) ^ s7) << 4));
+      asw = *reinterpret_cast<const uint16_t*>(a_sc + rb * 32 * 4);
+    };
+    i32x8_t af[3];
+    uint32_t aw[3];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) frag(f, af[f], aw[f]);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      if (f + 2 < NF) frag(f + 2, af[(f + 2) % 3], aw[(f + 2) % 3]);
+      const int s = f / NRB, rb = f % NRB;
+      const uint32_t b0s = s == 0 ? (sb0 & 0xffu) : (sb0 >> 8);
+      const uint32_t b1s = s == 0 ? (sb1 & 0xffu) : (sb1 >> 8);
+      const uint32_t as = s == 0 ? (aw[f % 3] & 0xffu) : (aw[f % 3] >> 8);
+      acc[rb][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          af[f % 3], bq[slot][0][s], acc[rb][0], 0, 0, 0, static_cast<int>(as), 0,
+          static_cast<int>(b0s));
+      acc[rb][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          af[f % 3], bq[slot][1][s], acc[rb][1], 0, 0, 0, static_cast<int>(as), 0,
+          static_cast<int>(b1s));
+    }
+  };
+  constexpr int NFR = 2 * NRB;
+  auto sched = [&](bool with_loads) __attribute__((always_inline)) {
+    if (with_loads) __builtin_amdgcn_sched_group_barrier(0x020, V, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+    for (int g = 0; g < NFR - 1; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  };
+  // one slab: wait for it, meet, issue a younger slab's loads, multiply
+  auto slab = [&](auto wait_c, const Tile& t_issue, int kt_issue, int slot_issue, int slot) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(decltype(wait_c)::value);
+    __builtin_amdgcn_s_barrier();
+    issue(t_issue, kt_issue, slot_issue);
+    compute(slot);
+    sched(true);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using W62 = std::integral_constant<int, vmcnt_imm(62)>;
+  using W2V = std::integral_constant<int, vmcnt_imm(2 * V)>;
+
+  // Later claims are one buffer atomic issued by every thread, only thread
+  // 0's inside the counters' range: the result register is written on
+  // every path, so nothing waits for it before it is used a tile later.
+  // (Claimed under "if (tid == 0)", the result joins the other threads'
+  // value after the branch, and every wave waits there for all of its
+  // loads in flight.)
+  const __amdgpu_buffer_rsrc_t schedr =
+      __builtin_amdgcn_make_buffer_rsrc(p.sched, (short)0, 32u, 0x00020000);
+  // ---- first tile, and the claim of the second (thread 0: pend, pend_ok)
+  int32_t pend = 0;
+  bool pend_ok = false;
+  if (tid == 0) {
+    const int32_t L0 = resolve(atomicAdd(p.sched + cx, 1));
+    if (L0 >= 0) {
+      pend = atomicAdd(p.sched + cx, 1);
+      pend_ok = true;
+    }
+    s_next[0] = L0;
+  }
+  __syncthreads();
+  int32_t Lc = __builtin_amdgcn_readfirstlane(s_next[0]);
+  if (Lc < 0) return;
+  Tile tc;
+  locate(Lc, tc);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(tc, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(tc, 1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(tc, 2, 2);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    // the stores an epilogue would have issued, into an empty resource (at
+    // distinct offsets, so that none of them is merged away)
+    const __amdgpu_buffer_rsrc_t none =
+        __builtin_amdgcn_make_buffer_rsrc(p.Cb, (short)0, 0u, 0x00020000);
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < NSTORE; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(z, none, 16 * tid + 4096 * i, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const int rbase = 4 * khalf;
+  const int srow = tid / RC, scol = (tid % RC) * 8;
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    // slabs 0..3: the first three behind the previous epilogue's stores
+    slab(W62{}, tc, 3, 3, 0);
+    slab(W62{}, tc, 4, 0, 1);
+    slab(W62{}, tc, 5, 1, 2);
+    slab(W2V{}, tc, 6, 2, 3);
+    int kt = 4;
+    for (; kt < nk - 4; kt += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) slab(W2V{}, tc, kt + u + 3, (u + 3) & 3, u);
+    }
+    // slab nk-4: the next tile is named (its claim was issued a whole tile
+    // ago) and located, and the tile after it claimed; thread 0's note is
+    // complete before the barrier.  (The drain below has no branch: the
+    // compiler would sink the MFMAs of the slab before it past it.)
+    int32_t Ln0 = -1;
+    if (tid == 0) {
+      Ln0 = pend_ok ? resolve(pend) : -1;
+      s_next[0] = Ln0;
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * V) & ~0x0F00);
+    __builtin_amdgcn_s_barrier();
+    pend_ok = Ln0 >= 0;
+    pend = __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(
+        1, schedr, tid == 0 && pend_ok ? 4 * cx : 32, 0, 0);
+    issue(tc, kt + 3, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    const int32_t Ln = __builtin_amdgcn_readfirstlane(s_next[0]);
+    // no next tile: the drain re-reads this tile's first slabs, unused (no
+    // branch here: the compiler would hoist the next slab's fragment reads
+    // above it and keep them in scratch across it)
+    Tile tn;
+    locate(Ln >= 0 ? Ln : Lc, tn);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0);
+    sched(false);
+    __builtin_amdgcn_sched_barrier(0);
+    // slabs nk-3 .. nk-1, each with one of the next tile's first three slabs
+    // in flight
+    slab(W2V{}, tn, 0, 0, 1);
+    slab(W2V{}, tn, 1, 1, 2);
+    slab(W2V{}, tn, 2, 2, 3);
+
+    // ---- epilogue: lane holds column lane%32 of its group and rows
+    // 32 rb + 8 (v/4) + 4 (lane/32) + v%4; quarters of 64 rows staged in
+    // slot 3 (bf16) and written as 16-byte row pieces through a resource
+    // that ends at the tile's last row
+    const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
+        p.Cb + static_cast<int64_t>(tc.m0) * p.ncols, (short)0,
+        static_cast<uint32_t>(tc.mcount) * static_cast<uint32_t>(p.ncols) * 2u, 0x00020000);
+    const uint32_t ostep = static_cast<uint32_t>(NTHR / RC) * static_cast<uint32_t>(p.ncols) * 2u;
+#pragma unroll
+    for (int qq = 0; qq < TM / QR; ++qq) {
+      // every quarter, also those past the tile's rows (their stores fall
+      // outside the resource): results used under a branch would let the
+      // compiler sink the last slab's MFMAs into it, past the barriers
+      lds_barrier();  // slot 3 read by every wave / the last quarter stored
+#pragma unroll
+      for (int rb = 2 * qq; rb < 2 * qq + 2; ++rb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rl = rbase + 32 * (rb - 2 * qq) + 8 * (v >> 2) + (v & 3);
+          stage[rl * OUTN + 64 * wave + (lane & 31)] =
+              __builtin_bit_cast(bf16_t, static_cast<__bf16>(acc[rb][0][v]));
+          stage[rl * OUTN + 64 * wave + 32 + (lane & 31)] =
+              __builtin_bit_cast(bf16_t, static_cast<__bf16>(acc[rb][1][v]));
+        }
+      }
+      lds_barrier();
+      const uint32_t obase =
+          (static_cast<uint32_t>(qq * QR + srow) * static_cast<uint32_t>(p.ncols) +
+           static_cast<uint32_t>(tc.n0 + scol)) * 2u;
+#pragma unroll
+      for (int i = 0; i < QR * RC / NTHR; ++i) {
+        const u32x4_t vv =
+            *reinterpret_cast<const u32x4_t*>(stage + (srow + i * (NTHR / RC)) * OUTN + scol);
+        __builtin_amdgcn_raw_buffer_store_b128(vv, crsrc, obase + i * ostep, 0, 0);
+      }
+    }
+    if (Ln < 0) break;
+    copy(tc, tn);
+    Lc = Ln;
+  }
+  // the unused slabs of the drain land in LDS before the workgroup ends
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+}
+
 // Activation quantizer: rows x K bf16 (row-major, rows gathered by nothing)
 // -> codes [rows][K] and scales [rows][K/32] in slab order (0, 2, 1, 3).
 // Four lanes per block, eight values per lane.
@@ -565,8 +945,10 @@ __global__ __launch_bounds__(256) void mxq_weights_kernel(const bf16_t* __restri
 }
 
 typedef void (*fwdq_fn)(QParams);
-// Tile heights 32 .. 256 (the 256-row down tile spills a few registers in
-// its tile setup and epilogue, none inside the k loop).
+// Tile heights 32 .. 256.  The 256-row down projection runs downq_kernel
+// when the reduction has at least eight slabs (launch_q); below that the
+// four-wave kernel's 256-row variant, which spills a few registers in its
+// tile setup and epilogue, none inside the k loop.
 fwdq_fn pick_q(int epi, int tm, int* per_cu) {
   *per_cu = tm <= 64 ? 2 : 1;
   if (epi == Q_SWIGLU) {
@@ -588,6 +970,10 @@ fwdq_fn pick_q(int epi, int tm, int* per_cu) {
 }
 
 hipError_t launch_q(int epi, int tm, const QParams& p, int cu, hipStream_t s) {
+  if (epi == Q_STORE && tm == 256 && p.K >= 8 * BKQ) {
+    hipLaunchKernelGGL(downq_kernel<true>, dim3(cu), dim3(NTHR), 0, s, p);
+    return hipGetLastError();
+  }
   int per_cu = 1;
   fwdq_fn k = pick_q(epi, tm, &per_cu);
   if (!k) return hipErrorInvalidValue;

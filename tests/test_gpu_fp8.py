@@ -180,6 +180,27 @@ def test_fp8_forward_is_deterministic():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("I", [1024, 2048])
+def test_fp8_forward_pipelined_down_tiles_on_any_grid(I):
+    # about 1000 rows per expert: 256-row tiles, whose down projection loads
+    # the next tile's first slabs under the current one's last slabs and
+    # epilogue; reductions of 8 and 16 slabs (the prefill layer's I = 2048).
+    # A token in every 32-row stretch of every expert against the oracle,
+    # then the same bits on grids of 64 and 8 workgroups, where each
+    # workgroup runs many tiles back to back.
+    sh = synth.LayerShape(f"fp8_down_i{I}", 11, 3000, 512, 8, 4, I, 4, "bf16", 0.05, "zero")
+    Lg = H.to_dev(synth.make_layer(sh, "cpu"))
+    desc = H.desc_of(sh)
+    print(f"[fp8 forward] {sh.name} T={sh.T}", flush=True)
+    route, out = run_mx(desc, Lg)
+    toks = H.covering_tokens(route.topk_idx.cpu().numpy(), sh.N, 32, seed=5)
+    check_case(sh, Lg, route, out, toks)
+    for lim in (64, 8):
+        print(f"[fp8 forward] {sh.name} cu_limit={lim}", flush=True)
+        _, b = run_mx(dataclasses.replace(desc, cu_limit=lim), Lg)
+        assert torch.equal(out, b)
+
+
 def big_case(sh, n_logit_tok=128, n_out_tok=16):
     print(f"[fp8 forward-big] {sh.name} T={sh.T}", flush=True)
     Lg = synth.make_layer(sh, "cuda")
