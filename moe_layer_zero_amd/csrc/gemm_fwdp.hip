@@ -214,20 +214,27 @@ __global__ __launch_bounds__(NTHR, 1) void fwdp_kernel(PParams p) {
     const int mcount = min(seg0 + 32 * bhi, seg1) - m0;
     const int n0 = nt * OUTN;
 
-    // ---- byte offsets of the RB A row pieces this lane copies per slab
+    // ---- byte offsets of the RB A row pieces this lane copies per slab.
+    // The gathered rows' slots are loaded all at once and without a branch
+    // (rows past the tile read its last row's slot, unused), so the RB
+    // loads wait once together instead of one round trip each.
+    int src[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int gm = m0 + min(8 * (RB * wave + i) + (lane >> 3), mcount - 1);
+      src[i] = GATHER ? p.perm[gm] : gm;
+    }
     uint32_t aoff[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int b = RB * wave + i;
       const int row = 8 * b + (lane >> 3);
       const int chunk = (lane & 7) ^ ((4 * b + (lane >> 4)) & 7);
-      if (row < mcount) {
-        const int gm = m0 + row;
-        const int src = GATHER ? p.perm[gm] / p.kdiv : gm;
-        aoff[i] = (static_cast<uint32_t>(src) * static_cast<uint32_t>(p.K) + chunk * 8) * 2u;
-      } else {
-        aoff[i] = p.a_bytes;  // out of range: the load returns zeros, reads nothing
-      }
+      const int tok = GATHER ? src[i] / p.kdiv : src[i];
+      // past the tile's rows: out of range, the load returns zeros, reads nothing
+      aoff[i] = row < mcount
+                    ? (static_cast<uint32_t>(tok) * static_cast<uint32_t>(p.K) + chunk * 8) * 2u
+                    : p.a_bytes;
     }
     // ---- packed B: this wave's two column groups of 32
     const int64_t mat = static_cast<int64_t>(p.ncols) * p.K;

@@ -200,31 +200,33 @@ __global__ __launch_bounds__(NTHR, 1) void fwdq_kernel(QParams p) {
     const int mcount = min(seg0 + 32 * bhi, seg1) - m0;
     const int n0 = nt * OUTN;
 
-    // ---- A code pieces (RB per wave per slab) and this wave's scale rows
+    // ---- A code pieces (RB per wave per slab) and this wave's scale rows.
+    // The gathered rows' slots are loaded all at once and without a branch
+    // (rows past the tile read its last row's slot, unused), so the loads
+    // wait once together instead of one round trip each.
+    constexpr bool GATHER = EPI == Q_SWIGLU;
+    int src[RB + 1];
+#pragma unroll
+    for (int i = 0; i <= RB; ++i) {
+      const int row = i < RB ? 8 * (RB * wave + i) + (lane >> 3) : 64 * wave + lane;
+      const int gm = m0 + min(row, mcount - 1);
+      src[i] = GATHER ? p.perm[gm] : gm;
+    }
     uint32_t aoff[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int b = RB * wave + i;
       const int row = 8 * b + (lane >> 3);
       const int chunk = (lane & 7) ^ ((4 * b + (lane >> 4)) & 7);
-      if (row < mcount) {
-        const int gm = m0 + row;
-        const int src = EPI == Q_SWIGLU ? p.perm[gm] / p.kdiv : gm;
-        aoff[i] = static_cast<uint32_t>(src) * static_cast<uint32_t>(p.K) + chunk * 16;
-      } else {
-        aoff[i] = p.a_bytes;
-      }
+      const int tok = GATHER ? src[i] / p.kdiv : src[i];
+      aoff[i] = row < mcount ? static_cast<uint32_t>(tok) * static_cast<uint32_t>(p.K) + chunk * 16
+                             : p.a_bytes;
     }
     uint32_t soff;
     {
       const int row = 64 * wave + lane;
-      if (row < mcount) {
-        const int gm = m0 + row;
-        const int src = EPI == Q_SWIGLU ? p.perm[gm] / p.kdiv : gm;
-        soff = static_cast<uint32_t>(src) * static_cast<uint32_t>(kb32);
-      } else {
-        soff = p.as_bytes;
-      }
+      const int tok = GATHER ? src[RB] / p.kdiv : src[RB];
+      soff = row < mcount ? static_cast<uint32_t>(tok) * static_cast<uint32_t>(kb32) : p.as_bytes;
     }
     // ---- quantized B: this wave's two column groups of 32
     const int64_t mat = static_cast<int64_t>(p.ncols) * p.K;

@@ -254,18 +254,25 @@ __global__ __launch_bounds__(NTHR, 1) void rmw_kernel(RParams p) {
     const int mcount = min(seg0 + 32 * bhi, seg1) - m0;
     const int n0 = nt * OUTN;
 
-    // ---- A copies: this wave's AIW / APC blocks of each piece
+    // ---- A copies: this wave's AIW / APC blocks of each piece.  The
+    // gathered rows' slots are loaded all at once and without a branch (rows
+    // past the tile read its last row's slot, unused), so the loads wait
+    // once together instead of one round trip each.
+    int src[AIW / APC];
+#pragma unroll
+    for (int i = 0; i < AIW / APC; ++i) {
+      const int gm = m0 + min(16 * ((AIW / APC) * wave + i) + (lane >> 2), mcount - 1);
+      src[i] = GATHER ? p.perm[gm] : gm;
+    }
     uint32_t aoff[AIW / APC];
 #pragma unroll
     for (int i = 0; i < AIW / APC; ++i) {
       const int row = 16 * ((AIW / APC) * wave + i) + (lane >> 2);
-      if (row < mcount) {
-        const int gm = m0 + row;
-        const int src = GATHER ? p.perm[gm] / p.kdiv : gm;
-        aoff[i] = (static_cast<uint32_t>(src) * static_cast<uint32_t>(p.lda) + lchunk) * 2u;
-      } else {
-        aoff[i] = p.a_bytes;  // out of range: the copy writes zeros, reads nothing
-      }
+      const int tok = GATHER ? src[i] / p.kdiv : src[i];
+      // past the tile's rows: out of range, the copy writes zeros, reads nothing
+      aoff[i] = row < mcount
+                    ? (static_cast<uint32_t>(tok) * static_cast<uint32_t>(p.lda) + lchunk) * 2u
+                    : p.a_bytes;
     }
     // ---- weight copies: buffers over expert e's matrices
     const uint32_t mbytes = static_cast<uint32_t>(p.mat * 2);
