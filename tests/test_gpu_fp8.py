@@ -180,15 +180,17 @@ def test_fp8_forward_is_deterministic():
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("I", [1024, 2048])
-def test_fp8_forward_pipelined_down_tiles_on_any_grid(I):
-    # about 1000 rows per expert: 256-row tiles, whose down projection loads
-    # the next tile's first slabs under the current one's last slabs and
-    # epilogue; reductions of 8 and 16 slabs (the prefill layer's I = 2048).
-    # A token in every 32-row stretch of every expert against the oracle,
-    # then the same bits on grids of 64 and 8 workgroups, where each
-    # workgroup runs many tiles back to back.
-    sh = synth.LayerShape(f"fp8_down_i{I}", 11, 3000, 512, 8, 4, I, 4, "bf16", 0.05, "zero")
+@pytest.mark.parametrize("d,I", [(512, 1024), (512, 2048), (1536, 512), (2048, 1024)])
+def test_fp8_forward_256_row_tiles_on_any_grid(d, I):
+    # about 1000 rows per expert: 256-row tiles.  The down projection
+    # (reduction I, at least 8 slabs of 128) loads the next tile's first
+    # slabs under the current one's last slabs and epilogue: the smallest
+    # reduction it takes and 16 slabs (the prefill layer's I = 2048); the
+    # gate/up projection with reductions of 4, 12 and 16 slabs.  A token in
+    # every 32-row stretch of every expert against the oracle, then the
+    # same bits on grids of 64 and 8 workgroups, where each workgroup runs
+    # many tiles back to back.
+    sh = synth.LayerShape(f"fp8_pipe_d{d}_i{I}", 11, 3000, d, 8, 4, I, 4, "bf16", 0.05, "zero")
     Lg = H.to_dev(synth.make_layer(sh, "cpu"))
     desc = H.desc_of(sh)
     print(f"[fp8 forward] {sh.name} T={sh.T}", flush=True)
