@@ -424,9 +424,35 @@ __global__ __launch_bounds__(NTHR, 1) void rmw_kernel(RParams p) {
       // ---- epilogue: lane holds column lane%32 of its column block and rows
       // 32 rb + 8 (v/4) + 4 (lane/32) + v%4
       const int rbase = 4 * khalf;
-      if constexpr (F32OUT) {
+      if constexpr (EPI == R_DX) {
         // fp32 results straight from the accumulators: each store covers 32
-        // consecutive columns (128 bytes) of a row
+        // consecutive columns (128 bytes) of a row, through a buffer that
+        // spans exactly the tile's rows (stores past them are dropped, no
+        // branch per row): expert dx 0.86 -> 0.84 ms per training step.
+        const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+            p.Cf + static_cast<int64_t>(m0) * p.ncols, (short)0,
+            static_cast<uint32_t>(mcount) * static_cast<uint32_t>(p.ncols) * 4u, 0x00020000);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int rl = rbase + 32 * rb + 8 * (v >> 2) + (v & 3);
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+              const uint32_t off = static_cast<uint32_t>(
+                  rl * p.ncols + n0 + 64 * wave + 32 * cb + (lane & 31)) * 4u;
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[rb][cb][v]), cr, off, 0, 0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (tid == 0) s_claim[0] = next_n;
+        __syncthreads();  // every wave done reading the ring before the next tile's loads
+        return;
+      } else if constexpr (F32OUT) {
+        // fp32 results straight from the accumulators: each store covers 32
+        // consecutive columns (128 bytes) of a row.  (For dh the form above
+        // with the gate scales staged in LDS measured 0.38 against 0.30 ms.)
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
