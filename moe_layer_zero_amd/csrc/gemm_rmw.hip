@@ -420,18 +420,31 @@ __global__ __launch_bounds__(NTHR, 1) void rmw_kernel(RParams p) {
       __builtin_amdgcn_sched_barrier(0);
       compute((nk - 1) & 3);
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (DENSE) {
+        // the last slab's MFMAs stay here: the compiler otherwise moves them
+        // into the epilogue and keeps their operands in scratch
+#pragma unroll
+        for (int i = 0; i < NRB; ++i) asm volatile("" ::"a"(acc[i][0]), "a"(acc[i][1]));
+      }
 
       // ---- epilogue: lane holds column lane%32 of its column block and rows
       // 32 rb + 8 (v/4) + 4 (lane/32) + v%4
       const int rbase = 4 * khalf;
-      if constexpr (EPI == R_DX) {
+      if constexpr (EPI == R_DX || DENSE) {
         // fp32 results straight from the accumulators: each store covers 32
         // consecutive columns (128 bytes) of a row, through a buffer that
         // spans exactly the tile's rows (stores past them are dropped, no
-        // branch per row): expert dx 0.86 -> 0.84 ms per training step.
+        // branch per row): expert dx 0.83 -> 0.81 ms per training step.
         const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
             p.Cf + static_cast<int64_t>(m0) * p.ncols, (short)0,
             static_cast<uint32_t>(mcount) * static_cast<uint32_t>(p.ncols) * 4u, 0x00020000);
+        // (router: the row pitch made opaque here, otherwise the compiler
+        // computes every store's offset once, before the tile loop, and keeps
+        // the 256 of them in scratch: router scores 0.274 -> 0.252 ms at
+        // prefill; the expert dx kernel does not spill and is faster without)
+        int pitch = p.ncols;
+        if constexpr (DENSE) asm volatile("" : "+s"(pitch));
+        const int cbase = n0 + 64 * wave + (lane & 31);
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
@@ -439,14 +452,20 @@ __global__ __launch_bounds__(NTHR, 1) void rmw_kernel(RParams p) {
             const int rl = rbase + 32 * rb + 8 * (v >> 2) + (v & 3);
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
-              const uint32_t off = static_cast<uint32_t>(
-                  rl * p.ncols + n0 + 64 * wave + 32 * cb + (lane & 31)) * 4u;
+              // (expert dx: written as below it measured 1% faster than
+              // with the router's form)
+              const uint32_t off =
+                  DENSE ? static_cast<uint32_t>(rl * pitch + cbase + 32 * cb) * 4u
+                        : static_cast<uint32_t>(rl * p.ncols + n0 + 64 * wave + 32 * cb +
+                                                (lane & 31)) * 4u;
               __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[rb][cb][v]), cr, off, 0, 0);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (tid == 0) s_claim[0] = next_n;
+        if constexpr (!DENSE) {
+          if (tid == 0) s_claim[0] = next_n;
+        }
         __syncthreads();  // every wave done reading the ring before the next tile's loads
         return;
       } else if constexpr (F32OUT) {
