@@ -15,6 +15,7 @@ namespace zc {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kCombineMaxThreads = 1024;
 constexpr int kMaxK = 32;
 
 // 16-byte vector of the layer dtype, widened to fp32.
@@ -89,8 +90,12 @@ __device__ __forceinline__ float load_picks(const int32_t* topk_idx, const float
   return *s_c;
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void combine_kernel(
+// G: picks whose row loads are issued together (4, 8, 12 or 16; the
+// smallest covering K, so a token's rows are in flight at once).  The
+// workgroup has one thread per 16-byte piece of a row (at most 1024), so
+// at the usual widths a token's loads all go out in one pass.
+template <typename T, int G>
+__global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
     const T* __restrict__ x, const T* __restrict__ y, const int32_t* __restrict__ topk_idx,
     const float* __restrict__ gate, const int32_t* __restrict__ inv, int d, int N, int K,
     float out_scale, T* __restrict__ out) {
@@ -100,24 +105,24 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   const int64_t t = blockIdx.x;
   const float c = load_picks(topk_idx, gate, inv, t, N, K, s_g, s_inv, &s_c);
   constexpr int V = V16<T>::n;
-  for (int j = threadIdx.x * V; j < d; j += kThreads * V) {
+  for (int j = threadIdx.x * V; j < d; j += blockDim.x * V) {
     float acc[V], v[V];
     V16<T>::load(x + t * d + j, v);
 #pragma unroll
     for (int e = 0; e < V; ++e) acc[e] = c * v[e];
-    // picks in groups of four: the group's row loads are issued together,
+    // picks in groups of G: the group's row loads are issued together,
     // then added in slot order
-    for (int r0 = 0; r0 < K; r0 += 4) {
+    for (int r0 = 0; r0 < K; r0 += G) {
       // (a slot past K or of a zero-computation pick loads the token's own
       // x piece, just read, and is skipped below)
-      typename V16<T>::raw_t w[4];
+      typename V16<T>::raw_t w[G];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < G; ++u) {
         const int q = r0 + u < K ? s_inv[r0 + u] : -1;
         w[u] = V16<T>::ld_raw(q >= 0 ? y + static_cast<int64_t>(q) * d + j : x + t * d + j);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < G; ++u) {
         if (r0 + u >= K || s_inv[r0 + u] < 0) continue;
         const float g = s_g[r0 + u];
         V16<T>::unpack(w[u], v);
@@ -294,8 +299,16 @@ hipError_t launch_combine(const T* x, const T* y, const int32_t* topk_idx, const
                           const int32_t* inv, int Tn, int d, int N, int K, float out_scale, T* out,
                           hipStream_t s) {
   if (Tn == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel<T>, dim3(Tn), dim3(kThreads), 0, s, x, y, topk_idx, gate, inv,
-                     d, N, K, out_scale, out);
+  const int pieces = (d + V16<T>::n - 1) / V16<T>::n;
+  const int threads = pieces < 64 ? 64 : (pieces > kCombineMaxThreads ? kCombineMaxThreads : (pieces + 63) / 64 * 64);
+#define ZC_COMBINE(G)                                                                      \
+  hipLaunchKernelGGL((combine_kernel<T, G>), dim3(Tn), dim3(threads), 0, s, x, y, topk_idx, \
+                     gate, inv, d, N, K, out_scale, out)
+  if (K <= 4) ZC_COMBINE(4);
+  else if (K <= 8) ZC_COMBINE(8);
+  else if (K <= 12) ZC_COMBINE(12);
+  else ZC_COMBINE(16);
+#undef ZC_COMBINE
   return hipGetLastError();
 }
 

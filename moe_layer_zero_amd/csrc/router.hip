@@ -65,6 +65,11 @@ __device__ __forceinline__ bool ahead(double ka, int ja, double kb, int jb) {
   return ka > kb || (ka == kb && ja < jb);
 }
 
+// The same without short-circuit evaluation (no branches in the selection).
+__device__ __forceinline__ bool ahead_nb(double ka, int ja, double kb, int jb) {
+  return static_cast<bool>(static_cast<int>(ka > kb) | (static_cast<int>(ka == kb) & static_cast<int>(ja < jb)));
+}
+
 constexpr int kWavesPerBlock = 4;
 
 // The routing exponentials of one token for one wavefront: lane L holds
@@ -95,7 +100,50 @@ __device__ __forceinline__ void token_exps(const float* __restrict__ l, int E, i
   S = part;
 }
 
+// One step of a wave-wide arg-max over (key, index) pairs: lane L compares
+// its pair with the pair of the lane that the DPP control CTRL routes to it
+// and keeps the one ahead.  The winner of a set of pairs is the same in
+// whatever order they are compared (the "ahead" order is total), so the
+// reduction can take the cheapest lane routes: in-row DPP moves, no LDS.
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(double& bk, int& bj) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, bk);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u), CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, 0xF, 0xF, false);
+  const int oj = __builtin_amdgcn_update_dpp(0, bj, CTRL, 0xF, 0xF, false);
+  const double ok = __builtin_bit_cast(double, static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
+  const bool take = ahead_nb(ok, oj, bk, bj);
+  bk = take ? ok : bk;
+  bj = take ? oj : bj;
+}
+
+// The same across the two 16-lane rows of each 32-lane half (swizzle, lane
+// xor 16).
+__device__ __forceinline__ void argmax_xor16(double& bk, int& bj) {
+  constexpr int kPat = 0x1F | (0x10 << 10);  // bit mode: and 0x1F, or 0, xor 0x10
+  const uint64_t u = __builtin_bit_cast(uint64_t, bk);
+  const uint32_t lo = __builtin_amdgcn_ds_swizzle(static_cast<int>(u), kPat);
+  const uint32_t hi = __builtin_amdgcn_ds_swizzle(static_cast<int>(u >> 32), kPat);
+  const int oj = __builtin_amdgcn_ds_swizzle(bj, kPat);
+  const double ok = __builtin_bit_cast(double, static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
+  const bool take = ahead_nb(ok, oj, bk, bj);
+  bk = take ? ok : bk;
+  bj = take ? oj : bj;
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(u), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(u >> 32), l);
+  return __builtin_bit_cast(double, static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
+}
+
 // One wavefront per token; NPER = register slots per lane (E <= 64*NPER).
+// Each of the K rounds finds the untaken expert whose key is ahead of all
+// others (larger key, then lower index): a lane's best over its slots, then
+// the wave's best by DPP moves inside 16-lane rows (quad xor 1, quad xor 2,
+// half-row mirror, row mirror), a swizzle across rows and the two halves
+// read as scalars; the winner's e_j is then read from its lane.
 template <int NPER>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int Tn, int E, int K,
@@ -115,33 +163,41 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void topk_kernel(
     if (kv[i] != kv[i]) kv[i] = -INFINITY;
   }
 
-  uint32_t taken = 0;
+  uint32_t taken = 0;  // slots of this lane already picked (or past E)
+#pragma unroll
+  for (int i = 0; i < NPER; ++i)
+    if (lane + 64 * i >= E) taken |= 1u << i;
   int my_j = 0;
   double my_e = 0.0, den = 0.0;
   for (int r = 0; r < K; ++r) {
-    double bk = -INFINITY, be = 0.0;
+    // this lane's best untaken slot, with its e_j
+    double bk = -INFINITY, be_l = 0.0;
     int bj = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
       const int j = lane + 64 * i;
-      if (j < E && !((taken >> i) & 1u) && ahead(kv[i], j, bk, bj)) {
-        bk = kv[i];
-        bj = j;
-        be = ev[i];
-      }
+      const bool take = static_cast<bool>(static_cast<int>(((taken >> i) & 1u) == 0u) &
+                                          static_cast<int>(ahead_nb(kv[i], j, bk, bj)));
+      bk = take ? kv[i] : bk;
+      bj = take ? j : bj;
+      be_l = take ? ev[i] : be_l;
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const double ok = __shfl_xor(bk, o);
-      const int oj = __shfl_xor(bj, o);
-      const double oe = __shfl_xor(be, o);
-      if (ahead(ok, oj, bk, bj)) {
-        bk = ok;
-        bj = oj;
-        be = oe;
-      }
+    argmax_dpp<0xB1>(bk, bj);   // quad_perm [1,0,3,2]: lane xor 1
+    argmax_dpp<0x4E>(bk, bj);   // quad_perm [2,3,0,1]: lane xor 2
+    argmax_dpp<0x141>(bk, bj);  // row_half_mirror: lane i <-> 7 - i in each 8
+    argmax_dpp<0x140>(bk, bj);  // row_mirror: lane i <-> 15 - i in each 16
+    argmax_xor16(bk, bj);
+    {
+      const double k0 = readlane_f64(bk, 0), k1 = readlane_f64(bk, 32);
+      const int j0 = __builtin_amdgcn_readlane(bj, 0), j1 = __builtin_amdgcn_readlane(bj, 32);
+      const bool second = ahead_nb(k1, j1, k0, j0);
+      bj = second ? j1 : j0;
     }
-    if ((bj & 63) == lane) taken |= 1u << (bj >> 6);
+    // bj is wave-uniform and below E (at most E picks are made, K <= E); the
+    // lane holding it has it as its own best, with its e_j
+    const int ws = bj >> 6, wl = bj & 63;
+    const double be = readlane_f64(be_l, wl);
+    if (wl == lane) taken |= 1u << ws;
     den = den + be;
     if (lane == r) {
       my_j = bj;

@@ -307,6 +307,20 @@ def test_forward_packed_four_slab_down_tiles_on_any_grid():
         assert torch.equal(out, b)
 
 
+def test_forward_packed_twelve_slab_gate_up_tiles_on_any_grid():
+    # d = 768: the 256-row gate/up tiles have twelve 64-step slabs (a short
+    # reduction next to the prefill's 96); grids of 8 and 64 workgroups make
+    # each workgroup claim many tiles back to back, across the XCDs' counters.
+    # Every token against the oracle, then the same bits on the smaller grids.
+    import dataclasses
+    sh = synth.LayerShape("gateup_k768", 11, 4096, 768, 8, 4, 256, 4, "bf16", 0.02, "zero")
+    L, Lg, desc, route, out, o = forward_case(sh, packed=True)
+    for lim in (64, 8):
+        print(f"[forward] {sh.name} packed, cu_limit={lim}", flush=True)
+        _, b, _ = H.run_forward(dataclasses.replace(desc, cu_limit=lim), Lg, packed=True)
+        assert torch.equal(out, b)
+
+
 def test_forward_packed_is_deterministic():
     sh = CF["small_bf16"]
     Lg = H.to_dev(synth.make_layer(sh, "cpu"))
