@@ -292,6 +292,13 @@ __global__ __launch_bounds__(kThreads) void dx_gather_kernel(
   }
 }
 
+// Workgroup size of the combine: one thread per V-element piece of a row of
+// d, a multiple of 64 between 64 and kCombineMaxThreads.
+int combine_threads(int d, int V) {
+  const int pieces = (d + V - 1) / V;
+  return pieces < 64 ? 64 : (pieces > kCombineMaxThreads ? kCombineMaxThreads : (pieces + 63) / 64 * 64);
+}
+
 }  // namespace
 
 template <typename T>
@@ -299,8 +306,7 @@ hipError_t launch_combine(const T* x, const T* y, const int32_t* topk_idx, const
                           const int32_t* inv, int Tn, int d, int N, int K, float out_scale, T* out,
                           hipStream_t s) {
   if (Tn == 0) return hipSuccess;
-  const int pieces = (d + V16<T>::n - 1) / V16<T>::n;
-  const int threads = pieces < 64 ? 64 : (pieces > kCombineMaxThreads ? kCombineMaxThreads : (pieces + 63) / 64 * 64);
+  const int threads = combine_threads(d, V16<T>::n);
 #define ZC_COMBINE(G)                                                                      \
   hipLaunchKernelGGL((combine_kernel<T, G>), dim3(Tn), dim3(threads), 0, s, x, y, topk_idx, \
                      gate, inv, d, N, K, out_scale, out)
