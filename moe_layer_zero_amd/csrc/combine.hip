@@ -26,6 +26,10 @@ template <> struct V16<bf16_t> {
   static __device__ __forceinline__ raw_t ld_raw(const bf16_t* p) {
     return *reinterpret_cast<const u32x4_t*>(p);
   }
+  // for data read exactly once (the expert output rows)
+  static __device__ __forceinline__ raw_t ld_raw_once(const bf16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  }
   static __device__ __forceinline__ void unpack(const raw_t& v, float* f) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -47,6 +51,9 @@ template <> struct V16<float> {
   typedef f32x4_t raw_t;
   static __device__ __forceinline__ raw_t ld_raw(const float* p) {
     return *reinterpret_cast<const f32x4_t*>(p);
+  }
+  static __device__ __forceinline__ raw_t ld_raw_once(const float* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
   }
   static __device__ __forceinline__ void unpack(const raw_t& v, float* f) {
 #pragma unroll
@@ -113,13 +120,14 @@ __global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(
     // picks in groups of G: the group's row loads are issued together,
     // then added in slot order
     for (int r0 = 0; r0 < K; r0 += G) {
-      // (a slot past K or of a zero-computation pick loads the token's own
-      // x piece, just read, and is skipped below)
+      // (a slot past K or of a zero-computation pick loads nothing and is
+      // skipped below; each y row is read by its one token only, so its
+      // loads carry the non-temporal hint)
       typename V16<T>::raw_t w[G];
 #pragma unroll
       for (int u = 0; u < G; ++u) {
         const int q = r0 + u < K ? s_inv[r0 + u] : -1;
-        w[u] = V16<T>::ld_raw(q >= 0 ? y + static_cast<int64_t>(q) * d + j : x + t * d + j);
+        w[u] = q >= 0 ? V16<T>::ld_raw_once(y + static_cast<int64_t>(q) * d + j) : typename V16<T>::raw_t{};
       }
 #pragma unroll
       for (int u = 0; u < G; ++u) {
