@@ -41,6 +41,10 @@ ROUTE_CASES = [
     ("no_ffn", 200, 0, 16, 4, "uniform", 0.5, 1),
     ("no_identity", 500, 96, 0, 6, "uniform", 0.5, 0),
     ("ties", 128, 24, 8, 5, "ties", 0.5, 1),
+    # eight slots per lane with a partial last one, ties in bias and scores
+    ("e400_ties", 700, 300, 100, 10, "ties", 0.5, 1),
+    # every expert picked: the last rounds find one free slot in the wave
+    ("k_eq_e32", 64, 20, 12, 32, "ties", 1.0, 0),
 ]
 
 
