@@ -60,12 +60,8 @@ __device__ __forceinline__ double key_exp(double z) {
   return __builtin_ldexp(p, static_cast<int>(k));
 }
 
-// Is candidate (ka, ja) ahead of (kb, jb)?  Larger key first, then lower index.
-__device__ __forceinline__ bool ahead(double ka, int ja, double kb, int jb) {
-  return ka > kb || (ka == kb && ja < jb);
-}
-
-// The same without short-circuit evaluation (no branches in the selection).
+// Is candidate (ka, ja) ahead of (kb, jb)?  Larger key first, then lower
+// index; evaluated without short-circuit branches.
 __device__ __forceinline__ bool ahead_nb(double ka, int ja, double kb, int jb) {
   return static_cast<bool>(static_cast<int>(ka > kb) | (static_cast<int>(ka == kb) & static_cast<int>(ja < jb)));
 }
@@ -103,7 +99,7 @@ __device__ __forceinline__ void token_exps(const float* __restrict__ l, int E, i
 // One step of a wave-wide arg-max over (key, index) pairs: lane L compares
 // its pair with the pair of the lane that the DPP control CTRL routes to it
 // and keeps the one ahead.  The winner of a set of pairs is the same in
-// whatever order they are compared (the "ahead" order is total), so the
+// whatever order they are compared (the order of ahead_nb is total), so the
 // reduction can take the cheapest lane routes: in-row DPP moves, no LDS.
 template <int CTRL>
 __device__ __forceinline__ void argmax_dpp(double& bk, int& bj) {
