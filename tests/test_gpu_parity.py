@@ -183,6 +183,15 @@ def test_forward_single_expert_mlp():
     forward_case(sh)
 
 
+def test_forward_more_than_sixteen_picks():
+    # K = 20: the combine issues its picks' row loads in a group of 16, then
+    # a group with 4 picks and 12 empty slots (bf16 row-major and packed, fp32)
+    sh = synth.LayerShape("k20", 13, 300, 256, 24, 8, 256, 20, "bf16", 0.02, "uniform")
+    forward_case(sh)
+    forward_case(sh, packed=True)
+    forward_case(synth.LayerShape("k20_f32", 14, 200, 128, 24, 8, 64, 20, "f32", 0.05, "uniform"))
+
+
 def test_forward_dense_mixture_k_equals_e():
     sh = synth.LayerShape("dense", 9, 130, 128, 6, 2, 64, 8, "f32", 0.05, "uniform")
     forward_case(sh)
